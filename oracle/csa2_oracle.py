@@ -1,0 +1,387 @@
+"""CPU oracle for the CSA2 decode/prefill hot path with an FP4 (E2M1 + E4M3/16) main KV cache.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path (the HIP library, its C-ABI, the Python
+binding) imports, calls or links this module. Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may use it.
+
+It is a plain, slow, obviously-correct restatement of what the method computes, in numpy fp64.
+Each function names the passage it follows. The sources are web pages about DeepSeek-V4.1-Flash:
+
+  [walkthrough]  "【论文解读】 DeepSeek-V4.1-Flash" (wkq9411.github.io, a walkthrough of the
+                 V4.1 tech report). Sections used:
+                   一(四) "Compressed Sparse Attention 2 (CSA2)" - the lightweight indexer,
+                          Top-K per query, attention over the selected entries;
+                   一(四)1 "Cross-Layer KV 和 Index Reuse" - Full / Reindex / Reuse modes;
+                   一(四)2 "Hierarchical Sparse Indexer" - block max, block selection, pool;
+                   一(五)4 "FP4 Main KV Cache" - E2M1 values, one E4M3 scale per 16 channels,
+                          no global scale, 448 x 6 = 2688, dequantize before attention;
+                   三(二)1 "模型设置" - 512 selected entries, 64 query heads of dim 512,
+                          2048 blocks x 8 positions.
+  [release note] ModelScope release note, section "压缩稀疏注意力 2（CSA2）" - the same modes,
+                 HSI and FP4 format in summary.
+
+Where the pages leave a step open the reading taken is stated at the function (R-n tags match
+the list of readings kept with the design notes of this repository).
+
+Parity status: every public function here is pinned by CPU tests against closed forms, library
+routines (torch float8_e4m3fn decode / rounding, torch scaled_dot_product_attention, full sorts),
+brute force on tiny inputs, hand-built ties, and the structural invariants the pages state.
+No function is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+# ---------------------------------------------------------------------------------------------
+# Format constants. [walkthrough] 一(五)4: E2M1 values, one E4M3 scale for every 16 channels.
+# ---------------------------------------------------------------------------------------------
+GROUP = 16            # channels per E4M3 scale
+D_LATENT = 512        # channels of one compressed KV entry (the attention head dim)
+
+
+def row_bytes(dim: int = D_LATENT) -> int:
+    """Bytes of one packed entry: 4 bits per channel plus one byte per 16-channel group.
+
+    For the 512-channel latent this is 256 + 32 = 288 bytes.
+    """
+    return dim // 2 + dim // GROUP
+
+
+# ---------------------------------------------------------------------------------------------
+# O1 / O2: decoding the two 4- and 8-bit formats from their bit fields.
+# ---------------------------------------------------------------------------------------------
+def e2m1_decode(codes) -> np.ndarray:
+    """O1. Value of E2M1 codes (1 sign, 2 exponent bits with bias 1, 1 mantissa bit).
+
+    [walkthrough] 一(五)4 names E2M1 as the value format. Exponent field 0 is subnormal
+    (0.5 * m); otherwise 2^(e-1) * (1 + m/2). Code 8 is -0.
+    """
+    c = np.asarray(codes).astype(np.int64)
+    s = (c >> 3) & 1
+    e = (c >> 1) & 3
+    m = c & 1
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, (e - 1).astype(np.int64)))
+    return np.where(s == 1, -mag, mag).astype(np.float64)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """O2. Value of OCP E4M3 ("FN") codes: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits.
+
+    [walkthrough] 一(五)4: one E4M3 scale per 16 channels, largest value 448. There is no
+    infinity; exponent 15 with mantissa 7 (0x7F, 0xFF) is NaN. Exponent 0 is subnormal
+    (m * 2^-9).
+    """
+    c = np.asarray(codes).astype(np.int64)
+    s = (c >> 7) & 1
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64)))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(s == 1, -mag, mag).astype(np.float64)
+
+
+# The 8 E2M1 magnitudes in code order, and the 127 finite non-negative E4M3 values in code
+# order (codes 0x00..0x7E); both derived from the decoders above.
+E2M1_MAGS = e2m1_decode(np.arange(8))
+E4M3_POS = e4m3_decode(np.arange(0x7F))
+
+
+# ---------------------------------------------------------------------------------------------
+# O3 / O4: quantizing and packing one entry.
+# ---------------------------------------------------------------------------------------------
+def _nearest_even(table: np.ndarray, target: np.ndarray) -> np.ndarray:
+    """Index of the table value nearest to each target, ties broken to the even index.
+
+    `table` is ascending. Distances are formed in fp64; for the operands used here (values with
+    few significant bits, fp32 targets) the ties are decided exactly.
+    """
+    hi = np.clip(np.searchsorted(table, target, side="left"), 1, len(table) - 1)
+    lo = hi - 1
+    d_lo = np.abs(target - table[lo])
+    d_hi = np.abs(table[hi] - target)
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    idx = np.where(pick_hi, hi, lo)
+    # targets beyond either end of the table saturate to that end
+    idx = np.where(target <= table[0], 0, idx)
+    idx = np.where(target >= table[-1], len(table) - 1, idx)
+    return idx
+
+
+def quantize_groups(x: np.ndarray):
+    """O3. Quantize groups of 16 values to 16 E2M1 codes and one E4M3 scale code each.
+
+    [walkthrough] 一(五)4 fixes the format (E2M1 values, one E4M3 scale per 16 channels, NVFP4
+    without the global scale) but not the rounding. Readings taken (R-1, R-2):
+      * scale = the E4M3 value nearest to amax/6 (round to nearest, ties to the even code,
+        saturating at 448), where amax = max |x| over the group; this is the nearest finite
+        E4M3 value s to amax/6, found by comparing 6*s with amax exactly;
+      * each value's magnitude code is the E2M1 magnitude m_j nearest to |x|/s (ties to even
+        j, saturating at 6), found by comparing s*m_j with |x| exactly;
+      * the sign bit is the sign bit of x (so -0 and negatives that round to 0 give code 8);
+      * a zero scale gives magnitude code 0 for all 16 values.
+    x: [..., 16] float array (fp32 or exact fp64). Returns (codes uint8 [..., 16],
+    scale codes uint8 [...]).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    assert x.shape[-1] == GROUP
+    ax = np.abs(x)
+    amax = ax.max(axis=-1)
+    sc = _nearest_even(6.0 * E4M3_POS, amax)             # exact compare of amax with 6*s
+    s = E4M3_POS[sc]
+    # magnitude codes: nearest of s*m_j to |x|, ties to even j
+    mj = _nearest_even_scaled(ax, s[..., None])
+    mj = np.where(s[..., None] == 0.0, 0, mj)
+    sign = np.signbit(x).astype(np.int64)
+    codes = (sign << 3) | mj
+    return codes.astype(np.uint8), sc.astype(np.uint8)
+
+
+def _nearest_even_scaled(ax: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """argmin_j | ax - s*m_j | over the 8 E2M1 magnitudes m_j, ties to the even j."""
+    cand = s * E2M1_MAGS                                # [..., 8], exact products
+    dist = np.abs(ax[..., None] - cand[..., None, :])    # [..., 16, 8]
+    dmin = dist.min(axis=-1, keepdims=True)
+    is_min = dist == dmin
+    # among the (at most two, adjacent) minimisers prefer the even index
+    even = is_min & (np.arange(8) % 2 == 0)
+    return np.where(even.any(axis=-1), even.argmax(axis=-1), is_min.argmax(axis=-1))
+
+
+def quantize_kv_fp4(src: np.ndarray, chunk_rows: int = 4096) -> np.ndarray:
+    """O3 + O4. Quantize and pack entries [rows, D] (fp32 values) into [rows, D/2 + D/16] bytes.
+
+    Layout (reading R-15; the pages give no byte layout): bytes
+    0 .. D/2-1 hold the codes, channel 2i in the low nibble of byte i and channel 2i+1 in the
+    high nibble; bytes D/2 .. D/2 + D/16 - 1 hold the E4M3 scale codes, group g covering
+    channels 16g .. 16g+15. For D = 512 that is 256 + 32 = 288 bytes.
+    """
+    src = np.asarray(src)
+    rows, d = src.shape
+    assert d % (2 * GROUP) == 0
+    out = np.empty((rows, row_bytes(d)), dtype=np.uint8)
+    for r0 in range(0, rows, chunk_rows):
+        x = src[r0:r0 + chunk_rows].astype(np.float64).reshape(-1, d // GROUP, GROUP)
+        codes, sc = quantize_groups(x)
+        codes = codes.reshape(-1, d).astype(np.uint16)
+        out[r0:r0 + chunk_rows, : d // 2] = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+        out[r0:r0 + chunk_rows, d // 2:] = sc
+    return out
+
+
+def dequant_kv_fp4(rows: np.ndarray, dim: int = D_LATENT) -> np.ndarray:
+    """O5. Unpack and dequantize [n, D/2 + D/16] bytes to fp64 [n, D]: x = E2M1(code) * E4M3(scale).
+
+    [walkthrough] 一(五)4: the cache is dequantized before attention, so attention runs on
+    these values. Every product has at most 6 significant bits and is exact.
+    """
+    rows = np.asarray(rows, dtype=np.uint8)
+    n = rows.shape[0]
+    assert rows.shape[1] == row_bytes(dim)
+    codes = np.empty((n, dim), dtype=np.uint8)
+    codes[:, 0::2] = rows[:, : dim // 2] & 0xF
+    codes[:, 1::2] = rows[:, : dim // 2] >> 4
+    scales = e4m3_decode(rows[:, dim // 2:])             # [n, dim/16]
+    return e2m1_decode(codes) * np.repeat(scales, GROUP, axis=1)
+
+
+# ---------------------------------------------------------------------------------------------
+# O6: the lightweight indexer.
+# ---------------------------------------------------------------------------------------------
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) to exact fp64 values."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def index_scores(q_idx: np.ndarray, k_idx: np.ndarray, n_vis) -> np.ndarray:
+    """O6. Indexer score of every visible entry for each query row, rounded once to fp32.
+
+    [walkthrough] 一(四): indexer Q and indexer K score the main-KV entries, and each query
+    keeps its Top-K. The pages print no score formula; the reading taken (R-4) is
+    s[r, n] = sum_h sum_d q_idx[r, h, d] * k_idx[n, h', d] with h' = h when keys have one head
+    per index head, and h' = 0 when keys have one shared head.
+    q_idx: [R, Hi, Di] exact values (fp64); k_idx: [N, Hk, Di] exact values; n_vis: [R] ints.
+    Returns fp32 [R, N]; columns n >= n_vis[r] are -inf (they are not part of the result).
+    Products of bf16 values are exact in fp64; the sum is fp64; one rounding to fp32 at the end.
+    """
+    q = np.asarray(q_idx, dtype=np.float64)
+    k = np.asarray(k_idx, dtype=np.float64)
+    R, Hi, Di = q.shape
+    N, Hk, _ = k.shape
+    assert Hk in (1, Hi)
+    if Hk == 1:
+        k = np.repeat(k, Hi, axis=1)
+    s = q.reshape(R, Hi * Di) @ k.reshape(N, Hi * Di).T      # [R, N] fp64
+    out = s.astype(np.float32)
+    n_vis = np.broadcast_to(np.asarray(n_vis), (R,))
+    out[np.arange(N)[None, :] >= n_vis[:, None]] = -np.inf
+    return out
+
+
+def prefill_n_vis(p0: int, T: int, ratio: int) -> np.ndarray:
+    """Causal visibility for query tokens at absolute positions p0 .. p0+T-1 (reading R-6).
+
+    A compressed entry covering source tokens [m*j, m*j + m) is visible once its last source
+    token is at or before the query position, so n_vis(p) = floor((p + 1) / m).
+    """
+    p = np.arange(p0, p0 + T, dtype=np.int64)
+    return ((p + 1) // ratio).astype(np.int64)
+
+
+# ---------------------------------------------------------------------------------------------
+# O7: Top-K.
+# ---------------------------------------------------------------------------------------------
+def topk(scores: np.ndarray, k: int, n_valid=None, col_to_pos=None) -> np.ndarray:
+    """O7. The k best columns of each row, as positions in ascending order, -1 padded.
+
+    [walkthrough] 一(四): each query selects its Top-K entries. Order used to choose (R-7):
+    score descending, then position ascending. Only the first n_valid[r] columns take part; with
+    col_to_pos, column c stands for position col_to_pos[r, c] and columns whose position is < 0
+    do not take part. The chosen positions are returned sorted ascending and padded with -1 to k
+    (R-8). Scores are compared in fp32 (the precision the scores are delivered in).
+    """
+    scores = np.asarray(scores, dtype=np.float32)
+    R, n = scores.shape
+    if n_valid is None:
+        n_valid = np.full(R, n)
+    n_valid = np.broadcast_to(np.asarray(n_valid), (R,))
+    out = np.full((R, k), -1, dtype=np.int64)
+    for r in range(R):
+        cols = np.arange(min(int(n_valid[r]), n))
+        pos = cols if col_to_pos is None else np.asarray(col_to_pos[r])[cols].astype(np.int64)
+        keep = pos >= 0
+        cols, pos = cols[keep], pos[keep]
+        s = scores[r, cols]
+        order = np.lexsort((pos, -s))                    # primary: -score, secondary: position
+        chosen = np.sort(pos[order[:k]])
+        out[r, : len(chosen)] = chosen
+    return out
+
+
+# ---------------------------------------------------------------------------------------------
+# O8 / O9: Hierarchical Sparse Indexer.
+# ---------------------------------------------------------------------------------------------
+def block_max(scores: np.ndarray, n_vis, block: int = 8) -> np.ndarray:
+    """O8, first half. Block score = the largest index score among the visible positions of the
+    block ([walkthrough] 一(四)2: a block's score is the max index score inside it).
+
+    Blocks are aligned runs of `block` positions (R-6). Returns fp32 [R, ceil(N/block)];
+    blocks with no visible position are -inf.
+    """
+    scores = np.asarray(scores, dtype=np.float32)
+    R, N = scores.shape
+    nb = -(-N // block)
+    n_vis = np.broadcast_to(np.asarray(n_vis), (R,))
+    padded = np.full((R, nb * block), -np.inf, dtype=np.float32)
+    padded[:, :N] = scores
+    padded[np.arange(nb * block)[None, :] >= n_vis[:, None]] = -np.inf
+    return padded.reshape(R, nb, block).max(axis=2)
+
+
+def hier_pool(bmax: np.ndarray, n_vis, n_sel_blocks: int, block: int = 8) -> np.ndarray:
+    """O8, second half. Choose the n_sel_blocks best blocks and gather their positions.
+
+    [walkthrough] 一(四)2: the highest-scoring blocks are selected and the positions they cover
+    form the candidate pool (2048 blocks x 8 positions = 16384 in the model). Block ties break by
+    block index (R-7). The pool lists the visible positions of the chosen blocks in ascending
+    order and is padded with -1 to n_sel_blocks * block.
+    """
+    bmax = np.asarray(bmax, dtype=np.float32)
+    R, nb = bmax.shape
+    n_vis = np.broadcast_to(np.asarray(n_vis), (R,))
+    n_valid_blocks = -(-n_vis // block)
+    chosen = topk(bmax, n_sel_blocks, n_valid=n_valid_blocks)   # ascending block ids, -1 pad
+    pool = np.full((R, n_sel_blocks * block), -1, dtype=np.int64)
+    for r in range(R):
+        blocks = chosen[r][chosen[r] >= 0]
+        pos = (blocks[:, None] * block + np.arange(block)[None, :]).reshape(-1)
+        pos = pos[pos < n_vis[r]]
+        pool[r, : len(pos)] = pos
+    return pool
+
+
+def pool_scores(q_idx: np.ndarray, k_idx: np.ndarray, pool: np.ndarray) -> np.ndarray:
+    """O9. Indexer scores evaluated only at the candidate positions of each query row.
+
+    [walkthrough] 一(四)2: later Reindex layers score only the candidate positions of the
+    query. Returns fp32 [R, P]; slots holding -1 are -inf.
+    """
+    q = np.asarray(q_idx, dtype=np.float64)
+    R, P = pool.shape
+    out = np.full((R, P), -np.inf, dtype=np.float32)
+    for r in range(R):
+        valid = pool[r] >= 0
+        s = index_scores(q[r:r + 1], np.asarray(k_idx)[pool[r][valid]], [int(valid.sum())])
+        out[r, valid] = s[0]
+    return out
+
+
+# ---------------------------------------------------------------------------------------------
+# O10: sparse attention over the selected entries.
+# ---------------------------------------------------------------------------------------------
+def sparse_attn(q: np.ndarray, kv: np.ndarray, idx: np.ndarray, sm_scale: float):
+    """O10. Softmax attention of each query head over its selected entries.
+
+    [walkthrough] 一(四): each query attends to its selected main-KV entries; one latent per
+    entry serves as key and value (MQA, reading R-5); 一(五)4: entries are dequantized first.
+    q: [R, H, D] exact values; kv: [N, D] dequantized fp64 entries; idx: [R, K] positions,
+    -1 = no entry. For each (r, h): l_j = sm_scale * q[r,h].kv[j] over selected j,
+    o = sum_j softmax(l)_j kv[j], lse = log(sum_j exp(l_j)). No selected entry: o = 0, lse = -inf.
+    Returns (out fp32 [R, H, D], lse fp32 [R, H]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kv = np.asarray(kv, dtype=np.float64)
+    R, H, D = q.shape
+    out = np.zeros((R, H, D), dtype=np.float64)
+    lse = np.full((R, H), -np.inf, dtype=np.float64)
+    for r in range(R):
+        sel = idx[r][idx[r] >= 0]
+        if len(sel) == 0:
+            continue
+        x = kv[sel]                                      # [S, D]
+        logits = sm_scale * (q[r] @ x.T)                 # [H, S]
+        mx = logits.max(axis=1, keepdims=True)
+        w = np.exp(logits - mx)
+        den = w.sum(axis=1, keepdims=True)
+        out[r] = (w @ x) / den
+        lse[r] = mx[:, 0] + np.log(den[:, 0])
+    return out.astype(np.float32), lse.astype(np.float32)
+
+
+# ---------------------------------------------------------------------------------------------
+# O11: one CSA2 layer step for one sequence.
+# ---------------------------------------------------------------------------------------------
+FULL, REINDEX, REUSE = 0, 1, 2
+
+
+def layer_step(mode: int, *, q, kv_deq, k_idx=None, q_idx=None, n_vis=None, k=None,
+               shared_topk=None, pool=None, pool_blocks: int = 0, block: int = 8,
+               sm_scale: float = 1.0 / np.sqrt(512.0)):
+    """O11. One layer of one sequence in the given static mode.
+
+    [walkthrough] 一(四)1: every layer computes its own query; Full scores all visible entries
+    with its own indexer query and produces new Top-K; Reindex re-scores the shared keys with
+    its own indexer query and produces new Top-K; Reuse attends with the newest Top-K of the
+    latest index-producing layer and computes no indexer query and no score. 一(四)2: with the
+    hierarchical indexer the Full layer also builds the candidate pool (pool_blocks > 0) and a
+    Reindex layer given a pool scores only the pool (reading R-9: the Full layer itself attends
+    over its flat Top-K).
+    Returns dict(out, lse, topk, pool, scores).
+    """
+    res = {"pool": pool, "scores": None}
+    if mode == REUSE:
+        sel = shared_topk
+    elif mode == FULL or pool is None:
+        s = index_scores(q_idx, k_idx, n_vis)
+        sel = topk(s, k, n_valid=n_vis)
+        res["scores"] = s
+        if mode == FULL and pool_blocks > 0:
+            res["pool"] = hier_pool(block_max(s, n_vis, block), n_vis, pool_blocks, block)
+    else:  # REINDEX on the candidate pool
+        s = pool_scores(q_idx, k_idx, pool)
+        sel = topk(s, k, col_to_pos=pool)
+        res["scores"] = s
+    out, lse = sparse_attn(q, kv_deq, sel, sm_scale)
+    res.update(out=out, lse=lse, topk=sel)
+    return res
