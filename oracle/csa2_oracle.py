@@ -138,14 +138,17 @@ def quantize_groups(x: np.ndarray):
 
 
 def _nearest_even_scaled(ax: np.ndarray, s: np.ndarray) -> np.ndarray:
-    """argmin_j | ax - s*m_j | over the 8 E2M1 magnitudes m_j, ties to the even j."""
+    """argmin_j | ax - s*m_j | over the 8 E2M1 magnitudes m_j, ties to the even j; values at or
+    beyond the largest magnitude 6*s saturate to j = 7 (for |x| far above 6*s the fp64 distances
+    would all round to the same number, so saturation is decided by a direct compare)."""
     cand = s * E2M1_MAGS                                # [..., 8], exact products
     dist = np.abs(ax[..., None] - cand[..., None, :])    # [..., 16, 8]
     dmin = dist.min(axis=-1, keepdims=True)
     is_min = dist == dmin
     # among the (at most two, adjacent) minimisers prefer the even index
     even = is_min & (np.arange(8) % 2 == 0)
-    return np.where(even.any(axis=-1), even.argmax(axis=-1), is_min.argmax(axis=-1))
+    j = np.where(even.any(axis=-1), even.argmax(axis=-1), is_min.argmax(axis=-1))
+    return np.where(ax >= 6.0 * s, 7, j)
 
 
 def quantize_kv_fp4(src: np.ndarray, chunk_rows: int = 4096) -> np.ndarray:

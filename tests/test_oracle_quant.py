@@ -110,6 +110,21 @@ def test_saturation_and_zero_groups():
     x = np.array([[1e4] + [0.0] * 15], dtype=np.float32)
     codes, sc = O.quantize_groups(x)
     assert sc[0] == 0x7E and codes[0, 0] == 7
+    # far beyond the range (up to the largest fp32): every value saturates to +-6 at scale 448
+    for big in (1e30, -1e30, 3.4028235e38):
+        x = np.full((1, 16), big, dtype=np.float32)
+        x[0, 3] = -x[0, 3]
+        codes, sc = O.quantize_groups(x)
+        assert sc[0] == 0x7E
+        want = np.where(np.signbit(x[0]), 15, 7)
+        assert np.array_equal(codes[0], want), (big, codes)
+        bc, bsc = _quantize_group_bruteforce(x[0])
+        assert bsc == 0x7E and bc == want.tolist()
+    # a huge value next to a small one: the small one is measured against scale 448
+    x = np.zeros((1, 16), np.float32)
+    x[0, 0], x[0, 1], x[0, 2] = 1e30, 100.0, 1000.0
+    codes, _ = O.quantize_groups(x)
+    assert codes[0, :3].tolist() == [7, 0, 4]             # 100/448 -> 0, 1000/448 ~ 2.23 -> 2
     z = np.zeros((1, 16), dtype=np.float32)
     codes, sc = O.quantize_groups(z)
     assert sc[0] == 0 and np.all(codes == 0)
