@@ -1,0 +1,276 @@
+"""Python binding of the CSA2 C ABI: the same six calls, over torch device tensors.
+
+This layer only marshals arguments (shapes, dtypes, pointers, the current HIP stream) and sizes
+scratch buffers through torch's allocator; every step of the computation runs in the HIP kernels
+of libcsa2.so. See include/csa2.h for the exact semantics of each call.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass, field
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import LayerArgs, SharedIdx, SharedKV, check
+
+FULL, REINDEX, REUSE = 0, 1, 2
+F32, BF16 = 0, 1
+D_LATENT = 512
+
+
+def row_bytes(dim: int = D_LATENT) -> int:
+    return dim // 2 + dim // 16
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, dev=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+def _ws(nbytes: int, dev, ws: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return ws
+    if ws is not None and ws.numel() * ws.element_size() >= nbytes:
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+
+# ---------------------------------------------------------------------------------------------
+def quantize_kv_fp4(src: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """[..., dim] fp32/bf16 -> [..., dim/2 + dim/16] uint8 FP4 entries (E2M1 + E4M3 per 16)."""
+    if src.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("src must be float32 or bfloat16")
+    _need(src, "src", None)
+    dim = src.shape[-1]
+    n_rows = src.numel() // dim if dim else 0
+    if out is None:
+        out = torch.empty(*src.shape[:-1], row_bytes(dim), dtype=torch.uint8, device=src.device)
+    _need(out, "out", torch.uint8, src.device)
+    if out.numel() != n_rows * row_bytes(dim):
+        raise ValueError("out has the wrong size")
+    code = _lib.lib().csa2_quantize_kv_fp4(_ptr(src), BF16 if src.dtype == torch.bfloat16 else F32,
+                                           n_rows, dim, _ptr(out), _stream(src.device))
+    check("csa2_quantize_kv_fp4", code)
+    return out
+
+
+def dequant_kv_fp4(rows: torch.Tensor, dim: int = D_LATENT) -> torch.Tensor:
+    """[..., dim/2 + dim/16] uint8 -> [..., dim] fp32 (exact)."""
+    _need(rows, "rows", torch.uint8)
+    if rows.shape[-1] != row_bytes(dim):
+        raise ValueError("last dim of rows must be dim/2 + dim/16")
+    n_rows = rows.numel() // row_bytes(dim)
+    out = torch.empty(*rows.shape[:-1], dim, dtype=torch.float32, device=rows.device)
+    check("csa2_dequant_kv_fp4",
+          _lib.lib().csa2_dequant_kv_fp4(_ptr(rows), n_rows, dim, _ptr(out), _stream(rows.device)))
+    return out
+
+
+def index_scores(q_idx: torch.Tensor, k_idx: torch.Tensor, n_vis: Optional[torch.Tensor] = None,
+                 cand: Optional[torch.Tensor] = None, block_max: bool = False,
+                 out: Optional[torch.Tensor] = None):
+    """Indexer scores. q_idx [B, T, Hi, Di] bf16, k_idx [B, N, Hk, Di] bf16.
+
+    Flat: returns scores [B*T, N] fp32 (entries >= n_vis unwritten) and, with block_max=True,
+    the 8-entry block maxima [B*T, ceil(N/8)]. Pool (cand [B*T, P] int32): scores [B*T, P].
+    """
+    _need(q_idx, "q_idx", torch.bfloat16)
+    _need(k_idx, "k_idx", torch.bfloat16, q_idx.device)
+    B, T, Hi, Di = q_idx.shape
+    B2, N, Hk, Di2 = k_idx.shape
+    if B2 != B or Di2 != Di:
+        raise ValueError("q_idx and k_idx disagree on B or Di")
+    dev = q_idx.device
+    if n_vis is not None:
+        _need(n_vis, "n_vis", torch.int32, dev)
+        if n_vis.numel() != B * T:
+            raise ValueError("n_vis must have B*T entries")
+    P = 0
+    if cand is not None:
+        _need(cand, "cand", torch.int32, dev)
+        P = cand.shape[-1]
+        if cand.numel() != B * T * P:
+            raise ValueError("cand must be [B*T, P]")
+    ncols = P if cand is not None else N
+    if out is None:
+        out = torch.empty(B * T, ncols, dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, dev)
+    bm = None
+    if block_max:
+        bm = torch.empty(B * T, (N + 7) // 8, dtype=torch.float32, device=dev)
+    code = _lib.lib().csa2_index_scores(_ptr(q_idx), _ptr(k_idx), B, T, Hi, Hk, Di, N, _ptr(n_vis),
+                                        _ptr(cand), P, _ptr(out), _ptr(bm), 8, _stream(dev))
+    check("csa2_index_scores", code)
+    return (out, bm) if block_max else out
+
+
+def topk(scores: torch.Tensor, k: int, n_valid: Optional[torch.Tensor] = None,
+         col_to_pos: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """k best columns per row as ascending positions, -1 padded. scores [rows, n] fp32."""
+    _need(scores, "scores", torch.float32)
+    rows, n = scores.shape
+    dev = scores.device
+    if n_valid is not None:
+        _need(n_valid, "n_valid", torch.int32, dev)
+    if col_to_pos is not None:
+        _need(col_to_pos, "col_to_pos", torch.int32, dev)
+        if col_to_pos.shape != scores.shape:
+            raise ValueError("col_to_pos must have the shape of scores")
+    idx = torch.empty(rows, k, dtype=torch.int32, device=dev)
+    L = _lib.lib()
+    nbytes = L.csa2_topk_workspace_size(rows, max(n, 1), k) if rows and k else 0
+    ws = _ws(nbytes, dev, ws)
+    code = L.csa2_topk(_ptr(scores), rows, n, _ptr(n_valid), _ptr(col_to_pos), k, _ptr(idx), _ptr(ws),
+                       nbytes, _stream(dev))
+    check("csa2_topk", code)
+    return idx
+
+
+def hier_pool(block_max: torch.Tensor, n_sel_blocks: int, n_vis: Optional[torch.Tensor] = None,
+              block: int = 8, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Candidate pool [rows, n_sel_blocks * block]: ascending visible positions of the best blocks."""
+    _need(block_max, "block_max", torch.float32)
+    rows, nb = block_max.shape
+    dev = block_max.device
+    if n_vis is not None:
+        _need(n_vis, "n_vis", torch.int32, dev)
+    pool = torch.empty(rows, n_sel_blocks * block, dtype=torch.int32, device=dev)
+    L = _lib.lib()
+    nbytes = L.csa2_hier_pool_workspace_size(rows, max(nb, 1), n_sel_blocks) if rows and n_sel_blocks else 0
+    ws = _ws(nbytes, dev, ws)
+    code = L.csa2_hier_pool(_ptr(block_max), rows, nb, _ptr(n_vis), block, n_sel_blocks, _ptr(pool), _ptr(ws),
+                            nbytes, _stream(dev))
+    check("csa2_hier_pool", code)
+    return pool
+
+
+def sparse_attn(q: torch.Tensor, rows: torch.Tensor, idx: torch.Tensor, sm_scale: float,
+                with_lse: bool = True, ws: Optional[torch.Tensor] = None):
+    """q [B, T, H, 512] bf16, rows [B, N, 288] uint8, idx [B, T, K] int32 -> out fp32 [B, T, H, 512], lse."""
+    _need(q, "q", torch.bfloat16)
+    dev = q.device
+    _need(rows, "rows", torch.uint8, dev)
+    _need(idx, "idx", torch.int32, dev)
+    B, T, H, D = q.shape
+    N = rows.shape[1]
+    K = idx.shape[-1]
+    if rows.shape[0] != B or rows.shape[2] != row_bytes(D) or idx.shape[:2] != (B, T):
+        raise ValueError("inconsistent shapes for q / rows / idx")
+    out = torch.empty(B, T, H, D, dtype=torch.float32, device=dev)
+    lse = torch.empty(B, T, H, dtype=torch.float32, device=dev) if with_lse else None
+    L = _lib.lib()
+    nbytes = L.csa2_sparse_attn_workspace_size(B, T, H, D, K)
+    ws = _ws(nbytes, dev, ws)
+    code = L.csa2_sparse_attn(_ptr(q), _ptr(rows), N, _ptr(idx), B, T, H, D, K, float(sm_scale), _ptr(out),
+                              _ptr(lse), _ptr(ws), nbytes, _stream(dev))
+    check("csa2_sparse_attn", code)
+    return out, lse
+
+
+def prefill_n_vis(p0: int, T: int, ratio: int, device) -> torch.Tensor:
+    """Visible compressed entries for query tokens at positions p0..p0+T-1: floor((p+1)/ratio)."""
+    p = torch.arange(p0 + 1, p0 + T + 1, dtype=torch.int64)
+    return torch.div(p, ratio, rounding_mode="floor").to(torch.int32).to(device)
+
+
+# ---------------------------------------------------------------------------------------------
+# Layer step with caller-owned shared state
+# ---------------------------------------------------------------------------------------------
+@dataclass
+class KVState:
+    """The cache of the most recent Full layer: FP4 rows and indexer keys (device tensors)."""
+    rows: torch.Tensor                 # [B, N, 288] uint8
+    k_idx: torch.Tensor                # [B, N, Hk, Di] bf16
+    n_vis: Optional[torch.Tensor] = None  # [B*T] int32
+    c: SharedKV = field(default_factory=SharedKV)
+
+    def __post_init__(self):
+        _need(self.rows, "rows", torch.uint8)
+        _need(self.k_idx, "k_idx", torch.bfloat16, self.rows.device)
+        B, N, rb = self.rows.shape
+        _, N2, Hk, Di = self.k_idx.shape
+        if N2 != N:
+            raise ValueError("rows and k_idx disagree on N")
+        self.c.rows, self.c.k_idx, self.c.n_vis = _ptr(self.rows), _ptr(self.k_idx), _ptr(self.n_vis)
+        self.c.B, self.c.n_max, self.c.D, self.c.Hk, self.c.Di = B, N, (rb * 16) // 9, Hk, Di
+        self.c.valid = 0
+
+    @property
+    def valid(self) -> bool:
+        return bool(self.c.valid)
+
+
+@dataclass
+class IdxState:
+    """The newest Top-K (and candidate pool) of the latest index-producing layer."""
+    topk: torch.Tensor                 # [B*T, K] int32
+    pool: Optional[torch.Tensor] = None  # [B*T, P] int32
+    c: SharedIdx = field(default_factory=SharedIdx)
+
+    @staticmethod
+    def empty(rows: int, k: int, device, pool_size: int = 0) -> "IdxState":
+        t = torch.full((rows, k), -1, dtype=torch.int32, device=device)
+        p = torch.full((rows, pool_size), -1, dtype=torch.int32, device=device) if pool_size else None
+        return IdxState(t, p)
+
+    def __post_init__(self):
+        _need(self.topk, "topk", torch.int32)
+        self.c.topk, self.c.K = _ptr(self.topk), self.topk.shape[-1]
+        if self.pool is not None:
+            _need(self.pool, "pool", torch.int32, self.topk.device)
+            self.c.pool, self.c.P = _ptr(self.pool), self.pool.shape[-1]
+        self.c.topk_valid = 0
+        self.c.pool_valid = 0
+
+
+def layer_workspace_size(mode: int, args: LayerArgs, kv: KVState, idx: IdxState) -> int:
+    n = C.c_size_t(0)
+    check("csa2_layer_workspace_size",
+          _lib.lib().csa2_layer_workspace_size(mode, C.byref(args), C.byref(kv.c), C.byref(idx.c), C.byref(n)))
+    return n.value
+
+
+def layer_step(mode: int, q: torch.Tensor, kv: KVState, idx: IdxState, q_idx: Optional[torch.Tensor] = None,
+               sm_scale: Optional[float] = None, use_pool: bool = False, pool_blocks: int = 0, block: int = 8,
+               with_lse: bool = True, ws: Optional[torch.Tensor] = None,
+               out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """One CSA2 layer (FULL / REINDEX / REUSE) over caller-owned shared state; returns (out, lse)."""
+    _need(q, "q", torch.bfloat16, kv.rows.device)
+    dev = q.device
+    B, T, H, D = q.shape
+    a = LayerArgs()
+    a.q = _ptr(q)
+    a.T, a.H = T, H
+    if q_idx is not None:
+        _need(q_idx, "q_idx", torch.bfloat16, dev)
+        a.q_idx, a.Hi = _ptr(q_idx), q_idx.shape[2]
+    a.sm_scale = float(sm_scale if sm_scale is not None else D ** -0.5)
+    a.use_pool, a.pool_blocks, a.block = int(use_pool), pool_blocks, block
+    if out is None:
+        out = torch.empty(B, T, H, D, dtype=torch.float32, device=dev)
+    lse = torch.empty(B, T, H, dtype=torch.float32, device=dev) if with_lse else None
+    a.out, a.lse = _ptr(out), _ptr(lse)
+    nbytes = layer_workspace_size(mode, a, kv, idx)
+    ws = _ws(nbytes, dev, ws)
+    a.ws, a.ws_bytes = _ptr(ws), nbytes
+    code = _lib.lib().csa2_layer_step(mode, C.byref(a), C.byref(kv.c), C.byref(idx.c), _stream(dev))
+    check("csa2_layer_step", code)
+    return out, lse

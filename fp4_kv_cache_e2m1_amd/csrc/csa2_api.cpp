@@ -1,0 +1,254 @@
+// C ABI of the CSA2 hot path: argument and state validation, workspace layout, dispatch to the
+// HIP kernels, and the per-layer mode logic of CSA2 (Full / Reindex / Reuse; DeepSeek-V4.1-Flash
+// walkthrough, wkq9411.github.io, 一(四)1 and 一(四)2). No call allocates, frees or
+// synchronizes; every launch goes to the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "../../include/csa2.h"
+#include "launch.h"
+
+using namespace csa2;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+csa2_status hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_E_HIP; }
+
+bool index_shape_ok(int32_t Hi, int32_t Hk, int32_t Di) {
+  return Hi >= 1 && (Hk == Hi || Hk == 1) && Di > 0 && Di % 8 == 0 && (Hk * Di) % 64 == 0 &&
+         Hi * Di <= 1024 && (Hk == 1 ? Di <= 1024 : true);
+}
+
+bool attn_shape_ok(int32_t H, int32_t D) { return D == 512 && H > 0 && H % 16 == 0 && (H <= 64 || H % 64 == 0); }
+
+constexpr int kMaxK = 8192;
+constexpr int64_t kMaxCols = 1 << 26;
+
+}  // namespace
+
+extern "C" {
+
+const char* csa2_status_string(csa2_status s) {
+  switch (s) {
+    case CSA2_OK: return "ok";
+    case CSA2_E_ARG: return "invalid argument (null pointer, negative size or bad enum)";
+    case CSA2_E_SHAPE: return "unsupported or inconsistent shape";
+    case CSA2_E_STATE: return "shared state needed by this mode is not valid";
+    case CSA2_E_WORKSPACE: return "workspace missing or too small";
+    case CSA2_E_UNSUPPORTED: return "not supported by this build";
+    case CSA2_E_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+csa2_status csa2_quantize_kv_fp4(const void* src, csa2_dtype src_dtype, int64_t n_rows, int32_t dim,
+                                 uint8_t* rows, void* stream) {
+  if (n_rows < 0 || (src_dtype != CSA2_F32 && src_dtype != CSA2_BF16)) return CSA2_E_ARG;
+  if (dim <= 0 || dim % 64 != 0 || dim > 4096) return CSA2_E_SHAPE;
+  if (n_rows == 0) return CSA2_OK;
+  if (!src || !rows) return CSA2_E_ARG;
+  if (reinterpret_cast<uintptr_t>(src) % 16 || reinterpret_cast<uintptr_t>(rows) % 4) return CSA2_E_ARG;
+  return hip_status(launch_quantize(src, src_dtype == CSA2_BF16, n_rows, dim, rows, as_stream(stream)));
+}
+
+csa2_status csa2_dequant_kv_fp4(const uint8_t* rows, int64_t n_rows, int32_t dim, float* out, void* stream) {
+  if (n_rows < 0) return CSA2_E_ARG;
+  if (dim <= 0 || dim % 64 != 0 || dim > 4096) return CSA2_E_SHAPE;
+  if (n_rows == 0) return CSA2_OK;
+  if (!rows || !out) return CSA2_E_ARG;
+  if (reinterpret_cast<uintptr_t>(rows) % 4 || reinterpret_cast<uintptr_t>(out) % 16) return CSA2_E_ARG;
+  return hip_status(launch_dequant(rows, n_rows, dim, out, as_stream(stream)));
+}
+
+csa2_status csa2_index_scores(const uint16_t* q_idx, const uint16_t* k_idx, int32_t B, int32_t T, int32_t Hi,
+                              int32_t Hk, int32_t Di, int32_t n_max, const int32_t* n_vis, const int32_t* cand,
+                              int32_t P, float* scores, float* block_max, int32_t block, void* stream) {
+  if (B < 0 || T < 0 || n_max < 0 || (cand && P < 0)) return CSA2_E_ARG;
+  if (!index_shape_ok(Hi, Hk, Di)) return CSA2_E_SHAPE;
+  if (block_max && (cand || block != 8)) return CSA2_E_UNSUPPORTED;
+  const int64_t rows = (int64_t)B * T;
+  const int32_t ncols = cand ? P : n_max;
+  if (rows == 0 || ncols == 0) return CSA2_OK;
+  if (!q_idx || !k_idx || !scores) return CSA2_E_ARG;
+  if (rows > INT32_MAX || ncols > kMaxCols) return CSA2_E_SHAPE;
+  if (reinterpret_cast<uintptr_t>(q_idx) % 16 || reinterpret_cast<uintptr_t>(k_idx) % 16) return CSA2_E_ARG;
+  hipStream_t s = as_stream(stream);
+  if (!cand && !block_max && index_prefill_supported(T, Hi, Hk, Di))
+    return hip_status(launch_index_prefill(q_idx, k_idx, B, T, Hi, Di, n_max, n_vis, scores, s));
+  return hip_status(launch_index_stream(q_idx, k_idx, B, T, Hi, Hk, Di, n_max, n_vis, cand, P, scores,
+                                        block_max, s));
+}
+
+size_t csa2_topk_workspace_size(int64_t rows, int32_t n_cols, int32_t k) {
+  if (rows <= 0 || n_cols <= 0 || k <= 0 || k > kMaxK || n_cols > kMaxCols) return 0;
+  return topk_workspace(rows, n_cols, k);
+}
+
+csa2_status csa2_topk(const float* scores, int64_t rows, int32_t n_cols, const int32_t* n_valid,
+                      const int32_t* col_to_pos, int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  if (rows < 0 || n_cols < 0 || k < 0) return CSA2_E_ARG;
+  if (k > kMaxK || n_cols > kMaxCols || rows > INT32_MAX) return CSA2_E_SHAPE;
+  if (rows == 0 || k == 0) return CSA2_OK;
+  if (!idx || (n_cols > 0 && !scores)) return CSA2_E_ARG;
+  const size_t need = csa2_topk_workspace_size(rows, std::max(n_cols, 1), k);
+  if (need > 0 && (!ws || ws_bytes < need)) return CSA2_E_WORKSPACE;
+  return hip_status(launch_topk(scores, rows, n_cols, n_valid, 1, col_to_pos, k, idx, 0, nullptr, 0, ws,
+                                as_stream(stream)));
+}
+
+size_t csa2_hier_pool_workspace_size(int64_t rows, int32_t n_blocks, int32_t n_sel_blocks) {
+  return csa2_topk_workspace_size(rows, n_blocks, n_sel_blocks);
+}
+
+csa2_status csa2_hier_pool(const float* block_max, int64_t rows, int32_t n_blocks, const int32_t* n_vis,
+                           int32_t block, int32_t n_sel_blocks, int32_t* pool, void* ws, size_t ws_bytes,
+                           void* stream) {
+  if (rows < 0 || n_blocks < 0 || n_sel_blocks < 0 || block <= 0) return CSA2_E_ARG;
+  if (block > 64 || n_sel_blocks > kMaxK || n_blocks > kMaxCols || rows > INT32_MAX) return CSA2_E_SHAPE;
+  if ((int64_t)n_blocks * block > INT32_MAX) return CSA2_E_SHAPE;
+  if (rows == 0 || n_sel_blocks == 0) return CSA2_OK;
+  if (!pool || (n_blocks > 0 && !block_max)) return CSA2_E_ARG;
+  const size_t need = csa2_hier_pool_workspace_size(rows, std::max(n_blocks, 1), n_sel_blocks);
+  if (need > 0 && (!ws || ws_bytes < need)) return CSA2_E_WORKSPACE;
+  return hip_status(launch_topk(block_max, rows, n_blocks, n_vis, block, nullptr, n_sel_blocks, pool, block,
+                                n_vis, n_blocks * block, ws, as_stream(stream)));
+}
+
+size_t csa2_sparse_attn_workspace_size(int32_t B, int32_t T, int32_t H, int32_t D, int32_t K) {
+  if (B <= 0 || T <= 0 || !attn_shape_ok(H, D) || K <= 0) return 0;
+  return attn_workspace(B, T, H, D, K);
+}
+
+csa2_status csa2_sparse_attn(const uint16_t* q, const uint8_t* rows, int32_t n_max, const int32_t* idx, int32_t B,
+                             int32_t T, int32_t H, int32_t D, int32_t K, float sm_scale, float* out, float* lse,
+                             void* ws, size_t ws_bytes, void* stream) {
+  if (B < 0 || T < 0 || n_max < 0 || K < 0 || H < 0) return CSA2_E_ARG;
+  if (!attn_shape_ok(H, D)) return CSA2_E_SHAPE;
+  if ((int64_t)B * T > INT32_MAX) return CSA2_E_SHAPE;
+  if (B == 0 || T == 0) return CSA2_OK;
+  if (!q || !out || (K > 0 && (!idx || (n_max > 0 && !rows)))) return CSA2_E_ARG;
+  if (reinterpret_cast<uintptr_t>(q) % 16 || reinterpret_cast<uintptr_t>(rows) % 16 ||
+      reinterpret_cast<uintptr_t>(out) % 16)
+    return CSA2_E_ARG;
+  const size_t need = csa2_sparse_attn_workspace_size(B, T, H, D, K);
+  if (need > 0 && (!ws || ws_bytes < need)) return CSA2_E_WORKSPACE;
+  return hip_status(launch_sparse_attn(q, rows, n_max, idx, B, T, H, D, K, sm_scale, out, lse, ws,
+                                       as_stream(stream)));
+}
+
+// ---------------------------------------------------------------------------------------------
+// Layer step. Workspace layout: [scores][block_max][top-k / pool scratch][attention partials].
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+struct LayerPlan {
+  bool score;           // runs the indexer (Full / Reindex)
+  bool on_pool;         // Reindex restricted to the candidate pool
+  bool build_pool;      // Full with the hierarchical indexer
+  int64_t rows;
+  int32_t ncols;        // score columns (n_max, or pool capacity)
+  int32_t n_blocks;
+  size_t off_scores, off_bmax, off_sel, off_attn, total;
+};
+
+csa2_status plan_layer(csa2_mode mode, const csa2_layer_args* a, const csa2_shared_kv* kv,
+                       const csa2_shared_idx* idx, LayerPlan* p) {
+  if (!a || !kv || !idx) return CSA2_E_ARG;
+  if (mode != CSA2_FULL && mode != CSA2_REINDEX && mode != CSA2_REUSE) return CSA2_E_ARG;
+  if (kv->B < 0 || kv->n_max < 0 || a->T < 0 || idx->K < 0) return CSA2_E_ARG;
+  if (!attn_shape_ok(a->H, kv->D)) return CSA2_E_SHAPE;
+  if (idx->K > kMaxK) return CSA2_E_SHAPE;
+  *p = LayerPlan{};
+  p->rows = (int64_t)kv->B * a->T;
+  p->score = mode != CSA2_REUSE;
+  p->build_pool = mode == CSA2_FULL && a->use_pool;
+  p->on_pool = mode == CSA2_REINDEX && a->use_pool && idx->pool_valid;
+  if (p->score) {
+    if (!index_shape_ok(a->Hi, kv->Hk, kv->Di)) return CSA2_E_SHAPE;
+    p->ncols = p->on_pool ? idx->P : kv->n_max;
+  }
+  if (p->build_pool) {
+    if (a->block != 8) return CSA2_E_UNSUPPORTED;
+    if (a->pool_blocks <= 0 || a->pool_blocks > kMaxK) return CSA2_E_SHAPE;
+    if (!idx->pool || idx->P != a->pool_blocks * a->block) return CSA2_E_SHAPE;
+    if (idx->K > a->pool_blocks * a->block) return CSA2_E_SHAPE;  // pool smaller than Top-K
+    p->n_blocks = (kv->n_max + 7) / 8;
+  }
+  if (p->on_pool && (!idx->pool || idx->P <= 0)) return CSA2_E_SHAPE;
+  size_t off = 0;
+  p->off_scores = off;
+  if (p->score) off = align_up(off + (size_t)p->rows * p->ncols * 4);
+  p->off_bmax = off;
+  if (p->build_pool) off = align_up(off + (size_t)p->rows * p->n_blocks * 4);
+  p->off_sel = off;
+  size_t sel = 0;
+  if (p->score && p->rows > 0 && p->ncols > 0 && idx->K > 0) sel = csa2_topk_workspace_size(p->rows, p->ncols, idx->K);
+  if (p->build_pool && p->rows > 0 && p->n_blocks > 0)
+    sel = std::max(sel, csa2_hier_pool_workspace_size(p->rows, p->n_blocks, a->pool_blocks));
+  off = align_up(off + sel);
+  p->off_attn = off;
+  if (kv->B > 0 && a->T > 0 && idx->K > 0) off = align_up(off + csa2_sparse_attn_workspace_size(kv->B, a->T, a->H, kv->D, idx->K));
+  p->total = off;
+  return CSA2_OK;
+}
+
+}  // namespace
+
+csa2_status csa2_layer_workspace_size(csa2_mode mode, const csa2_layer_args* a, const csa2_shared_kv* kv,
+                                      const csa2_shared_idx* idx, size_t* bytes) {
+  if (!bytes) return CSA2_E_ARG;
+  LayerPlan p;
+  const csa2_status st = plan_layer(mode, a, kv, idx, &p);
+  if (st != CSA2_OK) return st;
+  *bytes = p.total;
+  return CSA2_OK;
+}
+
+csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_shared_kv* kv, csa2_shared_idx* idx,
+                            void* stream) {
+  LayerPlan p;
+  csa2_status st = plan_layer(mode, a, kv, idx, &p);
+  if (st != CSA2_OK) return st;
+  if (mode != CSA2_FULL && !kv->valid) return CSA2_E_STATE;
+  if (mode == CSA2_REUSE && !idx->topk_valid) return CSA2_E_STATE;
+  if (!a->out || !idx->topk || !kv->rows || !a->q) return CSA2_E_ARG;
+  if (p.score && (!a->q_idx || !kv->k_idx)) return CSA2_E_ARG;
+  if (p.total > 0 && (!a->ws || a->ws_bytes < p.total)) return CSA2_E_WORKSPACE;
+
+  uint8_t* ws = static_cast<uint8_t*>(a->ws);
+  float* scores = reinterpret_cast<float*>(ws + p.off_scores);
+  float* bmax = p.build_pool ? reinterpret_cast<float*>(ws + p.off_bmax) : nullptr;
+  void* sel_ws = ws + p.off_sel;
+  void* attn_ws = ws + p.off_attn;
+  const size_t sel_bytes = p.off_attn - p.off_sel;
+  const size_t attn_bytes = p.total - p.off_attn;
+
+  if (p.score) {
+    st = csa2_index_scores(a->q_idx, kv->k_idx, kv->B, a->T, a->Hi, kv->Hk, kv->Di, kv->n_max, kv->n_vis,
+                           p.on_pool ? idx->pool : nullptr, p.on_pool ? idx->P : 0, scores, bmax, 8, stream);
+    if (st != CSA2_OK) return st;
+    st = csa2_topk(scores, p.rows, p.ncols, p.on_pool ? nullptr : kv->n_vis, p.on_pool ? idx->pool : nullptr,
+                   idx->K, idx->topk, sel_ws, sel_bytes, stream);
+    if (st != CSA2_OK) return st;
+    idx->topk_valid = 1;
+    if (p.build_pool) {
+      if (p.rows > 0 && a->pool_blocks > 0) {
+        const hipError_t e = launch_topk(bmax, p.rows, p.n_blocks, kv->n_vis, 8, nullptr, a->pool_blocks, idx->pool,
+                                         8, kv->n_vis, kv->n_max, sel_ws, as_stream(stream));
+        if (e != hipSuccess) return CSA2_E_HIP;
+      }
+      idx->pool_valid = 1;
+    }
+  }
+  st = csa2_sparse_attn(a->q, kv->rows, kv->n_max, idx->topk, kv->B, a->T, a->H, kv->D, idx->K, a->sm_scale,
+                        a->out, a->lse, attn_ws, attn_bytes, stream);
+  if (st == CSA2_OK && mode == CSA2_FULL) kv->valid = 1;
+  return st;
+}
+
+}  // extern "C"

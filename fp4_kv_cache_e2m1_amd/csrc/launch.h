@@ -1,0 +1,44 @@
+// Internal launchers of the CSA2 kernels (host side). Each validates nothing: the C-ABI layer in
+// csa2_api.cpp checks arguments before calling these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/csa2.h"
+
+namespace csa2 {
+
+// fp4_codec.hip
+hipError_t launch_quantize(const void* src, bool bf16, int64_t n_rows, int dim, uint8_t* rows,
+                           hipStream_t s);
+hipError_t launch_dequant(const uint8_t* rows, int64_t n_rows, int dim, float* out, hipStream_t s);
+
+// index_decode.hip: streaming indexer (flat or pool), optional fused 8-block max
+hipError_t launch_index_stream(const uint16_t* q, const uint16_t* k, int B, int T, int Hi, int Hk,
+                               int Di, int n_max, const int32_t* n_vis, const int32_t* cand, int P,
+                               float* scores, float* block_max, hipStream_t s);
+
+// index_prefill.hip: MFMA tiles for many query rows, causal tile skipping
+bool index_prefill_supported(int T, int Hi, int Hk, int Di);
+hipError_t launch_index_prefill(const uint16_t* q, const uint16_t* k, int B, int T, int Hi, int Di,
+                                int n_max, const int32_t* n_vis, float* scores, hipStream_t s);
+
+// topk.hip
+size_t topk_workspace(int64_t rows, int n_cols, int k);
+// n_valid[r] (nullable) counts valid entries; ceil(n_valid[r] / valid_div) columns take part.
+// expand_block > 0 writes each chosen column c as positions c*b .. c*b+b-1 (those >= expand_n_vis[r]
+// become -1, or >= expand_limit when expand_n_vis is null); the candidate-pool form.
+hipError_t launch_topk(const float* scores, int64_t rows, int n_cols, const int32_t* n_valid,
+                       int valid_div, const int32_t* col_to_pos, int k, int32_t* idx,
+                       int expand_block, const int32_t* expand_n_vis, int expand_limit, void* ws,
+                       hipStream_t s);
+
+// sparse_attn.hip
+size_t attn_workspace(int B, int T, int H, int D, int K);
+hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* rows, int n_max, const int32_t* idx,
+                              int B, int T, int H, int D, int K, float sm_scale, float* out,
+                              float* lse, void* ws, hipStream_t s);
+
+}  // namespace csa2

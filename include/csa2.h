@@ -1,0 +1,234 @@
+/*
+ * csa2.h - C ABI of the CSA2 sparse-attention hot path with an FP4 main KV cache, for AMD
+ * MI355X (gfx950).
+ *
+ * What is computed follows the model pages on DeepSeek-V4.1-Flash:
+ *   [walkthrough]  "DeepSeek-V4.1-Flash" tech-report walkthrough (wkq9411.github.io):
+ *                  section 一(四) Compressed Sparse Attention 2 (indexer, Top-K, attention over
+ *                  the selected entries), 一(四)1 Cross-Layer KV and Index Reuse (Full / Reindex /
+ *                  Reuse), 一(四)2 Hierarchical Sparse Indexer (block max, block selection,
+ *                  candidate pool), 一(五)4 FP4 Main KV Cache (E2M1 values, one E4M3 scale per
+ *                  16 channels, no global scale, dequantized before attention).
+ *   [release note] ModelScope release note, section 压缩稀疏注意力 2（CSA2）.
+ *
+ * Conventions shared by every call
+ *   - Every data pointer is a DEVICE pointer owned by the caller, unless a comment says "host".
+ *     The library never allocates, frees or synchronizes; scratch space comes from a caller
+ *     buffer `ws` whose size the matching *_workspace_size call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Calls only enqueue
+ *     work on it and return; results are valid once the caller has synchronized the stream.
+ *   - Return codes report synchronous argument / shape / state checks and launch errors only.
+ *     Device faults surface at the caller's next synchronization (the HIP convention).
+ *     On any non-OK return nothing has been enqueued, except CSA2_E_HIP (a launch failed
+ *     part-way).
+ *   - bf16 tensors are passed as uint16_t bit patterns. All arrays are dense row-major.
+ *   - Scores and query values must be finite (-inf is allowed for scores); this is a
+ *     precondition, not checked.
+ *   - Calls that overlap on one stream are ordered; the library keeps no state between calls
+ *     and is reentrant.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CSA2_OK = 0,
+  CSA2_E_ARG = 1,          /* null pointer, negative size, bad enum */
+  CSA2_E_SHAPE = 2,        /* unsupported or inconsistent shape */
+  CSA2_E_STATE = 3,        /* Reindex/Reuse without the shared state they need */
+  CSA2_E_WORKSPACE = 4,    /* workspace missing or smaller than required */
+  CSA2_E_UNSUPPORTED = 5,  /* valid request this build does not implement */
+  CSA2_E_HIP = 6           /* a HIP launch failed */
+} csa2_status;
+
+typedef enum { CSA2_FULL = 0, CSA2_REINDEX = 1, CSA2_REUSE = 2 } csa2_mode;
+typedef enum { CSA2_F32 = 0, CSA2_BF16 = 1 } csa2_dtype;
+
+/* Packed entry size in bytes for `dim` channels: dim/2 code bytes + dim/16 scale bytes
+ * (288 for the 512-channel latent). */
+#define CSA2_ROW_BYTES(dim) ((dim) / 2 + (dim) / 16)
+
+const char* csa2_status_string(csa2_status s);
+
+/* ------------------------------------------------------------------------------------------
+ * csa2_quantize_kv_fp4 - pack entries into the FP4 main-KV format.
+ * [walkthrough] 一(五)4: E2M1 values with one E4M3 scale per 16 channels, no global scale,
+ * quantized after RoPE (so all channels are treated alike).
+ *
+ * src       [n_rows, dim] fp32 or bf16 (src_dtype) values, finite.
+ * rows      [n_rows, dim/2 + dim/16] bytes, written. Byte i < dim/2 holds channel 2i in its low
+ *           nibble and channel 2i+1 in its high nibble; byte dim/2 + g holds the E4M3 scale of
+ *           channels 16g .. 16g+15.
+ * Rounding: per group, scale = the E4M3 value nearest to amax/6 (ties to the even code,
+ *           saturating at 448; amax = largest |x|); each code = sign bit of x and the E2M1
+ *           magnitude nearest to |x|/scale (ties to even, saturating at 6); a zero scale gives
+ *           zero magnitudes. All decisions are exact comparisons.
+ * dim       multiple of 64, at most 4096.  n_rows >= 0 (0 enqueues nothing).
+ * ------------------------------------------------------------------------------------------ */
+csa2_status csa2_quantize_kv_fp4(const void* src, csa2_dtype src_dtype, int64_t n_rows,
+                                 int32_t dim, uint8_t* rows, void* stream);
+
+/* csa2_dequant_kv_fp4 - inverse of the packing: out[r, c] = E2M1(code) * E4M3(scale), exact.
+ * [walkthrough] 一(五)4: the cache is dequantized before attention. The attention kernel
+ * dequantizes in registers/LDS; this stand-alone form writes fp32 [n_rows, dim]. */
+csa2_status csa2_dequant_kv_fp4(const uint8_t* rows, int64_t n_rows, int32_t dim, float* out,
+                                void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * csa2_index_scores - the lightweight indexer.
+ * [walkthrough] 一(四): indexer Q and indexer K score the main-KV entries; 一(四)2: later
+ * layers may score only a candidate pool.
+ *
+ * score[r, n] = sum_{h < Hi} sum_{d < Di} q_idx[r, h, d] * k_idx[b(r), n, h', d]
+ *   with r = b*T + t, h' = h if Hk == Hi, h' = 0 if Hk == 1. Products are exact, the sum is
+ *   fp32 (so results match an exact sum to about 1e-6 of sum |q*k|).
+ *
+ * q_idx     [B, T, Hi, Di] bf16.
+ * k_idx     [B, n_max, Hk, Di] bf16.
+ * n_vis     [B*T] int32 visible entries per query row (device), or NULL for all n_max.
+ *           Entries n >= n_vis[r] are not scored; their score slots are left unwritten.
+ * cand      NULL: flat mode, scores is [B*T, n_max].
+ *           else [B*T, P] int32 positions per query row (pool mode, -1 = empty slot);
+ *           scores is [B*T, P] and slot p holds the score of position cand[r, p]
+ *           (-inf for an empty slot or a position outside [0, n_max)).
+ * block_max NULL, or (flat mode only) [B*T, ceil(n_max / block)]: the max score over the
+ *           visible positions of each aligned block of `block` entries ([walkthrough]
+ *           一(四)2, a block's score is the max index score inside it). Blocks with no visible
+ *           position are left unwritten. block must be 8 when block_max is given.
+ * Requires Hk in {1, Hi}, Di % 8 == 0, Hk*Di % 64 == 0, Hi*Di <= 1024.
+ * Decode-shaped calls (T small, or pool mode) stream the keys once per query row; prefill
+ * calls (T >= 16, flat mode, Hk == Hi, Hi*Di % 64 == 0) run as MFMA tiles with causal tile
+ * skipping.
+ * ------------------------------------------------------------------------------------------ */
+csa2_status csa2_index_scores(const uint16_t* q_idx, const uint16_t* k_idx, int32_t B, int32_t T,
+                              int32_t Hi, int32_t Hk, int32_t Di, int32_t n_max,
+                              const int32_t* n_vis, const int32_t* cand, int32_t P,
+                              float* scores, float* block_max, int32_t block, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * csa2_topk - Top-K selection per row.
+ * [walkthrough] 一(四): each query keeps its Top-K entries (512 in the model, 三(二)1).
+ *
+ * Chooses, for each row r, the k best columns among c < n_valid[r] (all n_cols if n_valid is
+ * NULL) whose position is >= 0, ordered by score descending then position ascending, and
+ * writes their positions in ASCENDING order to idx[r, 0 ..), padding with -1 up to k.
+ * position(c) = c, or col_to_pos[r, c] when col_to_pos is given (pool slot -> global position;
+ * the pool must be ascending in its valid slots, which csa2_hier_pool guarantees).
+ * -0.0 and +0.0 are equal scores. The result is deterministic.
+ *
+ * scores     [rows, n_cols] fp32.     idx  [rows, k] int32, written.
+ * ws         scratch of csa2_topk_workspace_size() bytes (may be NULL if that size is 0).
+ * ------------------------------------------------------------------------------------------ */
+size_t csa2_topk_workspace_size(int64_t rows, int32_t n_cols, int32_t k);
+csa2_status csa2_topk(const float* scores, int64_t rows, int32_t n_cols, const int32_t* n_valid,
+                      const int32_t* col_to_pos, int32_t k, int32_t* idx, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * csa2_hier_pool - candidate pool of the Hierarchical Sparse Indexer.
+ * [walkthrough] 一(四)2: the first Full layer scores every visible position, takes each
+ * block's max, selects the highest-scoring blocks, and the positions they cover form the pool
+ * that later Reindex layers score (2048 blocks x 8 = 16384 positions in the model).
+ *
+ * block_max  [rows, n_blocks] fp32 (from csa2_index_scores).
+ * n_vis      [rows] visible positions per row (device) or NULL (= n_blocks * block).
+ *            Blocks at or beyond ceil(n_vis / block) do not take part.
+ * pool       [rows, n_sel_blocks * block] int32, written: the visible positions of the chosen
+ *            blocks (block ties broken by block index) in ascending order, then -1.
+ * ws         scratch of csa2_hier_pool_workspace_size() bytes.
+ * ------------------------------------------------------------------------------------------ */
+size_t csa2_hier_pool_workspace_size(int64_t rows, int32_t n_blocks, int32_t n_sel_blocks);
+csa2_status csa2_hier_pool(const float* block_max, int64_t rows, int32_t n_blocks,
+                           const int32_t* n_vis, int32_t block, int32_t n_sel_blocks,
+                           int32_t* pool, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * csa2_sparse_attn - attention of each query over its selected FP4 entries.
+ * [walkthrough] 一(四): each query attends to its selected main-KV entries; one 512-channel
+ * latent per entry is both key and value (MQA over H heads); 一(五)4: entries are dequantized
+ * before attention.
+ *
+ * For each (b, t, h): l_j = sm_scale * q[b,t,h,:] . x_j over selected j, out = sum softmax(l)_j
+ * x_j, lse = ln sum_j exp(l_j), with x_j the dequantized entry idx[b,t,j] of sequence b.
+ * Indices < 0 or >= n_max are skipped; with nothing selected out = 0 and lse = -inf.
+ * q K^T runs on bf16 MFMA (dequantized values are exact in bf16), softmax in fp32, P V on f16
+ * MFMA (values exact in f16, probabilities rounded to f16), fp32 accumulation.
+ *
+ * q     [B, T, H, D] bf16.        rows [B, n_max, D/2 + D/16] bytes (16-byte aligned base).
+ * idx   [B, T, K] int32.          out  [B, T, H, D] fp32.   lse [B, T, H] fp32 or NULL.
+ * Requires D == 512, H % 16 == 0.
+ * ws    scratch of csa2_sparse_attn_workspace_size() bytes (split-K partial results).
+ * ------------------------------------------------------------------------------------------ */
+size_t csa2_sparse_attn_workspace_size(int32_t B, int32_t T, int32_t H, int32_t D, int32_t K);
+csa2_status csa2_sparse_attn(const uint16_t* q, const uint8_t* rows, int32_t n_max,
+                             const int32_t* idx, int32_t B, int32_t T, int32_t H, int32_t D,
+                             int32_t K, float sm_scale, float* out, float* lse, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * csa2_layer_step - one CSA2 layer in its static mode.
+ * [walkthrough] 一(四)1: every layer computes its own query. Full scores every visible entry
+ * with its own indexer query and produces new Top-K; Reindex re-scores the latest shared keys
+ * with its own indexer query and produces new Top-K; Reuse attends with the newest Top-K of
+ * the latest index-producing layer and computes no indexer query and no score. Main KV and
+ * indexer K come from the most recent Full layer. 一(四)2: with the hierarchical indexer the
+ * (first) Full layer also builds the candidate pool and later Reindex layers score only it.
+ *
+ * Shared state is described by plain host structs pointing at caller-owned device buffers:
+ *   csa2_shared_kv   the cache of the most recent Full layer. The caller fills the pointers
+ *                    and shapes before the Full layer; FULL marks it valid.
+ *   csa2_shared_idx  the newest Top-K (and pool). FULL and REINDEX write topk and set
+ *                    topk_valid; FULL with use_pool writes pool and sets pool_valid.
+ * Modes:
+ *   FULL     index scores over all visible entries -> Top-K (-> block max -> pool) -> attention.
+ *   REINDEX  needs kv->valid. With use_pool and idx->pool_valid it scores only the pool;
+ *            otherwise all visible entries. -> Top-K -> attention.
+ *   REUSE    needs kv->valid and idx->topk_valid. Attention over idx->topk only.
+ * Errors: CSA2_E_STATE when the needed shared state is not valid.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct {
+  const uint8_t* rows;     /* [B, n_max, D/2 + D/16] FP4 entries */
+  const uint16_t* k_idx;   /* [B, n_max, Hk, Di] bf16 indexer keys */
+  const int32_t* n_vis;    /* [B*T] visible entries per query row, or NULL (= n_max) */
+  int32_t B, n_max, D, Hk, Di;
+  int32_t valid;           /* set by FULL */
+} csa2_shared_kv;
+
+typedef struct {
+  int32_t* topk;           /* [B*T, K] positions, ascending, -1 padded */
+  int32_t K;
+  int32_t* pool;           /* [B*T, P] candidate positions or NULL */
+  int32_t P;               /* pool capacity = pool_blocks * block */
+  int32_t topk_valid, pool_valid;
+} csa2_shared_idx;
+
+typedef struct {
+  const uint16_t* q;       /* [B, T, H, D] bf16 attention query of this layer */
+  const uint16_t* q_idx;   /* [B, T, Hi, Di] bf16 indexer query (Full / Reindex) */
+  int32_t T, H, Hi;
+  float sm_scale;
+  int32_t use_pool;        /* Full: build the pool; Reindex: score only the pool */
+  int32_t pool_blocks;     /* blocks kept in the pool (Full with use_pool) */
+  int32_t block;           /* positions per block (8) */
+  float* out;              /* [B, T, H, D] fp32 */
+  float* lse;              /* [B, T, H] fp32 or NULL */
+  void* ws;
+  size_t ws_bytes;
+} csa2_layer_args;
+
+csa2_status csa2_layer_workspace_size(csa2_mode mode, const csa2_layer_args* a,
+                                      const csa2_shared_kv* kv, const csa2_shared_idx* idx,
+                                      size_t* bytes);
+csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_shared_kv* kv,
+                            csa2_shared_idx* idx, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

@@ -1,0 +1,140 @@
+"""The C ABI library (CPU-side checks, no GPU needed).
+
+The library must build for gfx950, load, and export every function include/csa2.h declares.
+Argument, shape, workspace and shared-state validation happens on the host before any HIP call,
+so those error paths are exercised here with null device pointers.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from fp4_kv_cache_e2m1_amd import _lib
+from fp4_kv_cache_e2m1_amd._lib import LayerArgs, SharedIdx, SharedKV
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+OK, E_ARG, E_SHAPE, E_STATE, E_WS, E_UNSUP = 0, 1, 2, 3, 4, 5
+FAKE = 0x1000  # a 4 KiB-aligned non-null pointer value; validation fails before it is used
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        from fp4_kv_cache_e2m1_amd import build_lib
+        build_lib.build(verbose=False)
+    return _lib.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(L):
+    declared = header_functions()
+    assert len(declared) >= 12
+    assert set(declared) == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for code in range(7):
+        assert L.csa2_status_string(code)
+    assert b"state" in L.csa2_status_string(E_STATE)
+
+
+def test_quantize_validation(L):
+    assert L.csa2_quantize_kv_fp4(None, 0, -1, 512, None, None) == E_ARG
+    assert L.csa2_quantize_kv_fp4(None, 7, 4, 512, None, None) == E_ARG
+    assert L.csa2_quantize_kv_fp4(None, 0, 4, 500, None, None) == E_SHAPE
+    assert L.csa2_quantize_kv_fp4(None, 0, 4, 8192, None, None) == E_SHAPE
+    assert L.csa2_quantize_kv_fp4(None, 0, 4, 512, None, None) == E_ARG
+    assert L.csa2_quantize_kv_fp4(FAKE + 4, 0, 4, 512, FAKE, None) == E_ARG   # misaligned src
+    assert L.csa2_quantize_kv_fp4(None, 0, 0, 512, None, None) == OK          # empty: nothing to do
+    assert L.csa2_dequant_kv_fp4(None, 3, 512, None, None) == E_ARG
+    assert L.csa2_dequant_kv_fp4(None, 3, 96, None, None) == E_SHAPE
+
+
+def test_index_scores_validation(L):
+    f = L.csa2_index_scores
+    # q, k, B, T, Hi, Hk, Di, n_max, n_vis, cand, P, scores, block_max, block, stream
+    assert f(None, None, -1, 1, 8, 8, 64, 10, None, None, 0, None, None, 8, None) == E_ARG
+    assert f(None, None, 1, 1, 8, 4, 64, 10, None, None, 0, None, None, 8, None) == E_SHAPE   # Hk not in {1, Hi}
+    assert f(None, None, 1, 1, 8, 8, 12, 10, None, None, 0, None, None, 8, None) == E_SHAPE   # Di % 8
+    assert f(None, None, 1, 1, 32, 32, 64, 10, None, None, 0, None, None, 8, None) == E_SHAPE  # Hi*Di > 1024
+    assert f(None, None, 1, 1, 8, 8, 64, 10, None, FAKE, 4, None, FAKE, 8, None) == E_UNSUP   # block max on pool
+    assert f(None, None, 1, 1, 8, 8, 64, 10, None, None, 0, None, FAKE, 4, None) == E_UNSUP   # block != 8
+    assert f(None, None, 1, 1, 8, 8, 64, 10, None, None, 0, None, None, 8, None) == E_ARG     # null tensors
+    assert f(None, None, 0, 1, 8, 8, 64, 10, None, None, 0, None, None, 8, None) == OK        # empty
+
+
+def test_topk_and_pool_validation(L):
+    assert L.csa2_topk(None, -1, 10, None, None, 4, None, None, 0, None) == E_ARG
+    assert L.csa2_topk(None, 2, 10, None, None, 9000, None, None, 0, None) == E_SHAPE
+    assert L.csa2_topk(None, 2, 10, None, None, 4, None, None, 0, None) == E_ARG
+    assert L.csa2_topk(None, 0, 10, None, None, 4, None, None, 0, None) == OK
+    need = L.csa2_topk_workspace_size(4, 262144, 512)
+    assert need > 0
+    assert L.csa2_topk(FAKE, 4, 262144, None, None, 512, FAKE, None, 0, None) == E_WS
+    assert L.csa2_topk(FAKE, 4, 262144, None, None, 512, FAKE, FAKE, need - 1, None) == E_WS
+    assert L.csa2_topk_workspace_size(32, 16384, 512) == 0       # one segment per row: no scratch
+    assert L.csa2_hier_pool(None, 2, 10, None, 0, 4, None, None, 0, None) == E_ARG
+    assert L.csa2_hier_pool(None, 2, 10, None, 128, 4, None, None, 0, None) == E_SHAPE
+    assert L.csa2_hier_pool(None, 2, 10, None, 8, 4, None, None, 0, None) == E_ARG
+
+
+def test_sparse_attn_validation(L):
+    f = L.csa2_sparse_attn
+    # q, rows, n_max, idx, B, T, H, D, K, scale, out, lse, ws, ws_bytes, stream
+    assert f(None, None, 10, None, 1, 1, 64, 256, 8, 1.0, None, None, None, 0, None) == E_SHAPE
+    assert f(None, None, 10, None, 1, 1, 24, 512, 8, 1.0, None, None, None, 0, None) == E_SHAPE
+    assert f(None, None, 10, None, 1, 1, 96, 512, 8, 1.0, None, None, None, 0, None) == E_SHAPE
+    assert f(None, None, 10, None, 1, 1, 64, 512, 8, 1.0, None, None, None, 0, None) == E_ARG
+    assert f(FAKE, FAKE + 8, 10, FAKE, 1, 1, 64, 512, 8, 1.0, FAKE, None, None, 0, None) == E_ARG  # misaligned
+    need = L.csa2_sparse_attn_workspace_size(32, 1, 64, 512, 512)
+    assert need > 0                                                # decode is split over the entries
+    assert f(FAKE, FAKE, 10, FAKE, 32, 1, 64, 512, 512, 1.0, FAKE, None, None, 0, None) == E_WS
+
+
+def _layer(T=1, H=64, Hi=8, K=512, pool_blocks=0, use_pool=0, block=8):
+    kv = SharedKV(rows=FAKE, k_idx=FAKE, n_vis=None, B=4, n_max=4096, D=512, Hk=8, Di=64, valid=0)
+    idx = SharedIdx(topk=FAKE, K=K, pool=FAKE if pool_blocks else None, P=pool_blocks * block,
+                    topk_valid=0, pool_valid=0)
+    a = LayerArgs(q=FAKE, q_idx=FAKE, T=T, H=H, Hi=Hi, sm_scale=0.04, use_pool=use_pool,
+                  pool_blocks=pool_blocks, block=block, out=FAKE, lse=None, ws=None, ws_bytes=0)
+    return a, kv, idx
+
+
+def test_layer_step_state_rules(L):
+    a, kv, idx = _layer()
+    # Reindex / Reuse before a Full layer published the cache
+    assert L.csa2_layer_step(1, C.byref(a), C.byref(kv), C.byref(idx), None) == E_STATE
+    assert L.csa2_layer_step(2, C.byref(a), C.byref(kv), C.byref(idx), None) == E_STATE
+    kv.valid = 1
+    # Reuse still needs a Top-K
+    assert L.csa2_layer_step(2, C.byref(a), C.byref(kv), C.byref(idx), None) == E_STATE
+    # Full without workspace
+    kv.valid = 0
+    assert L.csa2_layer_step(0, C.byref(a), C.byref(kv), C.byref(idx), None) == E_WS
+    assert L.csa2_layer_step(7, C.byref(a), C.byref(kv), C.byref(idx), None) == E_ARG
+    n = C.c_size_t(0)
+    assert L.csa2_layer_workspace_size(0, C.byref(a), C.byref(kv), C.byref(idx), C.byref(n)) == OK
+    assert n.value >= 4 * 4096 * 4                                 # at least the score rows
+    assert L.csa2_layer_workspace_size(2, C.byref(a), C.byref(kv), C.byref(idx), C.byref(n)) == OK
+
+
+def test_layer_step_pool_rules(L):
+    a, kv, idx = _layer(pool_blocks=128, use_pool=1)
+    n = C.c_size_t(0)
+    assert L.csa2_layer_workspace_size(0, C.byref(a), C.byref(kv), C.byref(idx), C.byref(n)) == OK
+    a2, kv2, idx2 = _layer(pool_blocks=32, use_pool=1)               # pool (256) smaller than K (512)
+    assert L.csa2_layer_workspace_size(0, C.byref(a2), C.byref(kv2), C.byref(idx2), C.byref(n)) == E_SHAPE
+    a3, kv3, idx3 = _layer(pool_blocks=128, use_pool=1, block=4)     # fused block max is 8 wide
+    assert L.csa2_layer_workspace_size(0, C.byref(a3), C.byref(kv3), C.byref(idx3), C.byref(n)) == E_UNSUP
+    idx.P = 100                                                      # capacity must equal blocks * 8
+    assert L.csa2_layer_workspace_size(0, C.byref(a), C.byref(kv), C.byref(idx), C.byref(n)) == E_SHAPE

@@ -1,0 +1,261 @@
+"""GPU parity of each HIP kernel against the CPU oracle (small and ragged shapes, edge cases).
+
+Bars: FP4 pack/unpack and Top-K / pool index sets bit-exact; indexer scores within 1e-3 of
+max(|s|, sum |q*k|); attention max-abs error within 2e-3 of the output row's L2 norm.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp4_kv_cache_e2m1_amd as P
+from fp4_kv_cache_e2m1_amd import workloads as W
+from oracle import csa2_oracle as O
+from parity_util import check_attn, check_scores, dev_bf16, f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _sync_np(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _codec_inputs(rows, dim, seed):
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((rows, dim)).astype(np.float32)
+    x *= (10.0 ** g.uniform(-7, 4, size=(rows, dim // 16, 1))).repeat(16, axis=2).reshape(rows, dim).astype(np.float32)
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.75, -5.0, 7.0, -0.0, 0.0], np.float32)
+    if rows >= 3:
+        x[0] = 0.0
+        x[1] = -0.0
+        x[2, :16] = 6.0
+        x[2, 1:1 + len(ties)] = ties                     # every E2M1 tie at scale 1.0
+        x[2, 16:32] = 1e30                                # saturates at 448 x 6
+        x[2, 32:48] = 3.0 * 2.0 ** -10                    # amax/6 exactly half the smallest subnormal
+    return x
+
+
+@pytest.mark.parametrize("dim,rows", [(512, 1), (512, 5), (512, 1001), (64, 7), (128, 33), (1024, 9)])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_quantize_bitexact(dim, rows, bf16):
+    x = _codec_inputs(rows, dim, seed=dim * 7 + rows)
+    if bf16:
+        src = torch.from_numpy(x).to(torch.bfloat16)
+        ref_in = src.to(torch.float32).numpy()
+    else:
+        src = torch.from_numpy(x)
+        ref_in = x
+    got = _sync_np(P.quantize_kv_fp4(src.cuda()))
+    want = O.quantize_kv_fp4(ref_in)
+    assert got.shape == want.shape == (rows, dim // 2 + dim // 16)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} bytes differ, first {bad[:5].tolist()}"
+
+
+def test_quantize_empty():
+    out = P.quantize_kv_fp4(torch.empty(0, 512, device="cuda"))
+    torch.cuda.synchronize()
+    assert out.shape == (0, 288)
+
+
+def test_dequant_exhaustive_codes_and_scales():
+    # 8 rows x 32 groups cover every scale byte 0..255; each group holds all 16 value codes
+    rows = np.zeros((8, 288), np.uint8)
+    for r in range(8):
+        for g in range(32):
+            rows[r, 256 + g] = (32 * r + g) % 256
+            for c in range(16):
+                ch = 16 * g + c
+                rows[r, ch // 2] |= np.uint8(c << (4 * (ch % 2)))
+    got = _sync_np(P.dequant_kv_fp4(torch.from_numpy(rows).cuda()))
+    want = O.dequant_kv_fp4(rows).astype(np.float32)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(want[ok]))
+
+
+def test_roundtrip_on_normal_data():
+    x = np.random.default_rng(1).standard_normal((300, 512)).astype(np.float32)
+    rows = P.quantize_kv_fp4(torch.from_numpy(x).cuda())
+    deq = _sync_np(P.dequant_kv_fp4(rows))
+    assert np.array_equal(deq, O.dequant_kv_fp4(O.quantize_kv_fp4(x)).astype(np.float32))
+
+
+# ---------------------------------------------------------------------------------------------
+def _abs_dot(q, k):
+    """sum_h sum_d |q||k| for every (row, entry): the scale of the dot product's rounding error."""
+    R, Hi, Di = q.shape
+    N, Hk, _ = k.shape
+    kk = np.repeat(k, Hi, axis=1) if Hk == 1 else k
+    return np.abs(q.reshape(R, -1)) @ np.abs(kk.reshape(N, -1)).T
+
+
+@pytest.mark.parametrize("B,N,Hi,Hk,Di", [(3, 1000, 8, 8, 64), (2, 777, 4, 4, 64), (2, 513, 8, 1, 64),
+                                          (1, 300, 16, 16, 64), (2, 64, 2, 2, 64), (1, 1, 8, 8, 64),
+                                          (2, 2049, 8, 8, 128)])
+def test_index_scores_decode(B, N, Hi, Hk, Di):
+    if Hi * Di > 1024:
+        pytest.skip("shape outside the streaming kernel")
+    g = np.random.default_rng(N + Hi)
+    qb = W.to_bf16_bits(g.standard_normal((B, 1, Hi, Di)).astype(np.float32))
+    kb = W.to_bf16_bits(g.standard_normal((B, N, Hk, Di)).astype(np.float32))
+    n_vis = np.array([N, max(1, N // 2), 3][:B], dtype=np.int32) if B > 1 else np.array([N], np.int32)
+    s, bm = P.index_scores(dev_bf16(qb), dev_bf16(kb), n_vis=torch.from_numpy(n_vis).cuda(), block_max=True)
+    s, bm = _sync_np(s), _sync_np(bm)
+    for b in range(B):
+        ref = O.index_scores(f64(qb[b]), f64(kb[b]), [n_vis[b]])[0]
+        mask = np.arange(N) < n_vis[b]
+        check_scores(s[b], ref, _abs_dot(f64(qb[b]), f64(kb[b]))[0], mask, f"b={b}")
+        # the fused block max is the max of the kernel's own scores over visible block members
+        nb = -(-int(n_vis[b]) // 8)
+        own = O.block_max(s[b:b + 1], [n_vis[b]])[0][:nb]
+        assert np.array_equal(bm[b, :nb], own)
+
+
+def test_index_scores_pool():
+    g = np.random.default_rng(5)
+    B, N, P_ = 3, 5000, 96
+    qb = W.to_bf16_bits(g.standard_normal((B, 1, 8, 64)).astype(np.float32))
+    kb = W.to_bf16_bits(g.standard_normal((B, N, 8, 64)).astype(np.float32))
+    pool = np.full((B, P_), -1, np.int32)
+    for b in range(B):
+        blocks = np.sort(g.choice(N // 8, size=10, replace=False))
+        pos = (blocks[:, None] * 8 + np.arange(8)).reshape(-1)[: P_ - 7 * b]
+        pool[b, : len(pos)] = pos
+    pool[2, -1] = N + 5                                   # out of range: treated as empty
+    s = _sync_np(P.index_scores(dev_bf16(qb), dev_bf16(kb), cand=torch.from_numpy(pool).cuda()))
+    for b in range(B):
+        clean = np.where((pool[b] >= 0) & (pool[b] < N), pool[b], -1)
+        ref = O.pool_scores(f64(qb[b]), f64(kb[b]), clean[None])[0]
+        valid = clean >= 0
+        assert np.all(np.isneginf(s[b][~valid]))
+        ad = _abs_dot(f64(qb[b]), f64(kb[b]))[0]
+        check_scores(s[b][valid], ref[valid], ad[clean[valid]], np.ones(valid.sum(), bool), f"pool b={b}")
+
+
+@pytest.mark.parametrize("B,T,N,p0,ratio", [(1, 200, 700, 2500, 4), (2, 64, 130, 0, 1), (1, 300, 5000, 19000, 4)])
+def test_index_scores_prefill_mfma(B, T, N, p0, ratio):
+    g = np.random.default_rng(T + N)
+    qb = W.to_bf16_bits(g.standard_normal((B, T, 8, 64)).astype(np.float32))
+    kb = W.to_bf16_bits(g.standard_normal((B, N, 8, 64)).astype(np.float32))
+    nv = P.prefill_n_vis(p0, T, ratio, "cuda")
+    nv_ref = O.prefill_n_vis(p0, T, ratio)
+    assert np.array_equal(nv.cpu().numpy(), nv_ref)
+    nv_all = torch.cat([torch.clamp(nv, max=N)] * B)
+    s = _sync_np(P.index_scores(dev_bf16(qb), dev_bf16(kb), n_vis=nv_all))
+    for b in range(B):
+        nvb = np.minimum(nv_ref, N)
+        ref = O.index_scores(f64(qb[b]), f64(kb[b]), nvb)
+        mask = np.arange(N)[None, :] < nvb[:, None]
+        check_scores(s[b * T:(b + 1) * T], ref, _abs_dot(f64(qb[b]), f64(kb[b])), mask, f"prefill b={b}")
+
+
+# ---------------------------------------------------------------------------------------------
+TOPK_CASES = [(1, 1, 1), (3, 7, 3), (4, 100, 17), (2, 5000, 512), (32, 16384, 512), (2, 40000, 1024),
+              (3, 100000, 512), (2, 262144, 512), (5, 300, 300), (2, 50, 64)]
+
+
+@pytest.mark.parametrize("rows,n,k", TOPK_CASES)
+@pytest.mark.parametrize("dist", ["normal", "ties", "signed_zero"])
+def test_topk_bitexact(rows, n, k, dist):
+    if dist != "normal" and n > 40000:
+        pytest.skip("tie distributions are covered at the smaller sizes")
+    s = W.random_scores(rows * 31 + k, rows, n, dist)
+    nv = np.array([n - (r * 37) % max(1, n // 3) for r in range(rows)], np.int32)
+    got = _sync_np(P.topk(torch.from_numpy(s).cuda(), k, n_valid=torch.from_numpy(nv).cuda()))
+    want = O.topk(s, k, n_valid=nv)
+    assert np.array_equal(got, want), f"rows differ: {np.where((got != want).any(1))[0][:5]}"
+
+
+def test_topk_const_rows_and_pool_columns():
+    s = W.random_scores(3, 4, 3000, "const")
+    got = _sync_np(P.topk(torch.from_numpy(s).cuda(), 100))
+    assert np.array_equal(got, O.topk(s, 100))
+    g = np.random.default_rng(0)
+    s = W.random_scores(4, 4, 2048, "ties")
+    pool = np.sort(g.choice(100000, size=(4, 2048), replace=False), axis=1).astype(np.int32)
+    pool[:, 1900:] = -1
+    got = _sync_np(P.topk(torch.from_numpy(s).cuda(), 256, col_to_pos=torch.from_numpy(pool).cuda()))
+    assert np.array_equal(got, O.topk(s, 256, col_to_pos=pool))
+
+
+@pytest.mark.parametrize("rows,n_pos,n_sel", [(2, 4003, 64), (4, 262144, 1024), (3, 800, 200), (1, 80, 16)])
+@pytest.mark.parametrize("dist", ["normal", "ties"])
+def test_hier_pool_bitexact(rows, n_pos, n_sel, dist):
+    s = W.random_scores(n_pos + n_sel, rows, n_pos, dist)
+    n_vis = np.array([n_pos - 13 * r for r in range(rows)], np.int32)
+    bm_ref = O.block_max(s, n_vis)
+    bm = torch.from_numpy(np.where(np.isneginf(bm_ref), np.float32(0), bm_ref)).cuda()
+    got = _sync_np(P.hier_pool(bm, n_sel, n_vis=torch.from_numpy(n_vis).cuda()))
+    want = O.hier_pool(bm_ref, n_vis, n_sel)
+    assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------------------------------------
+def _attn_case(B, T, H, N, K, seed, neg_frac=0.1, oob=False):
+    g = np.random.default_rng(seed)
+    src = g.standard_normal((B, N, 512)).astype(np.float32)
+    rows = np.stack([O.quantize_kv_fp4(src[b]) for b in range(B)])
+    qb = W.to_bf16_bits(g.standard_normal((B, T, H, 512)).astype(np.float32))
+    idx = np.stack([[g.choice(N, size=K, replace=K > N) for _ in range(T)] for _ in range(B)]).astype(np.int32)
+    idx[g.random(idx.shape) < neg_frac] = -1
+    if oob:
+        m = min(3, K)
+        idx[0, 0, :m] = N + np.arange(m)
+    return rows, qb, idx
+
+
+def _attn_ref(rows, qb, idx, scale):
+    B, T = idx.shape[:2]
+    N = rows.shape[1]
+    outs, lses = [], []
+    for b in range(B):
+        clean = np.where((idx[b] >= 0) & (idx[b] < N), idx[b], -1)
+        o, l = O.sparse_attn(f64(qb[b]), O.dequant_kv_fp4(rows[b]), clean, scale)
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs), np.stack(lses)
+
+
+@pytest.mark.parametrize("B,T,H,N,K", [(2, 1, 64, 300, 512), (3, 1, 64, 1000, 100), (1, 3, 16, 200, 33),
+                                       (2, 2, 32, 90, 64), (1, 1, 128, 500, 256), (1, 1, 48, 70, 31),
+                                       (4, 1, 64, 2000, 1), (1, 40, 64, 600, 96)])
+def test_sparse_attn(B, T, H, N, K):
+    rows, qb, idx = _attn_case(B, T, H, N, K, seed=B * 1000 + N + K, oob=True)
+    scale = 1 / np.sqrt(512)
+    out, lse = P.sparse_attn(dev_bf16(qb), torch.from_numpy(rows).cuda(), torch.from_numpy(idx).cuda(), scale)
+    out, lse = _sync_np(out), _sync_np(lse)
+    ref, lref = _attn_ref(rows, qb, idx, scale)
+    check_attn(out, ref, lse, lref, f"attn B={B} T={T} H={H} K={K}")
+
+
+def test_sparse_attn_full_selection_and_empty():
+    rows, qb, _ = _attn_case(1, 2, 64, 128, 1, seed=3)
+    scale = 0.07
+    idx = np.stack([np.arange(128, dtype=np.int32), np.full(128, -1, np.int32)])[None]
+    out, lse = P.sparse_attn(dev_bf16(qb), torch.from_numpy(rows).cuda(), torch.from_numpy(idx).cuda(), scale)
+    out, lse = _sync_np(out), _sync_np(lse)
+    ref, lref = _attn_ref(rows, qb, idx, scale)
+    check_attn(out, ref, lse, lref, "full / empty")
+    assert np.all(out[0, 1] == 0) and np.all(np.isneginf(lse[0, 1]))
+
+
+def test_sparse_attn_single_entry_is_exact():
+    rows, qb, _ = _attn_case(1, 1, 16, 50, 1, seed=4)
+    idx = np.array([[[-1, 17, -1]]], np.int32)
+    out, _ = P.sparse_attn(dev_bf16(qb), torch.from_numpy(rows).cuda(), torch.from_numpy(idx).cuda(), 0.1)
+    out = _sync_np(out)
+    x = O.dequant_kv_fp4(rows[0, 17:18])[0].astype(np.float32)
+    assert np.array_equal(out[0, 0], np.broadcast_to(x, (16, 512)))
+
+
+def test_determinism():
+    rows, qb, idx = _attn_case(2, 1, 64, 400, 512, seed=9)
+    args = (dev_bf16(qb), torch.from_numpy(rows).cuda(), torch.from_numpy(idx).cuda(), 0.05)
+    a, la = P.sparse_attn(*args)
+    b, lb = P.sparse_attn(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(la, lb)
+    s = torch.from_numpy(W.random_scores(1, 8, 70000, "ties")).cuda()
+    assert torch.equal(P.topk(s, 512), P.topk(s, 512))

@@ -1,0 +1,238 @@
+"""GPU parity of the CSA2 layer modes (Full / Reindex / Reuse, hierarchical pool) against the
+oracle, first at small shapes, then at the five workload sizes with sampled sequences.
+
+End-to-end, the GPU Top-K comes from the GPU's own fp32 scores and the oracle's from its fp64
+ones, so the sets must be identical or differ only among entries whose oracle score is within
+1e-6 of the K-th best. Attention is compared with the oracle on rows whose sets agree; on any row
+where they do not, the GPU attention kernel is checked on the oracle's own indices instead.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp4_kv_cache_e2m1_amd as P
+from fp4_kv_cache_e2m1_amd import workloads as W
+from oracle import csa2_oracle as O
+from parity_util import (check_attn, check_scores, compare_topk, dev_bf16, f64, k_idx_device, kv_rows_device,
+                         q_device)
+
+pytestmark = pytest.mark.gpu
+
+
+def _np(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def run_stack_gpu(wl, rows, kidx, n_vis=None):
+    """Run the workload's layer stack through csa2_layer_step; returns per-layer (out, lse, topk, pool)."""
+    kv = P.KVState(rows, kidx, n_vis)
+    pool_size = wl.pool_blocks * wl.block
+    idx = P.IdxState.empty(wl.B * wl.T, wl.k, "cuda", pool_size=pool_size)
+    res = []
+    for layer, mode in enumerate(wl.modes):
+        q = q_device(wl, layer, "q")
+        qi = q_device(wl, layer, "q_idx") if mode != P.REUSE else None
+        use_pool = wl.pool_blocks > 0
+        out, lse = P.layer_step(mode, q, kv, idx, q_idx=qi, use_pool=use_pool, pool_blocks=wl.pool_blocks)
+        res.append((_np(out), _np(lse), _np(idx.topk).copy(), _np(idx.pool).copy() if idx.pool is not None else None))
+    return res, kv, idx
+
+
+def oracle_sequence(wl, b, tr):
+    """Oracle layer stack for sequence b, query rows tr (indices into the T query tokens)."""
+    seq = W.sequence(wl, b)
+    kq = f64(seq["k_idx"])
+    N = wl.N
+    n_vis = np.full(wl.T, N) if wl.T == 1 else np.minimum(O.prefill_n_vis(wl.p0, wl.T, wl.ratio), N)
+    n_vis = n_vis[tr]
+    out = []
+    shared_topk, pool = None, None
+    for layer, mode in enumerate(wl.modes):
+        q = f64(seq["q"][layer])[tr]
+        qi = f64(seq["q_idx"][layer])[tr]
+        bmax = None
+        if mode == W.REUSE:
+            sel, scores = shared_topk, None
+        elif mode == W.FULL or pool is None:
+            scores = O.index_scores(qi, kq, n_vis)
+            sel = O.topk(scores, wl.k, n_valid=n_vis)
+            if mode == W.FULL and wl.pool_blocks:
+                bmax = O.block_max(scores, n_vis)
+                pool = O.hier_pool(bmax, n_vis, wl.pool_blocks)
+        else:
+            scores = O.pool_scores(qi, kq, pool)
+            sel = O.topk(scores, wl.k, col_to_pos=pool)
+        shared_topk = sel
+        out.append(dict(mode=mode, scores=scores, topk=sel, pool=pool, bmax=bmax, q=q))
+    return out, seq["kv_src"]
+
+
+def attn_oracle_rows(src, sel_rows, q, scale, rows_gpu_b=None):
+    """Oracle attention over the selected entries, quantizing only the entries it needs; when the
+    GPU's packed rows are given, the bytes of those entries are checked equal."""
+    need = np.unique(sel_rows[sel_rows >= 0])
+    packed = O.quantize_kv_fp4(src[need])
+    if rows_gpu_b is not None:
+        assert np.array_equal(rows_gpu_b[need], packed), "GPU FP4 rows differ from the oracle's"
+    remap = np.full(src.shape[0], -1, np.int64)
+    remap[need] = np.arange(len(need))
+    local = np.where(sel_rows >= 0, remap[np.maximum(sel_rows, 0)], -1)
+    return O.sparse_attn(q, O.dequant_kv_fp4(packed), local, scale)
+
+
+def _blocks(pool_row):
+    bl = np.unique(pool_row[pool_row >= 0] // 8)
+    return np.concatenate([bl, -np.ones(0, np.int64)])
+
+
+def verify(wl, gpu_res, bs, rows_gpu, sample_rows=None):
+    """Compare GPU layer results for sequences bs (query rows sample_rows) against the oracle.
+    Returns (rows with identical index sets, rows with an allowed near-tie swap)."""
+    scale = wl.sm_scale
+    tr = np.arange(wl.T) if sample_rows is None else np.asarray(sample_rows)
+    n_same = n_swap = 0
+    for b in bs:
+        ora, src = oracle_sequence(wl, b, tr)
+        rows_b = rows_gpu[b].cpu().numpy()
+        row_ok = np.ones(len(tr), bool)      # GPU and oracle agree on everything upstream
+        for layer, o in enumerate(ora):
+            out_g, lse_g, topk_g, pool_g = gpu_res[layer]
+            tg = topk_g[b * wl.T + tr]
+            if o["mode"] == W.FULL and o["pool"] is not None:
+                pg = pool_g[b * wl.T + tr]
+                for i in range(len(tr)):
+                    bg, bo = _blocks(pg[i]), _blocks(o["pool"][i])
+                    same = compare_topk(np.concatenate([bg, -np.ones(wl.pool_blocks - len(bg), np.int64)]),
+                                        np.concatenate([bo, -np.ones(wl.pool_blocks - len(bo), np.int64)]),
+                                        lambda j, i=i: o["bmax"][i, j], f"pool b={b} t={tr[i]}")
+                    if same:
+                        assert np.array_equal(pg[i], o["pool"][i])
+                    row_ok[i] &= same
+            same_rows = np.zeros(len(tr), bool)
+            for i, t in enumerate(tr):
+                if not row_ok[i]:
+                    continue
+                if o["scores"] is None:
+                    assert np.array_equal(tg[i], o["topk"][i]), f"Reuse must carry the source indices (b={b})"
+                    same_rows[i] = True
+                    continue
+                if o["mode"] == W.REINDEX and o["pool"] is not None:
+                    smap = dict(zip(o["pool"][i].tolist(), o["scores"][i].tolist()))
+                    f = lambda p, smap=smap: smap[p]
+                else:
+                    f = lambda p, i=i: o["scores"][i, p]
+                same_rows[i] = compare_topk(tg[i], o["topk"][i], f, f"b={b} layer={layer} t={t}")
+            n_same += int(same_rows.sum())
+            n_swap += int((~same_rows).sum())
+            ref_out, ref_lse = attn_oracle_rows(src, o["topk"], o["q"], scale, rows_b)
+            go, gl = out_g[b][tr], lse_g[b][tr]
+            if same_rows.any():
+                check_attn(go[same_rows], ref_out[same_rows], gl[same_rows], ref_lse[same_rows],
+                           f"b={b} layer={layer}")
+            if (~same_rows).any():
+                # rows where the sets differ: the attention kernel on the oracle's own indices
+                idx_o = torch.from_numpy(o["topk"][~same_rows].astype(np.int32)).cuda()[None]
+                qd = torch.from_numpy(o["q"][~same_rows].astype(np.float32)).to(torch.bfloat16).cuda()[None]
+                oo, ll = P.sparse_attn(qd, rows_gpu[b:b + 1], idx_o, scale)
+                check_attn(_np(oo)[0], ref_out[~same_rows], _np(ll)[0], ref_lse[~same_rows],
+                           f"b={b} layer={layer} (oracle indices)")
+            row_ok &= same_rows
+    assert n_swap <= max(1, n_same // 50), f"too many rows with near-tie swaps: {n_swap} of {n_same + n_swap}"
+    return n_same, n_swap
+
+
+# ---------------------------------------------------------------------------------------------
+SMALL = {
+    "stack": W.CONFIGS[3].scaled(B=3, N=3000, k=128),
+    "hsi": W.CONFIGS[4].scaled(B=2, N=6000, k=128, pool_blocks=64),
+    "full_h16": W.CONFIGS[1].scaled(B=2, N=1001, k=64),
+    "prefill": W.CONFIGS[5].scaled(T=160, N=2700, p0=10600, n_existing=2650, k=256),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_stack_small(name):
+    wl = SMALL[name]
+    rows = kv_rows_device(wl)
+    kidx = k_idx_device(wl)
+    n_vis = None
+    if wl.T > 1:
+        n_vis = torch.clamp(P.prefill_n_vis(wl.p0, wl.T, wl.ratio, "cuda"), max=wl.N).repeat(wl.B)
+    res, kv, idx = run_stack_gpu(wl, rows, kidx, n_vis)
+    assert kv.valid and idx.c.topk_valid
+    verify(wl, res, range(wl.B), rows)
+
+
+def test_reuse_is_attention_on_source_indices():
+    wl = SMALL["stack"]
+    rows, kidx = kv_rows_device(wl), k_idx_device(wl)
+    res, kv, idx = run_stack_gpu(wl, rows, kidx)
+    # Reuse (layer 2) output equals the attention kernel applied to the Reindex layer's indices
+    q2 = q_device(wl, 2, "q")
+    src_idx = torch.from_numpy(res[1][2]).cuda().view(wl.B, wl.T, wl.k)
+    o, l = P.sparse_attn(q2, rows, src_idx, wl.sm_scale)
+    assert np.array_equal(_np(o), res[2][0]) and np.array_equal(_np(l), res[2][1])
+    assert np.array_equal(res[2][2], res[1][2])
+
+
+def test_reindex_with_full_query_reproduces_full_topk():
+    # with at least K blocks in the pool, every Top-K position's block is chosen
+    wl = SMALL["hsi"].scaled(k=64)
+    rows, kidx = kv_rows_device(wl), k_idx_device(wl)
+    kv = P.KVState(rows, kidx)
+    idx = P.IdxState.empty(wl.B, wl.k, "cuda", pool_size=wl.pool_blocks * 8)
+    q, qi = q_device(wl, 0, "q"), q_device(wl, 0, "q_idx")
+    o_full, _ = P.layer_step(P.FULL, q, kv, idx, q_idx=qi, use_pool=True, pool_blocks=wl.pool_blocks)
+    t_full = _np(idx.topk).copy()
+    pool = _np(idx.pool)
+    assert all(set(t_full[r][t_full[r] >= 0]) <= set(pool[r]) for r in range(wl.B))
+    o_re, _ = P.layer_step(P.REINDEX, q, kv, idx, q_idx=qi, use_pool=True)
+    assert np.array_equal(_np(idx.topk), t_full)
+    assert torch.equal(o_full, o_re)
+
+
+def test_hierarchical_equals_flat_when_pool_is_everything():
+    wl = W.CONFIGS[4].scaled(B=2, N=1600, k=128, pool_blocks=200)
+    rows, kidx = kv_rows_device(wl), k_idx_device(wl)
+    q0, qi0 = q_device(wl, 0, "q"), q_device(wl, 0, "q_idx")
+    q1, qi1 = q_device(wl, 1, "q"), q_device(wl, 1, "q_idx")
+    kv = P.KVState(rows, kidx)
+    idx = P.IdxState.empty(wl.B, wl.k, "cuda", pool_size=1600)
+    P.layer_step(P.FULL, q0, kv, idx, q_idx=qi0, use_pool=True, pool_blocks=200)
+    assert np.array_equal(_np(idx.pool), np.tile(np.arange(1600, dtype=np.int32), (2, 1)))
+    o_h, _ = P.layer_step(P.REINDEX, q1, kv, idx, q_idx=qi1, use_pool=True)
+    t_h = _np(idx.topk).copy()
+    o_f, _ = P.layer_step(P.REINDEX, q1, kv, idx, q_idx=qi1, use_pool=False)
+    assert np.array_equal(_np(idx.topk), t_h)
+    assert torch.equal(o_h, o_f)
+
+
+# ---------------------------------------------------------------------------------------------
+# The five workloads at full size; the oracle checks sampled sequences (and query rows).
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("cfg,sample", [(1, [0]), (2, [0, 17, 31]), (3, [0, 15]), (4, [0, 3]), (5, [0])])
+def test_config_full_size(cfg, sample):
+    wl = W.CONFIGS[cfg]
+    print(f"[config {cfg}] {wl.name}: generating inputs", flush=True)
+    rows = kv_rows_device(wl)
+    kidx = k_idx_device(wl)
+    n_vis = None
+    if wl.T > 1:
+        n_vis = torch.clamp(P.prefill_n_vis(wl.p0, wl.T, wl.ratio, "cuda"), max=wl.N).repeat(wl.B)
+    print(f"[config {cfg}] running the layer stack on the GPU", flush=True)
+    res, kv, idx = run_stack_gpu(wl, rows, kidx, n_vis)
+    for layer in range(len(wl.modes)):
+        assert np.all(np.isfinite(res[layer][0])), f"non-finite output at layer {layer}"
+    sample_rows = None
+    if wl.T > 1:
+        sample_rows = np.array([0, 1, 1023, 2048, wl.T - 1])
+    print(f"[config {cfg}] oracle on sequences {sample}", flush=True)
+    verify(wl, res, sample, rows, sample_rows=sample_rows)
+    if cfg == 4:
+        # structured workload: the Full layer's Top-K lies inside the planted entries, and the pool
+        # holds it (block count 1024 >= K)
+        t = res[0][2]
+        pool = res[0][3]
+        for r in range(wl.B):
+            assert set(t[r][t[r] >= 0].tolist()) <= set(pool[r].tolist())
