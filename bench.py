@@ -1,0 +1,256 @@
+"""Benchmark of the CSA2 decode hot path on one MI355X.
+
+Default workload: one Full-mode CSA2 layer, decode, 32 sequences x 1 query token, 16384 FP4
+entries of 512 channels per sequence (a 65536-token context at compression 4), 64 query heads,
+8 x 64 bf16 indexer heads, Top-K 512. A step is one csa2_layer_step(FULL): indexer scores over
+every entry -> Top-K -> sparse attention over the selected FP4 rows. Inputs are seeded and
+synthetic and already resident in HBM; two copies of the per-step inputs alternate so the
+256 MB last-level cache cannot hold one step's keys for the next.
+
+Prints one JSON line: query-tokens/s, achieved HBM GB/s of the dominant kernel (the streaming
+indexer) against the 8 TB/s peak, and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
+    python bench.py --calibrate-copy     # a plain 1 GiB copy, for rocprofv3 counter scaling
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+COUNTERS = os.path.join(ROOT, "profiles", "index_stream_full_decode_b32_n16384.counters.json")
+INDEX_SOURCES = ["fp4_kv_cache_e2m1_amd/csrc/index_decode.hip", "fp4_kv_cache_e2m1_amd/csrc/common.h"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def dev_bf16(bits, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def build_inputs(wl, dev, copies):
+    """Device inputs of the workload: FP4 cache (quantized on the GPU), indexer keys, queries."""
+    import torch
+    import fp4_kv_cache_e2m1_amd as P
+    from fp4_kv_cache_e2m1_amd import workloads as W
+    rows = torch.empty(wl.B, wl.N, P.row_bytes(wl.D), dtype=torch.uint8, device=dev)
+    kidx = torch.empty(wl.B, wl.N, wl.Hk, wl.Di, dtype=torch.bfloat16, device=dev)
+    for b in range(wl.B):
+        P.quantize_kv_fp4(torch.from_numpy(W.kv_source(wl, b)).to(dev), out=rows[b])
+        kidx[b] = dev_bf16(W.k_idx(wl, b), dev)
+    nl = len(wl.modes)
+    q = [torch.stack([dev_bf16(W.q_main(wl, b, l), dev) for b in range(wl.B)]) for l in range(nl)]
+    qi = [torch.stack([dev_bf16(W.q_idx(wl, b, l), dev) for b in range(wl.B)]) for l in range(nl)]
+    sets = [dict(rows=rows, kidx=kidx, q=q, qi=qi)]
+    for _ in range(copies - 1):
+        sets.append(dict(rows=rows.clone(), kidx=kidx.clone(), q=[t.clone() for t in q], qi=[t.clone() for t in qi]))
+    return sets
+
+
+def algorithmic_bytes(wl):
+    """Bytes the method must move per step: for every index-producing layer the indexer keys it
+    scores (all entries, or the pool), its indexer query, the pool it reads or writes and the
+    Top-K it writes; for every layer the Top-K it reads, the 288-byte FP4 rows it gathers, its
+    bf16 query and its fp32 output. Score arrays are intermediates and are not counted."""
+    R = wl.B * wl.T
+    kbytes = wl.Hk * wl.Di * 2
+    row_b = wl.D // 2 + wl.D // 16
+    P = wl.pool_blocks * wl.block
+    total = 0
+    for l, mode in enumerate(wl.modes):
+        if mode == 0:                                   # Full: every entry
+            total += wl.B * wl.N * kbytes + R * wl.Hi * wl.Di * 2 + R * wl.k * 4
+            if P:
+                total += R * P * 4                      # pool written
+        elif mode == 1:                                 # Reindex: the pool, or every entry
+            keys = R * P * kbytes + R * P * 4 if P else wl.B * wl.N * kbytes
+            total += keys + R * wl.Hi * wl.Di * 2 + R * wl.k * 4
+        total += R * wl.k * 4 + R * wl.k * row_b + R * wl.H * wl.D * 2 + R * wl.H * wl.D * 4
+    return total
+
+
+def index_kernel_bytes(wl):
+    """Algorithmic bytes of one flat indexer launch: every key row once plus the queries."""
+    return wl.B * wl.N * wl.Hk * wl.Di * 2 + wl.B * wl.T * wl.Hi * wl.Di * 2
+
+
+def sources_sha():
+    h = hashlib.sha256()
+    for p in INDEX_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_counters(launch_bytes):
+    """HBM bytes per indexer launch from committed rocprofv3 counters, if the kernel is unchanged."""
+    if not os.path.exists(COUNTERS):
+        return None
+    c = json.load(open(COUNTERS))
+    if c.get("sources_sha") != sources_sha():
+        return None
+    return float(c["fetch_bytes_per_launch"] + c["write_bytes_per_launch"])
+
+
+def cpu_baseline(wl, n_seq):
+    """The oracle's layer step on n_seq sequences of the workload (host cores), query-tokens/s."""
+    import threadpoolctl
+    from fp4_kv_cache_e2m1_amd import workloads as W
+    from oracle import csa2_oracle as O
+    f64 = lambda b: W.bf16_bits_to_f32(b).astype(np.float64)
+    prepared = []
+    for b in range(n_seq):
+        seq = W.sequence(wl, b)
+        prepared.append((seq, O.quantize_kv_fp4(seq["kv_src"])))
+    threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) if threadpoolctl.threadpool_info() else 1
+    t0 = time.perf_counter()
+    for seq, packed in prepared:
+        kv = O.dequant_kv_fp4(packed)
+        O.layer_step(O.FULL, q=f64(seq["q"][0]), kv_deq=kv, k_idx=f64(seq["k_idx"]), q_idx=f64(seq["q_idx"][0]),
+                     n_vis=[wl.N], k=wl.k, sm_scale=wl.sm_scale)
+    dt = time.perf_counter() - t0
+    return {"value": round(n_seq * wl.T / dt, 3), "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_seq} of {wl.B} sequences, full Full-layer step each (dequantize cache, score "
+                      f"{wl.N} entries, Top-{wl.k}, attention over {wl.H} heads); numpy fp64, {dt:.1f} s"}
+
+
+def calibrate_copy(dev):
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copied {n} bytes x 5")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--copies", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=8)
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path has no "
+              "multi-GPU mode in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp4_kv_cache_e2m1_amd as P
+    from fp4_kv_cache_e2m1_amd import _lib, workloads as W
+    if not os.path.exists(_lib.LIB_PATH):
+        from fp4_kv_cache_e2m1_amd import build_lib
+        build_lib.build()
+    dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        calibrate_copy(dev)
+        return
+
+    wl = W.CONFIGS[args.config]
+    log(f"[bench] workload {wl.name}: generating inputs")
+    sets = build_inputs(wl, dev, args.copies)
+    stream = torch.cuda.current_stream(dev)
+    R = wl.B * wl.T
+    n_vis = None
+    if wl.T > 1:
+        n_vis = torch.clamp(P.prefill_n_vis(wl.p0, wl.T, wl.ratio, dev), max=wl.N).repeat(wl.B)
+    # per-set shared state and buffers, allocated once
+    state = []
+    for s in sets:
+        kv = P.KVState(s["rows"], s["kidx"], n_vis)
+        idx = P.IdxState.empty(R, wl.k, dev, pool_size=wl.pool_blocks * wl.block)
+        outs = [torch.empty(wl.B, wl.T, wl.H, wl.D, dtype=torch.float32, device=dev) for _ in wl.modes]
+        state.append((s, kv, idx, outs))
+    ws = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+
+    def step(i):
+        s, kv, idx, outs = state[i % len(state)]
+        for l, mode in enumerate(wl.modes):
+            P.layer_step(mode, s["q"][l], kv, idx, q_idx=s["qi"][l] if mode != 2 else None,
+                         sm_scale=wl.sm_scale, use_pool=wl.pool_blocks > 0, pool_blocks=wl.pool_blocks,
+                         with_lse=False, ws=ws, out=outs[l])
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # dominant kernel: the flat streaming indexer, timed alone on the same stream
+    sc = torch.empty(R, wl.N, dtype=torch.float32, device=dev)
+    for i in range(3):
+        s = sets[i % len(sets)]
+        P.index_scores(s["qi"][0], s["kidx"], n_vis=n_vis, out=sc)
+    torch.cuda.synchronize()
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record(stream)
+    for i in range(args.steps):
+        s = sets[i % len(sets)]
+        P.index_scores(s["qi"][0], s["kidx"], n_vis=n_vis, out=sc)
+    k1.record(stream)
+    torch.cuda.synchronize()
+    kms = k0.elapsed_time(k1) / args.steps
+    kbytes = index_kernel_bytes(wl)
+    achieved = kbytes / (kms * 1e-3) / 1e9
+
+    step_bytes = algorithmic_bytes(wl)
+    value = R / (ms * 1e-3)
+    line = {
+        "metric": "CSA2 decode query-tokens/s + achieved HBM GB/s (% of peak) at 1 MI355X",
+        "value": round(value, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.B, "query_tokens": wl.T, "entries": wl.N,
+                   "latent_dim": wl.D, "heads": wl.H, "index_heads": wl.Hi, "index_dim": wl.Di,
+                   "topk": wl.k, "layers": [["FULL", "REINDEX", "REUSE"][m] for m in wl.modes],
+                   "pool_blocks": wl.pool_blocks, "kv_format": "E2M1 + E4M3 per 16 channels (288 B/entry)"},
+        "step_hbm_gbs": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_algorithmic_bytes": step_bytes,
+        "roofline": {"kernel": "index_stream_kernel (flat indexer scores)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_counters(kbytes),
+                     "algorithmic_bytes_per_launch": kbytes, "avg_launch_us": round(kms * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline and args.config == 2:
+        log(f"[bench] CPU oracle on {args.cpu_sample} sequences")
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
