@@ -148,6 +148,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=8)
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="replay each step from a captured HIP graph")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path has no "
@@ -193,6 +194,30 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    if args.graph:
+        # one graph per input set; replays alternate like the eager steps
+        graphs = []
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            for i in range(len(state)):
+                step(i)
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        for i in range(len(state)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        eager_step = step
+
+        def step(i):  # noqa: F811
+            graphs[i % len(graphs)].replay()
+
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -238,6 +263,7 @@ def main():
                    "latent_dim": wl.D, "heads": wl.H, "index_heads": wl.Hi, "index_dim": wl.Di,
                    "topk": wl.k, "layers": [["FULL", "REINDEX", "REUSE"][m] for m in wl.modes],
                    "pool_blocks": wl.pool_blocks, "kv_format": "E2M1 + E4M3 per 16 channels (288 B/entry)"},
+        "launch": "hip graph replay" if args.graph else "eager",
         "step_hbm_gbs": round(step_bytes / (ms * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes": step_bytes,

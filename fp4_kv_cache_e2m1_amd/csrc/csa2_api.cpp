@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
+#include <mutex>
 
 #include "../../include/csa2.h"
 #include "launch.h"
@@ -14,9 +16,19 @@ using namespace csa2;
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr int kPipelineChunks = 8;   // most chunks the pipeline may use
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int pipeline_chunks() {
+  static const int n = [] {
+    const char* e = std::getenv("CSA2_PIPELINE_CHUNKS");
+    const int v = e ? std::atoi(e) : 1;
+    return v < 1 ? 1 : (v > kPipelineChunks ? kPipelineChunks : v);
+  }();
+  return n;
+}
 csa2_status hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_E_HIP; }
 
 bool index_shape_ok(int32_t Hi, int32_t Hk, int32_t Di) {
@@ -26,8 +38,39 @@ bool index_shape_ok(int32_t Hi, int32_t Hk, int32_t Di) {
 
 bool attn_shape_ok(int32_t H, int32_t D) { return D == 512 && H > 0 && H % 16 == 0 && (H <= 64 || H % 64 == 0); }
 
-constexpr int kMaxK = 8192;
+constexpr int kMaxK = 4096;
 constexpr int64_t kMaxCols = 1 << 26;
+
+// Per-device auxiliary stream and events for the chunk pipeline of csa2_layer_step. Created on
+// first use and kept for the life of the process; a mutex serializes the enqueue sequences that
+// share them (the enqueue itself is short; the work runs asynchronously).
+struct AuxDevice {
+  bool ready = false;
+  hipStream_t aux = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t chunk[kPipelineChunks] = {};
+};
+constexpr int kMaxDevices = 64;
+AuxDevice g_aux[kMaxDevices];
+std::mutex g_aux_mu;
+
+hipError_t aux_for_current_device(AuxDevice** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  AuxDevice& a = g_aux[dev];
+  if (!a.ready) {
+    if ((e = hipStreamCreateWithFlags(&a.aux, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&a.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&a.join, hipEventDisableTiming)) != hipSuccess) return e;
+    for (auto& ev : a.chunk)
+      if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return e;
+    a.ready = true;
+  }
+  *out = &a;
+  return hipSuccess;
+}
 
 }  // namespace
 
@@ -147,6 +190,7 @@ csa2_status csa2_sparse_attn(const uint16_t* q, const uint8_t* rows, int32_t n_m
 namespace {
 
 struct LayerPlan {
+  int nch;              // batch chunks pipelined across the caller's stream and the aux stream
   bool score;           // runs the indexer (Full / Reindex)
   bool on_pool;         // Reindex restricted to the candidate pool
   bool build_pool;      // Full with the hierarchical indexer
@@ -180,19 +224,29 @@ csa2_status plan_layer(csa2_mode mode, const csa2_layer_args* a, const csa2_shar
     p->n_blocks = (kv->n_max + 7) / 8;
   }
   if (p->on_pool && (!idx->pool || idx->P <= 0)) return CSA2_E_SHAPE;
+  // Index-producing layers with several sequences may be pipelined over chunks of the batch
+  // (CSA2_PIPELINE_CHUNKS, default 1 = off: in eager mode a cross-stream wait costs ~11 us).
+  p->nch = (p->score && kv->B >= 2) ? std::min(kv->B, pipeline_chunks()) : 1;
   size_t off = 0;
   p->off_scores = off;
   if (p->score) off = align_up(off + (size_t)p->rows * p->ncols * 4);
   p->off_bmax = off;
   if (p->build_pool) off = align_up(off + (size_t)p->rows * p->n_blocks * 4);
   p->off_sel = off;
-  size_t sel = 0;
-  if (p->score && p->rows > 0 && p->ncols > 0 && idx->K > 0) sel = csa2_topk_workspace_size(p->rows, p->ncols, idx->K);
-  if (p->build_pool && p->rows > 0 && p->n_blocks > 0)
-    sel = std::max(sel, csa2_hier_pool_workspace_size(p->rows, p->n_blocks, a->pool_blocks));
+  // scratch of the chunk-wise Top-K / pool / attention calls (they run one after another)
+  size_t sel = 0, attn = 0;
+  for (int c = 0; c < p->nch; ++c) {
+    const int b0 = (int)((int64_t)kv->B * c / p->nch), b1 = (int)((int64_t)kv->B * (c + 1) / p->nch);
+    const int64_t rows_c = (int64_t)(b1 - b0) * a->T;
+    if (rows_c == 0) continue;
+    if (p->score && p->ncols > 0 && idx->K > 0) sel = std::max(sel, csa2_topk_workspace_size(rows_c, p->ncols, idx->K));
+    if (p->build_pool && p->n_blocks > 0)
+      sel = std::max(sel, csa2_hier_pool_workspace_size(rows_c, p->n_blocks, a->pool_blocks));
+    if (idx->K > 0) attn = std::max(attn, csa2_sparse_attn_workspace_size(b1 - b0, a->T, a->H, kv->D, idx->K));
+  }
   off = align_up(off + sel);
   p->off_attn = off;
-  if (kv->B > 0 && a->T > 0 && idx->K > 0) off = align_up(off + csa2_sparse_attn_workspace_size(kv->B, a->T, a->H, kv->D, idx->K));
+  off = align_up(off + attn);
   p->total = off;
   return CSA2_OK;
 }
@@ -227,28 +281,66 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_share
   void* attn_ws = ws + p.off_attn;
   const size_t sel_bytes = p.off_attn - p.off_sel;
   const size_t attn_bytes = p.total - p.off_attn;
+  const int T = a->T;
+  const int64_t kbytes_row = (int64_t)kv->Hk * kv->Di;          // bf16 elements per key row
+  const int64_t rb = CSA2_ROW_BYTES(kv->D);
 
-  if (p.score) {
-    st = csa2_index_scores(a->q_idx, kv->k_idx, kv->B, a->T, a->Hi, kv->Hk, kv->Di, kv->n_max, kv->n_vis,
-                           p.on_pool ? idx->pool : nullptr, p.on_pool ? idx->P : 0, scores, bmax, 8, stream);
-    if (st != CSA2_OK) return st;
-    st = csa2_topk(scores, p.rows, p.ncols, p.on_pool ? nullptr : kv->n_vis, p.on_pool ? idx->pool : nullptr,
-                   idx->K, idx->topk, sel_ws, sel_bytes, stream);
-    if (st != CSA2_OK) return st;
-    idx->topk_valid = 1;
-    if (p.build_pool) {
-      if (p.rows > 0 && a->pool_blocks > 0) {
-        const hipError_t e = launch_topk(bmax, p.rows, p.n_blocks, kv->n_vis, 8, nullptr, a->pool_blocks, idx->pool,
-                                         8, kv->n_vis, kv->n_max, sel_ws, as_stream(stream));
+  // One chunk of whole sequences [b0, b1): scores on `s_idx`, then (after the event) Top-K,
+  // pool and attention on `s_sel`.
+  auto run_chunk = [&](int b0, int b1, void* s_idx, void* s_sel, hipEvent_t ev, hipStream_t aux) -> csa2_status {
+    const int nb = b1 - b0;
+    const int64_t r0 = (int64_t)b0 * T, rows_c = (int64_t)nb * T;
+    const int32_t* n_vis_c = kv->n_vis ? kv->n_vis + r0 : nullptr;
+    int32_t* pool_c = idx->pool ? idx->pool + r0 * idx->P : nullptr;
+    float* scores_c = scores + r0 * p.ncols;
+    csa2_status s2 = CSA2_OK;
+    if (p.score) {
+      s2 = csa2_index_scores(a->q_idx + r0 * a->Hi * kv->Di, kv->k_idx + (int64_t)b0 * kv->n_max * kbytes_row, nb,
+                             T, a->Hi, kv->Hk, kv->Di, kv->n_max, n_vis_c, p.on_pool ? pool_c : nullptr,
+                             p.on_pool ? idx->P : 0, scores_c, bmax ? bmax + r0 * p.n_blocks : nullptr, 8, s_idx);
+      if (s2 != CSA2_OK) return s2;
+      if (ev) {
+        if (hipEventRecord(ev, as_stream(s_idx)) != hipSuccess) return CSA2_E_HIP;
+        if (hipStreamWaitEvent(aux, ev, 0) != hipSuccess) return CSA2_E_HIP;
+      }
+      s2 = csa2_topk(scores_c, rows_c, p.ncols, p.on_pool ? nullptr : n_vis_c, p.on_pool ? pool_c : nullptr,
+                     idx->K, idx->topk + r0 * idx->K, sel_ws, sel_bytes, s_sel);
+      if (s2 != CSA2_OK) return s2;
+      if (p.build_pool && a->pool_blocks > 0) {
+        const hipError_t e = launch_topk(bmax + r0 * p.n_blocks, rows_c, p.n_blocks, n_vis_c, 8, nullptr,
+                                         a->pool_blocks, pool_c, 8, n_vis_c, kv->n_max, sel_ws, as_stream(s_sel));
         if (e != hipSuccess) return CSA2_E_HIP;
       }
-      idx->pool_valid = 1;
     }
+    return csa2_sparse_attn(a->q + r0 * a->H * kv->D, kv->rows + (int64_t)b0 * kv->n_max * rb, kv->n_max,
+                            idx->topk + r0 * idx->K, nb, T, a->H, kv->D, idx->K, a->sm_scale,
+                            a->out + r0 * a->H * kv->D, a->lse ? a->lse + r0 * a->H : nullptr, attn_ws, attn_bytes,
+                            s_sel);
+  };
+
+  if (p.nch <= 1) {
+    st = run_chunk(0, kv->B, stream, stream, nullptr, nullptr);
+  } else {
+    std::lock_guard<std::mutex> lock(g_aux_mu);
+    AuxDevice* ad = nullptr;
+    if (aux_for_current_device(&ad) != hipSuccess) return CSA2_E_HIP;
+    hipStream_t s = as_stream(stream);
+    // the aux stream starts after everything already queued on the caller's stream
+    if (hipEventRecord(ad->fork, s) != hipSuccess || hipStreamWaitEvent(ad->aux, ad->fork, 0) != hipSuccess)
+      return CSA2_E_HIP;
+    for (int c = 0; c < p.nch && st == CSA2_OK; ++c) {
+      const int b0 = (int)((int64_t)kv->B * c / p.nch), b1 = (int)((int64_t)kv->B * (c + 1) / p.nch);
+      if (b1 > b0) st = run_chunk(b0, b1, stream, ad->aux, ad->chunk[c], ad->aux);
+    }
+    // join: the caller's stream continues after the last chunk's attention
+    if (hipEventRecord(ad->join, ad->aux) != hipSuccess || hipStreamWaitEvent(s, ad->join, 0) != hipSuccess)
+      return CSA2_E_HIP;
   }
-  st = csa2_sparse_attn(a->q, kv->rows, kv->n_max, idx->topk, kv->B, a->T, a->H, kv->D, idx->K, a->sm_scale,
-                        a->out, a->lse, attn_ws, attn_bytes, stream);
-  if (st == CSA2_OK && mode == CSA2_FULL) kv->valid = 1;
-  return st;
+  if (st != CSA2_OK) return st;
+  if (p.score) idx->topk_valid = 1;
+  if (p.build_pool) idx->pool_valid = 1;
+  if (mode == CSA2_FULL) kv->valid = 1;
+  return CSA2_OK;
 }
 
 }  // extern "C"

@@ -5,13 +5,19 @@
 //
 // A workgroup owns one query token, up to 64 heads (16 per wave) and a contiguous slice of its
 // selected entries, walked in chunks of 32:
-//   1. gather: the 32 selected 288-byte rows are copied to LDS, 18 lanes x 16 B per row;
-//   2. dequantize in LDS: each (2 entries x 32 channels) item is decoded once into a bf16 copy
-//      X[key][ch] (operand of q.x) and an f16 transposed copy Xt[ch][key] (operand of p.x). Both
-//      are exact: every E2M1 x E4M3 product has at most 6 significant bits;
-//   3. S^T = X Q^T on v_mfma_f32_16x16x32_bf16 (two 16-key tiles x 16 heads per wave): each lane
-//      ends up with 8 keys of one head, which is exactly the B operand layout P^T needs next;
-//   4. online softmax in fp32 (exp2 domain), per head, across the 4 lanes sharing a head;
+//   1. gather: the chunk's 288-byte rows are loaded into registers one chunk ahead (18 x 16 B
+//      per row) and stored to LDS, so the loads of chunk c+1 overlap the math of chunk c;
+//   2. dequantize in LDS with v_cvt_scalef32_pk_f16_fp4 (two E2M1 codes -> two f16, unscaled)
+//      and one packed f16 multiply by the group's E4M3 scale: both exact, since every
+//      E2M1 x E4M3 product has at most 6 significant bits and lies in f16's normal range. Each
+//      entry is written once as X[key][ch] (operand of q.x) and once transposed as Xt[ch][key]
+//      (operand of p.x);
+//   3. S^T = X Q^T on v_mfma_f32_16x16x32_f16 (two 16-key tiles x 16 heads per wave). q is
+//      scaled per head by a power of two so the bf16 query converts to f16 exactly; the scale is
+//      folded into the softmax scale. Each lane ends up with 8 keys of one head, exactly the B
+//      operand layout P^T needs next;
+//   4. online softmax in fp32 (exp2 domain), per head, across the 4 lanes sharing a head
+//      (v_permlane16/32_swap exchanges);
 //   5. O^T += Xt P^T on v_mfma_f32_16x16x32_f16, 32 channel tiles, fp32 accumulators.
 // Decode rows (few query tokens) are split over the selected entries; a second kernel merges the
 // per-split (max, sum, unnormalized output) triples.
@@ -27,31 +33,34 @@ namespace csa2 {
 constexpr int kD = 512;                  // latent channels
 constexpr int kRowB = 288;               // packed bytes per entry
 constexpr int kKC = 32;                  // entries per chunk
-constexpr int kXbPitch = kD + 8;         // bf16 elements per X row (pad against bank conflicts)
+constexpr int kMaxKPS = 1024;            // entries per split (indices staged in LDS)
+constexpr int kXPitch = kD + 8;          // f16 elements per X row (pad against bank conflicts)
 constexpr int kXtPitch = kKC + 4;        // f16 elements per Xt row
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Dequantize channels 32 cs .. 32 cs + 31 of staged entry `key`: fp32 values to v, and their bf16
-// patterns (exact, so the top half of each fp32 pattern) to X[key][32 cs ..].
-CSA2_DEV void decode_slab(const uint4* raw, int key, int cs, uint16_t* xb, float* v) {
-  const uint8_t* rb = reinterpret_cast<const uint8_t*>(raw) + key * kRowB;
-  const uint4 codes = *reinterpret_cast<const uint4*>(rb + 16 * cs);
-  const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(rb + 256 + 2 * cs);
-  const float h0 = 0.5f * e4m3_value(sc2 & 0xFF), h1 = 0.5f * e4m3_value(sc2 >> 8);
-  e2m1x8_to_f32(codes.x, h0, v);
-  e2m1x8_to_f32(codes.y, h0, v + 8);
-  e2m1x8_to_f32(codes.z, h1, v + 16);
-  e2m1x8_to_f32(codes.w, h1, v + 24);
-  uint4* dst = reinterpret_cast<uint4*>(xb + key * kXbPitch + 32 * cs);
-#pragma unroll
-  for (int qd = 0; qd < 4; ++qd) {
-    uint32_t w[4];
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-      w[h] = (__float_as_uint(v[8 * qd + 2 * h]) >> 16) | (__float_as_uint(v[8 * qd + 2 * h + 1]) & 0xFFFF0000u);
-    dst[qd] = make_uint4(w[0], w[1], w[2], w[3]);
-  }
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// Values of the 4 lanes that share a head (lanes l, l^16, l^32, l^48) combined.
+CSA2_DEV float head_max(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+CSA2_DEV float head_sum(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Eight E2M1 codes (one word) times an E4M3 scale as four packed f16 pairs (exact).
+CSA2_DEV void e2m1x8_to_f16(uint32_t w, f16x2_t s2, uint32_t* out) {
+  out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2);
+  out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2);
+  out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2);
+  out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2);
 }
 
 template <int NW>
@@ -61,10 +70,11 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
   constexpr int NT = NW * 64;
+  constexpr int GATHER = (kKC * 18 + NT - 1) / NT;     // 16-byte row pieces per thread per chunk
   __shared__ uint4 raw[kKC * (kRowB / 16)];
-  __shared__ __attribute__((aligned(16))) uint16_t xb[kKC * kXbPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[kKC * kXPitch];
   __shared__ __attribute__((aligned(16))) uint16_t xt[kD * kXtPitch];
-  __shared__ int kvalid[kKC];
+  __shared__ int sidx[kMaxKPS];
 
   const int qr = blockIdx.x, split = blockIdx.y, hg = blockIdx.z;
   const int n_splits = gridDim.y;
@@ -73,81 +83,135 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
   const int l16 = lane & 15, g = lane >> 4;
   const int head = hg * (NW * 16) + wave * 16 + l16;   // this lane's head
 
-  // Q^T operand: lane holds q[head][32 kk + 8 g .. +8] for kk = 0..15
-  bf16x8_t qv[16];
+  const int kbeg = split * keys_per_split;
+  const int kend = min(K, kbeg + keys_per_split);
+  const int nk = max(0, kend - kbeg);
+  const int32_t* irow = idx + (int64_t)qr * K + kbeg;
+  const uint8_t* rbase = rows + (int64_t)b * n_max * kRowB;
+
+  // stage this split's indices (out-of-range -> -1)
+  for (int i = tid; i < nk; i += NT) {
+    const int p = irow[i];
+    sidx[i] = (p >= 0 && p < n_max) ? p : -1;
+  }
+  __syncthreads();
+
+  // gather of one chunk into registers
+  uint4 gr[GATHER];
+  auto gather = [&](int c0) {
+#pragma unroll
+    for (int m = 0; m < GATHER; ++m) {
+      const int it = tid + m * NT;
+      gr[m] = make_uint4(0, 0, 0, 0);
+      if (it < kKC * 18) {
+        const int kr = it / 18, part = it - kr * 18;
+        const int ks = c0 + kr;
+        const int p = ks < nk ? sidx[ks] : -1;
+        if (p >= 0) gr[m] = *reinterpret_cast<const uint4*>(rbase + (int64_t)p * kRowB + 16 * part);
+      }
+    }
+  };
+  if (nk > 0) gather(0);
+
+  // Q^T operand in f16: lane holds q[head][32 kk + 8 g .. +8] * 2^qe for kk = 0..15
+  f16x8_t qv[16];
+  float qscale;
   {
     const uint4* qp = reinterpret_cast<const uint4*>(q + ((int64_t)qr * H + head) * kD);
+    uint4 raw_q[16];
+    float amax = 0.0f;
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) qv[kk] = __builtin_bit_cast(bf16x8_t, qp[4 * kk + g]);
+    for (int kk = 0; kk < 16; ++kk) {
+      raw_q[kk] = qp[4 * kk + g];
+      const uint32_t w[4] = {raw_q[kk].x, raw_q[kk].y, raw_q[kk].z, raw_q[kk].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w[e] << 16)), fabsf(__uint_as_float(w[e] & 0xFFFF0000u))));
+    }
+    amax = head_max(amax);
+    // power of two that brings the head's largest |q| into [2^14, 2^15): f16 holds every value
+    const int qe = amax > 0.0f ? 14 - ilogbf(amax) : 0;
+    const float sc = ldexpf(1.0f, qe);
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      const uint32_t w[4] = {raw_q[kk].x, raw_q[kk].y, raw_q[kk].z, raw_q[kk].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qv[kk][2 * e] = (_Float16)(__uint_as_float(w[e] << 16) * sc);
+        qv[kk][2 * e + 1] = (_Float16)(__uint_as_float(w[e] & 0xFFFF0000u) * sc);
+      }
+    }
+    qscale = sm_scale * kLog2e * ldexpf(1.0f, -qe);
   }
+
   f32x4_t acc[32];
 #pragma unroll
   for (int mt = 0; mt < 32; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;
-  const float qscale = sm_scale * kLog2e;
 
-  const int kbeg = split * keys_per_split;
-  const int kend = min(K, kbeg + keys_per_split);
-  const int32_t* irow = idx + (int64_t)qr * K;
-  const uint8_t* rbase = rows + (int64_t)b * n_max * kRowB;
-
-  for (int c0 = kbeg; c0 < kend; c0 += kKC) {
-    // ---- 1. gather the chunk's rows into LDS ----
-    if (tid < kKC) {
-      const int kslot = c0 + tid;
-      const int p = kslot < kend ? irow[kslot] : -1;
-      kvalid[tid] = (p >= 0 && p < n_max) ? p : -1;
+  for (int c0 = 0; c0 < nk; c0 += kKC) {
+    // ---- 1. gathered rows -> LDS; prefetch the next chunk ----
+#pragma unroll
+    for (int m = 0; m < GATHER; ++m) {
+      const int it = tid + m * NT;
+      if (it < kKC * 18) raw[it] = gr[m];
     }
     __syncthreads();
-    for (int it = tid; it < kKC * 18; it += NT) {
-      const int kr = it / 18, part = it - kr * 18;
-      const int p = kvalid[kr];
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (p >= 0) v = *reinterpret_cast<const uint4*>(rbase + (int64_t)p * kRowB + 16 * part);
-      raw[it] = v;
-    }
-    __syncthreads();
+    if (c0 + kKC < nk) gather(c0 + kKC);
     // ---- 2. dequantize: item = (key pair kp, 32-channel slab cs) ----
     for (int it = tid; it < 16 * 16; it += NT) {
       const int kp = it & 15, cs = it >> 4;
-      float v0[32], v1[32];
-      decode_slab(raw, 2 * kp, cs, xb, v0);
-      decode_slab(raw, 2 * kp + 1, cs, xb, v1);
-      // f16 transposed copy: one 32-bit word (2 keys) per channel
+      uint32_t va[16], vb[16];
 #pragma unroll
-      for (int c = 0; c < 32; ++c) {
-        const _Float16 a = (_Float16)v0[c], bb = (_Float16)v1[c];
-        const uint32_t w = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, bb) << 16);
-        *reinterpret_cast<uint32_t*>(xt + (32 * cs + c) * kXtPitch + 2 * kp) = w;
+      for (int e = 0; e < 2; ++e) {
+        const int key = 2 * kp + e;
+        const uint8_t* rb = reinterpret_cast<const uint8_t*>(raw) + key * kRowB;
+        const uint4 codes = *reinterpret_cast<const uint4*>(rb + 16 * cs);
+        const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(rb + 256 + 2 * cs);
+        const _Float16 s0 = (_Float16)e4m3_value(sc2 & 0xFF), s1 = (_Float16)e4m3_value(sc2 >> 8);
+        uint32_t* v = e ? vb : va;
+        e2m1x8_to_f16(codes.x, f16x2_t{s0, s0}, v);
+        e2m1x8_to_f16(codes.y, f16x2_t{s0, s0}, v + 4);
+        e2m1x8_to_f16(codes.z, f16x2_t{s1, s1}, v + 8);
+        e2m1x8_to_f16(codes.w, f16x2_t{s1, s1}, v + 12);
+        uint4* dst = reinterpret_cast<uint4*>(xs + key * kXPitch + 32 * cs);
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) dst[qd] = make_uint4(v[4 * qd], v[4 * qd + 1], v[4 * qd + 2], v[4 * qd + 3]);
+      }
+      // transposed copy: one word = (key 2kp, key 2kp+1) for each channel
+      uint32_t* xtp = reinterpret_cast<uint32_t*>(xt + (32 * cs) * kXtPitch + 2 * kp);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        xtp[(2 * i) * (kXtPitch / 2)] = __builtin_amdgcn_perm(vb[i], va[i], 0x05040100u);
+        xtp[(2 * i + 1) * (kXtPitch / 2)] = __builtin_amdgcn_perm(vb[i], va[i], 0x07060302u);
       }
     }
     __syncthreads();
     // ---- 3. S^T = X Q^T for this wave's 16 heads ----
-    f32x4_t s[2];
+    f32x4_t sacc[2];
 #pragma unroll
     for (int tl = 0; tl < 2; ++tl) {
-      s[tl] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* xr = xb + (16 * tl + l16) * kXbPitch + 8 * g;
+      sacc[tl] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const uint16_t* xr = xs + (16 * tl + l16) * kXPitch + 8 * g;
 #pragma unroll
       for (int kk = 0; kk < 16; ++kk) {
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(xr + 32 * kk));
-        s[tl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qv[kk], s[tl], 0, 0, 0);
+        const f16x8_t a = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(xr + 32 * kk));
+        sacc[tl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qv[kk], sacc[tl], 0, 0, 0);
       }
     }
-    // ---- 4. online softmax; lane holds keys 16 tl + 4 g + i of head l16 ----
+    // ---- 4. online softmax; lane holds keys c0 + 16 tl + 4 g + i of head l16 ----
     float t[8];
     float cmax = -INFINITY;
 #pragma unroll
     for (int tl = 0; tl < 2; ++tl)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key = 16 * tl + 4 * g + i;
-        const float x = kvalid[key] >= 0 ? s[tl][i] * qscale : -INFINITY;
+        const int ks = c0 + 16 * tl + 4 * g + i;
+        const float x = (ks < nk && sidx[ks] >= 0) ? sacc[tl][i] * qscale : -INFINITY;
         t[4 * tl + i] = x;
         cmax = fmaxf(cmax, x);
       }
-    cmax = fmaxf(cmax, shfl_xor_f(cmax, 16));
-    cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
+    cmax = head_max(cmax);
     const float m_new = fmaxf(m_run, cmax);
     float psum = 0.0f;
     f16x8_t pb;
@@ -155,21 +219,21 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
 #pragma unroll
       for (int i = 0; i < 8; ++i) pb[i] = (_Float16)0.0f;
     } else {
-      const float alpha = exp2f(m_run - m_new);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const _Float16 p = (_Float16)exp2f(t[i] - m_new);
         psum += (float)p;   // normalize by the weights the f16 MFMA actually uses
         pb[i] = p;
       }
-      l_run *= alpha;
+      if (m_new != m_run) {
+        const float alpha = exp2f(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-      for (int mt = 0; mt < 32; ++mt) acc[mt] *= alpha;
-      m_run = m_new;
+        for (int mt = 0; mt < 32; ++mt) acc[mt] *= alpha;
+        m_run = m_new;
+      }
     }
-    psum += shfl_xor_f(psum, 16);
-    psum += shfl_xor_f(psum, 32);
-    l_run += psum;
+    l_run += head_sum(psum);
     // ---- 5. O^T += Xt P^T; A rows are channels, k slots are keys {4g..4g+3, 16+4g..16+4g+3} ----
 #pragma unroll
     for (int mt = 0; mt < 32; ++mt) {
@@ -179,7 +243,6 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
       const f16x8_t a = __builtin_bit_cast(f16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
       acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb, acc[mt], 0, 0, 0);
     }
-    __syncthreads();
   }
 
   // ---- epilogue: lane holds O^T[16 mt + 4 g + i][head] ----
@@ -199,6 +262,262 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
     if (g == 0) {
       part_ml[2 * prow] = m_run;
       part_ml[2 * prow + 1] = l_run;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Decode form: few query rows. A workgroup owns (query row, 16-head group, slice of entries); its
+// 4 waves share the dequantized chunk of 64 entries in LDS and each takes 16 of them, so every
+// wave keeps one running (max, sum, 16 heads x 512 channels) state and the 4 states are merged in
+// LDS at the end. This keeps the per-workgroup output at 16 heads (32 KB) instead of 64 heads,
+// so splitting a row over several workgroups moves 4x fewer partial bytes.
+// The chunk is dequantized once into X[entry][channel] (f16, exact). S^T = X Q^T runs on 16x16x32
+// f16 MFMA (16 entries x 16 heads per wave). O^T += X^T P^T runs on 16x16x16 f16 MFMA: its A
+// operand (4 consecutive entries of one channel per lane) comes straight from X through the
+// transposing LDS read ds_read_b64_tr_b16, and its B operand (4 entries of one head per lane) is
+// exactly the S^T accumulator layout. The softmax reference max is only moved when a new score
+// exceeds it by more than 2^8, so probabilities stay <= 256 (exact enough in f16) and the
+// accumulators are rescaled rarely.
+constexpr int kDKC = 64;                        // entries per chunk
+constexpr int kDSmemX = kDKC * kXPitch * 2;     // 66560
+constexpr int kDSmemMerge = 2 * 32 * 64 * 16;   // 65536: two waves' accumulators (reuses X)
+constexpr int kDSmemBig = kDSmemMerge > kDSmemX ? kDSmemMerge : kDSmemX;
+constexpr int kDSmemRaw = kDKC * kRowB;         // 18432
+constexpr int kDSmemIdx = kMaxKPS * 4;          // 4096
+constexpr int kDSmemMl = 4 * 16 * 2 * 4;        // 512
+constexpr int kDSmemQ = 16 * kXPitch * 2;       // 16640: the 16 heads' scaled f16 queries
+constexpr int kDSmem = kDSmemBig + kDSmemRaw + kDSmemIdx + kDSmemMl + kDSmemQ;
+constexpr float kLazyRescale = 8.0f;            // log2 headroom before the reference max moves
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// Two E4M3 scale bytes (low half of w) as f16 (exact: E4M3 values fit f16).
+CSA2_DEV f16x2_t e4m3x2_to_f16(uint32_t w) { return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false); }
+
+__global__ __launch_bounds__(256) void sparse_attn_decode_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ rows, int n_max,
+    const int32_t* __restrict__ idx, int T, int H, int K, int keys_per_split, float sm_scale,
+    float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
+  constexpr int NT = 256;
+  constexpr int GATHER = (kDKC * 18 + NT - 1) / NT;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kDSmem];
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
+  float* mbuf = reinterpret_cast<float*>(smem);   // merge buffer, reuses X after the loop
+  uint4* raw = reinterpret_cast<uint4*>(smem + kDSmemBig);
+  int* sidx = reinterpret_cast<int*>(smem + kDSmemBig + kDSmemRaw);
+  float* ml = reinterpret_cast<float*>(smem + kDSmemBig + kDSmemRaw + kDSmemIdx);
+  uint16_t* qs = reinterpret_cast<uint16_t*>(smem + kDSmemBig + kDSmemRaw + kDSmemIdx + kDSmemMl);
+
+  const int qr = blockIdx.x, split = blockIdx.y, hg = blockIdx.z;
+  const int n_splits = gridDim.y;
+  const int b = qr / T;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int head = hg * 16 + l16;
+
+  const int kbeg = split * keys_per_split;
+  const int kend = min(K, kbeg + keys_per_split);
+  const int nk = max(0, kend - kbeg);
+  const int32_t* irow = idx + (int64_t)qr * K + kbeg;
+  const uint8_t* rbase = rows + (int64_t)b * n_max * kRowB;
+
+  for (int i = tid; i < nk; i += NT) {
+    const int p = irow[i];
+    sidx[i] = (p >= 0 && p < n_max) ? p : -1;
+  }
+  __syncthreads();
+
+  uint4 gr[GATHER];
+  auto gather = [&](int c0) {
+#pragma unroll
+    for (int m = 0; m < GATHER; ++m) {
+      const int it = tid + m * NT;
+      gr[m] = make_uint4(0, 0, 0, 0);
+      if (it < kDKC * 18) {
+        const int kr = it / 18, part = it - kr * 18;
+        const int ks = c0 + kr;
+        const int p = ks < nk ? sidx[ks] : -1;
+        if (p >= 0) gr[m] = *reinterpret_cast<const uint4*>(rbase + (int64_t)p * kRowB + 16 * part);
+      }
+    }
+  };
+  if (nk > 0) gather(0);
+
+  // the 16 heads' queries, scaled per head by a power of two and converted to f16, into LDS
+  // (every wave computes the scale; wave w writes channel quarter w)
+  float qscale;
+  {
+    const uint4* qp = reinterpret_cast<const uint4*>(q + ((int64_t)qr * H + head) * kD);
+    uint4 raw_q[16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      raw_q[kk] = qp[4 * kk + g];
+      const uint32_t w[4] = {raw_q[kk].x, raw_q[kk].y, raw_q[kk].z, raw_q[kk].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w[e] << 16)), fabsf(__uint_as_float(w[e] & 0xFFFF0000u))));
+    }
+    amax = head_max(amax);
+    const int qe = amax > 0.0f ? 14 - ilogbf(amax) : 0;
+    const float sc = ldexpf(1.0f, qe);
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq) {
+      const int kk = 4 * wave + kq;
+      const uint32_t w[4] = {raw_q[kk].x, raw_q[kk].y, raw_q[kk].z, raw_q[kk].w};
+      f16x8_t h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h[2 * e] = (_Float16)(__uint_as_float(w[e] << 16) * sc);
+        h[2 * e + 1] = (_Float16)(__uint_as_float(w[e] & 0xFFFF0000u) * sc);
+      }
+      *reinterpret_cast<f16x8_t*>(qs + l16 * kXPitch + 32 * kk + 8 * g) = h;
+    }
+    qscale = sm_scale * kLog2e * ldexpf(1.0f, -qe);
+  }
+
+  f32x4_t acc[32];
+#pragma unroll
+  for (int mt = 0; mt < 32; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;
+  // transposing-read base of this lane for the P.V operand: entry 16 wave + 4 g + l16/4, channel 4 (l16%4)
+  const uint16_t* xtr = xs + (16 * wave + 4 * g + (l16 >> 2)) * kXPitch + 4 * (l16 & 3);
+
+  for (int c0 = 0; c0 < nk; c0 += kDKC) {
+#pragma unroll
+    for (int m = 0; m < GATHER; ++m) {
+      const int it = tid + m * NT;
+      if (it < kDKC * 18) raw[it] = gr[m];
+    }
+    __syncthreads();
+    if (c0 + kDKC < nk) gather(c0 + kDKC);
+    // dequantize: item = (entry 0..63, 64-channel slab 0..7)
+    for (int it = tid; it < kDKC * 8; it += NT) {
+      const int key = it & 63, cs = it >> 6;
+      const uint8_t* rb = reinterpret_cast<const uint8_t*>(raw) + key * kRowB;
+      const uint4 c01 = *reinterpret_cast<const uint4*>(rb + 32 * cs);
+      const uint4 c23 = *reinterpret_cast<const uint4*>(rb + 32 * cs + 16);
+      const uint32_t sc4 = *reinterpret_cast<const uint32_t*>(rb + 256 + 4 * cs);
+      const f16x2_t s01 = e4m3x2_to_f16(sc4), s23 = e4m3x2_to_f16(sc4 >> 16);
+      const f16x2_t sg[4] = {f16x2_t{s01[0], s01[0]}, f16x2_t{s01[1], s01[1]}, f16x2_t{s23[0], s23[0]},
+                             f16x2_t{s23[1], s23[1]}};
+      const uint32_t cw[8] = {c01.x, c01.y, c01.z, c01.w, c23.x, c23.y, c23.z, c23.w};
+      uint4* dst = reinterpret_cast<uint4*>(xs + key * kXPitch + 64 * cs);
+#pragma unroll
+      for (int wi = 0; wi < 8; ++wi) {
+        uint32_t v[4];
+        e2m1x8_to_f16(cw[wi], sg[wi >> 1], v);
+        dst[wi] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+    }
+    __syncthreads();
+    // S^T for this wave's 16 entries (chunk entries 16 wave .. 16 wave + 15) x 16 heads
+    f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    {
+      const uint16_t* xr = xs + (16 * wave + l16) * kXPitch + 8 * g;
+      const uint16_t* qr16 = qs + l16 * kXPitch + 8 * g;
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) {
+        const f16x8_t a = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(xr + 32 * kk));
+        const f16x8_t bq = *reinterpret_cast<const f16x8_t*>(qr16 + 32 * kk);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq, sacc, 0, 0, 0);
+      }
+    }
+    // online softmax: lane holds entries 16 wave + 4 g + i of head l16
+    float t[4];
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ks = c0 + 16 * wave + 4 * g + i;
+      t[i] = (ks < nk && sidx[ks] >= 0) ? sacc[i] * qscale : -INFINITY;
+      cmax = fmaxf(cmax, t[i]);
+    }
+    cmax = head_max(cmax);
+    if (m_run == -INFINITY) {
+      m_run = cmax;                 // first entries of this head: nothing accumulated yet
+    } else if (__builtin_expect(__ballot(cmax > m_run + kLazyRescale) != 0, 0)) {
+      const float mn = fmaxf(m_run, cmax);
+      const float alpha = exp2f(m_run - mn);
+      l_run *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < 32; ++mt) acc[mt] *= alpha;
+      m_run = mn;
+    }
+    float psum = 0.0f;
+    f16x4_t pb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const _Float16 pv = m_run == -INFINITY ? (_Float16)0.0f : (_Float16)exp2f(t[i] - m_run);
+      psum += (float)pv;
+      pb[i] = pv;
+    }
+    l_run += head_sum(psum);
+    // O^T += X^T P^T over this wave's 16 entries; A via the transposing LDS read
+#pragma unroll
+    for (int mt = 0; mt < 32; ++mt) {
+      const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(xtr + 16 * mt));
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), pb, acc[mt], 0, 0, 0);
+    }
+  }
+
+  // ---- merge the 4 waves' states ----
+  __syncthreads();                                   // everyone is done with X
+  if (g == 0) {
+    ml[(wave * 16 + l16) * 2] = m_run;
+    ml[(wave * 16 + l16) * 2 + 1] = l_run;
+  }
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, ml[(w * 16 + l16) * 2]);
+  float L = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float mw = ml[(w * 16 + l16) * 2];
+    if (mw != -INFINITY) L += exp2f(mw - M) * ml[(w * 16 + l16) * 2 + 1];
+  }
+  const float f = m_run != -INFINITY ? exp2f(m_run - M) : 0.0f;
+#pragma unroll
+  for (int mt = 0; mt < 32; ++mt) acc[mt] *= f;
+  // pairwise merge through LDS, layout [slot][mt][lane][4]: waves 2,3 -> 0,1, then 1 -> 0
+  float4* mb = reinterpret_cast<float4*>(mbuf);
+  if (wave >= 2)
+#pragma unroll
+    for (int mt = 0; mt < 32; ++mt) mb[((wave - 2) * 32 + mt) * 64 + lane] = make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
+  __syncthreads();
+  if (wave < 2)
+#pragma unroll
+    for (int mt = 0; mt < 32; ++mt) {
+      const float4 v = mb[(wave * 32 + mt) * 64 + lane];
+      acc[mt] += f32x4_t{v.x, v.y, v.z, v.w};
+    }
+  __syncthreads();
+  if (wave == 1)
+#pragma unroll
+    for (int mt = 0; mt < 32; ++mt) mb[mt * 64 + lane] = make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
+  __syncthreads();
+  const int64_t orow = (int64_t)qr * H + head;
+  const bool final_out = n_splits == 1;
+  if (wave == 0) {
+    const float inv = final_out ? (L > 0.0f ? 1.0f / L : 0.0f) : 1.0f;
+    float* dst = final_out ? out + orow * kD : part_o + ((int64_t)split * gridDim.x * H + orow) * kD;
+#pragma unroll
+    for (int mt = 0; mt < 32; ++mt) {
+      const float4 v = mb[mt * 64 + lane];
+      reinterpret_cast<float4*>(dst)[4 * mt + g] =
+          make_float4((acc[mt][0] + v.x) * inv, (acc[mt][1] + v.y) * inv, (acc[mt][2] + v.z) * inv, (acc[mt][3] + v.w) * inv);
+    }
+  }
+  if (wave == 0 && g == 0) {
+    if (final_out) {
+      if (lse) lse[orow] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    } else {
+      const int64_t prow = (int64_t)split * gridDim.x * H + orow;
+      part_ml[2 * prow] = M;
+      part_ml[2 * prow + 1] = L;
     }
   }
 }
@@ -236,7 +555,15 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   if (lse && lane == 0) lse[rh] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
+// Decode form for few query rows (16 heads per workgroup), wide form otherwise (64 heads).
+static bool use_decode_form(int B, int T) { return (int64_t)B * T < 512; }
+
 static int attn_splits(int B, int T, int H, int K) {
+  if (use_decode_form(B, T)) {
+    const int64_t wgs = (int64_t)B * T * (H / 16);
+    const int by_fill = (int)std::max<int64_t>(1, (256 + wgs - 1) / wgs);
+    return std::max(1, std::min((K + kDKC - 1) / kDKC, by_fill));
+  }
   const int hpw = H >= 64 ? 64 : H;
   const int64_t wgs = (int64_t)B * T * (H / hpw);
   if (wgs >= 256 || K <= 2 * kKC) return 1;
@@ -244,8 +571,18 @@ static int attn_splits(int B, int T, int H, int K) {
   return std::max(1, splits);
 }
 
+static int split_count(int B, int T, int H, int K, int* kps_out) {
+  const int chunk = use_decode_form(B, T) ? kDKC : kKC;
+  const int sp = std::max(attn_splits(B, T, H, K), (K + kMaxKPS - 1) / kMaxKPS);
+  int kps = (K + sp - 1) / sp;
+  kps = std::max(chunk, (kps + chunk - 1) / chunk * chunk);
+  kps = std::min(kps, kMaxKPS);
+  if (kps_out) *kps_out = kps;
+  return std::max(1, (K + kps - 1) / kps);
+}
+
 size_t attn_workspace(int B, int T, int H, int D, int K) {
-  const int sp = attn_splits(B, T, H, K);
+  const int sp = split_count(B, T, H, K, nullptr);
   if (sp == 1) return 0;
   const size_t rows_h = (size_t)B * T * H;
   return sp * rows_h * (size_t)D * 4 + sp * rows_h * 8 + 256;
@@ -256,23 +593,27 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* rows, int n_max,
                               float* lse, void* ws, hipStream_t s) {
   const int64_t nq = (int64_t)B * T;
   if (nq == 0 || H == 0) return hipSuccess;
-  const int sp = attn_splits(B, T, H, K);
-  int kps = (K + sp - 1) / sp;
-  kps = std::max(kKC, (kps + kKC - 1) / kKC * kKC);
-  const int n_splits = std::max(1, (K + kps - 1) / kps);
-  const int hpw = H >= 64 ? 64 : H;
+  int kps = 0;
+  const int n_splits = split_count(B, T, H, K, &kps);
   float* part_o = nullptr;
   float* part_ml = nullptr;
   if (n_splits > 1) {
     part_o = static_cast<float*>(ws);
     part_ml = part_o + (size_t)n_splits * nq * H * kD;
   }
-  dim3 grid((unsigned)nq, (unsigned)n_splits, (unsigned)(H / hpw));
-  switch (hpw / 16) {
-    case 1: hipLaunchKernelGGL(sparse_attn_kernel<1>, grid, dim3(64), 0, s, q, rows, n_max, idx, T, H, K, kps, sm_scale, out, lse, part_o, part_ml); break;
-    case 2: hipLaunchKernelGGL(sparse_attn_kernel<2>, grid, dim3(128), 0, s, q, rows, n_max, idx, T, H, K, kps, sm_scale, out, lse, part_o, part_ml); break;
-    case 3: hipLaunchKernelGGL(sparse_attn_kernel<3>, grid, dim3(192), 0, s, q, rows, n_max, idx, T, H, K, kps, sm_scale, out, lse, part_o, part_ml); break;
-    default: hipLaunchKernelGGL(sparse_attn_kernel<4>, grid, dim3(256), 0, s, q, rows, n_max, idx, T, H, K, kps, sm_scale, out, lse, part_o, part_ml); break;
+  if (use_decode_form(B, T)) {
+    dim3 grid((unsigned)nq, (unsigned)n_splits, (unsigned)(H / 16));
+    hipLaunchKernelGGL(sparse_attn_decode_kernel, grid, dim3(256), 0, s, q, rows, n_max, idx, T, H, K, kps,
+                       sm_scale, out, lse, part_o, part_ml);
+  } else {
+    const int hpw = H >= 64 ? 64 : H;
+    dim3 grid((unsigned)nq, (unsigned)n_splits, (unsigned)(H / hpw));
+    switch (hpw / 16) {
+      case 1: hipLaunchKernelGGL(sparse_attn_kernel<1>, grid, dim3(64), 0, s, q, rows, n_max, idx, T, H, K, kps, sm_scale, out, lse, part_o, part_ml); break;
+      case 2: hipLaunchKernelGGL(sparse_attn_kernel<2>, grid, dim3(128), 0, s, q, rows, n_max, idx, T, H, K, kps, sm_scale, out, lse, part_o, part_ml); break;
+      case 3: hipLaunchKernelGGL(sparse_attn_kernel<3>, grid, dim3(192), 0, s, q, rows, n_max, idx, T, H, K, kps, sm_scale, out, lse, part_o, part_ml); break;
+      default: hipLaunchKernelGGL(sparse_attn_kernel<4>, grid, dim3(256), 0, s, q, rows, n_max, idx, T, H, K, kps, sm_scale, out, lse, part_o, part_ml); break;
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_splits == 1) return e;

@@ -123,6 +123,7 @@ csa2_status csa2_index_scores(const uint16_t* q_idx, const uint16_t* k_idx, int3
  * -0.0 and +0.0 are equal scores. The result is deterministic.
  *
  * scores     [rows, n_cols] fp32.     idx  [rows, k] int32, written.
+ * Limits     k <= 4096, n_cols <= 2^26 (CSA2_E_SHAPE otherwise).
  * ws         scratch of csa2_topk_workspace_size() bytes (may be NULL if that size is 0).
  * ------------------------------------------------------------------------------------------ */
 size_t csa2_topk_workspace_size(int64_t rows, int32_t n_cols, int32_t k);
@@ -142,6 +143,7 @@ csa2_status csa2_topk(const float* scores, int64_t rows, int32_t n_cols, const i
  * pool       [rows, n_sel_blocks * block] int32, written: the visible positions of the chosen
  *            blocks (block ties broken by block index) in ascending order, then -1.
  * ws         scratch of csa2_hier_pool_workspace_size() bytes.
+ * Limits     n_sel_blocks <= 4096, block <= 64.
  * ------------------------------------------------------------------------------------------ */
 size_t csa2_hier_pool_workspace_size(int64_t rows, int32_t n_blocks, int32_t n_sel_blocks);
 csa2_status csa2_hier_pool(const float* block_max, int64_t rows, int32_t n_blocks,

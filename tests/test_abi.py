@@ -75,7 +75,7 @@ def test_index_scores_validation(L):
 
 def test_topk_and_pool_validation(L):
     assert L.csa2_topk(None, -1, 10, None, None, 4, None, None, 0, None) == E_ARG
-    assert L.csa2_topk(None, 2, 10, None, None, 9000, None, None, 0, None) == E_SHAPE
+    assert L.csa2_topk(None, 2, 10, None, None, 5000, None, None, 0, None) == E_SHAPE
     assert L.csa2_topk(None, 2, 10, None, None, 4, None, None, 0, None) == E_ARG
     assert L.csa2_topk(None, 0, 10, None, None, 4, None, None, 0, None) == OK
     need = L.csa2_topk_workspace_size(4, 262144, 512)

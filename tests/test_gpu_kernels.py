@@ -220,7 +220,8 @@ def _attn_ref(rows, qb, idx, scale):
 
 @pytest.mark.parametrize("B,T,H,N,K", [(2, 1, 64, 300, 512), (3, 1, 64, 1000, 100), (1, 3, 16, 200, 33),
                                        (2, 2, 32, 90, 64), (1, 1, 128, 500, 256), (1, 1, 48, 70, 31),
-                                       (4, 1, 64, 2000, 1), (1, 40, 64, 600, 96)])
+                                       (4, 1, 64, 2000, 1), (1, 40, 64, 600, 96), (1, 600, 64, 300, 70),
+                                       (2, 1, 16, 5000, 1024), (1, 1, 64, 3000, 2048)])
 def test_sparse_attn(B, T, H, N, K):
     rows, qb, idx = _attn_case(B, T, H, N, K, seed=B * 1000 + N + K, oob=True)
     scale = 1 / np.sqrt(512)
