@@ -324,14 +324,9 @@ __global__ __launch_bounds__(256) void sparse_attn_decode_kernel(
   const int32_t* irow = idx + (int64_t)qr * K + kbeg;
   const uint8_t* rbase = rows + (int64_t)b * n_max * kRowB;
 
-  for (int i = tid; i < nk; i += NT) {
-    const int p = irow[i];
-    sidx[i] = (p >= 0 && p < n_max) ? p : -1;
-  }
-  __syncthreads();
-
   uint4 gr[GATHER];
-  auto gather = [&](int c0) {
+  // gather of one chunk into registers; entry positions from LDS (or, for chunk 0, from global)
+  auto gather = [&](int c0, bool from_global) {
 #pragma unroll
     for (int m = 0; m < GATHER; ++m) {
       const int it = tid + m * NT;
@@ -339,35 +334,46 @@ __global__ __launch_bounds__(256) void sparse_attn_decode_kernel(
       if (it < kDKC * 18) {
         const int kr = it / 18, part = it - kr * 18;
         const int ks = c0 + kr;
-        const int p = ks < nk ? sidx[ks] : -1;
+        int p = -1;
+        if (ks < nk) {
+          p = from_global ? irow[ks] : sidx[ks];
+          if (p >= n_max) p = -1;
+        }
         if (p >= 0) gr[m] = *reinterpret_cast<const uint4*>(rbase + (int64_t)p * kRowB + 16 * part);
       }
     }
   };
-  if (nk > 0) gather(0);
-
-  // the 16 heads' queries, scaled per head by a power of two and converted to f16, into LDS
-  // (every wave computes the scale; wave w writes channel quarter w)
+  if (nk > 0) gather(0, true);
+  // this wave's quarter of the 16 heads' queries (channel blocks 4 wave .. 4 wave + 3)
+  const uint4* qp = reinterpret_cast<const uint4*>(q + ((int64_t)qr * H + head) * kD);
+  uint4 raw_q[4];
+#pragma unroll
+  for (int kq = 0; kq < 4; ++kq) raw_q[kq] = qp[4 * (4 * wave + kq) + g];
+  for (int i = tid; i < nk; i += NT) {
+    const int p = irow[i];
+    sidx[i] = (p >= 0 && p < n_max) ? p : -1;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int kq = 0; kq < 4; ++kq) {
+    const uint32_t w[4] = {raw_q[kq].x, raw_q[kq].y, raw_q[kq].z, raw_q[kq].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w[e] << 16)), fabsf(__uint_as_float(w[e] & 0xFFFF0000u))));
+  }
+  amax = head_max(amax);
+  if (g == 0) ml[wave * 16 + l16] = amax;
+  __syncthreads();
+  // the queries, scaled per head by a power of two and converted to f16 (exact), into LDS
   float qscale;
   {
-    const uint4* qp = reinterpret_cast<const uint4*>(q + ((int64_t)qr * H + head) * kD);
-    uint4 raw_q[16];
-    float amax = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      raw_q[kk] = qp[4 * kk + g];
-      const uint32_t w[4] = {raw_q[kk].x, raw_q[kk].y, raw_q[kk].z, raw_q[kk].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w[e] << 16)), fabsf(__uint_as_float(w[e] & 0xFFFF0000u))));
-    }
-    amax = head_max(amax);
+    amax = fmaxf(fmaxf(ml[l16], ml[16 + l16]), fmaxf(ml[32 + l16], ml[48 + l16]));
     const int qe = amax > 0.0f ? 14 - ilogbf(amax) : 0;
     const float sc = ldexpf(1.0f, qe);
 #pragma unroll
     for (int kq = 0; kq < 4; ++kq) {
       const int kk = 4 * wave + kq;
-      const uint32_t w[4] = {raw_q[kk].x, raw_q[kk].y, raw_q[kk].z, raw_q[kk].w};
+      const uint32_t w[4] = {raw_q[kq].x, raw_q[kq].y, raw_q[kq].z, raw_q[kq].w};
       f16x8_t h;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -393,7 +399,7 @@ __global__ __launch_bounds__(256) void sparse_attn_decode_kernel(
       if (it < kDKC * 18) raw[it] = gr[m];
     }
     __syncthreads();
-    if (c0 + kDKC < nk) gather(c0 + kDKC);
+    if (c0 + kDKC < nk) gather(c0 + kDKC, false);
     // dequantize: item = (entry 0..63, 64-channel slab 0..7)
     for (int it = tid; it < kDKC * 8; it += NT) {
       const int key = it & 63, cs = it >> 6;
@@ -415,16 +421,22 @@ __global__ __launch_bounds__(256) void sparse_attn_decode_kernel(
     }
     __syncthreads();
     // S^T for this wave's 16 entries (chunk entries 16 wave .. 16 wave + 15) x 16 heads
-    f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t sacc;
     {
+      // two independent accumulation chains halve the MFMA dependency latency
+      f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;
       const uint16_t* xr = xs + (16 * wave + l16) * kXPitch + 8 * g;
       const uint16_t* qr16 = qs + l16 * kXPitch + 8 * g;
 #pragma unroll
-      for (int kk = 0; kk < 16; ++kk) {
-        const f16x8_t a = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(xr + 32 * kk));
-        const f16x8_t bq = *reinterpret_cast<const f16x8_t*>(qr16 + 32 * kk);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq, sacc, 0, 0, 0);
+      for (int kk = 0; kk < 16; kk += 2) {
+        const f16x8_t a0 = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(xr + 32 * kk));
+        const f16x8_t b0 = *reinterpret_cast<const f16x8_t*>(qr16 + 32 * kk);
+        const f16x8_t a1 = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(xr + 32 * kk + 32));
+        const f16x8_t b1 = *reinterpret_cast<const f16x8_t*>(qr16 + 32 * kk + 32);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, s1, 0, 0, 0);
       }
+      sacc = s0 + s1;
     }
     // online softmax: lane holds entries 16 wave + 4 g + i of head l16
     float t[4];
@@ -480,36 +492,33 @@ __global__ __launch_bounds__(256) void sparse_attn_decode_kernel(
     if (mw != -INFINITY) L += exp2f(mw - M) * ml[(w * 16 + l16) * 2 + 1];
   }
   const float f = m_run != -INFINITY ? exp2f(m_run - M) : 0.0f;
-#pragma unroll
-  for (int mt = 0; mt < 32; ++mt) acc[mt] *= f;
-  // pairwise merge through LDS, layout [slot][mt][lane][4]: waves 2,3 -> 0,1, then 1 -> 0
-  float4* mb = reinterpret_cast<float4*>(mbuf);
-  if (wave >= 2)
-#pragma unroll
-    for (int mt = 0; mt < 32; ++mt) mb[((wave - 2) * 32 + mt) * 64 + lane] = make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
-  __syncthreads();
-  if (wave < 2)
-#pragma unroll
-    for (int mt = 0; mt < 32; ++mt) {
-      const float4 v = mb[(wave * 32 + mt) * 64 + lane];
-      acc[mt] += f32x4_t{v.x, v.y, v.z, v.w};
-    }
-  __syncthreads();
-  if (wave == 1)
-#pragma unroll
-    for (int mt = 0; mt < 32; ++mt) mb[mt * 64 + lane] = make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
-  __syncthreads();
   const int64_t orow = (int64_t)qr * H + head;
   const bool final_out = n_splits == 1;
-  if (wave == 0) {
-    const float inv = final_out ? (L > 0.0f ? 1.0f / L : 0.0f) : 1.0f;
-    float* dst = final_out ? out + orow * kD : part_o + ((int64_t)split * gridDim.x * H + orow) * kD;
+  const float scale = f * (final_out ? (L > 0.0f ? 1.0f / L : 0.0f) : 1.0f);
+  float* dst = final_out ? out + orow * kD : part_o + ((int64_t)split * gridDim.x * H + orow) * kD;
+  // two rounds of 16 channel tiles: every wave stores its scaled tiles, then sums 4 of them over
+  // the 4 waves and writes them out. Layout [wave][tile][lane][4].
+  float4* mb = reinterpret_cast<float4*>(mbuf);
 #pragma unroll
-    for (int mt = 0; mt < 32; ++mt) {
-      const float4 v = mb[mt * 64 + lane];
-      reinterpret_cast<float4*>(dst)[4 * mt + g] =
-          make_float4((acc[mt][0] + v.x) * inv, (acc[mt][1] + v.y) * inv, (acc[mt][2] + v.z) * inv, (acc[mt][3] + v.w) * inv);
+  for (int r = 0; r < 2; ++r) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const f32x4_t v = acc[16 * r + j] * scale;
+      mb[(wave * 16 + j) * 64 + lane] = make_float4(v[0], v[1], v[2], v[3]);
     }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tj = 4 * wave + j;
+      float4 o = mb[tj * 64 + lane];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        const float4 v = mb[(w * 16 + tj) * 64 + lane];
+        o.x += v.x; o.y += v.y; o.z += v.z; o.w += v.w;
+      }
+      reinterpret_cast<float4*>(dst)[4 * (16 * r + tj) + g] = o;
+    }
+    __syncthreads();
   }
   if (wave == 0 && g == 0) {
     if (final_out) {
@@ -522,7 +531,9 @@ __global__ __launch_bounds__(256) void sparse_attn_decode_kernel(
   }
 }
 
-// Merge of split results: one wave per (query row, head), lane owns 8 channels.
+// Merge of split results: one wave per (query row, head), lane owns 8 channels. All splits'
+// (max, sum) pairs are read first, then every split's partial row is loaded in one batch.
+constexpr int kMaxSplits = 64;
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
                                                            int n_splits, int64_t n_rows_h,
@@ -531,21 +542,41 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   const int lane = threadIdx.x & 63;
   const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (rh >= n_rows_h) return;
-  float M = -INFINITY;
-  for (int sp = 0; sp < n_splits; ++sp) M = fmaxf(M, part_ml[2 * (sp * n_rows_h + rh)]);
+  // lane s < n_splits holds split s's (m, l)
+  float ms = -INFINITY, ls = 0.0f;
+  if (lane < n_splits) {
+    ms = part_ml[2 * (lane * n_rows_h + rh)];
+    ls = part_ml[2 * (lane * n_rows_h + rh) + 1];
+  }
+  float M = ms;
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  const float w_lane = (ms == -INFINITY) ? 0.0f : exp2f(ms - M);
+  float L = w_lane * ls;
+  for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off, 64);
   float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  float L = 0.0f;
   if (M != -INFINITY) {
-    for (int sp = 0; sp < n_splits; ++sp) {
-      const int64_t pr = sp * n_rows_h + rh;
-      const float m = part_ml[2 * pr];
-      if (m == -INFINITY) continue;
-      const float w = exp2f(m - M);
-      L += w * part_ml[2 * pr + 1];
-      const float4* pp = reinterpret_cast<const float4*>(part_o + pr * kD) + 2 * lane;
-      const float4 a = pp[0], c = pp[1];
-      o[0] += w * a.x; o[1] += w * a.y; o[2] += w * a.z; o[3] += w * a.w;
-      o[4] += w * c.x; o[5] += w * c.y; o[6] += w * c.z; o[7] += w * c.w;
+    for (int s0 = 0; s0 < n_splits; s0 += 8) {
+      float4 a[8], c[8];
+      float w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int sp = s0 + u;
+        w[u] = __shfl(w_lane, sp < n_splits ? sp : 0, 64);
+        if (sp < n_splits) {
+          const float4* pp = reinterpret_cast<const float4*>(part_o + (sp * n_rows_h + rh) * kD) + 2 * lane;
+          a[u] = pp[0];
+          c[u] = pp[1];
+        } else {
+          w[u] = 0.0f;
+          a[u] = c[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (w[u] == 0.0f) continue;
+        o[0] += w[u] * a[u].x; o[1] += w[u] * a[u].y; o[2] += w[u] * a[u].z; o[3] += w[u] * a[u].w;
+        o[4] += w[u] * c[u].x; o[5] += w[u] * c[u].y; o[6] += w[u] * c[u].z; o[7] += w[u] * c[u].w;
+      }
     }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
@@ -577,6 +608,9 @@ static int split_count(int B, int T, int H, int K, int* kps_out) {
   int kps = (K + sp - 1) / sp;
   kps = std::max(chunk, (kps + chunk - 1) / chunk * chunk);
   kps = std::min(kps, kMaxKPS);
+  // the merge kernel reads at most kMaxSplits splits
+  const int min_kps = (K + kMaxSplits - 1) / kMaxSplits;
+  if (kps < min_kps) kps = (min_kps + chunk - 1) / chunk * chunk;
   if (kps_out) *kps_out = kps;
   return std::max(1, (K + kps - 1) / kps);
 }
