@@ -134,21 +134,27 @@ def test_index_scores_pool():
         check_scores(s[b][valid], ref[valid], ad[clean[valid]], np.ones(valid.sum(), bool), f"pool b={b}")
 
 
-@pytest.mark.parametrize("B,T,N,p0,ratio", [(1, 200, 700, 2500, 4), (2, 64, 130, 0, 1), (1, 300, 5000, 19000, 4)])
-def test_index_scores_prefill_mfma(B, T, N, p0, ratio):
-    g = np.random.default_rng(T + N)
-    qb = W.to_bf16_bits(g.standard_normal((B, T, 8, 64)).astype(np.float32))
-    kb = W.to_bf16_bits(g.standard_normal((B, N, 8, 64)).astype(np.float32))
+@pytest.mark.parametrize("B,T,N,p0,ratio,Hi", [
+    (1, 200, 700, 2500, 4, 8), (2, 64, 130, 0, 1, 8), (1, 300, 5000, 19000, 4, 8),
+    (1, 520, 3000, 9000, 4, 4),      # 256 channels, three query slabs, ragged
+    (2, 100, 900, 400, 4, 2),        # 128 channels: tiled form
+    (1, 260, 1200, 2000, 4, 6)])     # 384 channels: tiled form, ragged
+def test_index_scores_prefill_mfma(B, T, N, p0, ratio, Hi):
+    g = np.random.default_rng(T + N + Hi)
+    qb = W.to_bf16_bits(g.standard_normal((B, T, Hi, 64)).astype(np.float32))
+    kb = W.to_bf16_bits(g.standard_normal((B, N, Hi, 64)).astype(np.float32))
     nv = P.prefill_n_vis(p0, T, ratio, "cuda")
     nv_ref = O.prefill_n_vis(p0, T, ratio)
     assert np.array_equal(nv.cpu().numpy(), nv_ref)
     nv_all = torch.cat([torch.clamp(nv, max=N)] * B)
-    s = _sync_np(P.index_scores(dev_bf16(qb), dev_bf16(kb), n_vis=nv_all))
+    out = torch.full((B * T, N), float("nan"), device="cuda")
+    s = _sync_np(P.index_scores(dev_bf16(qb), dev_bf16(kb), n_vis=nv_all, out=out))
     for b in range(B):
         nvb = np.minimum(nv_ref, N)
         ref = O.index_scores(f64(qb[b]), f64(kb[b]), nvb)
         mask = np.arange(N)[None, :] < nvb[:, None]
         check_scores(s[b * T:(b + 1) * T], ref, _abs_dot(f64(qb[b]), f64(kb[b])), mask, f"prefill b={b}")
+        assert np.all(np.isnan(s[b * T:(b + 1) * T][~mask])), "slots past n_vis must stay unwritten"
 
 
 # ---------------------------------------------------------------------------------------------
