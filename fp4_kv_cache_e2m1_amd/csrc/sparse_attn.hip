@@ -267,28 +267,38 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// Decode form: few query rows. A workgroup owns (query row, 16-head group, slice of entries); its
-// 4 waves share the dequantized chunk of 64 entries in LDS and each takes 16 of them, so every
-// wave keeps one running (max, sum, 16 heads x 512 channels) state and the 4 states are merged in
-// LDS at the end. This keeps the per-workgroup output at 16 heads (32 KB) instead of 64 heads,
-// so splitting a row over several workgroups moves 4x fewer partial bytes.
-// The chunk is dequantized once into X[entry][channel] (f16, exact). S^T = X Q^T runs on 16x16x32
-// f16 MFMA (16 entries x 16 heads per wave). O^T += X^T P^T runs on 16x16x16 f16 MFMA: its A
-// operand (4 consecutive entries of one channel per lane) comes straight from X through the
-// transposing LDS read ds_read_b64_tr_b16, and its B operand (4 entries of one head per lane) is
-// exactly the S^T accumulator layout. The softmax reference max is only moved when a new score
-// exceeds it by more than 2^8, so probabilities stay <= 256 (exact enough in f16) and the
-// accumulators are rescaled rarely.
-constexpr int kDKC = 64;                        // entries per chunk
-constexpr int kDSmemX = kDKC * kXPitch * 2;     // 66560
-constexpr int kDSmemMerge = 2 * 32 * 64 * 16;   // 65536: two waves' accumulators (reuses X)
-constexpr int kDSmemBig = kDSmemMerge > kDSmemX ? kDSmemMerge : kDSmemX;
-constexpr int kDSmemRaw = kDKC * kRowB;         // 18432
-constexpr int kDSmemIdx = kMaxKPS * 4;          // 4096
-constexpr int kDSmemMl = 4 * 16 * 2 * 4;        // 512
-constexpr int kDSmemQ = 16 * kXPitch * 2;       // 16640: the 16 heads' scaled f16 queries
-constexpr int kDSmem = kDSmemBig + kDSmemRaw + kDSmemIdx + kDSmemMl + kDSmemQ;
+// Decode form: few query rows. A workgroup owns (query row, 16-head group, slice of entries) and
+// walks the slice in chunks of KC entries that its 4 waves share in LDS. Wave w owns channels
+// 128w .. 128w+127 throughout:
+//   - the chunk is dequantized once into X[entry][channel] (f16, exact);
+//   - scores: each wave computes partial S^T = X Q^T over its own 128 channels for all KC
+//     entries x 16 heads (16x16x32 f16 MFMA) and writes them to a small LDS tile; after one
+//     barrier every wave adds the 4 partials, so all waves hold the same complete scores;
+//   - every wave runs the same online softmax (identical inputs and arithmetic, so the running
+//     (max, sum) agree across waves), then O^T += X^T P^T for its 128 channels over the chunk
+//     (16x16x16 f16 MFMA). The A operand (4 consecutive entries of one channel per lane) comes
+//     straight from X through the transposing LDS read ds_read_b64_tr_b16; the B operand (4
+//     entries of one head per lane) is the lane's own softmax output.
+// Waves never exchange accumulators: each writes its own channels. The gathers of the next PF
+// chunks are in flight while a chunk is processed (the query is loaded first, so it does not
+// queue behind them). Workgroups are placed so that all of a query row's run on one XCD and share
+// its L2. The softmax reference max is only moved when a new score exceeds it by more than 2^8,
+// so probabilities stay <= 256 (exact enough in f16) and the accumulators are rescaled rarely.
 constexpr float kLazyRescale = 8.0f;            // log2 headroom before the reference max moves
+constexpr int kDKC = 64;                        // decode entries per chunk
+constexpr int kDPF = 2;                         // decode chunks gathered ahead
+constexpr int kDecodeFill = 256;                // decode workgroups wanted: one per CU
+
+template <int KC>
+struct DecodeSmem {
+  static constexpr int kX = KC * kXPitch * 2;
+  static constexpr int kRaw = KC * kRowB;
+  static constexpr int kIdx = kMaxKPS * 4;
+  static constexpr int kS = 4 * KC * 16 * 4;    // the 4 waves' partial scores, KC entries x 16 heads
+  static constexpr int kMl = 4 * 16 * 4;
+  static constexpr int kQ = 16 * kXPitch * 2;   // the 16 heads' scaled f16 queries
+  static constexpr int kTotal = kX + kRaw + kIdx + kS + kMl + kQ;
+};
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
@@ -296,23 +306,31 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 // Two E4M3 scale bytes (low half of w) as f16 (exact: E4M3 values fit f16).
 CSA2_DEV f16x2_t e4m3x2_to_f16(uint32_t w) { return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false); }
 
+template <int KC, int PF>
 __global__ __launch_bounds__(256) void sparse_attn_decode_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ rows, int n_max,
     const int32_t* __restrict__ idx, int T, int H, int K, int keys_per_split, float sm_scale,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
-    float* __restrict__ part_ml) {
-  constexpr int NT = 256;
-  constexpr int GATHER = (kDKC * 18 + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kDSmem];
+    float* __restrict__ part_ml, int n_rows, int n_splits, int per_xcd) {
+  using Sm = DecodeSmem<KC>;
+  constexpr int NT = 256, NS = KC / 16;         // NS entry steps of 16 per chunk
+  static_assert(KC % 16 == 0 && (KC * 8) % NT == 0 && KC <= 64, "dequant items must tile the workgroup");
+  constexpr int GATHER = (KC * 18 + NT - 1) / NT;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[Sm::kTotal];
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-  float* mbuf = reinterpret_cast<float*>(smem);   // merge buffer, reuses X after the loop
-  uint4* raw = reinterpret_cast<uint4*>(smem + kDSmemBig);
-  int* sidx = reinterpret_cast<int*>(smem + kDSmemBig + kDSmemRaw);
-  float* ml = reinterpret_cast<float*>(smem + kDSmemBig + kDSmemRaw + kDSmemIdx);
-  uint16_t* qs = reinterpret_cast<uint16_t*>(smem + kDSmemBig + kDSmemRaw + kDSmemIdx + kDSmemMl);
+  uint4* raw = reinterpret_cast<uint4*>(smem + Sm::kX);
+  int* sidx = reinterpret_cast<int*>(smem + Sm::kX + Sm::kRaw);
+  float4* sp4 = reinterpret_cast<float4*>(smem + Sm::kX + Sm::kRaw + Sm::kIdx);
+  float* ml = reinterpret_cast<float*>(smem + Sm::kX + Sm::kRaw + Sm::kIdx + Sm::kS);
+  uint16_t* qs = reinterpret_cast<uint16_t*>(smem + Sm::kX + Sm::kRaw + Sm::kIdx + Sm::kS + Sm::kMl);
 
-  const int qr = blockIdx.x, split = blockIdx.y, hg = blockIdx.z;
-  const int n_splits = gridDim.y;
+  // Workgroup i runs on XCD i mod 8; each XCD takes a contiguous range of work items ordered
+  // (query row, split, head group), so all workgroups of a query row share one L2: the rows they
+  // gather and the query they load are fetched from HBM about once.
+  const int n_hg = H / 16;
+  const int u = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (u >= n_rows * n_splits * n_hg) return;
+  const int qr = u / (n_splits * n_hg), split = (u / n_hg) % n_splits, hg = u % n_hg;
   const int b = qr / T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -324,31 +342,31 @@ __global__ __launch_bounds__(256) void sparse_attn_decode_kernel(
   const int32_t* irow = idx + (int64_t)qr * K + kbeg;
   const uint8_t* rbase = rows + (int64_t)b * n_max * kRowB;
 
-  uint4 gr[GATHER];
-  // gather of one chunk into registers; entry positions from LDS (or, for chunk 0, from global)
-  auto gather = [&](int c0, bool from_global) {
-#pragma unroll
-    for (int m = 0; m < GATHER; ++m) {
-      const int it = tid + m * NT;
-      gr[m] = make_uint4(0, 0, 0, 0);
-      if (it < kDKC * 18) {
-        const int kr = it / 18, part = it - kr * 18;
-        const int ks = c0 + kr;
-        int p = -1;
-        if (ks < nk) {
-          p = from_global ? irow[ks] : sidx[ks];
-          if (p >= n_max) p = -1;
-        }
-        if (p >= 0) gr[m] = *reinterpret_cast<const uint4*>(rbase + (int64_t)p * kRowB + 16 * part);
-      }
-    }
-  };
-  if (nk > 0) gather(0, true);
   // this wave's quarter of the 16 heads' queries (channel blocks 4 wave .. 4 wave + 3)
   const uint4* qp = reinterpret_cast<const uint4*>(q + ((int64_t)qr * H + head) * kD);
   uint4 raw_q[4];
 #pragma unroll
   for (int kq = 0; kq < 4; ++kq) raw_q[kq] = qp[4 * (4 * wave + kq) + g];
+  // gathers run PF chunks ahead: registers gr[u] hold chunk c0 + u KC of the current group
+  uint4 gr[PF][GATHER];
+  auto gather = [&](uint4* dst, int c0) {
+#pragma unroll
+    for (int m = 0; m < GATHER; ++m) {
+      const int it = tid + m * NT;
+      dst[m] = make_uint4(0, 0, 0, 0);
+      if (it < KC * 18) {
+        const int kr = it / 18, part = it - kr * 18;
+        const int ks = c0 + kr;
+        if (ks < nk) {
+          const int p = irow[ks];
+          if (p >= 0 && p < n_max) dst[m] = *reinterpret_cast<const uint4*>(rbase + (int64_t)p * kRowB + 16 * part);
+        }
+      }
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < PF; ++u)
+    if (u * KC < nk) gather(gr[u], u * KC);
   for (int i = tid; i < nk; i += NT) {
     const int p = irow[i];
     sidx[i] = (p >= 0 && p < n_max) ? p : -1;
@@ -385,24 +403,33 @@ __global__ __launch_bounds__(256) void sparse_attn_decode_kernel(
     qscale = sm_scale * kLog2e * ldexpf(1.0f, -qe);
   }
 
-  f32x4_t acc[32];
+  // output tiles of this wave: channels 128 wave + 16 j + (4 g + i), head l16
+  f32x4_t acc[8];
 #pragma unroll
-  for (int mt = 0; mt < 32; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;
-  // transposing-read base of this lane for the P.V operand: entry 16 wave + 4 g + l16/4, channel 4 (l16%4)
-  const uint16_t* xtr = xs + (16 * wave + 4 * g + (l16 >> 2)) * kXPitch + 4 * (l16 & 3);
+  // transposing-read base for the P.V operand: entry 4 g + l16/4 (+16 s), channel 128 wave + 4 (l16%4) (+16 j)
+  const uint16_t* xtr = xs + (4 * g + (l16 >> 2)) * kXPitch + 128 * wave + 4 * (l16 & 3);
+  // partial-score tile layout: [wave][entry / 4][head][entry % 4] (a lane's 4 entries are one float4)
+  float4* my_sp = sp4 + wave * (KC / 4) * 16;
 
-  for (int c0 = 0; c0 < nk; c0 += kDKC) {
+  for (int cg = 0; cg < nk; cg += PF * KC)
+#pragma unroll
+  for (int u = 0; u < PF; ++u) {
+    const int c0 = cg + u * KC;
+    if (c0 >= nk) break;
 #pragma unroll
     for (int m = 0; m < GATHER; ++m) {
       const int it = tid + m * NT;
-      if (it < kDKC * 18) raw[it] = gr[m];
+      if (it < KC * 18) raw[it] = gr[u][m];
     }
     __syncthreads();
-    if (c0 + kDKC < nk) gather(c0 + kDKC, false);
-    // dequantize: item = (entry 0..63, 64-channel slab 0..7)
-    for (int it = tid; it < kDKC * 8; it += NT) {
-      const int key = it & 63, cs = it >> 6;
+    if (c0 + PF * KC < nk) gather(gr[u], c0 + PF * KC);
+    // dequantize: item = (entry, 64-channel slab 0..7)
+#pragma unroll
+    for (int it0 = 0; it0 < KC * 8; it0 += NT) {
+      const int it = it0 + tid;
+      const int key = it % KC, cs = it / KC;
       const uint8_t* rb = reinterpret_cast<const uint8_t*>(raw) + key * kRowB;
       const uint4 c01 = *reinterpret_cast<const uint4*>(rb + 32 * cs);
       const uint4 c23 = *reinterpret_cast<const uint4*>(rb + 32 * cs + 16);
@@ -420,32 +447,52 @@ __global__ __launch_bounds__(256) void sparse_attn_decode_kernel(
       }
     }
     __syncthreads();
-    // S^T for this wave's 16 entries (chunk entries 16 wave .. 16 wave + 15) x 16 heads
-    f32x4_t sacc;
+    // partial S^T over this wave's channels: entry tile t, lane holds entries 16 t + 4 g + i of head l16
     {
-      // two independent accumulation chains halve the MFMA dependency latency
-      f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;
-      const uint16_t* xr = xs + (16 * wave + l16) * kXPitch + 8 * g;
-      const uint16_t* qr16 = qs + l16 * kXPitch + 8 * g;
+      const uint16_t* xr = xs + l16 * kXPitch + 128 * wave + 8 * g;
+      const uint16_t* qr16 = qs + l16 * kXPitch + 128 * wave + 8 * g;
+      f16x8_t qb[4];
 #pragma unroll
-      for (int kk = 0; kk < 16; kk += 2) {
-        const f16x8_t a0 = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(xr + 32 * kk));
-        const f16x8_t b0 = *reinterpret_cast<const f16x8_t*>(qr16 + 32 * kk);
-        const f16x8_t a1 = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(xr + 32 * kk + 32));
-        const f16x8_t b1 = *reinterpret_cast<const f16x8_t*>(qr16 + 32 * kk + 32);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, s1, 0, 0, 0);
+      for (int kk = 0; kk < 4; ++kk) qb[kk] = *reinterpret_cast<const f16x8_t*>(qr16 + 32 * kk);
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
+        f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;  // two chains halve the dependency latency
+#pragma unroll
+        for (int kk = 0; kk < 4; kk += 2) {
+          const f16x8_t a0 = *reinterpret_cast<const f16x8_t*>(xr + 16 * t * kXPitch + 32 * kk);
+          const f16x8_t a1 = *reinterpret_cast<const f16x8_t*>(xr + 16 * t * kXPitch + 32 * kk + 32);
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qb[kk], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qb[kk + 1], s1, 0, 0, 0);
+        }
+        const f32x4_t sv = s0 + s1;
+        my_sp[(4 * t + g) * 16 + l16] = make_float4(sv[0], sv[1], sv[2], sv[3]);
       }
-      sacc = s0 + s1;
     }
-    // online softmax: lane holds entries 16 wave + 4 g + i of head l16
-    float t[4];
+    __syncthreads();
+    // complete scores and online softmax over the chunk: lane holds entries 16 s + 4 g + i of head l16
+    uint64_t vmask;                  // bit e: entry c0 + e is a real entry
+    {
+      int pe = -1;
+      if (lane < KC && c0 + lane < nk) pe = sidx[c0 + lane];
+      vmask = __ballot(pe >= 0);
+    }
+    float tv[NS][4];
     float cmax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ks = c0 + 16 * wave + 4 * g + i;
-      t[i] = (ks < nk && sidx[ks] >= 0) ? sacc[i] * qscale : -INFINITY;
-      cmax = fmaxf(cmax, t[i]);
+    for (int s = 0; s < NS; ++s) {
+      float4 a = sp4[(4 * s + g) * 16 + l16];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        const float4 v = sp4[w * (KC / 4) * 16 + (4 * s + g) * 16 + l16];
+        a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+      }
+      const float sv[4] = {a.x, a.y, a.z, a.w};
+      const uint32_t vb = (uint32_t)(vmask >> (16 * s + 4 * g)) & 15u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        tv[s][i] = ((vb >> i) & 1u) ? sv[i] * qscale : -INFINITY;
+        cmax = fmaxf(cmax, tv[s][i]);
+      }
     }
     cmax = head_max(cmax);
     if (m_run == -INFINITY) {
@@ -455,78 +502,47 @@ __global__ __launch_bounds__(256) void sparse_attn_decode_kernel(
       const float alpha = exp2f(m_run - mn);
       l_run *= alpha;
 #pragma unroll
-      for (int mt = 0; mt < 32; ++mt) acc[mt] *= alpha;
+      for (int j = 0; j < 8; ++j) acc[j] *= alpha;
       m_run = mn;
     }
     float psum = 0.0f;
-    f16x4_t pb;
+    f16x4_t pb[NS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const _Float16 pv = m_run == -INFINITY ? (_Float16)0.0f : (_Float16)exp2f(t[i] - m_run);
-      psum += (float)pv;
-      pb[i] = pv;
-    }
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const _Float16 pv = m_run == -INFINITY ? (_Float16)0.0f : (_Float16)exp2f(tv[s][i] - m_run);
+        psum += (float)pv;
+        pb[s][i] = pv;
+      }
     l_run += head_sum(psum);
-    // O^T += X^T P^T over this wave's 16 entries; A via the transposing LDS read
+    // O^T += X^T P^T: this wave's 8 channel tiles over the chunk's entry steps
 #pragma unroll
-    for (int mt = 0; mt < 32; ++mt) {
-      const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(xtr + 16 * mt));
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), pb, acc[mt], 0, 0, 0);
-    }
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(xtr + 16 * s * kXPitch + 16 * j));
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), pb[s], acc[j], 0, 0, 0);
+      }
   }
 
-  // ---- merge the 4 waves' states ----
-  __syncthreads();                                   // everyone is done with X
-  if (g == 0) {
-    ml[(wave * 16 + l16) * 2] = m_run;
-    ml[(wave * 16 + l16) * 2 + 1] = l_run;
-  }
-  __syncthreads();
-  float M = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) M = fmaxf(M, ml[(w * 16 + l16) * 2]);
-  float L = 0.0f;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float mw = ml[(w * 16 + l16) * 2];
-    if (mw != -INFINITY) L += exp2f(mw - M) * ml[(w * 16 + l16) * 2 + 1];
-  }
-  const float f = m_run != -INFINITY ? exp2f(m_run - M) : 0.0f;
+  // every wave holds the same (m_run, l_run) and disjoint channels: write directly
   const int64_t orow = (int64_t)qr * H + head;
   const bool final_out = n_splits == 1;
-  const float scale = f * (final_out ? (L > 0.0f ? 1.0f / L : 0.0f) : 1.0f);
-  float* dst = final_out ? out + orow * kD : part_o + ((int64_t)split * gridDim.x * H + orow) * kD;
-  // two rounds of 16 channel tiles: every wave stores its scaled tiles, then sums 4 of them over
-  // the 4 waves and writes them out. Layout [wave][tile][lane][4].
-  float4* mb = reinterpret_cast<float4*>(mbuf);
+  const float scale = final_out ? (l_run > 0.0f ? 1.0f / l_run : 0.0f) : 1.0f;
+  float* dst = final_out ? out + orow * kD : part_o + ((int64_t)split * n_rows * H + orow) * kD;
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const f32x4_t v = acc[16 * r + j] * scale;
-      mb[(wave * 16 + j) * 64 + lane] = make_float4(v[0], v[1], v[2], v[3]);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tj = 4 * wave + j;
-      float4 o = mb[tj * 64 + lane];
-#pragma unroll
-      for (int w = 1; w < 4; ++w) {
-        const float4 v = mb[(w * 16 + tj) * 64 + lane];
-        o.x += v.x; o.y += v.y; o.z += v.z; o.w += v.w;
-      }
-      reinterpret_cast<float4*>(dst)[4 * (16 * r + tj) + g] = o;
-    }
-    __syncthreads();
+  for (int j = 0; j < 8; ++j) {
+    const f32x4_t v = acc[j] * scale;
+    *reinterpret_cast<float4*>(dst + 128 * wave + 16 * j + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
   }
   if (wave == 0 && g == 0) {
     if (final_out) {
-      if (lse) lse[orow] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+      if (lse) lse[orow] = l_run > 0.0f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
     } else {
-      const int64_t prow = (int64_t)split * gridDim.x * H + orow;
-      part_ml[2 * prow] = M;
-      part_ml[2 * prow + 1] = L;
+      const int64_t prow = (int64_t)split * n_rows * H + orow;
+      part_ml[2 * prow] = m_run;
+      part_ml[2 * prow + 1] = l_run;
     }
   }
 }
@@ -592,7 +608,7 @@ static bool use_decode_form(int B, int T) { return (int64_t)B * T < 512; }
 static int attn_splits(int B, int T, int H, int K) {
   if (use_decode_form(B, T)) {
     const int64_t wgs = (int64_t)B * T * (H / 16);
-    const int by_fill = (int)std::max<int64_t>(1, (256 + wgs - 1) / wgs);
+    const int by_fill = (int)std::max<int64_t>(1, (kDecodeFill + wgs - 1) / wgs);
     return std::max(1, std::min((K + kDKC - 1) / kDKC, by_fill));
   }
   const int hpw = H >= 64 ? 64 : H;
@@ -636,9 +652,11 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* rows, int n_max,
     part_ml = part_o + (size_t)n_splits * nq * H * kD;
   }
   if (use_decode_form(B, T)) {
-    dim3 grid((unsigned)nq, (unsigned)n_splits, (unsigned)(H / 16));
-    hipLaunchKernelGGL(sparse_attn_decode_kernel, grid, dim3(256), 0, s, q, rows, n_max, idx, T, H, K, kps,
-                       sm_scale, out, lse, part_o, part_ml);
+    const int64_t items = nq * n_splits * (H / 16);
+    const int per_xcd = (int)((items + 7) / 8);
+    hipLaunchKernelGGL((sparse_attn_decode_kernel<kDKC, kDPF>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, q,
+                       rows, n_max, idx, T, H, K, kps, sm_scale, out, lse, part_o, part_ml, (int)nq, n_splits,
+                       per_xcd);
   } else {
     const int hpw = H >= 64 ? 64 : H;
     dim3 grid((unsigned)nq, (unsigned)n_splits, (unsigned)(H / hpw));

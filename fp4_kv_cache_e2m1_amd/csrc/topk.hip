@@ -3,17 +3,24 @@
 // Top-K entries) and 一(四)2 (the highest-scoring blocks are chosen and the positions they
 // cover become the candidate pool).
 //
+// Order: score descending, then position ascending (so ties go to the lower position). Scores
+// become order-preserving 32-bit keys (key 0 = not a candidate; -0 and +0 share a key).
+//
 // One workgroup (16 waves) selects the k best of a segment of up to 16384 columns. Lane l of
-// wave w holds columns 64*(w*EPL + i) + l (i < EPL) in registers as order-preserving 32-bit keys
-// (key 0 = not a candidate), so a wave's i-th register row is 64 consecutive columns:
-//   1. pruning bound: each lane's EPL columns form a group; at least k group maxima are >= the
-//      k-th largest group maximum, so the k-th best column is too. One 12-bit histogram of the
-//      group maxima gives a lower edge L of that maximum's bin, and every column below L is
-//      dropped (typically ~95% of them) before any further work;
-//   2. MSB-first radix select over the survivors with 12, 12 and 8-bit digits (LDS histograms,
-//      DPP prefix scans to locate the bin), stopping once the threshold bin is taken whole;
+// wave w holds columns 64*(w*EPL + i) + l (i < EPL) in registers, so a wave's i-th register row
+// is 64 consecutive columns. The selection is a short chain of barrier-separated phases, each
+// a few LDS operations, because at decode sizes (a few rows) latency, not bandwidth, is the cost:
+//   0. all loads of the segment are issued at once (no per-element branches); the count of
+//      valid columns and of non-empty lane groups come out of one block reduction;
+//   1. pruning bound: the EPL columns of a lane form a group; at least k group maxima are >= the
+//      k-th largest group maximum, so the k-th best column is too. A 12-bit histogram of the
+//      group maxima gives a lower edge L of that maximum's bin and every column below L is
+//      dropped (typically ~95% of them);
+//   2. MSB-first radix select over the survivors with 12, 12 and 8-bit digits, stopping as soon
+//      as the threshold bin is taken whole. Two histogram buffers alternate, so the next one is
+//      cleared while the current one fills and no phase needs an extra barrier;
 //   3. compaction in ascending column order with ballot + mbcnt per register row (no shuffles),
-//      so the result is deterministic and ties go to the lower position.
+//      so the result is deterministic.
 // Rows longer than one segment are split: each segment's k best (key, position) pairs go to
 // scratch, and the same kernel selects again over those candidates; the global k best always
 // survive their segment.
@@ -29,30 +36,25 @@ constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kSegMax = 16384;        // columns per workgroup: 16 per lane
 constexpr int kHistBins = 4096;       // largest radix digit: 12 bits
 
-struct TopkIn {
-  // scores mode
-  const float* scores;
-  int64_t ld;                  // row stride of scores / col_to_pos
-  const int32_t* n_valid;      // nullable
-  int valid_div;               // columns valid per row = ceil(n_valid[r] / valid_div)
-  const int32_t* col_to_pos;   // nullable
-  // candidate mode
-  const uint32_t* ckeys;
-  const int32_t* cpos;
-  int64_t cld;                 // row stride of candidate arrays
-  int n_in;                    // columns per row
-};
+enum TopkSrc { kSrcScores = 0, kSrcMapped = 1, kSrcCand = 2 };
+enum TopkDst { kDstIdx = 0, kDstExpand = 1, kDstCand = 2 };
 
-struct TopkOut {
-  // final mode
-  int32_t* idx;                // [rows, k * expand]
-  int expand;                  // 0: plain positions; b > 0: block b expansion
-  const int32_t* expand_n_vis; // nullable, positions >= n_vis[r] become -1 when expanding
-  int expand_limit;            // used instead when expand_n_vis is null
-  // partial mode
-  uint32_t* okeys;
+struct TopkArgs {
+  const float* scores;         // [rows, ld] (kSrcScores, kSrcMapped)
+  const int32_t* map;          // [rows, ld] column -> position, -1 = empty (kSrcMapped)
+  const uint32_t* ckeys;       // [rows, ld] candidate keys (kSrcCand)
+  const int32_t* cpos;         // [rows, ld] candidate positions, -1 = empty (kSrcCand)
+  const int32_t* n_valid;      // nullable: columns valid per row = ceil(n_valid[r] / valid_div)
+  int valid_div;
+  int n_in;                    // columns per row
+  int64_t ld;                  // row stride of the inputs
+  int32_t* idx;                // [rows, k * (expand or 1)] (kDstIdx, kDstExpand)
+  int expand;                  // kDstExpand: each selected block b becomes b*expand .. +expand-1
+  const int32_t* exp_nvis;     // nullable, expanded positions >= n_vis[r] become -1
+  int exp_limit;               // used instead of exp_nvis when it is null
+  uint32_t* okeys;             // kDstCand: [rows, old]
   int32_t* opos;
-  int64_t old;                 // row stride of partial outputs (= segments * k)
+  int64_t old;
 };
 
 // Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts, then row broadcasts).
@@ -71,10 +73,10 @@ CSA2_DEV int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Block-wide sum (every thread gets it). Uses red[0..kTopkWaves).
+// Block-wide sum (every thread gets it). One barrier; red[] must not be rewritten before the
+// next barrier.
 CSA2_DEV int block_sum(int v, int* red) {
   v = __builtin_amdgcn_readlane(wave_incl_scan(v), 63);
-  __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   int t = 0;
@@ -84,7 +86,9 @@ CSA2_DEV int block_sum(int v, int* red) {
 }
 
 // Given a filled histogram of nbins bins, find the bin d holding the krem-th largest entry:
-// count above d < krem <= count above d + hist[d]. Returns (d, above, hist[d]) to every thread.
+// count above d < krem <= count above d + hist[d]. Returns (d, above, hist[d]) to every
+// thread. Two barriers; info[] is read after the second and rewritten only after the first
+// barrier of the next call.
 CSA2_DEV void find_bin(const uint32_t* hist, int nbins, int krem, int* red, int* info, int& d, int& above,
                        int& cnt) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -119,12 +123,11 @@ CSA2_DEV void find_bin(const uint32_t* hist, int nbins, int krem, int* red, int*
   d = info[0];
   above = info[1];
   cnt = info[2];
-  __syncthreads();
 }
 
-template <bool kFromCand, bool kFinal, int EPL>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkIn in, TopkOut out, int seg_len, int k) {
-  __shared__ uint32_t hist[kHistBins];
+template <int SRC, int DST, int EPL>
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a, int seg_len, int k) {
+  __shared__ uint32_t hist[2][kHistBins];
   __shared__ int red[kTopkWaves];
   __shared__ int info[4];
   __shared__ int wcnt[kTopkWaves][2];
@@ -132,96 +135,107 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkIn in, TopkOut o
   const int r = blockIdx.x, seg = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c0 = seg * seg_len;
-  const int n = min(seg_len, in.n_in - c0);
-  const int lim = kFromCand ? in.n_in
-                            : (in.n_valid ? min((in.n_valid[r] + in.valid_div - 1) / in.valid_div, in.n_in)
-                                          : in.n_in);
-  const int wbase = wave * 64 * EPL;       // this wave's first column (segment-relative)
+  const int n = min(seg_len, a.n_in - c0);
+  int lim = n;                              // valid columns of this segment: [0, lim)
+  if (SRC != kSrcCand && a.n_valid) {
+    const int nv_cols = (a.n_valid[r] + a.valid_div - 1) / a.valid_div;
+    lim = max(0, min(n, nv_cols - c0));
+  }
+  const int wbase = wave * 64 * EPL;        // this wave's first column (segment-relative)
+  const int64_t rowoff = (int64_t)r * a.ld + c0;
 
-  // ---- load keys into registers: register i of lane l is column wbase + 64 i + l ----
+  // ---- 0. load: register i of lane l is column wbase + 64 i + l ----
   uint32_t key[EPL];
+  int32_t pos[EPL];
+  if (lim > 0) {
+    float sv[EPL];
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = wbase + 64 * i + lane, c = c0 + e;
-    uint32_t kv = 0;
-    if (kFromCand) {
-      if (e < n) {
-        const int64_t off = r * in.cld + c;
-        if (in.cpos[off] >= 0) kv = in.ckeys[off];
+    for (int i = 0; i < EPL; ++i) {
+      const int e = min(wbase + 64 * i + lane, lim - 1);  // clamped: every load is in bounds
+      if (SRC == kSrcCand) {
+        key[i] = a.ckeys[rowoff + e];
+        pos[i] = a.cpos[rowoff + e];
+      } else {
+        sv[i] = a.scores[rowoff + e];
+        if (SRC == kSrcMapped) pos[i] = a.map[rowoff + e];
       }
-    } else if (e < n && c < lim) {
-      const int p = in.col_to_pos ? in.col_to_pos[r * in.ld + c] : c;
-      if (p >= 0) kv = score_key(in.scores[r * in.ld + c]);
     }
-    key[i] = kv;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = wbase + 64 * i + lane;
+      bool ok = e < lim;
+      if (SRC == kSrcScores) pos[i] = c0 + e;
+      else ok = ok && pos[i] >= 0;
+      if (SRC != kSrcCand) key[i] = score_key(sv[i]);
+      key[i] = ok ? key[i] : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) { key[i] = 0u; pos[i] = -1; }
   }
   int cnt = 0;
+  uint32_t gm = 0;
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) cnt += key[i] != 0;
-  int total = block_sum(cnt, red);
+  for (int i = 0; i < EPL; ++i) {
+    cnt += key[i] != 0;
+    gm = max(gm, key[i]);
+  }
+  for (int i = tid; i < kHistBins; i += kTopkThreads) hist[0][i] = 0;
+  // valid columns (<= 16384) in the low 16 bits, non-empty groups (<= 1024) above
+  const int packed = block_sum(cnt | ((gm != 0) << 16), red);
+  const int total = packed & 0xFFFF, ng = packed >> 16;
   const int kk = min(k, total);
 
   // ---- threshold range [lo, hi] and how many of it to take (krem) ----
   uint32_t lo = 1, hi = 0xFFFFFFFFu;
   int krem = kk;
+  int cur = 0;                              // histogram buffer filled next
   if (kk > 0 && kk < total) {
     // 1. pruning bound from the per-lane group maxima (needs >= k non-empty groups)
-    if (EPL >= 4) {
-      uint32_t gm = 0;
+    if (EPL >= 4 && ng >= kk) {
+      if (gm != 0) atomicAdd(&hist[0][gm >> 20], 1u);
+      for (int i = tid; i < kHistBins; i += kTopkThreads) hist[1][i] = 0;
+      __syncthreads();
+      int d, ab, c;
+      find_bin(hist[0], kHistBins, kk, red, info, d, ab, c);
+      const uint32_t L = (uint32_t)d << 20;
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) gm = max(gm, key[i]);
-      const int ng = block_sum(gm != 0, red);
-      if (ng >= kk) {
-        for (int i = tid; i < kHistBins; i += kTopkThreads) hist[i] = 0;
-        __syncthreads();
-        if (gm != 0) atomicAdd(&hist[gm >> 20], 1u);
-        __syncthreads();
-        int d, ab, c;
-        find_bin(hist, kHistBins, kk, red, info, d, ab, c);
-        const uint32_t L = (uint32_t)d << 20;
-        cnt = 0;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-          if (key[i] < L) key[i] = 0;
-          cnt += key[i] != 0;
-        }
-        total = block_sum(cnt, red);
-      }
+      for (int i = 0; i < EPL; ++i)
+        if (key[i] < L) key[i] = 0;
+      cur = 1;
     }
-    // 2. radix select over the survivors
-    if (kk < total) {
-      uint32_t prefix = 0, mask = 0;
-      constexpr int kShift[3] = {20, 8, 0};
-      constexpr int kBits[3] = {12, 12, 8};
-      for (int pass = 0; pass < 3; ++pass) {
-        const int shift = kShift[pass];
-        const uint32_t dmask = (1u << kBits[pass]) - 1u;
-        const int nbins = 1 << kBits[pass];
-        for (int i = tid; i < nbins; i += kTopkThreads) hist[i] = 0;
-        __syncthreads();
+    // 2. radix select over the survivors (the buffer `cur` is clear)
+    uint32_t prefix = 0, mask = 0;
+    constexpr int kShift[3] = {20, 8, 0};
+    constexpr int kBits[3] = {12, 12, 8};
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = kShift[pass];
+      const uint32_t dmask = (1u << kBits[pass]) - 1u;
+      uint32_t* h = hist[cur];
 #pragma unroll
-        for (int i = 0; i < EPL; ++i)
-          if (key[i] != 0 && (key[i] & mask) == prefix) atomicAdd(&hist[(key[i] >> shift) & dmask], 1u);
-        __syncthreads();
-        int d, ab, c;
-        find_bin(hist, nbins, krem, red, info, d, ab, c);
-        krem -= ab;
-        prefix |= (uint32_t)d << shift;
-        mask |= dmask << shift;
-        if (c == krem) break;
-      }
-      lo = prefix;
-      hi = prefix | ~mask;
+      for (int i = 0; i < EPL; ++i)
+        if (key[i] != 0 && (key[i] & mask) == prefix) atomicAdd(&h[(key[i] >> shift) & dmask], 1u);
+      for (int i = tid; i < kHistBins; i += kTopkThreads) hist[cur ^ 1][i] = 0;
+      __syncthreads();
+      int d, ab, c;
+      find_bin(h, 1 << kBits[pass], krem, red, info, d, ab, c);
+      krem -= ab;
+      prefix |= (uint32_t)d << shift;
+      mask |= dmask << shift;
+      cur ^= 1;
+      if (c == krem) break;
     }
+    lo = prefix;
+    hi = prefix | ~mask;
   }
 
-  // ---- compaction in ascending column order ----
+  // ---- 3. compaction in ascending column order ----
   int gt = 0, eq = 0;
   if (kk > 0) {
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      gt += __popcll(__ballot(key[i] != 0 && key[i] > hi));
-      eq += __popcll(__ballot(key[i] != 0 && key[i] >= lo && key[i] <= hi));
+      gt += __popcll(__ballot(key[i] > hi));
+      eq += __popcll(__ballot(key[i] >= lo && key[i] <= hi));
     }
   }
   if (lane == 0) { wcnt[wave][0] = gt; wcnt[wave][1] = eq; }
@@ -236,33 +250,25 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkIn in, TopkOut o
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const uint32_t kv = key[i];
-      const bool is_gt = kv != 0 && kv > hi;
-      const bool is_eq = kv != 0 && kv >= lo && kv <= hi;
+      const bool is_gt = kv > hi;                  // lo >= 1, so key 0 is never taken
+      const bool is_eq = kv >= lo && kv <= hi;
       const uint64_t be = __ballot(is_eq);
-      const uint64_t bg = __ballot(is_gt);
-      if ((be | bg) == 0) continue;
       const bool take = is_gt || (is_eq && eq_before + lanes_below(be) < krem);
       const uint64_t bt = __ballot(take);
       if (take) {
         const int o = out_pos + lanes_below(bt);
-        const int c = c0 + wbase + 64 * i + lane;
-        int pos;
-        if (kFromCand) pos = in.cpos[r * in.cld + c];
-        else pos = in.col_to_pos ? in.col_to_pos[r * in.ld + c] : c;
-        if (kFinal) {
-          if (out.expand > 0) {
-            const int nv = out.expand_n_vis ? out.expand_n_vis[r] : out.expand_limit;
-            int32_t* dst = out.idx + ((int64_t)r * k + o) * out.expand;
-            for (int v = 0; v < out.expand; ++v) {
-              const int p = pos * out.expand + v;
-              dst[v] = p < nv ? p : -1;
-            }
-          } else {
-            out.idx[(int64_t)r * k + o] = pos;
+        if (DST == kDstIdx) {
+          a.idx[(int64_t)r * k + o] = pos[i];
+        } else if (DST == kDstExpand) {
+          const int nv = a.exp_nvis ? a.exp_nvis[r] : a.exp_limit;
+          int32_t* dst = a.idx + ((int64_t)r * k + o) * a.expand;
+          for (int v = 0; v < a.expand; ++v) {
+            const int p = pos[i] * a.expand + v;
+            dst[v] = p < nv ? p : -1;
           }
         } else {
-          out.okeys[r * out.old + (int64_t)seg * k + o] = kv;
-          out.opos[r * out.old + (int64_t)seg * k + o] = pos;
+          a.okeys[r * a.old + (int64_t)seg * k + o] = kv;
+          a.opos[r * a.old + (int64_t)seg * k + o] = pos[i];
         }
       }
       out_pos += __popcll(bt);
@@ -271,31 +277,38 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkIn in, TopkOut o
   }
   // ---- padding ----
   for (int o = kk + tid; o < k; o += kTopkThreads) {
-    if (kFinal) {
-      const int e = out.expand > 0 ? out.expand : 1;
-      for (int v = 0; v < e; ++v) out.idx[((int64_t)r * k + o) * e + v] = -1;
+    if (DST == kDstIdx) {
+      a.idx[(int64_t)r * k + o] = -1;
+    } else if (DST == kDstExpand) {
+      for (int v = 0; v < a.expand; ++v) a.idx[((int64_t)r * k + o) * a.expand + v] = -1;
     } else {
-      out.okeys[r * out.old + (int64_t)seg * k + o] = 0u;
-      out.opos[r * out.old + (int64_t)seg * k + o] = -1;
+      a.okeys[r * a.old + (int64_t)seg * k + o] = 0u;
+      a.opos[r * a.old + (int64_t)seg * k + o] = -1;
     }
   }
 }
 
-template <bool A, bool B>
-static hipError_t launch_one(dim3 grid, const TopkIn& in, const TopkOut& out, int seg_len, int k,
-                             hipStream_t s) {
+template <int SRC, int DST>
+static hipError_t launch_one(dim3 grid, const TopkArgs& a, int seg_len, int k, hipStream_t s) {
   const dim3 blk(kTopkThreads);
   if (seg_len <= kTopkThreads * 1)
-    hipLaunchKernelGGL((topk_kernel<A, B, 1>), grid, blk, 0, s, in, out, seg_len, k);
+    hipLaunchKernelGGL((topk_kernel<SRC, DST, 1>), grid, blk, 0, s, a, seg_len, k);
   else if (seg_len <= kTopkThreads * 2)
-    hipLaunchKernelGGL((topk_kernel<A, B, 2>), grid, blk, 0, s, in, out, seg_len, k);
+    hipLaunchKernelGGL((topk_kernel<SRC, DST, 2>), grid, blk, 0, s, a, seg_len, k);
   else if (seg_len <= kTopkThreads * 4)
-    hipLaunchKernelGGL((topk_kernel<A, B, 4>), grid, blk, 0, s, in, out, seg_len, k);
+    hipLaunchKernelGGL((topk_kernel<SRC, DST, 4>), grid, blk, 0, s, a, seg_len, k);
   else if (seg_len <= kTopkThreads * 8)
-    hipLaunchKernelGGL((topk_kernel<A, B, 8>), grid, blk, 0, s, in, out, seg_len, k);
+    hipLaunchKernelGGL((topk_kernel<SRC, DST, 8>), grid, blk, 0, s, a, seg_len, k);
   else
-    hipLaunchKernelGGL((topk_kernel<A, B, 16>), grid, blk, 0, s, in, out, seg_len, k);
+    hipLaunchKernelGGL((topk_kernel<SRC, DST, 16>), grid, blk, 0, s, a, seg_len, k);
   return hipGetLastError();
+}
+
+template <int SRC>
+static hipError_t launch_src(dim3 grid, const TopkArgs& a, bool last, int seg_len, int k, hipStream_t s) {
+  if (!last) return launch_one<SRC, kDstCand>(grid, a, seg_len, k, s);
+  if (a.expand > 0) return launch_one<SRC, kDstExpand>(grid, a, seg_len, k, s);
+  return launch_one<SRC, kDstIdx>(grid, a, seg_len, k, s);
 }
 
 // Plan of segment sizes: returns the number of stages and fills seg lengths / segment counts.
@@ -348,44 +361,39 @@ hipError_t launch_topk(const float* scores, int64_t rows, int n_cols, const int3
   half = (half + 255) & ~(size_t)255;
   uint8_t* wsb = static_cast<uint8_t*>(ws);
 
-  TopkOut fin{};
-  fin.idx = idx;
-  fin.expand = expand_block;
-  fin.expand_n_vis = expand_n_vis;
-  fin.expand_limit = expand_limit;
-  TopkIn in{};
-  in.scores = scores;
-  in.ld = n_cols;
-  in.n_valid = n_valid;
-  in.valid_div = valid_div > 0 ? valid_div : 1;
-  in.col_to_pos = col_to_pos;
-  in.n_in = n_cols;
+  TopkArgs a{};
+  a.scores = scores;
+  a.map = col_to_pos;
+  a.n_valid = n_valid;
+  a.valid_div = valid_div > 0 ? valid_div : 1;
+  a.n_in = n_cols;
+  a.ld = n_cols;
+  a.idx = idx;
+  a.expand = expand_block;
+  a.exp_nvis = expand_n_vis;
+  a.exp_limit = expand_limit;
   for (int st = 0; st < p.stages; ++st) {
     const bool last = st + 1 == p.stages;
     dim3 grid((unsigned)rows, (unsigned)p.nseg[st]);
-    TopkOut o = fin;
     if (!last) {
       uint8_t* buf = wsb + (st & 1) * half;
       const size_t cnt = (size_t)rows * p.nseg[st] * k;
-      o.okeys = reinterpret_cast<uint32_t*>(buf);
-      o.opos = reinterpret_cast<int32_t*>(buf + cnt * 4);
-      o.old = (int64_t)p.nseg[st] * k;
+      a.okeys = reinterpret_cast<uint32_t*>(buf);
+      a.opos = reinterpret_cast<int32_t*>(buf + cnt * 4);
+      a.old = (int64_t)p.nseg[st] * k;
     }
     hipError_t e;
-    if (st == 0)
-      e = last ? launch_one<false, true>(grid, in, o, p.seg[st], k, s)
-               : launch_one<false, false>(grid, in, o, p.seg[st], k, s);
-    else
-      e = last ? launch_one<true, true>(grid, in, o, p.seg[st], k, s)
-               : launch_one<true, false>(grid, in, o, p.seg[st], k, s);
+    if (st > 0) e = launch_src<kSrcCand>(grid, a, last, p.seg[st], k, s);
+    else if (col_to_pos) e = launch_src<kSrcMapped>(grid, a, last, p.seg[st], k, s);
+    else e = launch_src<kSrcScores>(grid, a, last, p.seg[st], k, s);
     if (e != hipSuccess) return e;
     if (!last) {
-      TopkIn next{};
-      next.ckeys = o.okeys;
-      next.cpos = o.opos;
-      next.cld = o.old;
-      next.n_in = (int)o.old;
-      in = next;
+      // the next stage reads this stage's candidates
+      a.ckeys = a.okeys;
+      a.cpos = a.opos;
+      a.n_valid = nullptr;
+      a.n_in = (int)a.old;
+      a.ld = a.old;
     }
   }
   return hipSuccess;
