@@ -267,37 +267,44 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// Decode form: few query rows. A workgroup owns (query row, 16-head group, slice of entries) and
-// walks the slice in chunks of KC entries that its 4 waves share in LDS. Wave w owns channels
-// 128w .. 128w+127 throughout:
+// Decode form: few query rows. A workgroup owns (query row, 16-head group, slice of entries). Its
+// NG sub-groups of 4 waves each take an equal part of the slice and walk it in chunks of KC
+// entries, in lockstep (shared barriers, separate LDS buffers), so each SIMD runs NG waves that
+// hide each other's latencies. Wave w of a sub-group owns channels 128w .. 128w+127 throughout:
 //   - the chunk is dequantized once into X[entry][channel] (f16, exact);
 //   - scores: each wave computes partial S^T = X Q^T over its own 128 channels for all KC
 //     entries x 16 heads (16x16x32 f16 MFMA) and writes them to a small LDS tile; after one
-//     barrier every wave adds the 4 partials, so all waves hold the same complete scores;
+//     barrier every wave adds the 4 partials, so the sub-group's waves hold the same scores;
 //   - every wave runs the same online softmax (identical inputs and arithmetic, so the running
-//     (max, sum) agree across waves), then O^T += X^T P^T for its 128 channels over the chunk
-//     (16x16x16 f16 MFMA). The A operand (4 consecutive entries of one channel per lane) comes
-//     straight from X through the transposing LDS read ds_read_b64_tr_b16; the B operand (4
-//     entries of one head per lane) is the lane's own softmax output.
-// Waves never exchange accumulators: each writes its own channels. The gathers of the next PF
+//     (max, sum) agree across the sub-group), then O^T += X^T P^T for its 128 channels over the
+//     chunk (16x16x16 f16 MFMA). The A operand (4 consecutive entries of one channel per lane)
+//     comes straight from X through the transposing LDS read ds_read_b64_tr_b16; the B operand
+//     (4 entries of one head per lane) is the lane's own softmax output.
+// At the end the sub-groups' (max, sum, output) states merge in LDS, so a query row needs no
+// second kernel unless its entries are also split over workgroups. The gathers of the next PF
 // chunks are in flight while a chunk is processed (the query is loaded first, so it does not
-// queue behind them). Workgroups are placed so that all of a query row's run on one XCD and share
-// its L2. The softmax reference max is only moved when a new score exceeds it by more than 2^8,
-// so probabilities stay <= 256 (exact enough in f16) and the accumulators are rescaled rarely.
+// queue behind them). Workgroups are placed so that all of a query row's run on one XCD and
+// share its L2. The softmax reference max is only moved when a new score exceeds it by more
+// than 2^8, so probabilities stay <= 256 (exact enough in f16) and the accumulators are rescaled
+// rarely.
 constexpr float kLazyRescale = 8.0f;            // log2 headroom before the reference max moves
-constexpr int kDKC = 64;                        // decode entries per chunk
+constexpr int kDKC = 32;                        // decode entries per chunk
 constexpr int kDPF = 2;                         // decode chunks gathered ahead
+constexpr int kDNG = 2;                         // decode sub-groups per workgroup
 constexpr int kDecodeFill = 256;                // decode workgroups wanted: one per CU
 
-template <int KC>
+template <int KC, int NG>
 struct DecodeSmem {
   static constexpr int kX = KC * kXPitch * 2;
   static constexpr int kRaw = KC * kRowB;
-  static constexpr int kIdx = kMaxKPS * 4;
   static constexpr int kS = 4 * KC * 16 * 4;    // the 4 waves' partial scores, KC entries x 16 heads
-  static constexpr int kMl = 4 * 16 * 4;
+  static constexpr int kGroup = kX + kRaw + kS; // one sub-group's buffers
+  static constexpr int kOut = 4 * 8 * 64 * 16;  // one sub-group's output tiles at the merge
+  static_assert(kGroup >= kOut, "the merge reuses a sub-group's buffers");
+  static constexpr int kIdx = kMaxKPS * 4;
+  static constexpr int kMl = (NG > 2 ? NG : 2) * 16 * 2 * 4;  // query amax, then per-group (max, sum)
   static constexpr int kQ = 16 * kXPitch * 2;   // the 16 heads' scaled f16 queries
-  static constexpr int kTotal = kX + kRaw + kIdx + kS + kMl + kQ;
+  static constexpr int kTotal = NG * kGroup + kIdx + kMl + kQ;
 };
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -306,23 +313,20 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 // Two E4M3 scale bytes (low half of w) as f16 (exact: E4M3 values fit f16).
 CSA2_DEV f16x2_t e4m3x2_to_f16(uint32_t w) { return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false); }
 
-template <int KC, int PF>
-__global__ __launch_bounds__(256) void sparse_attn_decode_kernel(
+template <int KC, int PF, int NG>
+__global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ rows, int n_max,
     const int32_t* __restrict__ idx, int T, int H, int K, int keys_per_split, float sm_scale,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float* __restrict__ part_ml, int n_rows, int n_splits, int per_xcd) {
-  using Sm = DecodeSmem<KC>;
-  constexpr int NT = 256, NS = KC / 16;         // NS entry steps of 16 per chunk
-  static_assert(KC % 16 == 0 && (KC * 8) % NT == 0 && KC <= 64, "dequant items must tile the workgroup");
-  constexpr int GATHER = (KC * 18 + NT - 1) / NT;
+  using Sm = DecodeSmem<KC, NG>;
+  constexpr int NT = 256 * NG, NS = KC / 16;    // NS entry steps of 16 per chunk
+  constexpr int GATHER = (KC * 18 + 255) / 256; // 16-byte row pieces per thread per chunk
+  static_assert(KC % 16 == 0 && KC <= 64, "whole 16-entry steps, one lane per entry for the mask");
   __shared__ __attribute__((aligned(16))) unsigned char smem[Sm::kTotal];
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-  uint4* raw = reinterpret_cast<uint4*>(smem + Sm::kX);
-  int* sidx = reinterpret_cast<int*>(smem + Sm::kX + Sm::kRaw);
-  float4* sp4 = reinterpret_cast<float4*>(smem + Sm::kX + Sm::kRaw + Sm::kIdx);
-  float* ml = reinterpret_cast<float*>(smem + Sm::kX + Sm::kRaw + Sm::kIdx + Sm::kS);
-  uint16_t* qs = reinterpret_cast<uint16_t*>(smem + Sm::kX + Sm::kRaw + Sm::kIdx + Sm::kS + Sm::kMl);
+  int* sidx = reinterpret_cast<int*>(smem + NG * Sm::kGroup);
+  float* ml = reinterpret_cast<float*>(smem + NG * Sm::kGroup + Sm::kIdx);
+  uint16_t* qs = reinterpret_cast<uint16_t*>(smem + NG * Sm::kGroup + Sm::kIdx + Sm::kMl);
 
   // Workgroup i runs on XCD i mod 8; each XCD takes a contiguous range of work items ordered
   // (query row, split, head group), so all workgroups of a query row share one L2: the rows they
@@ -333,124 +337,143 @@ __global__ __launch_bounds__(256) void sparse_attn_decode_kernel(
   const int qr = u / (n_splits * n_hg), split = (u / n_hg) % n_splits, hg = u % n_hg;
   const int b = qr / T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sg = wave >> 2, w4 = wave & 3, t4 = tid & 255;   // sub-group, wave and thread within it
   const int l16 = lane & 15, g = lane >> 4;
   const int head = hg * 16 + l16;
 
+  unsigned char* gbase = smem + sg * Sm::kGroup;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(gbase);
+  uint4* raw = reinterpret_cast<uint4*>(gbase + Sm::kX);
+  float4* sp4 = reinterpret_cast<float4*>(gbase + Sm::kX + Sm::kRaw);
+
   const int kbeg = split * keys_per_split;
-  const int kend = min(K, kbeg + keys_per_split);
-  const int nk = max(0, kend - kbeg);
+  const int nk = max(0, min(K, kbeg + keys_per_split) - kbeg);        // entries of this workgroup
+  const int sub_len = ((nk + NG - 1) / NG + KC - 1) / KC * KC;          // entries per sub-group
+  const int sbeg = sg * sub_len;
+  const int snk = max(0, min(nk - sbeg, sub_len));                     // entries of this sub-group
   const int32_t* irow = idx + (int64_t)qr * K + kbeg;
   const uint8_t* rbase = rows + (int64_t)b * n_max * kRowB;
 
-  // this wave's quarter of the 16 heads' queries (channel blocks 4 wave .. 4 wave + 3)
-  const uint4* qp = reinterpret_cast<const uint4*>(q + ((int64_t)qr * H + head) * kD);
+  // sub-group 0 loads the 16 heads' queries, wave w4 its channel blocks 4 w4 .. 4 w4 + 3
   uint4 raw_q[4];
+  if (sg == 0) {
+    const uint4* qp = reinterpret_cast<const uint4*>(q + ((int64_t)qr * H + head) * kD);
 #pragma unroll
-  for (int kq = 0; kq < 4; ++kq) raw_q[kq] = qp[4 * (4 * wave + kq) + g];
-  // gathers run PF chunks ahead: registers gr[u] hold chunk c0 + u KC of the current group
+    for (int kq = 0; kq < 4; ++kq) raw_q[kq] = qp[4 * (4 * w4 + kq) + g];
+  }
+  // gathers run PF chunks ahead: registers gr[v] hold chunk c0 + v KC of the current group
   uint4 gr[PF][GATHER];
   auto gather = [&](uint4* dst, int c0) {
 #pragma unroll
     for (int m = 0; m < GATHER; ++m) {
-      const int it = tid + m * NT;
+      const int it = t4 + m * 256;
       dst[m] = make_uint4(0, 0, 0, 0);
       if (it < KC * 18) {
         const int kr = it / 18, part = it - kr * 18;
         const int ks = c0 + kr;
-        if (ks < nk) {
-          const int p = irow[ks];
+        if (ks < snk) {
+          const int p = irow[sbeg + ks];
           if (p >= 0 && p < n_max) dst[m] = *reinterpret_cast<const uint4*>(rbase + (int64_t)p * kRowB + 16 * part);
         }
       }
     }
   };
 #pragma unroll
-  for (int u = 0; u < PF; ++u)
-    if (u * KC < nk) gather(gr[u], u * KC);
+  for (int v = 0; v < PF; ++v)
+    if (v * KC < snk) gather(gr[v], v * KC);
   for (int i = tid; i < nk; i += NT) {
     const int p = irow[i];
     sidx[i] = (p >= 0 && p < n_max) ? p : -1;
   }
-  float amax = 0.0f;
+  if (sg == 0) {
+    float amax = 0.0f;
 #pragma unroll
-  for (int kq = 0; kq < 4; ++kq) {
-    const uint32_t w[4] = {raw_q[kq].x, raw_q[kq].y, raw_q[kq].z, raw_q[kq].w};
+    for (int kq = 0; kq < 4; ++kq) {
+      const uint32_t w[4] = {raw_q[kq].x, raw_q[kq].y, raw_q[kq].z, raw_q[kq].w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w[e] << 16)), fabsf(__uint_as_float(w[e] & 0xFFFF0000u))));
+      for (int e = 0; e < 4; ++e)
+        amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w[e] << 16)), fabsf(__uint_as_float(w[e] & 0xFFFF0000u))));
+    }
+    amax = head_max(amax);
+    if (g == 0) ml[w4 * 16 + l16] = amax;
   }
-  amax = head_max(amax);
-  if (g == 0) ml[wave * 16 + l16] = amax;
   __syncthreads();
   // the queries, scaled per head by a power of two and converted to f16 (exact), into LDS
   float qscale;
   {
-    amax = fmaxf(fmaxf(ml[l16], ml[16 + l16]), fmaxf(ml[32 + l16], ml[48 + l16]));
+    const float amax = fmaxf(fmaxf(ml[l16], ml[16 + l16]), fmaxf(ml[32 + l16], ml[48 + l16]));
     const int qe = amax > 0.0f ? 14 - ilogbf(amax) : 0;
-    const float sc = ldexpf(1.0f, qe);
+    if (sg == 0) {
+      const float sc = ldexpf(1.0f, qe);
 #pragma unroll
-    for (int kq = 0; kq < 4; ++kq) {
-      const int kk = 4 * wave + kq;
-      const uint32_t w[4] = {raw_q[kq].x, raw_q[kq].y, raw_q[kq].z, raw_q[kq].w};
-      f16x8_t h;
+      for (int kq = 0; kq < 4; ++kq) {
+        const int kk = 4 * w4 + kq;
+        const uint32_t w[4] = {raw_q[kq].x, raw_q[kq].y, raw_q[kq].z, raw_q[kq].w};
+        f16x8_t h;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        h[2 * e] = (_Float16)(__uint_as_float(w[e] << 16) * sc);
-        h[2 * e + 1] = (_Float16)(__uint_as_float(w[e] & 0xFFFF0000u) * sc);
+        for (int e = 0; e < 4; ++e) {
+          h[2 * e] = (_Float16)(__uint_as_float(w[e] << 16) * sc);
+          h[2 * e + 1] = (_Float16)(__uint_as_float(w[e] & 0xFFFF0000u) * sc);
+        }
+        *reinterpret_cast<f16x8_t*>(qs + l16 * kXPitch + 32 * kk + 8 * g) = h;
       }
-      *reinterpret_cast<f16x8_t*>(qs + l16 * kXPitch + 32 * kk + 8 * g) = h;
     }
     qscale = sm_scale * kLog2e * ldexpf(1.0f, -qe);
   }
 
-  // output tiles of this wave: channels 128 wave + 16 j + (4 g + i), head l16
+  // output tiles of this wave: channels 128 w4 + 16 j + (4 g + i), head l16
   f32x4_t acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;
-  // transposing-read base for the P.V operand: entry 4 g + l16/4 (+16 s), channel 128 wave + 4 (l16%4) (+16 j)
-  const uint16_t* xtr = xs + (4 * g + (l16 >> 2)) * kXPitch + 128 * wave + 4 * (l16 & 3);
+  // transposing-read base for the P.V operand: entry 4 g + l16/4 (+16 s), channel 128 w4 + 4 (l16%4) (+16 j)
+  const uint16_t* xtr = xs + (4 * g + (l16 >> 2)) * kXPitch + 128 * w4 + 4 * (l16 & 3);
   // partial-score tile layout: [wave][entry / 4][head][entry % 4] (a lane's 4 entries are one float4)
-  float4* my_sp = sp4 + wave * (KC / 4) * 16;
+  float4* my_sp = sp4 + w4 * (KC / 4) * 16;
 
-  for (int cg = 0; cg < nk; cg += PF * KC)
+  // every sub-group runs the same number of chunk steps (barriers are shared); steps past its
+  // entries do no work
+  for (int cg = 0; cg < sub_len; cg += PF * KC)
 #pragma unroll
-  for (int u = 0; u < PF; ++u) {
-    const int c0 = cg + u * KC;
-    if (c0 >= nk) break;
+  for (int v = 0; v < PF; ++v) {
+    const int c0 = cg + v * KC;
+    if (c0 >= sub_len) break;
+    const bool active = c0 < snk;
+    if (active) {
 #pragma unroll
-    for (int m = 0; m < GATHER; ++m) {
-      const int it = tid + m * NT;
-      if (it < KC * 18) raw[it] = gr[u][m];
+      for (int m = 0; m < GATHER; ++m) {
+        const int it = t4 + m * 256;
+        if (it < KC * 18) raw[it] = gr[v][m];
+      }
     }
     __syncthreads();
-    if (c0 + PF * KC < nk) gather(gr[u], c0 + PF * KC);
+    if (active && c0 + PF * KC < snk) gather(gr[v], c0 + PF * KC);
     // dequantize: item = (entry, 64-channel slab 0..7)
+    if (active) {
+      for (int it = t4; it < KC * 8; it += 256) {
+        const int key = it % KC, cs = it / KC;
+        const uint8_t* rb = reinterpret_cast<const uint8_t*>(raw) + key * kRowB;
+        const uint4 c01 = *reinterpret_cast<const uint4*>(rb + 32 * cs);
+        const uint4 c23 = *reinterpret_cast<const uint4*>(rb + 32 * cs + 16);
+        const uint32_t sc4 = *reinterpret_cast<const uint32_t*>(rb + 256 + 4 * cs);
+        const f16x2_t s01 = e4m3x2_to_f16(sc4), s23 = e4m3x2_to_f16(sc4 >> 16);
+        const f16x2_t sgm[4] = {f16x2_t{s01[0], s01[0]}, f16x2_t{s01[1], s01[1]}, f16x2_t{s23[0], s23[0]},
+                                f16x2_t{s23[1], s23[1]}};
+        const uint32_t cw[8] = {c01.x, c01.y, c01.z, c01.w, c23.x, c23.y, c23.z, c23.w};
+        uint4* dst = reinterpret_cast<uint4*>(xs + key * kXPitch + 64 * cs);
 #pragma unroll
-    for (int it0 = 0; it0 < KC * 8; it0 += NT) {
-      const int it = it0 + tid;
-      const int key = it % KC, cs = it / KC;
-      const uint8_t* rb = reinterpret_cast<const uint8_t*>(raw) + key * kRowB;
-      const uint4 c01 = *reinterpret_cast<const uint4*>(rb + 32 * cs);
-      const uint4 c23 = *reinterpret_cast<const uint4*>(rb + 32 * cs + 16);
-      const uint32_t sc4 = *reinterpret_cast<const uint32_t*>(rb + 256 + 4 * cs);
-      const f16x2_t s01 = e4m3x2_to_f16(sc4), s23 = e4m3x2_to_f16(sc4 >> 16);
-      const f16x2_t sg[4] = {f16x2_t{s01[0], s01[0]}, f16x2_t{s01[1], s01[1]}, f16x2_t{s23[0], s23[0]},
-                             f16x2_t{s23[1], s23[1]}};
-      const uint32_t cw[8] = {c01.x, c01.y, c01.z, c01.w, c23.x, c23.y, c23.z, c23.w};
-      uint4* dst = reinterpret_cast<uint4*>(xs + key * kXPitch + 64 * cs);
-#pragma unroll
-      for (int wi = 0; wi < 8; ++wi) {
-        uint32_t v[4];
-        e2m1x8_to_f16(cw[wi], sg[wi >> 1], v);
-        dst[wi] = make_uint4(v[0], v[1], v[2], v[3]);
+        for (int wi = 0; wi < 8; ++wi) {
+          uint32_t vv[4];
+          e2m1x8_to_f16(cw[wi], sgm[wi >> 1], vv);
+          dst[wi] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
+        }
       }
     }
     __syncthreads();
     // partial S^T over this wave's channels: entry tile t, lane holds entries 16 t + 4 g + i of head l16
-    {
-      const uint16_t* xr = xs + l16 * kXPitch + 128 * wave + 8 * g;
-      const uint16_t* qr16 = qs + l16 * kXPitch + 128 * wave + 8 * g;
+    if (active) {
+      const uint16_t* xr = xs + l16 * kXPitch + 128 * w4 + 8 * g;
+      const uint16_t* qr16 = qs + l16 * kXPitch + 128 * w4 + 8 * g;
       f16x8_t qb[4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) qb[kk] = *reinterpret_cast<const f16x8_t*>(qr16 + 32 * kk);
@@ -469,11 +492,12 @@ __global__ __launch_bounds__(256) void sparse_attn_decode_kernel(
       }
     }
     __syncthreads();
+    if (!active) continue;
     // complete scores and online softmax over the chunk: lane holds entries 16 s + 4 g + i of head l16
-    uint64_t vmask;                  // bit e: entry c0 + e is a real entry
+    uint64_t vmask;                  // bit e: entry c0 + e of the sub-group is a real entry
     {
       int pe = -1;
-      if (lane < KC && c0 + lane < nk) pe = sidx[c0 + lane];
+      if (lane < KC && c0 + lane < snk) pe = sidx[sbeg + c0 + lane];
       vmask = __ballot(pe >= 0);
     }
     float tv[NS][4];
@@ -483,8 +507,8 @@ __global__ __launch_bounds__(256) void sparse_attn_decode_kernel(
       float4 a = sp4[(4 * s + g) * 16 + l16];
 #pragma unroll
       for (int w = 1; w < 4; ++w) {
-        const float4 v = sp4[w * (KC / 4) * 16 + (4 * s + g) * 16 + l16];
-        a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+        const float4 x = sp4[w * (KC / 4) * 16 + (4 * s + g) * 16 + l16];
+        a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
       }
       const float sv[4] = {a.x, a.y, a.z, a.w};
       const uint32_t vb = (uint32_t)(vmask >> (16 * s + 4 * g)) & 15u;
@@ -526,23 +550,58 @@ __global__ __launch_bounds__(256) void sparse_attn_decode_kernel(
       }
   }
 
-  // every wave holds the same (m_run, l_run) and disjoint channels: write directly
+  // merge the sub-groups: groups 1.. leave (max, sum) and their tiles in LDS, group 0 combines
+  float M = m_run, L = l_run;
+  if (NG > 1) {
+    __syncthreads();                               // every group is done with its buffers
+    float4* ob = reinterpret_cast<float4*>(gbase);  // [w4][j][lane]
+    if (sg > 0) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ob[(w4 * 8 + j) * 64 + lane] = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+      if (w4 == 0 && g == 0) {
+        ml[(sg * 16 + l16) * 2] = m_run;
+        ml[(sg * 16 + l16) * 2 + 1] = l_run;
+      }
+    }
+    __syncthreads();
+    if (sg > 0) return;
+#pragma unroll
+    for (int k = 1; k < NG; ++k) M = fmaxf(M, ml[(k * 16 + l16) * 2]);
+    const float f0 = m_run == -INFINITY ? 0.0f : exp2f(m_run - M);
+    L = l_run * f0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= f0;
+#pragma unroll
+    for (int k = 1; k < NG; ++k) {
+      const float mk = ml[(k * 16 + l16) * 2];
+      const float fk = mk == -INFINITY ? 0.0f : exp2f(mk - M);
+      L += ml[(k * 16 + l16) * 2 + 1] * fk;
+      const float4* obk = reinterpret_cast<const float4*>(smem + k * Sm::kGroup);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float4 o = obk[(w4 * 8 + j) * 64 + lane];
+        acc[j] += f32x4_t{o.x, o.y, o.z, o.w} * fk;
+      }
+    }
+  }
+
+  // every wave holds the same (M, L) and disjoint channels: write directly
   const int64_t orow = (int64_t)qr * H + head;
   const bool final_out = n_splits == 1;
-  const float scale = final_out ? (l_run > 0.0f ? 1.0f / l_run : 0.0f) : 1.0f;
+  const float scale = final_out ? (L > 0.0f ? 1.0f / L : 0.0f) : 1.0f;
   float* dst = final_out ? out + orow * kD : part_o + ((int64_t)split * n_rows * H + orow) * kD;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const f32x4_t v = acc[j] * scale;
-    *reinterpret_cast<float4*>(dst + 128 * wave + 16 * j + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(dst + 128 * w4 + 16 * j + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
   }
-  if (wave == 0 && g == 0) {
+  if (w4 == 0 && g == 0) {
     if (final_out) {
-      if (lse) lse[orow] = l_run > 0.0f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+      if (lse) lse[orow] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
     } else {
       const int64_t prow = (int64_t)split * n_rows * H + orow;
-      part_ml[2 * prow] = m_run;
-      part_ml[2 * prow + 1] = l_run;
+      part_ml[2 * prow] = M;
+      part_ml[2 * prow + 1] = L;
     }
   }
 }
@@ -609,7 +668,8 @@ static int attn_splits(int B, int T, int H, int K) {
   if (use_decode_form(B, T)) {
     const int64_t wgs = (int64_t)B * T * (H / 16);
     const int by_fill = (int)std::max<int64_t>(1, (kDecodeFill + wgs - 1) / wgs);
-    return std::max(1, std::min((K + kDKC - 1) / kDKC, by_fill));
+    // at least one chunk per sub-group
+    return std::max(1, std::min((K + kDKC * kDNG - 1) / (kDKC * kDNG), by_fill));
   }
   const int hpw = H >= 64 ? 64 : H;
   const int64_t wgs = (int64_t)B * T * (H / hpw);
@@ -654,7 +714,7 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* rows, int n_max,
   if (use_decode_form(B, T)) {
     const int64_t items = nq * n_splits * (H / 16);
     const int per_xcd = (int)((items + 7) / 8);
-    hipLaunchKernelGGL((sparse_attn_decode_kernel<kDKC, kDPF>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, q,
+    hipLaunchKernelGGL((sparse_attn_decode_kernel<kDKC, kDPF, kDNG>), dim3((unsigned)(8 * per_xcd)), dim3(256 * kDNG), 0, s, q,
                        rows, n_max, idx, T, H, K, kps, sm_scale, out, lse, part_o, part_ml, (int)nq, n_splits,
                        per_xcd);
   } else {
