@@ -300,7 +300,7 @@ struct DecodeSmem {
   static constexpr int kS = 4 * KC * 16 * 4;    // the 4 waves' partial scores, KC entries x 16 heads
   static constexpr int kGroup = kX + kRaw + kS; // one sub-group's buffers
   static constexpr int kOut = 4 * 8 * 64 * 16;  // one sub-group's output tiles at the merge
-  static_assert(kGroup >= kOut, "the merge reuses a sub-group's buffers");
+  static_assert(NG * kGroup >= (NG - 1) * kOut, "the merge reuses the sub-groups' buffers");
   static constexpr int kIdx = kMaxKPS * 4;
   static constexpr int kMl = (NG > 2 ? NG : 2) * 16 * 2 * 4;  // query amax, then per-group (max, sum)
   static constexpr int kQ = 16 * kXPitch * 2;   // the 16 heads' scaled f16 queries
@@ -323,6 +323,7 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
   constexpr int NT = 256 * NG, NS = KC / 16;    // NS entry steps of 16 per chunk
   constexpr int GATHER = (KC * 18 + 255) / 256; // 16-byte row pieces per thread per chunk
   static_assert(KC % 16 == 0 && KC <= 64, "whole 16-entry steps, one lane per entry for the mask");
+  static_assert(NG >= 1 && NG <= 4, "sub-groups");
   __shared__ __attribute__((aligned(16))) unsigned char smem[Sm::kTotal];
   int* sidx = reinterpret_cast<int*>(smem + NG * Sm::kGroup);
   float* ml = reinterpret_cast<float*>(smem + NG * Sm::kGroup + Sm::kIdx);
@@ -554,8 +555,8 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
   float M = m_run, L = l_run;
   if (NG > 1) {
     __syncthreads();                               // every group is done with its buffers
-    float4* ob = reinterpret_cast<float4*>(gbase);  // [w4][j][lane]
     if (sg > 0) {
+      float4* ob = reinterpret_cast<float4*>(smem + (sg - 1) * Sm::kOut);  // [w4][j][lane]
 #pragma unroll
       for (int j = 0; j < 8; ++j) ob[(w4 * 8 + j) * 64 + lane] = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
       if (w4 == 0 && g == 0) {
@@ -576,7 +577,7 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
       const float mk = ml[(k * 16 + l16) * 2];
       const float fk = mk == -INFINITY ? 0.0f : exp2f(mk - M);
       L += ml[(k * 16 + l16) * 2 + 1] * fk;
-      const float4* obk = reinterpret_cast<const float4*>(smem + k * Sm::kGroup);
+      const float4* obk = reinterpret_cast<const float4*>(smem + (k - 1) * Sm::kOut);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float4 o = obk[(w4 * 8 + j) * 64 + lane];

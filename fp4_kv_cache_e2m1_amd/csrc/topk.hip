@@ -6,7 +6,7 @@
 // Order: score descending, then position ascending (so ties go to the lower position). Scores
 // become order-preserving 32-bit keys (key 0 = not a candidate; -0 and +0 share a key).
 //
-// One workgroup (16 waves) selects the k best of a segment of up to 16384 columns. Lane l of
+// One workgroup (16 waves) selects the k best of a segment of up to 40960 columns. Lane l of
 // wave w holds columns 64*(w*EPL + i) + l (i < EPL) in registers, so a wave's i-th register row
 // is 64 consecutive columns. The selection is a short chain of barrier-separated phases, each
 // a few LDS operations, because at decode sizes (a few rows) latency, not bandwidth, is the cost:
@@ -21,9 +21,10 @@
 //      cleared while the current one fills and no phase needs an extra barrier;
 //   3. compaction in ascending column order with ballot + mbcnt per register row (no shuffles),
 //      so the result is deterministic.
-// Rows longer than one segment are split: each segment's k best (key, position) pairs go to
-// scratch, and the same kernel selects again over those candidates; the global k best always
-// survive their segment.
+// With many rows (prefill) one workgroup per row keeps the chip busy, so rows up to 40960 columns
+// are one segment. With few rows (decode) rows longer than 16384 columns are split for
+// parallelism: each segment's k best (key, position) pairs go to scratch, and the same kernel
+// selects again over those candidates; the global k best always survive their segment.
 #include <algorithm>
 
 #include "common.h"
@@ -33,7 +34,8 @@ namespace csa2 {
 
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / kWave;
-constexpr int kSegMax = 16384;        // columns per workgroup: 16 per lane
+constexpr int kSegMax = 40960;        // columns per workgroup: up to 40 per lane
+constexpr int kSegSplit = 16384;      // segment length when a row is split over workgroups
 constexpr int kHistBins = 4096;       // largest radix digit: 12 bits
 
 enum TopkSrc { kSrcScores = 0, kSrcMapped = 1, kSrcCand = 2 };
@@ -145,8 +147,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a, int seg_
   const int64_t rowoff = (int64_t)r * a.ld + c0;
 
   // ---- 0. load: register i of lane l is column wbase + 64 i + l ----
+  constexpr int NP = SRC == kSrcScores ? 1 : EPL;   // positions are kept only when not implied
   uint32_t key[EPL];
-  int32_t pos[EPL];
+  int32_t pos[NP];
   if (lim > 0) {
     float sv[EPL];
 #pragma unroll
@@ -154,24 +157,23 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a, int seg_
       const int e = min(wbase + 64 * i + lane, lim - 1);  // clamped: every load is in bounds
       if (SRC == kSrcCand) {
         key[i] = a.ckeys[rowoff + e];
-        pos[i] = a.cpos[rowoff + e];
+        pos[i % NP] = a.cpos[rowoff + e];
       } else {
         sv[i] = a.scores[rowoff + e];
-        if (SRC == kSrcMapped) pos[i] = a.map[rowoff + e];
+        if (SRC == kSrcMapped) pos[i % NP] = a.map[rowoff + e];
       }
     }
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = wbase + 64 * i + lane;
       bool ok = e < lim;
-      if (SRC == kSrcScores) pos[i] = c0 + e;
-      else ok = ok && pos[i] >= 0;
+      if (SRC != kSrcScores) ok = ok && pos[i % NP] >= 0;
       if (SRC != kSrcCand) key[i] = score_key(sv[i]);
       key[i] = ok ? key[i] : 0u;
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) { key[i] = 0u; pos[i] = -1; }
+    for (int i = 0; i < EPL; ++i) key[i] = 0u;
   }
   int cnt = 0;
   uint32_t gm = 0;
@@ -257,18 +259,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a, int seg_
       const uint64_t bt = __ballot(take);
       if (take) {
         const int o = out_pos + lanes_below(bt);
+        const int32_t p_i = SRC == kSrcScores ? c0 + wbase + 64 * i + lane : pos[i % NP];
         if (DST == kDstIdx) {
-          a.idx[(int64_t)r * k + o] = pos[i];
+          a.idx[(int64_t)r * k + o] = p_i;
         } else if (DST == kDstExpand) {
           const int nv = a.exp_nvis ? a.exp_nvis[r] : a.exp_limit;
           int32_t* dst = a.idx + ((int64_t)r * k + o) * a.expand;
           for (int v = 0; v < a.expand; ++v) {
-            const int p = pos[i] * a.expand + v;
+            const int p = p_i * a.expand + v;
             dst[v] = p < nv ? p : -1;
           }
         } else {
           a.okeys[r * a.old + (int64_t)seg * k + o] = kv;
-          a.opos[r * a.old + (int64_t)seg * k + o] = pos[i];
+          a.opos[r * a.old + (int64_t)seg * k + o] = p_i;
         }
       }
       out_pos += __popcll(bt);
@@ -299,8 +302,14 @@ static hipError_t launch_one(dim3 grid, const TopkArgs& a, int seg_len, int k, h
     hipLaunchKernelGGL((topk_kernel<SRC, DST, 4>), grid, blk, 0, s, a, seg_len, k);
   else if (seg_len <= kTopkThreads * 8)
     hipLaunchKernelGGL((topk_kernel<SRC, DST, 8>), grid, blk, 0, s, a, seg_len, k);
-  else
+  else if (seg_len <= kTopkThreads * 16)
     hipLaunchKernelGGL((topk_kernel<SRC, DST, 16>), grid, blk, 0, s, a, seg_len, k);
+  else if (seg_len <= kTopkThreads * 24)
+    hipLaunchKernelGGL((topk_kernel<SRC, DST, 24>), grid, blk, 0, s, a, seg_len, k);
+  else if (seg_len <= kTopkThreads * 32)
+    hipLaunchKernelGGL((topk_kernel<SRC, DST, 32>), grid, blk, 0, s, a, seg_len, k);
+  else
+    hipLaunchKernelGGL((topk_kernel<SRC, DST, 40>), grid, blk, 0, s, a, seg_len, k);
   return hipGetLastError();
 }
 
@@ -319,20 +328,22 @@ struct TopkPlan {
   int n_in[8];
 };
 
-static TopkPlan make_plan(int n_cols, int k) {
+static TopkPlan make_plan(int64_t rows, int n_cols, int k) {
   TopkPlan p{};
   int n = n_cols;
   int st = 0;
   while (true) {
     p.n_in[st] = n;
-    if (n <= kSegMax || st == 7) {
+    // many rows: one workgroup per row is enough parallelism; few rows: split long rows
+    const int single = rows >= 256 ? kSegMax : kSegSplit;
+    if (n <= single || st == 7) {
       p.seg[st] = n;
       p.nseg[st] = 1;
       p.stages = st + 1;
       return p;
     }
     // segments of at least 2k columns, so each stage shrinks the row
-    const int seg = std::min(kSegMax, std::max(n <= 4 * kSegMax ? 4096 : kSegMax, 4 * k));
+    const int seg = std::min(kSegSplit, std::max(n <= 4 * kSegSplit ? 4096 : kSegSplit, 4 * k));
     p.seg[st] = seg;
     p.nseg[st] = (n + seg - 1) / seg;
     n = p.nseg[st] * k;
@@ -341,7 +352,7 @@ static TopkPlan make_plan(int n_cols, int k) {
 }
 
 size_t topk_workspace(int64_t rows, int n_cols, int k) {
-  const TopkPlan p = make_plan(n_cols, k);
+  const TopkPlan p = make_plan(rows, n_cols, k);
   size_t largest = 0;
   for (int st = 0; st + 1 < p.stages; ++st)
     largest = std::max(largest, (size_t)rows * p.nseg[st] * k * 8);
@@ -354,7 +365,7 @@ hipError_t launch_topk(const float* scores, int64_t rows, int n_cols, const int3
                        int expand_block, const int32_t* expand_n_vis, int expand_limit, void* ws,
                        hipStream_t s) {
   if (rows == 0 || k == 0) return hipSuccess;
-  const TopkPlan p = make_plan(n_cols, k);
+  const TopkPlan p = make_plan(rows, n_cols, k);
   if (p.seg[p.stages - 1] > kSegMax) return hipErrorInvalidValue;
   size_t half = 0;
   for (int st = 0; st + 1 < p.stages; ++st) half = std::max(half, (size_t)rows * p.nseg[st] * k * 8);
