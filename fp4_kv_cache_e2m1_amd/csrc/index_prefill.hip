@@ -168,15 +168,15 @@ __global__ __launch_bounds__(64 * WM * WN) void index_prefill_kernel(
 }
 
 
-template <int C, int KT, int PD>
-__global__ __launch_bounds__(512) void index_prefill_qs_kernel(
+template <int C, int KT, int PD, int NW, int RB, bool kBufStore>
+__global__ __launch_bounds__(64 * NW) void index_prefill_qs_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int T, int n_max,
     const int32_t* __restrict__ n_vis, float* __restrict__ scores, int m_slabs, int n_chunks,
     int chunk_keys, int per_xcd) {
-  constexpr int NW = 8, NT = 64 * NW, BM = 32 * NW, KS = C / 16;
+  constexpr int NT = 64 * NW, WR = 32 * RB, BM = WR * NW, KS = C / 16;
   constexpr int P = C + 8;                        // bf16 per LDS key row (16-byte pad)
   constexpr int LOADS = KT * (C / 8) / NT;        // 16-byte loads per thread per key tile
-  constexpr int NS = KS * (KT / 32);              // MFMA steps per tile: step = s * (KT/32) + j
+  constexpr int NS = KS * (KT / 32);              // key-fragment steps per tile: step = s * (KT/32) + j
   static_assert(KT % 32 == 0 && KT * (C / 8) % NT == 0, "key tile split");
   __shared__ __attribute__((aligned(16))) uint16_t ks[2][KT * P];
   __shared__ int row_nv[BM];
@@ -185,7 +185,8 @@ __global__ __launch_bounds__(512) void index_prefill_qs_kernel(
   const int u = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
   if (u >= m_slabs * n_chunks) return;
   const int t0 = (u % m_slabs) * BM, n_begin = (u / m_slabs) * chunk_keys, b = blockIdx.y;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: row bases stay scalar
   const int lr = lane & 31, lh = lane >> 5;
   if (tid == 0) slab_nv = 0;
   __syncthreads();
@@ -199,16 +200,17 @@ __global__ __launch_bounds__(512) void index_prefill_qs_kernel(
   const int n_end = min(n_begin + chunk_keys, slab_nv);
   if (n_end <= n_begin) return;  // uniform: nothing visible in this chunk
 
-  // A fragments: row 32*wave + lane%32, channels 16s + 8*(lane/32) .. +7
-  bf16x8_t qa[KS];
-  {
-    const int t = t0 + 32 * wave + lr;
+  // A fragments: row block rb holds rows WR*wave + 32 rb + lane%32, channels 16s + 8*(lane/32) .. +7
+  bf16x8_t qa[RB][KS];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int t = t0 + WR * wave + 32 * rb + lr;
     const uint16_t* qr = q + ((int64_t)b * T + t) * C + 8 * lh;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       u32x4_t v = {0u, 0u, 0u, 0u};
       if (t < T) v = *reinterpret_cast<const u32x4_t*>(qr + 16 * s);
-      qa[s] = __builtin_bit_cast(bf16x8_t, v);
+      qa[rb][s] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
   const uint16_t* kb = k + (int64_t)b * n_max * C;
@@ -229,7 +231,15 @@ __global__ __launch_bounds__(512) void index_prefill_qs_kernel(
     }
   };
 
-  float* sw = scores + ((int64_t)b * T + t0 + 32 * wave) * n_max;  // this wave's first row
+  float* sw = scores + ((int64_t)b * T + t0 + WR * wave) * n_max;  // this wave's first row
+  // this wave's rows as one buffer range (used when WR rows fit in 2^31 bytes)
+  __amdgpu_buffer_rsrc_t srsrc;
+  {
+    const uint64_t a = reinterpret_cast<uint64_t>(sw);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a), hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const int bytes = __builtin_amdgcn_readfirstlane(kBufStore ? max(0, min(WR, T - t0 - WR * wave)) * n_max * 4 : 0);
+    srsrc = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), 0, bytes, 0x00020000);
+  }
   gload(n_begin);
   lstore(0);
   __syncthreads();
@@ -237,12 +247,14 @@ __global__ __launch_bounds__(512) void index_prefill_qs_kernel(
   for (int n0 = n_begin; n0 < n_end; n0 += KT) {
     const bool more = n0 + KT < n_end;
     if (more) gload(n0 + KT);
-    f32x16_t acc[KT / 32];
+    f32x16_t acc[RB][KT / 32];
 #pragma unroll
-    for (int j = 0; j < KT / 32; ++j)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
-    // B fragments: key 32j + lane%32 of the tile, channels 16s + 8*(lane/32) .. +7
+      for (int j = 0; j < KT / 32; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[rb][j][r] = 0.f;
+    // B fragments: key 32j + lane%32 of the tile, channels 16s + 8*(lane/32) .. +7; each feeds RB MFMAs
     const uint16_t* kt = &ks[buf][lr * P + 8 * lh];
     auto bload = [&](int step) {
       return *reinterpret_cast<const bf16x8_t*>(kt + 32 * (step % (KT / 32)) * P + 16 * (step / (KT / 32)));
@@ -254,21 +266,32 @@ __global__ __launch_bounds__(512) void index_prefill_qs_kernel(
     for (int step = 0; step < NS; ++step) {
       const bf16x8_t cur = bq[step % PD];
       if (step + PD < NS) bq[step % PD] = bload(step + PD);
-      acc[step % (KT / 32)] =
-          __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[step / (KT / 32)], cur, acc[step % (KT / 32)], 0, 0, 0);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        acc[rb][step % (KT / 32)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            qa[rb][step / (KT / 32)], cur, acc[rb][step % (KT / 32)], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);  // keep the reads PD steps ahead of their MFMAs
     }
-    // accumulator r of block j: row 8(r/4) + 4(lane/32) + r%4 of the wave, key n0 + 32j + lane%32
+    // accumulator r of block (rb, j): row 32 rb + 8(r/4) + 4(lane/32) + r%4 of the wave, key n0 + 32j + lane%32
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 8 * (r >> 2) + 4 * lh + (r & 3);
-      const int nv = row_nv[32 * wave + row];  // 0 for rows past T
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int j = 0; j < KT / 32; ++j) {
-        const int n = n0 + 32 * j + lr;
-        if (n < nv) sw[(int64_t)row * n_max + n] = acc[j][r];
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * rb + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const int nv = row_nv[WR * wave + row];  // 0 for rows past T
+#pragma unroll
+        for (int j = 0; j < KT / 32; ++j) {
+          const int n = n0 + 32 * j + lr;
+          if (kBufStore) {
+            // unconditional: masked lanes get an offset past the range, which the hardware drops,
+            // so the compiler can count the stores and never waits for them
+            const int off = n < nv ? (row * n_max + n) * 4 : (int)0x80000000;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[rb][j][r]), srsrc, off, 0, 0);
+          } else if (n < nv) {
+            sw[(int64_t)row * n_max + n] = acc[rb][j][r];
+          }
+        }
       }
-    }
     if (more) lstore(buf ^ 1);
     __syncthreads();
     buf ^= 1;
@@ -292,10 +315,10 @@ hipError_t launch_prefill_cfg(const uint16_t* q, const uint16_t* k, int B, int T
 }
 
 
-template <int C>
+template <int C, int NW, int RB>
 hipError_t launch_prefill_qs(const uint16_t* q, const uint16_t* k, int B, int T, int n_max,
                              const int32_t* n_vis, float* scores, hipStream_t s) {
-  constexpr int KT = 32, BM = 256;
+  constexpr int KT = 32, BM = 32 * RB * NW;
   const int m_slabs = (T + BM - 1) / BM;
   // about one workgroup per CU: split the keys into chunks of whole tiles
   int n_chunks = std::max(1, 256 / m_slabs);
@@ -304,11 +327,15 @@ hipError_t launch_prefill_qs(const uint16_t* q, const uint16_t* k, int B, int T,
   n_chunks = (n_max + chunk_keys - 1) / chunk_keys;
   const int64_t items = (int64_t)m_slabs * n_chunks;
   const int per_xcd = (int)((items + 7) / 8);
-  hipLaunchKernelGGL((index_prefill_qs_kernel<C, KT, 8>), dim3((unsigned)(8 * per_xcd), (unsigned)B), dim3(512), 0,
-                     s, q, k, T, n_max, n_vis, scores, m_slabs, n_chunks, chunk_keys, per_xcd);
+  const dim3 grid((unsigned)(8 * per_xcd), (unsigned)B), block(64 * NW);
+  if ((int64_t)32 * RB * n_max * 4 <= ((int64_t)1 << 31) - 4)
+    hipLaunchKernelGGL((index_prefill_qs_kernel<C, KT, 8, NW, RB, true>), grid, block, 0, s, q, k, T, n_max, n_vis,
+                       scores, m_slabs, n_chunks, chunk_keys, per_xcd);
+  else
+    hipLaunchKernelGGL((index_prefill_qs_kernel<C, KT, 8, NW, RB, false>), grid, block, 0, s, q, k, T, n_max, n_vis,
+                       scores, m_slabs, n_chunks, chunk_keys, per_xcd);
   return hipGetLastError();
 }
-
 }  // namespace
 
 bool index_prefill_supported(int T, int Hi, int Hk, int Di) {
@@ -319,8 +346,8 @@ hipError_t launch_index_prefill(const uint16_t* q, const uint16_t* k, int B, int
                                 int n_max, const int32_t* n_vis, float* scores, hipStream_t s) {
   if (B == 0 || T == 0 || n_max == 0) return hipSuccess;
   const int C = Hi * Di;
-  if (C == 512) return launch_prefill_qs<512>(q, k, B, T, n_max, n_vis, scores, s);
-  if (C == 256) return launch_prefill_qs<256>(q, k, B, T, n_max, n_vis, scores, s);
+  if (C == 512) return launch_prefill_qs<512, 8, 1>(q, k, B, T, n_max, n_vis, scores, s);
+  if (C == 256) return launch_prefill_qs<256, 8, 1>(q, k, B, T, n_max, n_vis, scores, s);
   // 8 waves of 128 x 64, 256 x 256 tiles, 64-channel slices
   return launch_prefill_cfg<2, 4, 4, 2, 64>(q, k, B, T, C, n_max, n_vis, scores, s);
 }
