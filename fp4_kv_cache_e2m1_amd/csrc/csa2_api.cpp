@@ -242,6 +242,8 @@ csa2_status plan_layer(csa2_mode mode, const csa2_layer_args* a, const csa2_shar
     if (p->score && p->ncols > 0 && idx->K > 0) sel = std::max(sel, csa2_topk_workspace_size(rows_c, p->ncols, idx->K));
     if (p->build_pool && p->n_blocks > 0)
       sel = std::max(sel, csa2_hier_pool_workspace_size(rows_c, p->n_blocks, a->pool_blocks));
+    if (p->build_pool && idx->P > 0 && idx->K > 0)  // Top-K taken from the pool's positions
+      sel = std::max(sel, csa2_topk_workspace_size(rows_c, idx->P, idx->K));
     if (idx->K > 0) attn = std::max(attn, csa2_sparse_attn_workspace_size(b1 - b0, a->T, a->H, kv->D, idx->K));
   }
   off = align_up(off + sel);
@@ -303,13 +305,25 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_share
         if (hipEventRecord(ev, as_stream(s_idx)) != hipSuccess) return CSA2_E_HIP;
         if (hipStreamWaitEvent(aux, ev, 0) != hipSuccess) return CSA2_E_HIP;
       }
-      s2 = csa2_topk(scores_c, rows_c, p.ncols, p.on_pool ? nullptr : n_vis_c, p.on_pool ? pool_c : nullptr,
-                     idx->K, idx->topk + r0 * idx->K, sel_ws, sel_bytes, s_sel);
-      if (s2 != CSA2_OK) return s2;
-      if (p.build_pool && a->pool_blocks > 0) {
-        const hipError_t e = launch_topk(bmax + r0 * p.n_blocks, rows_c, p.n_blocks, n_vis_c, 8, nullptr,
-                                         a->pool_blocks, pool_c, 8, n_vis_c, kv->n_max, sel_ws, as_stream(s_sel));
+      if (p.build_pool && a->pool_blocks >= idx->K) {
+        // The pool of the best pool_blocks >= K blocks holds the layer's own flat Top-K: each Top-K
+        // position's block max is at least its score, so a block left out would be outranked by
+        // >= K block maxima. The pool is chosen first and the Top-K taken from its positions.
+        hipError_t e = launch_topk(bmax + r0 * p.n_blocks, rows_c, p.n_blocks, n_vis_c, 8, nullptr, a->pool_blocks,
+                                   pool_c, 8, n_vis_c, kv->n_max, sel_ws, as_stream(s_sel));
         if (e != hipSuccess) return CSA2_E_HIP;
+        e = launch_topk_gather(scores_c, p.ncols, rows_c, pool_c, idx->P, idx->K, idx->topk + r0 * idx->K, sel_ws,
+                               as_stream(s_sel));
+        if (e != hipSuccess) return CSA2_E_HIP;
+      } else {
+        s2 = csa2_topk(scores_c, rows_c, p.ncols, p.on_pool ? nullptr : n_vis_c, p.on_pool ? pool_c : nullptr,
+                       idx->K, idx->topk + r0 * idx->K, sel_ws, sel_bytes, s_sel);
+        if (s2 != CSA2_OK) return s2;
+        if (p.build_pool && a->pool_blocks > 0) {
+          const hipError_t e = launch_topk(bmax + r0 * p.n_blocks, rows_c, p.n_blocks, n_vis_c, 8, nullptr,
+                                           a->pool_blocks, pool_c, 8, n_vis_c, kv->n_max, sel_ws, as_stream(s_sel));
+          if (e != hipSuccess) return CSA2_E_HIP;
+        }
       }
     }
     return csa2_sparse_attn(a->q + r0 * a->H * kv->D, kv->rows + (int64_t)b0 * kv->n_max * rb, kv->n_max,

@@ -34,6 +34,10 @@ hipError_t launch_topk(const float* scores, int64_t rows, int n_cols, const int3
                        int valid_div, const int32_t* col_to_pos, int k, int32_t* idx,
                        int expand_block, const int32_t* expand_n_vis, int expand_limit, void* ws,
                        hipStream_t s);
+// Top-K over the positions listed in cand [rows, P] (-1 = empty), scored from the full score rows
+// scores [rows, n_max]; the chosen positions are written ascending. Scratch as topk_workspace(rows, P, k).
+hipError_t launch_topk_gather(const float* scores, int n_max, int64_t rows, const int32_t* cand, int P, int k,
+                              int32_t* idx, void* ws, hipStream_t s);
 
 // sparse_attn.hip
 size_t attn_workspace(int B, int T, int H, int D, int K);

@@ -38,12 +38,14 @@ constexpr int kSegMax = 40960;        // columns per workgroup: up to 40 per lan
 constexpr int kSegSplit = 16384;      // segment length when a row is split over workgroups
 constexpr int kHistBins = 4096;       // largest radix digit: 12 bits
 
-enum TopkSrc { kSrcScores = 0, kSrcMapped = 1, kSrcCand = 2 };
+enum TopkSrc { kSrcScores = 0, kSrcMapped = 1, kSrcCand = 2, kSrcGather = 3 };
 enum TopkDst { kDstIdx = 0, kDstExpand = 1, kDstCand = 2 };
 
 struct TopkArgs {
   const float* scores;         // [rows, ld] (kSrcScores, kSrcMapped)
-  const int32_t* map;          // [rows, ld] column -> position, -1 = empty (kSrcMapped)
+  const int32_t* map;          // [rows, ld] column -> position, -1 = empty (kSrcMapped, kSrcGather)
+  const float* gscores;        // kSrcGather: scores [rows, gld] indexed by position
+  int64_t gld;
   const uint32_t* ckeys;       // [rows, ld] candidate keys (kSrcCand)
   const int32_t* cpos;         // [rows, ld] candidate positions, -1 = empty (kSrcCand)
   const int32_t* n_valid;      // nullable: columns valid per row = ceil(n_valid[r] / valid_div)
@@ -158,16 +160,25 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a, int seg_
       if (SRC == kSrcCand) {
         key[i] = a.ckeys[rowoff + e];
         pos[i % NP] = a.cpos[rowoff + e];
+      } else if (SRC == kSrcGather) {
+        pos[i % NP] = a.map[rowoff + e];
       } else {
         sv[i] = a.scores[rowoff + e];
         if (SRC == kSrcMapped) pos[i % NP] = a.map[rowoff + e];
       }
+    }
+    if (SRC == kSrcGather) {
+      // scores of the listed positions (clamped into the row: every load is in bounds)
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        sv[i] = a.gscores[(int64_t)r * a.gld + min(max(pos[i % NP], 0), (int)a.gld - 1)];
     }
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = wbase + 64 * i + lane;
       bool ok = e < lim;
       if (SRC != kSrcScores) ok = ok && pos[i % NP] >= 0;
+      if (SRC == kSrcGather) ok = ok && pos[i % NP] < a.gld;
       if (SRC != kSrcCand) key[i] = score_key(sv[i]);
       key[i] = ok ? key[i] : 0u;
     }
@@ -360,10 +371,10 @@ size_t topk_workspace(int64_t rows, int n_cols, int k) {
   return 2 * largest;
 }
 
-hipError_t launch_topk(const float* scores, int64_t rows, int n_cols, const int32_t* n_valid,
-                       int valid_div, const int32_t* col_to_pos, int k, int32_t* idx,
-                       int expand_block, const int32_t* expand_n_vis, int expand_limit, void* ws,
-                       hipStream_t s) {
+static hipError_t run_topk(const float* scores, int64_t rows, int n_cols, const int32_t* n_valid,
+                           int valid_div, const int32_t* col_to_pos, int64_t gather_ld, int k, int32_t* idx,
+                           int expand_block, const int32_t* expand_n_vis, int expand_limit, void* ws,
+                           hipStream_t s) {
   if (rows == 0 || k == 0) return hipSuccess;
   const TopkPlan p = make_plan(rows, n_cols, k);
   if (p.seg[p.stages - 1] > kSegMax) return hipErrorInvalidValue;
@@ -375,6 +386,8 @@ hipError_t launch_topk(const float* scores, int64_t rows, int n_cols, const int3
   TopkArgs a{};
   a.scores = scores;
   a.map = col_to_pos;
+  a.gscores = scores;
+  a.gld = gather_ld;
   a.n_valid = n_valid;
   a.valid_div = valid_div > 0 ? valid_div : 1;
   a.n_in = n_cols;
@@ -395,6 +408,7 @@ hipError_t launch_topk(const float* scores, int64_t rows, int n_cols, const int3
     }
     hipError_t e;
     if (st > 0) e = launch_src<kSrcCand>(grid, a, last, p.seg[st], k, s);
+    else if (gather_ld > 0) e = launch_src<kSrcGather>(grid, a, last, p.seg[st], k, s);
     else if (col_to_pos) e = launch_src<kSrcMapped>(grid, a, last, p.seg[st], k, s);
     else e = launch_src<kSrcScores>(grid, a, last, p.seg[st], k, s);
     if (e != hipSuccess) return e;
@@ -408,6 +422,20 @@ hipError_t launch_topk(const float* scores, int64_t rows, int n_cols, const int3
     }
   }
   return hipSuccess;
+}
+
+hipError_t launch_topk(const float* scores, int64_t rows, int n_cols, const int32_t* n_valid,
+                       int valid_div, const int32_t* col_to_pos, int k, int32_t* idx,
+                       int expand_block, const int32_t* expand_n_vis, int expand_limit, void* ws,
+                       hipStream_t s) {
+  return run_topk(scores, rows, n_cols, n_valid, valid_div, col_to_pos, 0, k, idx, expand_block, expand_n_vis,
+                  expand_limit, ws, s);
+}
+
+hipError_t launch_topk_gather(const float* scores, int n_max, int64_t rows, const int32_t* cand, int P, int k,
+                              int32_t* idx, void* ws, hipStream_t s) {
+  if (n_max <= 0) return hipErrorInvalidValue;
+  return run_topk(scores, rows, P, nullptr, 1, cand, n_max, k, idx, 0, nullptr, 0, ws, s);
 }
 
 }  // namespace csa2

@@ -15,9 +15,9 @@ from parity_util import k_idx_device, kv_rows_device, q_device
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("pool", [False, True])
-def test_layer_step_graph_replay(pool):
-    wl = W.CONFIGS[4 if pool else 3].scaled(B=4, N=3000, k=128, pool_blocks=64 if pool else 0)
+@pytest.mark.parametrize("pool,pool_blocks", [(False, 0), (True, 64), (True, 256)])
+def test_layer_step_graph_replay(pool, pool_blocks):
+    wl = W.CONFIGS[4 if pool else 3].scaled(B=4, N=3000, k=128, pool_blocks=pool_blocks)
     rows, kidx = kv_rows_device(wl), k_idx_device(wl)
     q0, qi0 = q_device(wl, 0, "q"), q_device(wl, 0, "q_idx")
     q1, qi1 = q_device(wl, 1, "q"), q_device(wl, 1, "q_idx")

@@ -266,3 +266,19 @@ def test_determinism():
     assert torch.equal(a, b) and torch.equal(la, lb)
     s = torch.from_numpy(W.random_scores(1, 8, 70000, "ties")).cuda()
     assert torch.equal(P.topk(s, 512), P.topk(s, 512))
+
+
+def test_split_merge_with_garbage_and_reused_workspace():
+    """Rows split over several workgroups leave partial results in the workspace: a workspace of
+    random bytes, reused for several calls of different shapes, must give the oracle's result
+    every time."""
+    g = torch.Generator().manual_seed(5)
+    ws = torch.randint(0, 256, (64 << 20,), dtype=torch.uint8, generator=g).cuda()
+    scale = 1 / np.sqrt(512)
+    for B, K, seed in [(2, 512, 21), (2, 512, 22), (3, 300, 23), (1, 1024, 24), (2, 512, 25)]:
+        rows, qb, idx = _attn_case(B, 1, 64, 1500, K, seed=seed)
+        out, lse = P.sparse_attn(dev_bf16(qb), torch.from_numpy(rows).cuda(), torch.from_numpy(idx).cuda(), scale,
+                                 ws=ws)
+        out, lse = _sync_np(out), _sync_np(lse)
+        ref, lref = _attn_ref(rows, qb, idx, scale)
+        check_attn(out, ref, lse, lref, f"split merge B={B} K={K} seed={seed}")
