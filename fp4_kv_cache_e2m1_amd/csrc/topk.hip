@@ -276,9 +276,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a, int seg_
         } else if (DST == kDstExpand) {
           const int nv = a.exp_nvis ? a.exp_nvis[r] : a.exp_limit;
           int32_t* dst = a.idx + ((int64_t)r * k + o) * a.expand;
-          for (int v = 0; v < a.expand; ++v) {
-            const int p = p_i * a.expand + v;
-            dst[v] = p < nv ? p : -1;
+          if (a.expand == 8 && (reinterpret_cast<uintptr_t>(a.idx) & 15) == 0) {  // HSI block: two 16-byte stores
+            const int p0 = p_i * 8;
+            const int4 lo = make_int4(p0 < nv ? p0 : -1, p0 + 1 < nv ? p0 + 1 : -1, p0 + 2 < nv ? p0 + 2 : -1,
+                                      p0 + 3 < nv ? p0 + 3 : -1);
+            const int4 hi = make_int4(p0 + 4 < nv ? p0 + 4 : -1, p0 + 5 < nv ? p0 + 5 : -1, p0 + 6 < nv ? p0 + 6 : -1,
+                                      p0 + 7 < nv ? p0 + 7 : -1);
+            reinterpret_cast<int4*>(dst)[0] = lo;
+            reinterpret_cast<int4*>(dst)[1] = hi;
+          } else {
+            for (int v = 0; v < a.expand; ++v) {
+              const int p = p_i * a.expand + v;
+              dst[v] = p < nv ? p : -1;
+            }
           }
         } else {
           a.okeys[r * a.old + (int64_t)seg * k + o] = kv;
