@@ -362,6 +362,15 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
 #pragma unroll
     for (int kq = 0; kq < 4; ++kq) raw_q[kq] = qp[4 * (4 * w4 + kq) + g];
   }
+  // the slice's entry positions: read from global once (issued together with the query loads),
+  // staged in LDS for every gather
+  constexpr int IPT = (kMaxKPS + NT - 1) / NT;
+  int ipos[IPT];
+#pragma unroll
+  for (int m = 0; m < IPT; ++m) {
+    const int i = tid + m * NT;
+    ipos[m] = i < nk ? irow[i] : -1;
+  }
   // gathers run PF chunks ahead: registers gr[v] hold chunk c0 + v KC of the current group
   uint4 gr[PF][GATHER];
   auto gather = [&](uint4* dst, int c0) {
@@ -373,18 +382,16 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
         const int kr = it / 18, part = it - kr * 18;
         const int ks = c0 + kr;
         if (ks < snk) {
-          const int p = irow[sbeg + ks];
-          if (p >= 0 && p < n_max) dst[m] = *reinterpret_cast<const uint4*>(rbase + (int64_t)p * kRowB + 16 * part);
+          const int p = sidx[sbeg + ks];
+          if (p >= 0) dst[m] = *reinterpret_cast<const uint4*>(rbase + (int64_t)p * kRowB + 16 * part);
         }
       }
     }
   };
 #pragma unroll
-  for (int v = 0; v < PF; ++v)
-    if (v * KC < snk) gather(gr[v], v * KC);
-  for (int i = tid; i < nk; i += NT) {
-    const int p = irow[i];
-    sidx[i] = (p >= 0 && p < n_max) ? p : -1;
+  for (int m = 0; m < IPT; ++m) {
+    const int i = tid + m * NT;
+    if (i < nk) sidx[i] = (ipos[m] >= 0 && ipos[m] < n_max) ? ipos[m] : -1;
   }
   if (sg == 0) {
     float amax = 0.0f;
@@ -399,6 +406,9 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
     if (g == 0) ml[w4 * 16 + l16] = amax;
   }
   __syncthreads();
+#pragma unroll
+  for (int v = 0; v < PF; ++v)
+    if (v * KC < snk) gather(gr[v], v * KC);
   // the queries, scaled per head by a power of two and converted to f16 (exact), into LDS
   float qscale;
   {
