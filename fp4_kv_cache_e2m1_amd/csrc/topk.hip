@@ -8,17 +8,20 @@
 //
 // One workgroup (16 waves) selects the k best of a segment of up to 40960 columns. Lane l of
 // wave w holds columns 64*(w*EPL + i) + l (i < EPL) in registers, so a wave's i-th register row
-// is 64 consecutive columns. The selection is a short chain of barrier-separated phases, each
-// a few LDS operations, because at decode sizes (a few rows) latency, not bandwidth, is the cost:
-//   0. all loads of the segment are issued at once (no per-element branches); the count of
-//      valid columns and of non-empty lane groups come out of one block reduction;
-//   1. pruning bound: the EPL columns of a lane form a group; at least k group maxima are >= the
-//      k-th largest group maximum, so the k-th best column is too. A 12-bit histogram of the
-//      group maxima gives a lower edge L of that maximum's bin and every column below L is
-//      dropped (typically ~95% of them);
-//   2. MSB-first radix select over the survivors with 12, 12 and 8-bit digits, stopping as soon
-//      as the threshold bin is taken whole. Two histogram buffers alternate, so the next one is
-//      cleared while the current one fills and no phase needs an extra barrier;
+// is 64 consecutive columns. At decode sizes (a few rows) latency, not bandwidth, is the cost, so
+// the selection is a short chain of phases with one barrier each:
+//   0. all loads of the segment are issued at once (no per-element branches); the number of
+//      valid columns and of non-empty lane groups and the key range come from one reduction;
+//   1. pruning bound: the EPL columns of a lane form a group (two groups, its halves, when k
+//      exceeds half the lanes); at least k group maxima are >= the k-th largest group maximum,
+//      so the k-th best column is too. A histogram of the group maxima gives a lower edge L of
+//      that maximum's bin and every column below L is dropped (typically ~95% of them). When
+//      they fit, the survivors are packed in column order into 4 registers per lane;
+//   2. MSB-first radix select over the survivors with digits of up to 12 bits, starting below
+//      the common prefix of the candidates' key range (so that close keys still spread over the
+//      bins; LDS atomics on one bin serialize), stopping once the threshold bin is taken whole.
+//      Each wave locates the bin itself from a 64-bin coarse histogram and the fine bins under
+//      it, and three histogram buffers rotate, so a pass needs a single barrier;
 //   3. compaction in ascending column order with ballot + mbcnt per register row (no shuffles),
 //      so the result is deterministic.
 // With many rows (prefill) one workgroup per row keeps the chip busy, so rows up to 40960 columns
@@ -37,6 +40,8 @@ constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kSegMax = 40960;        // columns per workgroup: up to 40 per lane
 constexpr int kSegSplit = 16384;      // segment length when a row is split over workgroups
 constexpr int kHistBins = 4096;       // largest radix digit: 12 bits
+constexpr int kCoarse = 64;           // coarse bins: the top 6 bits of a digit
+constexpr int kCompact = 4 * kTopkThreads;  // pruning survivors packed 4 per lane
 
 enum TopkSrc { kSrcScores = 0, kSrcMapped = 1, kSrcCand = 2, kSrcGather = 3 };
 enum TopkDst { kDstIdx = 0, kDstExpand = 1, kDstCand = 2 };
@@ -77,67 +82,230 @@ CSA2_DEV int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Block-wide sum (every thread gets it). One barrier; red[] must not be rewritten before the
-// next barrier.
-CSA2_DEV int block_sum(int v, int* red) {
-  v = __builtin_amdgcn_readlane(wave_incl_scan(v), 63);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  int t = 0;
-#pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) t += red[w];
-  return t;
+// Bin of the krem-th largest entry of a histogram, found by each wave on its own (no barrier):
+// lane l reads coarse bin 63 - l (the top 6 bits of the digit), a prefix scan over the lanes
+// picks the coarse bin holding the krem-th entry, and the 2^fshift fine bins inside it are
+// scanned the same way. Returns the digit d, the count in bins above d and the count in d.
+// Every wave reads the same histograms, so every wave gets the same answer.
+CSA2_DEV void find_bin(const uint32_t* fine, const uint32_t* coarse, int fshift, int krem, int& d, int& above,
+                       int& cnt) {
+  const int lane = threadIdx.x & 63;
+  const int hc = (int)coarse[63 - lane];
+  const int ic = wave_incl_scan(hc);
+  const uint64_t mc = __ballot(ic >= krem);
+  const int lc = mc ? (int)__builtin_ctzll(mc) : 0;
+  const int cb = 63 - lc;
+  const int ab = __builtin_amdgcn_readlane(ic - hc, lc);
+  const int nf = 1 << fshift;
+  const int hf = lane < nf ? (int)fine[cb * nf + nf - 1 - lane] : 0;
+  const int inf = wave_incl_scan(hf);
+  const uint64_t mf = __ballot(ab + inf >= krem);
+  const int lf = mf ? (int)__builtin_ctzll(mf) : 0;
+  d = cb * nf + nf - 1 - lf;
+  above = ab + __builtin_amdgcn_readlane(inf - hf, lf);
+  cnt = __builtin_amdgcn_readlane(hf, lf);
 }
 
-// Given a filled histogram of nbins bins, find the bin d holding the krem-th largest entry:
-// count above d < krem <= count above d + hist[d]. Returns (d, above, hist[d]) to every
-// thread. Two barriers; info[] is read after the second and rewritten only after the first
-// barrier of the next call.
-CSA2_DEV void find_bin(const uint32_t* hist, int nbins, int krem, int* red, int* info, int& d, int& above,
-                       int& cnt) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int bpt = nbins >= kTopkThreads ? nbins / kTopkThreads : 1;
-  const bool owner = tid * bpt < nbins;
-  int h[4] = {0, 0, 0, 0};
-  int tot = 0;
-  if (owner)
-    for (int u = 0; u < bpt; ++u) { h[u] = hist[tid * bpt + u]; tot += h[u]; }
-  const int pre = wave_incl_scan(tot);
-  if (lane == 63) red[wave] = pre;
-  __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) {
-    const int x = red[w];
-    before += w < wave ? x : 0;
-    all += x;
+// Histograms of one selection phase: 12-bit (or 8-bit) digit counts and their 64 coarse bins.
+struct alignas(16) TopkHist {
+  uint32_t fine[kHistBins];
+  uint32_t coarse[kCoarse];
+};
+
+CSA2_DEV void clear_hist(TopkHist& h) {
+  reinterpret_cast<uint4*>(h.fine)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+  static_assert(kHistBins == 4 * kTopkThreads, "one 16-byte clear per thread");
+  if (threadIdx.x < kCoarse) h.coarse[threadIdx.x] = 0u;
+}
+
+// Called by the lanes that hold a candidate (divergent). LDS atomics on one address serialize;
+// with AGG (dense candidates, whose coarse bins are few) the lanes of a wave that share the first
+// such lane's coarse bin add their count in one atomic.
+template <bool AGG>
+CSA2_DEV void hist_add(TopkHist& h, uint32_t digit, int fshift) {
+  atomicAdd(&h.fine[digit], 1u);
+  const uint32_t cb = digit >> fshift;
+  if (AGG) {
+    const uint32_t c0 = __builtin_amdgcn_readfirstlane(cb);
+    const uint64_t m = __ballot(cb == c0);
+    if (cb != c0) atomicAdd(&h.coarse[cb], 1u);
+    else if (lanes_below(m) == 0) atomicAdd(&h.coarse[c0], (uint32_t)__popcll(m));
+  } else {
+    atomicAdd(&h.coarse[cb], 1u);
   }
-  int ab = all - before - pre;    // entries in bins above this thread's bins
-  if (owner && ab < krem && krem <= ab + tot) {
-    for (int u = bpt - 1; u >= 0; --u) {
-      if (ab < krem && krem <= ab + h[u]) {
-        info[0] = tid * bpt + u;
-        info[1] = ab;
-        info[2] = h[u];
+}
+
+// Maximum over the 64 lanes of a wave (every lane gets it).
+CSA2_DEV uint32_t wave_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Bits below the common prefix of two keys (0 when equal), and the mask of that prefix.
+CSA2_DEV int low_bits(uint32_t lo, uint32_t hi) {
+  const uint32_t x = lo ^ hi;
+  return x ? 32 - __builtin_clz(x) : 0;
+}
+CSA2_DEV uint32_t prefix_mask(int rb) { return rb >= 32 ? 0u : ~0u << rb; }
+
+// Shared memory of one selection. Three histogram buffers rotate so that each phase needs one
+// barrier: a phase fills its buffer, clears the one two phases ahead, and every wave then reads
+// its own copy of the answer; the buffer cleared in a phase was last read before the previous
+// phase's barrier.
+template <int NLIST>
+struct TopkSmem {
+  TopkHist hist[3];
+  uint32_t list_key[NLIST];      // survivors of the pruning bound, in column order
+  int32_t list_pos[NLIST];
+  int totals[3];                 // valid columns, non-empty lane groups, non-empty half groups
+  uint32_t kmax, kmin;           // largest and smallest key
+  uint32_t gmin[2];              // smallest non-empty group maximum (whole, half groups)
+  int wcnt[kTopkWaves][2];
+};
+
+// Radix select, compaction and output over R register rows per lane. Row i of lane l in wave w is
+// the (w, i, l)-th candidate in column order; key 0 marks an empty slot. Positions are pos[i] when
+// EXPL, else implied as col0 + 64 i + lane. kk of the candidates are taken; `sel` says a
+// threshold must be found (kk < number of candidates), and every candidate key lies in
+// [lo0, hi0]. The digits start below the common prefix of lo0 and hi0: candidates that survived
+// selection so far are close in value, and a digit over bits they all share would send them to
+// a few bins, whose LDS atomics then serialize. DENSE: most register slots hold candidates. The
+// first radix pass fills hist[1] (clear on entry) and clears hist[2].
+template <int SRC, int DST, int R, bool EXPL, bool DENSE, int NPOS, int NLIST>
+CSA2_DEV void topk_finish(const TopkArgs& a, TopkSmem<NLIST>& sm, uint32_t (&key)[R], const int32_t (&pos)[NPOS],
+                          int col0, int k, int kk, bool sel, uint32_t lo0, uint32_t hi0, int r, int seg) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // loaded now so that no store of the output waits on it (loads and stores share one counter)
+  const int exp_nv = DST == kDstExpand ? (a.exp_nvis ? a.exp_nvis[r] : a.exp_limit) : 0;
+  // ---- threshold range [lo, hi] and how many of it to take (krem) ----
+  uint32_t lo = 1, hi = 0xFFFFFFFFu;
+  int krem = kk;
+  if (sel) {
+    // MSB-first radix select over the rb bits below the common prefix, up to 12 bits a pass;
+    // pass p fills buffer (p + 1) % 3 and clears (p + 2) % 3
+    int rb = low_bits(lo0, hi0);
+    uint32_t mask = prefix_mask(rb);
+    uint32_t prefix = hi0 & mask;
+    for (int pass = 0; pass < 3 && rb > 0; ++pass) {
+      const int bits = min(12, rb);
+      const int shift = rb - bits;
+      const int fshift = max(0, bits - 6);
+      const uint32_t dmask = (1u << bits) - 1u;
+      TopkHist& h = sm.hist[(pass + 1) % 3];
+      if (DENSE && pass == 0) {
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+          if (key[i] != 0) hist_add<true>(h, (key[i] >> shift) & dmask, fshift);
+      } else {
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+          if (key[i] != 0 && (key[i] & mask) == prefix) hist_add<false>(h, (key[i] >> shift) & dmask, fshift);
       }
-      ab += h[u];
+      clear_hist(sm.hist[(pass + 2) % 3]);
+      __syncthreads();
+      int d, ab, c;
+      find_bin(h.fine, h.coarse, fshift, krem, d, ab, c);
+      krem -= ab;
+      prefix |= (uint32_t)d << shift;
+      mask |= dmask << shift;
+      rb -= bits;
+      if (c == krem) break;
+    }
+    lo = prefix;
+    hi = prefix | ~mask;
+  }
+
+  // ---- compaction in ascending column order ----
+  int gt = 0, eq = 0;
+  if (kk > 0) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      gt += __popcll(__ballot(key[i] > hi));
+      eq += __popcll(__ballot(key[i] >= lo && key[i] <= hi));
     }
   }
+  if (lane == 0) { sm.wcnt[wave][0] = gt; sm.wcnt[wave][1] = eq; }
   __syncthreads();
-  d = info[0];
-  above = info[1];
-  cnt = info[2];
+  // output offset of this wave: the waves before it take all their keys above the threshold
+  // range and, in column order, the first krem keys inside it
+  int out_pos = 0, eq_before = 0;
+  {
+    const int g = lane < kTopkWaves ? sm.wcnt[lane][0] : 0;
+    const int e = lane < kTopkWaves ? sm.wcnt[lane][1] : 0;
+    const int eb = wave_incl_scan(e) - e;
+    const int take = g + max(0, min(e, krem - eb));
+    const int tb = wave_incl_scan(take) - take;
+    out_pos = __builtin_amdgcn_readlane(tb, wave);
+    eq_before = __builtin_amdgcn_readlane(eb, wave);
+  }
+  if (kk > 0) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const uint32_t kv = key[i];
+      const bool is_gt = kv > hi;                  // lo >= 1, so key 0 is never taken
+      const bool is_eq = kv >= lo && kv <= hi;
+      const uint64_t be = __ballot(is_eq);
+      const bool take = is_gt || (is_eq && eq_before + lanes_below(be) < krem);
+      const uint64_t bt = __ballot(take);
+      if (take) {
+        const int o = out_pos + lanes_below(bt);
+        const int32_t p_i = EXPL ? pos[i % NPOS] : col0 + 64 * i + lane;
+        if (DST == kDstIdx) {
+          a.idx[(int64_t)r * k + o] = p_i;
+        } else if (DST == kDstExpand) {
+          const int nv = exp_nv;
+          int32_t* dst = a.idx + ((int64_t)r * k + o) * a.expand;
+          if (a.expand == 8 && (reinterpret_cast<uintptr_t>(a.idx) & 15) == 0) {  // HSI block: two 16-byte stores
+            const int p0 = p_i * 8;
+            const int4 lo4 = make_int4(p0 < nv ? p0 : -1, p0 + 1 < nv ? p0 + 1 : -1, p0 + 2 < nv ? p0 + 2 : -1,
+                                       p0 + 3 < nv ? p0 + 3 : -1);
+            const int4 hi4 = make_int4(p0 + 4 < nv ? p0 + 4 : -1, p0 + 5 < nv ? p0 + 5 : -1,
+                                       p0 + 6 < nv ? p0 + 6 : -1, p0 + 7 < nv ? p0 + 7 : -1);
+            reinterpret_cast<int4*>(dst)[0] = lo4;
+            reinterpret_cast<int4*>(dst)[1] = hi4;
+          } else {
+            for (int v = 0; v < a.expand; ++v) {
+              const int p = p_i * a.expand + v;
+              dst[v] = p < nv ? p : -1;
+            }
+          }
+        } else {
+          a.okeys[r * a.old + (int64_t)seg * k + o] = kv;
+          a.opos[r * a.old + (int64_t)seg * k + o] = p_i;
+        }
+      }
+      out_pos += __popcll(bt);
+      eq_before += __popcll(be);
+    }
+  }
+  // ---- padding ----
+  for (int o = kk + (int)threadIdx.x; o < k; o += kTopkThreads) {
+    if (DST == kDstIdx) {
+      a.idx[(int64_t)r * k + o] = -1;
+    } else if (DST == kDstExpand) {
+      for (int v = 0; v < a.expand; ++v) a.idx[((int64_t)r * k + o) * a.expand + v] = -1;
+    } else {
+      a.okeys[r * a.old + (int64_t)seg * k + o] = 0u;
+      a.opos[r * a.old + (int64_t)seg * k + o] = -1;
+    }
+  }
 }
 
 template <int SRC, int DST, int EPL>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a, int seg_len, int k) {
-  __shared__ uint32_t hist[2][kHistBins];
-  __shared__ int red[kTopkWaves];
-  __shared__ int info[4];
-  __shared__ int wcnt[kTopkWaves][2];
+  // pruning survivors are packed when there are more than 4 registers per lane to gain from it
+  constexpr bool kPack = EPL > 4;
+  __shared__ TopkSmem<kPack ? kCompact : 1> sm;
 
   const int r = blockIdx.x, seg = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c0 = seg * seg_len;
   const int n = min(seg_len, a.n_in - c0);
   int lim = n;                              // valid columns of this segment: [0, lim)
@@ -152,8 +320,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a, int seg_
   constexpr int NP = SRC == kSrcScores ? 1 : EPL;   // positions are kept only when not implied
   uint32_t key[EPL];
   int32_t pos[NP];
+  float sv[EPL];
   if (lim > 0) {
-    float sv[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = min(wbase + 64 * i + lane, lim - 1);  // clamped: every load is in bounds
@@ -167,6 +335,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a, int seg_
         if (SRC == kSrcMapped) pos[i % NP] = a.map[rowoff + e];
       }
     }
+  }
+  // the first two phases' buffers are cleared while the loads are in flight
+  clear_hist(sm.hist[0]);
+  clear_hist(sm.hist[1]);
+  if (tid < 3) sm.totals[tid] = 0;
+  if (tid == 0) {
+    sm.kmax = 0u;
+    sm.kmin = 0xFFFFFFFFu;
+    sm.gmin[0] = 0xFFFFFFFFu;
+    sm.gmin[1] = 0xFFFFFFFFu;
+  }
+  __syncthreads();
+  if (lim > 0) {
     if (SRC == kSrcGather) {
       // scores of the listed positions (clamped into the row: every load is in bounds)
 #pragma unroll
@@ -186,130 +367,113 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a, int seg_
 #pragma unroll
     for (int i = 0; i < EPL; ++i) key[i] = 0u;
   }
+  // group maxima: a lane's EPL columns (gm) and its two halves (gh[0], gh[1])
+  constexpr int HALF = EPL >= 8 ? EPL / 2 : EPL;
   int cnt = 0;
-  uint32_t gm = 0;
+  uint32_t gh[2] = {0u, 0u}, mn = 0u;       // mn: complement of the smallest key
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     cnt += key[i] != 0;
-    gm = max(gm, key[i]);
+    gh[i / HALF > 0] = max(gh[i / HALF > 0], key[i]);
+    mn = max(mn, key[i] ? ~key[i] : 0u);
   }
-  for (int i = tid; i < kHistBins; i += kTopkThreads) hist[0][i] = 0;
-  // valid columns (<= 16384) in the low 16 bits, non-empty groups (<= 1024) above
-  const int packed = block_sum(cnt | ((gm != 0) << 16), red);
-  const int total = packed & 0xFFFF, ng = packed >> 16;
-  const int kk = min(k, total);
-
-  // ---- threshold range [lo, hi] and how many of it to take (krem) ----
-  uint32_t lo = 1, hi = 0xFFFFFFFFu;
-  int krem = kk;
-  int cur = 0;                              // histogram buffer filled next
-  if (kk > 0 && kk < total) {
-    // 1. pruning bound from the per-lane group maxima (needs >= k non-empty groups)
-    if (EPL >= 4 && ng >= kk) {
-      if (gm != 0) atomicAdd(&hist[0][gm >> 20], 1u);
-      for (int i = tid; i < kHistBins; i += kTopkThreads) hist[1][i] = 0;
-      __syncthreads();
-      int d, ab, c;
-      find_bin(hist[0], kHistBins, kk, red, info, d, ab, c);
-      const uint32_t L = (uint32_t)d << 20;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (key[i] < L) key[i] = 0;
-      cur = 1;
-    }
-    // 2. radix select over the survivors (the buffer `cur` is clear)
-    uint32_t prefix = 0, mask = 0;
-    constexpr int kShift[3] = {20, 8, 0};
-    constexpr int kBits[3] = {12, 12, 8};
-    for (int pass = 0; pass < 3; ++pass) {
-      const int shift = kShift[pass];
-      const uint32_t dmask = (1u << kBits[pass]) - 1u;
-      uint32_t* h = hist[cur];
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (key[i] != 0 && (key[i] & mask) == prefix) atomicAdd(&h[(key[i] >> shift) & dmask], 1u);
-      for (int i = tid; i < kHistBins; i += kTopkThreads) hist[cur ^ 1][i] = 0;
-      __syncthreads();
-      int d, ab, c;
-      find_bin(h, 1 << kBits[pass], krem, red, info, d, ab, c);
-      krem -= ab;
-      prefix |= (uint32_t)d << shift;
-      mask |= dmask << shift;
-      cur ^= 1;
-      if (c == krem) break;
-    }
-    lo = prefix;
-    hi = prefix | ~mask;
-  }
-
-  // ---- 3. compaction in ascending column order ----
-  int gt = 0, eq = 0;
-  if (kk > 0) {
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      gt += __popcll(__ballot(key[i] > hi));
-      eq += __popcll(__ballot(key[i] >= lo && key[i] <= hi));
+  const uint32_t gm = max(gh[0], gh[1]);
+  // phase 0: counts and key range
+  {
+    const int wc = __builtin_amdgcn_readlane(wave_incl_scan(cnt), 63);
+    const int wg = (int)__popcll(__ballot(gm != 0));
+    const int wh = (int)(__popcll(__ballot(gh[0] != 0)) + __popcll(__ballot(gh[1] != 0)));
+    const uint32_t wmax = wave_max(gm), wmn = wave_max(mn), wgmn = wave_max(gm ? ~gm : 0u);
+    const uint32_t whmn = wave_max(max(gh[0] ? ~gh[0] : 0u, gh[1] ? ~gh[1] : 0u));
+    if (lane == 0) {
+      atomicAdd(&sm.totals[0], wc);
+      atomicAdd(&sm.totals[1], wg);
+      atomicAdd(&sm.totals[2], wh);
+      atomicMax(&sm.kmax, wmax);
+      atomicMin(&sm.kmin, ~wmn);
+      atomicMin(&sm.gmin[0], ~wgmn);
+      atomicMin(&sm.gmin[1], ~whmn);
     }
   }
-  if (lane == 0) { wcnt[wave][0] = gt; wcnt[wave][1] = eq; }
   __syncthreads();
-  int out_pos = 0, eq_before = 0;
-  for (int w = 0; w < wave; ++w) {
-    const int g = wcnt[w][0], e = wcnt[w][1];
-    out_pos += g + max(0, min(e, krem - eq_before));
-    eq_before += e;
-  }
-  if (kk > 0) {
+  const int total = sm.totals[0];
+  const uint32_t kmax = sm.kmax, kmin = sm.kmin;
+  const int kk = min(k, total);
+  const bool sel = kk > 0 && kk < total;
+  // half groups when kk is more than half the lane groups: the kk-th largest of the lane group
+  // maxima would be a weak bound
+  const bool halves = EPL >= 8 && 2 * kk > sm.totals[1];
+  const int ng = sm.totals[halves ? 2 : 1];
+
+  // 1. pruning bound: at least kk (disjoint) group maxima are >= the kk-th largest group maximum,
+  //    so the kk-th best column is too; every column below that maximum's bin is dropped. The
+  //    bins are up to 12 bits below the common prefix of the group maxima.
+  if (EPL >= 4 && sel && ng >= kk) {
+    const uint32_t gmin = sm.gmin[halves ? 1 : 0];
+    const int rb = low_bits(gmin, kmax);
+    uint32_t L = kmax;                      // all group maxima equal
+    if (rb > 0) {
+      // 12-bit bins: when the group maxima span both signs, the top 6 bits alone would put
+      // every positive one in a single bin
+      const int bits = min(12, rb), shift = rb - bits, fshift = max(0, bits - 6);
+      const uint32_t dm = (1u << bits) - 1u;
+      if (halves) {
+        if (gh[0] != 0) hist_add<true>(sm.hist[0], (gh[0] >> shift) & dm, fshift);
+        if (gh[1] != 0) hist_add<true>(sm.hist[0], (gh[1] >> shift) & dm, fshift);
+      } else {
+        if (gm != 0) hist_add<true>(sm.hist[0], (gm >> shift) & dm, fshift);
+      }
+      __syncthreads();
+      int d, ab, c;
+      find_bin(sm.hist[0].fine, sm.hist[0].coarse, fshift, kk, d, ab, c);
+      L = (kmax & prefix_mask(rb)) | ((uint32_t)d << shift);
+    }
+    L = max(L, 1u);
+    int surv = 0;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      const uint32_t kv = key[i];
-      const bool is_gt = kv > hi;                  // lo >= 1, so key 0 is never taken
-      const bool is_eq = kv >= lo && kv <= hi;
-      const uint64_t be = __ballot(is_eq);
-      const bool take = is_gt || (is_eq && eq_before + lanes_below(be) < krem);
-      const uint64_t bt = __ballot(take);
-      if (take) {
-        const int o = out_pos + lanes_below(bt);
-        const int32_t p_i = SRC == kSrcScores ? c0 + wbase + 64 * i + lane : pos[i % NP];
-        if (DST == kDstIdx) {
-          a.idx[(int64_t)r * k + o] = p_i;
-        } else if (DST == kDstExpand) {
-          const int nv = a.exp_nvis ? a.exp_nvis[r] : a.exp_limit;
-          int32_t* dst = a.idx + ((int64_t)r * k + o) * a.expand;
-          if (a.expand == 8 && (reinterpret_cast<uintptr_t>(a.idx) & 15) == 0) {  // HSI block: two 16-byte stores
-            const int p0 = p_i * 8;
-            const int4 lo = make_int4(p0 < nv ? p0 : -1, p0 + 1 < nv ? p0 + 1 : -1, p0 + 2 < nv ? p0 + 2 : -1,
-                                      p0 + 3 < nv ? p0 + 3 : -1);
-            const int4 hi = make_int4(p0 + 4 < nv ? p0 + 4 : -1, p0 + 5 < nv ? p0 + 5 : -1, p0 + 6 < nv ? p0 + 6 : -1,
-                                      p0 + 7 < nv ? p0 + 7 : -1);
-            reinterpret_cast<int4*>(dst)[0] = lo;
-            reinterpret_cast<int4*>(dst)[1] = hi;
-          } else {
-            for (int v = 0; v < a.expand; ++v) {
-              const int p = p_i * a.expand + v;
-              dst[v] = p < nv ? p : -1;
-            }
+      if (key[i] < L) key[i] = 0;
+      surv += (int)__popcll(__ballot(key[i] != 0));
+    }
+    // The survivors are usually a few percent of the columns. When they fit, they are packed in
+    // column order into 4 rows per lane, so the passes below touch 4 registers, not EPL.
+    if constexpr (kPack) {
+      if (lane == 0) sm.wcnt[wave][0] = surv;
+      __syncthreads();
+      const int sw = lane < kTopkWaves ? sm.wcnt[lane][0] : 0;
+      const int sincl = wave_incl_scan(sw);
+      const int s_total = __builtin_amdgcn_readlane(sincl, kTopkWaves - 1);
+      if (s_total <= kCompact) {
+        int o = __builtin_amdgcn_readlane(sincl - sw, wave);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+          const bool live = key[i] != 0;
+          const uint64_t m = __ballot(live);
+          if (live) {
+            const int j = o + lanes_below(m);
+            sm.list_key[j] = key[i];
+            sm.list_pos[j] = SRC != kSrcScores ? pos[i % NP] : c0 + wbase + 64 * i + lane;
           }
-        } else {
-          a.okeys[r * a.old + (int64_t)seg * k + o] = kv;
-          a.opos[r * a.old + (int64_t)seg * k + o] = p_i;
+          o += (int)__popcll(m);
         }
+        __syncthreads();
+        uint32_t key4[4];
+        int32_t pos4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int j = wave * 256 + 64 * u + lane;
+          key4[u] = j < s_total ? sm.list_key[j] : 0u;
+          pos4[u] = sm.list_pos[min(j, kCompact - 1)];
+        }
+        topk_finish<SRC, DST, 4, true, false>(a, sm, key4, pos4, 0, k, kk, true, L, kmax, r, seg);
+        return;
       }
-      out_pos += __popcll(bt);
-      eq_before += __popcll(be);
+      // wcnt is rewritten only after the next barrier, which every wave reaches after reading it
     }
+    topk_finish<SRC, DST, EPL, SRC != kSrcScores, true>(a, sm, key, pos, c0 + wbase, k, kk, true, L, kmax, r, seg);
+    return;
   }
-  // ---- padding ----
-  for (int o = kk + tid; o < k; o += kTopkThreads) {
-    if (DST == kDstIdx) {
-      a.idx[(int64_t)r * k + o] = -1;
-    } else if (DST == kDstExpand) {
-      for (int v = 0; v < a.expand; ++v) a.idx[((int64_t)r * k + o) * a.expand + v] = -1;
-    } else {
-      a.okeys[r * a.old + (int64_t)seg * k + o] = 0u;
-      a.opos[r * a.old + (int64_t)seg * k + o] = -1;
-    }
-  }
+  topk_finish<SRC, DST, EPL, SRC != kSrcScores, true>(a, sm, key, pos, c0 + wbase, k, kk, sel, kmin, kmax, r, seg);
 }
 
 template <int SRC, int DST>
