@@ -617,53 +617,73 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
   }
 }
 
-// Merge of split results: one wave per (query row, head), lane owns 8 channels. All splits'
-// (max, sum) pairs are read first, then every split's partial row is loaded in one batch.
+// Merge of split results: one wave per (query row, head), lane owns 8 channels. The first 8
+// splits' partial rows are loaded together with all splits' (max, sum) pairs, so the common case
+// waits on memory once. Workgroups are placed on the XCD whose L2 holds the partials: the
+// attention kernels give each XCD a contiguous range of query rows, and so does this mapping.
 constexpr int kMaxSplits = 64;
+
+// wave-wide max / sum of one value per lane (DPP row shifts, then row broadcasts)
+CSA2_DEV float wave_fmax(float v) {
+  const int ninf = __float_as_int(-INFINITY);
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x111, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x112, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x114, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x118, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x142, 0xA, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x143, 0xC, 0xF, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+CSA2_DEV float wave_fsum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
                                                            int n_splits, int64_t n_rows_h,
                                                            float* __restrict__ out,
-                                                           float* __restrict__ lse) {
+                                                           float* __restrict__ lse, int per_xcd) {
   const int lane = threadIdx.x & 63;
-  const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t u = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  const int64_t rh = u * 4 + (threadIdx.x >> 6);
   if (rh >= n_rows_h) return;
+  float4 a[8], c[8];
+#pragma unroll
+  for (int sp = 0; sp < 8; ++sp) {
+    if (sp < n_splits) {
+      const float4* pp = reinterpret_cast<const float4*>(part_o + (sp * n_rows_h + rh) * kD) + 2 * lane;
+      a[sp] = pp[0];
+      c[sp] = pp[1];
+    }
+  }
   // lane s < n_splits holds split s's (m, l)
   float ms = -INFINITY, ls = 0.0f;
   if (lane < n_splits) {
     ms = part_ml[2 * (lane * n_rows_h + rh)];
     ls = part_ml[2 * (lane * n_rows_h + rh) + 1];
   }
-  float M = ms;
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  const float M = wave_fmax(ms);
   const float w_lane = (ms == -INFINITY) ? 0.0f : exp2f(ms - M);
-  float L = w_lane * ls;
-  for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off, 64);
+  const float L = wave_fsum(w_lane * ls);
   float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (M != -INFINITY) {
-    for (int s0 = 0; s0 < n_splits; s0 += 8) {
-      float4 a[8], c[8];
-      float w[8];
+  // empty splits (weight 0) may hold anything: they are skipped, not multiplied
+  auto add = [&](float w, const float4& x, const float4& y) {
+    if (w == 0.0f) return;
+    o[0] += w * x.x; o[1] += w * x.y; o[2] += w * x.z; o[3] += w * x.w;
+    o[4] += w * y.x; o[5] += w * y.y; o[6] += w * y.z; o[7] += w * y.w;
+  };
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int sp = s0 + u;
-        w[u] = __shfl(w_lane, sp < n_splits ? sp : 0, 64);
-        if (sp < n_splits) {
-          const float4* pp = reinterpret_cast<const float4*>(part_o + (sp * n_rows_h + rh) * kD) + 2 * lane;
-          a[u] = pp[0];
-          c[u] = pp[1];
-        } else {
-          w[u] = 0.0f;
-          a[u] = c[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (w[u] == 0.0f) continue;
-        o[0] += w[u] * a[u].x; o[1] += w[u] * a[u].y; o[2] += w[u] * a[u].z; o[3] += w[u] * a[u].w;
-        o[4] += w[u] * c[u].x; o[5] += w[u] * c[u].y; o[6] += w[u] * c[u].z; o[7] += w[u] * c[u].w;
-      }
-    }
+  for (int sp = 0; sp < 8; ++sp)
+    if (sp < n_splits) add(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), sp)), a[sp], c[sp]);
+  for (int sp = 8; sp < n_splits; ++sp) {
+    const float4* pp = reinterpret_cast<const float4*>(part_o + (sp * n_rows_h + rh) * kD) + 2 * lane;
+    add(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), sp)), pp[0], pp[1]);
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   float4* op = reinterpret_cast<float4*>(out + rh * kD) + 2 * lane;
@@ -741,8 +761,9 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* rows, int n_max,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_splits == 1) return e;
   const int64_t rows_h = nq * H;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)((rows_h + 3) / 4)), dim3(256), 0, s, part_o, part_ml,
-                     n_splits, rows_h, out, lse);
+  const int per_xcd = (int)(((rows_h + 3) / 4 + 7) / 8);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, part_o, part_ml,
+                     n_splits, rows_h, out, lse, per_xcd);
   return hipGetLastError();
 }
 

@@ -16,7 +16,7 @@
 //      exceeds half the lanes); at least k group maxima are >= the k-th largest group maximum,
 //      so the k-th best column is too. A histogram of the group maxima gives a lower edge L of
 //      that maximum's bin and every column below L is dropped (typically ~95% of them). When
-//      they fit, the survivors are packed in column order into 4 registers per lane;
+//      they fit, each wave packs its survivors in column order into 4 registers per lane;
 //   2. MSB-first radix select over the survivors with digits of up to 12 bits, starting below
 //      the common prefix of the candidates' key range (so that close keys still spread over the
 //      bins; LDS atomics on one bin serialize), stopping once the threshold bin is taken whole.
@@ -25,7 +25,7 @@
 //   3. compaction in ascending column order with ballot + mbcnt per register row (no shuffles),
 //      so the result is deterministic.
 // With many rows (prefill) one workgroup per row keeps the chip busy, so rows up to 40960 columns
-// are one segment. With few rows (decode) rows longer than 16384 columns are split for
+// are one segment. With few rows (decode) rows longer than 32768 columns are split for
 // parallelism: each segment's k best (key, position) pairs go to scratch, and the same kernel
 // selects again over those candidates; the global k best always survive their segment.
 #include <algorithm>
@@ -39,9 +39,11 @@ constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kSegMax = 40960;        // columns per workgroup: up to 40 per lane
 constexpr int kSegSplit = 16384;      // segment length when a row is split over workgroups
+constexpr int kSegSingle = 32768;     // few rows: longest row kept in one workgroup
 constexpr int kHistBins = 4096;       // largest radix digit: 12 bits
 constexpr int kCoarse = 64;           // coarse bins: the top 6 bits of a digit
 constexpr int kCompact = 4 * kTopkThreads;  // pruning survivors packed 4 per lane
+constexpr int kWaveSlots = kCompact / kTopkWaves;
 
 enum TopkSrc { kSrcScores = 0, kSrcMapped = 1, kSrcCand = 2, kSrcGather = 3 };
 enum TopkDst { kDstIdx = 0, kDstExpand = 1, kDstCand = 2 };
@@ -429,41 +431,37 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a, int seg_
       L = (kmax & prefix_mask(rb)) | ((uint32_t)d << shift);
     }
     L = max(L, 1u);
-    int surv = 0;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
+    for (int i = 0; i < EPL; ++i)
       if (key[i] < L) key[i] = 0;
-      surv += (int)__popcll(__ballot(key[i] != 0));
-    }
     // The survivors are usually a few percent of the columns. When they fit, they are packed in
     // column order into 4 rows per lane, so the passes below touch 4 registers, not EPL.
     if constexpr (kPack) {
-      if (lane == 0) sm.wcnt[wave][0] = surv;
-      __syncthreads();
-      const int sw = lane < kTopkWaves ? sm.wcnt[lane][0] : 0;
-      const int sincl = wave_incl_scan(sw);
-      const int s_total = __builtin_amdgcn_readlane(sincl, kTopkWaves - 1);
-      if (s_total <= kCompact) {
-        int o = __builtin_amdgcn_readlane(sincl - sw, wave);
+      // each wave packs its survivors, in column order, into its own kWaveSlots slots; when no
+      // wave overflows, every wave continues from its slots (the slot order keeps column order)
+      int o = 0;
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-          const bool live = key[i] != 0;
-          const uint64_t m = __ballot(live);
-          if (live) {
-            const int j = o + lanes_below(m);
-            sm.list_key[j] = key[i];
-            sm.list_pos[j] = SRC != kSrcScores ? pos[i % NP] : c0 + wbase + 64 * i + lane;
-          }
-          o += (int)__popcll(m);
+      for (int i = 0; i < EPL; ++i) {
+        const bool live = key[i] != 0;
+        const uint64_t m = __ballot(live);
+        const int j = o + lanes_below(m);
+        if (live && j < kWaveSlots) {
+          sm.list_key[wave * kWaveSlots + j] = key[i];
+          sm.list_pos[wave * kWaveSlots + j] = SRC != kSrcScores ? pos[i % NP] : c0 + wbase + 64 * i + lane;
         }
-        __syncthreads();
+        o += (int)__popcll(m);
+      }
+      if (lane == 0) sm.wcnt[wave][0] = o;
+      __syncthreads();
+      const int most = (int)wave_max((uint32_t)(lane < kTopkWaves ? sm.wcnt[lane][0] : 0));
+      if (most <= kWaveSlots) {
         uint32_t key4[4];
         int32_t pos4[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int j = wave * 256 + 64 * u + lane;
-          key4[u] = j < s_total ? sm.list_key[j] : 0u;
-          pos4[u] = sm.list_pos[min(j, kCompact - 1)];
+          const int j = 64 * u + lane;
+          key4[u] = j < o ? sm.list_key[wave * kWaveSlots + j] : 0u;
+          pos4[u] = sm.list_pos[wave * kWaveSlots + j];
         }
         topk_finish<SRC, DST, 4, true, false>(a, sm, key4, pos4, 0, k, kk, true, L, kmax, r, seg);
         return;
@@ -520,7 +518,7 @@ static TopkPlan make_plan(int64_t rows, int n_cols, int k) {
   while (true) {
     p.n_in[st] = n;
     // many rows: one workgroup per row is enough parallelism; few rows: split long rows
-    const int single = rows >= 256 ? kSegMax : kSegSplit;
+    const int single = rows >= 256 ? kSegMax : kSegSingle;
     if (n <= single || st == 7) {
       p.seg[st] = n;
       p.nseg[st] = 1;
