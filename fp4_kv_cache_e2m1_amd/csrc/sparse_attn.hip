@@ -271,10 +271,13 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
 // NG sub-groups of 4 waves each take an equal part of the slice and walk it in chunks of KC
 // entries, in lockstep (shared barriers, separate LDS buffers), so each SIMD runs NG waves that
 // hide each other's latencies. Wave w of a sub-group owns channels 128w .. 128w+127 throughout:
-//   - the chunk is dequantized once into X[entry][channel] (f16, exact);
+//   - it gathers only the bytes of its channels (a lane: one entry's 64-channel slab, 32 code
+//     bytes and 4 scale bytes, straight into registers) and dequantizes them into its own slab
+//     of X[entry][channel] (f16, exact), which only it reads, so no barrier guards X;
 //   - scores: each wave computes partial S^T = X Q^T over its own 128 channels for all KC
-//     entries x 16 heads (16x16x32 f16 MFMA) and writes them to a small LDS tile; after one
-//     barrier every wave adds the 4 partials, so the sub-group's waves hold the same scores;
+//     entries x 16 heads (16x16x32 f16 MFMA) and writes them to a small LDS tile (two, used in
+//     turn); after the chunk's one barrier every wave adds the 4 partials, so the sub-group's
+//     waves hold the same scores;
 //   - every wave runs the same online softmax (identical inputs and arithmetic, so the running
 //     (max, sum) agree across the sub-group), then O^T += X^T P^T for its 128 channels over the
 //     chunk (16x16x16 f16 MFMA). The A operand (4 consecutive entries of one channel per lane)
@@ -296,9 +299,8 @@ constexpr int kDecodeFill = 256;                // decode workgroups wanted: one
 template <int KC, int NG>
 struct DecodeSmem {
   static constexpr int kX = KC * kXPitch * 2;
-  static constexpr int kRaw = KC * kRowB;
   static constexpr int kS = 4 * KC * 16 * 4;    // the 4 waves' partial scores, KC entries x 16 heads
-  static constexpr int kGroup = kX + kRaw + kS; // one sub-group's buffers
+  static constexpr int kGroup = kX + 2 * kS;    // one sub-group's buffers (two score tiles)
   static constexpr int kOut = 4 * 8 * 64 * 16;  // one sub-group's output tiles at the merge
   static_assert(NG * kGroup >= (NG - 1) * kOut, "the merge reuses the sub-groups' buffers");
   static constexpr int kIdx = kMaxKPS * 4;
@@ -321,8 +323,7 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
     float* __restrict__ part_ml, int n_rows, int n_splits, int per_xcd) {
   using Sm = DecodeSmem<KC, NG>;
   constexpr int NT = 256 * NG, NS = KC / 16;    // NS entry steps of 16 per chunk
-  constexpr int GATHER = (KC * 18 + 255) / 256; // 16-byte row pieces per thread per chunk
-  static_assert(KC % 16 == 0 && KC <= 64, "whole 16-entry steps, one lane per entry for the mask");
+  static_assert(KC == 32, "a wave's 64 lanes gather the chunk's 32 entries x 2 slabs of 64 channels");
   static_assert(NG >= 1 && NG <= 4, "sub-groups");
   __shared__ __attribute__((aligned(16))) unsigned char smem[Sm::kTotal];
   int* sidx = reinterpret_cast<int*>(smem + NG * Sm::kGroup);
@@ -338,14 +339,13 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
   const int qr = u / (n_splits * n_hg), split = (u / n_hg) % n_splits, hg = u % n_hg;
   const int b = qr / T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int sg = wave >> 2, w4 = wave & 3, t4 = tid & 255;   // sub-group, wave and thread within it
+  const int sg = wave >> 2, w4 = wave & 3;   // sub-group and wave within it
   const int l16 = lane & 15, g = lane >> 4;
   const int head = hg * 16 + l16;
 
   unsigned char* gbase = smem + sg * Sm::kGroup;
   uint16_t* xs = reinterpret_cast<uint16_t*>(gbase);
-  uint4* raw = reinterpret_cast<uint4*>(gbase + Sm::kX);
-  float4* sp4 = reinterpret_cast<float4*>(gbase + Sm::kX + Sm::kRaw);
+  float4* sp4b = reinterpret_cast<float4*>(gbase + Sm::kX);
 
   const int kbeg = split * keys_per_split;
   const int nk = max(0, min(K, kbeg + keys_per_split) - kbeg);        // entries of this workgroup
@@ -355,6 +355,16 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
   const int32_t* irow = idx + (int64_t)qr * K + kbeg;
   const uint8_t* rbase = rows + (int64_t)b * n_max * kRowB;
 
+  // Lane: entry gkey of a chunk, channel slab gcs (64 channels) of this wave's 128. The
+  // positions of its entries in the first PF chunks are loaded first, so that those gathers can
+  // start without waiting for the LDS copy of the positions.
+  const int gkey = lane & 31, gcs = 2 * w4 + (lane >> 5);
+  int pos0[PF];
+#pragma unroll
+  for (int v = 0; v < PF; ++v) {
+    const int ks = v * KC + gkey;
+    pos0[v] = ks < snk ? irow[sbeg + ks] : -1;
+  }
   // sub-group 0 loads the 16 heads' queries, wave w4 its channel blocks 4 w4 .. 4 w4 + 3
   uint4 raw_q[4];
   if (sg == 0) {
@@ -372,22 +382,27 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
     ipos[m] = i < nk ? irow[i] : -1;
   }
   // gathers run PF chunks ahead: registers gr[v] hold chunk c0 + v KC of the current group
-  uint4 gr[PF][GATHER];
-  auto gather = [&](uint4* dst, int c0) {
-#pragma unroll
-    for (int m = 0; m < GATHER; ++m) {
-      const int it = t4 + m * 256;
-      dst[m] = make_uint4(0, 0, 0, 0);
-      if (it < KC * 18) {
-        const int kr = it / 18, part = it - kr * 18;
-        const int ks = c0 + kr;
-        if (ks < snk) {
-          const int p = sidx[sbeg + ks];
-          if (p >= 0) dst[m] = *reinterpret_cast<const uint4*>(rbase + (int64_t)p * kRowB + 16 * part);
-        }
-      }
+  struct Piece {
+    uint4 c01, c23;     // the slab's 64 E2M1 codes
+    uint32_t sc;        // its 4 E4M3 scales
+  };
+  Piece gr[PF];
+  auto gather_at = [&](Piece& d, int p) {   // p: position, or anything outside [0, n_max)
+    d.c01 = d.c23 = make_uint4(0, 0, 0, 0);
+    d.sc = 0u;
+    if (p >= 0 && p < n_max) {
+      const uint8_t* rp = rbase + (int64_t)p * kRowB;
+      d.c01 = *reinterpret_cast<const uint4*>(rp + 32 * gcs);
+      d.c23 = *reinterpret_cast<const uint4*>(rp + 32 * gcs + 16);
+      d.sc = *reinterpret_cast<const uint32_t*>(rp + 256 + 4 * gcs);
     }
   };
+  auto gather = [&](Piece& d, int c0) {
+    const int ks = c0 + gkey;
+    gather_at(d, ks < snk ? sidx[sbeg + ks] : -1);
+  };
+#pragma unroll
+  for (int v = 0; v < PF; ++v) gather_at(gr[v], pos0[v]);
 #pragma unroll
   for (int m = 0; m < IPT; ++m) {
     const int i = tid + m * NT;
@@ -406,9 +421,6 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
     if (g == 0) ml[w4 * 16 + l16] = amax;
   }
   __syncthreads();
-#pragma unroll
-  for (int v = 0; v < PF; ++v)
-    if (v * KC < snk) gather(gr[v], v * KC);
   // the queries, scaled per head by a power of two and converted to f16 (exact), into LDS
   float qscale;
   {
@@ -431,6 +443,13 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
     }
     qscale = sm_scale * kLog2e * ldexpf(1.0f, -qe);
   }
+  __syncthreads();                                 // the scaled queries are in LDS
+  f16x8_t qb[4];                                   // this wave's query fragments, kept in registers
+  {
+    const uint16_t* qr16 = qs + l16 * kXPitch + 128 * w4 + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qb[kk] = *reinterpret_cast<const f16x8_t*>(qr16 + 32 * kk);
+  }
 
   // output tiles of this wave: channels 128 w4 + 16 j + (4 g + i), head l16
   f32x4_t acc[8];
@@ -440,7 +459,6 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
   // transposing-read base for the P.V operand: entry 4 g + l16/4 (+16 s), channel 128 w4 + 4 (l16%4) (+16 j)
   const uint16_t* xtr = xs + (4 * g + (l16 >> 2)) * kXPitch + 128 * w4 + 4 * (l16 & 3);
   // partial-score tile layout: [wave][entry / 4][head][entry % 4] (a lane's 4 entries are one float4)
-  float4* my_sp = sp4 + w4 * (KC / 4) * 16;
 
   // every sub-group runs the same number of chunk steps (barriers are shared); steps past its
   // entries do no work
@@ -450,44 +468,27 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
     const int c0 = cg + v * KC;
     if (c0 >= sub_len) break;
     const bool active = c0 < snk;
+    float4* sp4 = sp4b + ((c0 / KC) & 1) * (4 * (KC / 4) * 16);
     if (active) {
+      // dequantize this lane's slab into X; the X slab of wave w4 is read by wave w4 only, and a
+      // wave's LDS operations complete in order, so the reads below see these writes
+      const Piece& pc = gr[v];
+      const f16x2_t s01 = e4m3x2_to_f16(pc.sc), s23 = e4m3x2_to_f16(pc.sc >> 16);
+      const f16x2_t sgm[4] = {f16x2_t{s01[0], s01[0]}, f16x2_t{s01[1], s01[1]}, f16x2_t{s23[0], s23[0]},
+                              f16x2_t{s23[1], s23[1]}};
+      const uint32_t cw[8] = {pc.c01.x, pc.c01.y, pc.c01.z, pc.c01.w, pc.c23.x, pc.c23.y, pc.c23.z, pc.c23.w};
+      uint4* dst = reinterpret_cast<uint4*>(xs + gkey * kXPitch + 64 * gcs);
 #pragma unroll
-      for (int m = 0; m < GATHER; ++m) {
-        const int it = t4 + m * 256;
-        if (it < KC * 18) raw[it] = gr[v][m];
+      for (int wi = 0; wi < 8; ++wi) {
+        uint32_t vv[4];
+        e2m1x8_to_f16(cw[wi], sgm[wi >> 1], vv);
+        dst[wi] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
       }
-    }
-    __syncthreads();
-    if (active && c0 + PF * KC < snk) gather(gr[v], c0 + PF * KC);
-    // dequantize: item = (entry, 64-channel slab 0..7)
-    if (active) {
-      for (int it = t4; it < KC * 8; it += 256) {
-        const int key = it % KC, cs = it / KC;
-        const uint8_t* rb = reinterpret_cast<const uint8_t*>(raw) + key * kRowB;
-        const uint4 c01 = *reinterpret_cast<const uint4*>(rb + 32 * cs);
-        const uint4 c23 = *reinterpret_cast<const uint4*>(rb + 32 * cs + 16);
-        const uint32_t sc4 = *reinterpret_cast<const uint32_t*>(rb + 256 + 4 * cs);
-        const f16x2_t s01 = e4m3x2_to_f16(sc4), s23 = e4m3x2_to_f16(sc4 >> 16);
-        const f16x2_t sgm[4] = {f16x2_t{s01[0], s01[0]}, f16x2_t{s01[1], s01[1]}, f16x2_t{s23[0], s23[0]},
-                                f16x2_t{s23[1], s23[1]}};
-        const uint32_t cw[8] = {c01.x, c01.y, c01.z, c01.w, c23.x, c23.y, c23.z, c23.w};
-        uint4* dst = reinterpret_cast<uint4*>(xs + key * kXPitch + 64 * cs);
-#pragma unroll
-        for (int wi = 0; wi < 8; ++wi) {
-          uint32_t vv[4];
-          e2m1x8_to_f16(cw[wi], sgm[wi >> 1], vv);
-          dst[wi] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
-        }
-      }
-    }
-    __syncthreads();
-    // partial S^T over this wave's channels: entry tile t, lane holds entries 16 t + 4 g + i of head l16
-    if (active) {
+      if (c0 + PF * KC < snk) gather(gr[v], c0 + PF * KC);
+      __builtin_amdgcn_wave_barrier();
+      // partial S^T over this wave's channels: entry tile t, lane holds entries 16 t + 4 g + i of head l16
       const uint16_t* xr = xs + l16 * kXPitch + 128 * w4 + 8 * g;
-      const uint16_t* qr16 = qs + l16 * kXPitch + 128 * w4 + 8 * g;
-      f16x8_t qb[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) qb[kk] = *reinterpret_cast<const f16x8_t*>(qr16 + 32 * kk);
+      float4* my_sp = sp4 + w4 * (KC / 4) * 16;
 #pragma unroll
       for (int t = 0; t < NS; ++t) {
         f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;  // two chains halve the dependency latency
