@@ -309,11 +309,16 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_share
         // The pool of the best pool_blocks >= K blocks holds the layer's own flat Top-K: each Top-K
         // position's block max is at least its score, so a block left out would be outranked by
         // >= K block maxima. The pool is chosen first and the Top-K taken from its positions.
-        hipError_t e = launch_topk(bmax + r0 * p.n_blocks, rows_c, p.n_blocks, n_vis_c, 8, nullptr, a->pool_blocks,
-                                   pool_c, 8, n_vis_c, kv->n_max, sel_ws, as_stream(s_sel));
-        if (e != hipSuccess) return CSA2_E_HIP;
-        e = launch_topk_gather(scores_c, p.ncols, rows_c, pool_c, idx->P, idx->K, idx->topk + r0 * idx->K, sel_ws,
-                               as_stream(s_sel));
+        hipError_t e = launch_pool_topk(bmax + r0 * p.n_blocks, rows_c, p.n_blocks, n_vis_c, a->pool_blocks, pool_c,
+                                        scores_c, p.ncols, idx->K, idx->topk + r0 * idx->K, as_stream(s_sel));
+        if (e == hipErrorNotSupported) {
+          (void)hipGetLastError();
+          e = launch_topk(bmax + r0 * p.n_blocks, rows_c, p.n_blocks, n_vis_c, 8, nullptr, a->pool_blocks, pool_c, 8,
+                          n_vis_c, kv->n_max, sel_ws, as_stream(s_sel));
+          if (e != hipSuccess) return CSA2_E_HIP;
+          e = launch_topk_gather(scores_c, p.ncols, rows_c, pool_c, idx->P, idx->K, idx->topk + r0 * idx->K, sel_ws,
+                                 as_stream(s_sel));
+        }
         if (e != hipSuccess) return CSA2_E_HIP;
       } else {
         s2 = csa2_topk(scores_c, rows_c, p.ncols, p.on_pool ? nullptr : n_vis_c, p.on_pool ? pool_c : nullptr,

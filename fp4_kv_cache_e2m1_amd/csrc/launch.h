@@ -38,6 +38,14 @@ hipError_t launch_topk(const float* scores, int64_t rows, int n_cols, const int3
 // scores [rows, n_max]; the chosen positions are written ascending. Scratch as topk_workspace(rows, P, k).
 hipError_t launch_topk_gather(const float* scores, int n_max, int64_t rows, const int32_t* cand, int P, int k,
                               int32_t* idx, void* ws, hipStream_t s);
+// Both selections of an HSI Full layer in one kernel (one workgroup per row): the pool of the
+// pool_blocks best blocks of block_max [rows, n_blocks] (as launch_topk with expand 8), then the
+// k best of the scores [rows, n_max] at the pool's positions (as launch_topk_gather). Returns
+// hipErrorNotSupported for sizes it does not cover (4096 < n_blocks <= 40960, 256 < pool_blocks
+// <= 2048); the caller then uses the two launches.
+hipError_t launch_pool_topk(const float* block_max, int64_t rows, int n_blocks, const int32_t* n_vis,
+                            int pool_blocks, int32_t* pool, const float* scores, int n_max, int k, int32_t* idx,
+                            hipStream_t s);
 
 // sparse_attn.hip
 size_t attn_workspace(int B, int T, int H, int D, int K);

@@ -45,14 +45,16 @@ constexpr int kCoarse = 64;           // coarse bins: the top 6 bits of a digit
 constexpr int kCompact = 4 * kTopkThreads;  // pruning survivors packed 4 per lane
 constexpr int kWaveSlots = kCompact / kTopkWaves;
 
-enum TopkSrc { kSrcScores = 0, kSrcMapped = 1, kSrcCand = 2, kSrcGather = 3 };
+enum TopkSrc { kSrcScores = 0, kSrcMapped = 1, kSrcCand = 2, kSrcGather = 3, kSrcBlocks = 4 };
 enum TopkDst { kDstIdx = 0, kDstExpand = 1, kDstCand = 2 };
 
 struct TopkArgs {
   const float* scores;         // [rows, ld] (kSrcScores, kSrcMapped)
   const int32_t* map;          // [rows, ld] column -> position, -1 = empty (kSrcMapped, kSrcGather)
-  const float* gscores;        // kSrcGather: scores [rows, gld] indexed by position
+  const float* gscores;        // kSrcGather, kSrcBlocks: scores [rows, gld] indexed by position
   int64_t gld;
+  const int32_t* blocks;       // kSrcBlocks (LDS): column c is position blocks[c / 8] * 8 + c % 8
+  int32_t* sel;                // kDstExpand, nullable (LDS): the selected blocks in output order
   const uint32_t* ckeys;       // [rows, ld] candidate keys (kSrcCand)
   const int32_t* cpos;         // [rows, ld] candidate positions, -1 = empty (kSrcCand)
   const int32_t* n_valid;      // nullable: columns valid per row = ceil(n_valid[r] / valid_div)
@@ -61,7 +63,7 @@ struct TopkArgs {
   int64_t ld;                  // row stride of the inputs
   int32_t* idx;                // [rows, k * (expand or 1)] (kDstIdx, kDstExpand)
   int expand;                  // kDstExpand: each selected block b becomes b*expand .. +expand-1
-  const int32_t* exp_nvis;     // nullable, expanded positions >= n_vis[r] become -1
+  const int32_t* exp_nvis;     // nullable, expanded positions >= n_vis[r] become -1 (also kSrcBlocks)
   int exp_limit;               // used instead of exp_nvis when it is null
   uint32_t* okeys;             // kDstCand: [rows, old]
   int32_t* opos;
@@ -261,6 +263,7 @@ CSA2_DEV void topk_finish(const TopkArgs& a, TopkSmem<NLIST>& sm, uint32_t (&key
         if (DST == kDstIdx) {
           a.idx[(int64_t)r * k + o] = p_i;
         } else if (DST == kDstExpand) {
+          if (a.sel) a.sel[o] = p_i;
           const int nv = exp_nv;
           int32_t* dst = a.idx + ((int64_t)r * k + o) * a.expand;
           if (a.expand == 8 && (reinterpret_cast<uintptr_t>(a.idx) & 15) == 0) {  // HSI block: two 16-byte stores
@@ -291,6 +294,7 @@ CSA2_DEV void topk_finish(const TopkArgs& a, TopkSmem<NLIST>& sm, uint32_t (&key
     if (DST == kDstIdx) {
       a.idx[(int64_t)r * k + o] = -1;
     } else if (DST == kDstExpand) {
+      if (a.sel) a.sel[o] = -1;
       for (int v = 0; v < a.expand; ++v) a.idx[((int64_t)r * k + o) * a.expand + v] = -1;
     } else {
       a.okeys[r * a.old + (int64_t)seg * k + o] = 0u;
@@ -299,13 +303,13 @@ CSA2_DEV void topk_finish(const TopkArgs& a, TopkSmem<NLIST>& sm, uint32_t (&key
   }
 }
 
-template <int SRC, int DST, int EPL>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a, int seg_len, int k) {
+// Selection of the k best columns of segment `seg` of row r by the whole workgroup.
+template <int SRC, int DST, int EPL, int NLIST>
+CSA2_DEV void topk_segment(const TopkArgs& a, int seg_len, int k, TopkSmem<NLIST>& sm, int r, int seg) {
   // pruning survivors are packed when there are more than 4 registers per lane to gain from it
   constexpr bool kPack = EPL > 4;
-  __shared__ TopkSmem<kPack ? kCompact : 1> sm;
+  static_assert(!kPack || NLIST >= kCompact, "room for the packed survivors");
 
-  const int r = blockIdx.x, seg = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c0 = seg * seg_len;
@@ -317,6 +321,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a, int seg_
   }
   const int wbase = wave * 64 * EPL;        // this wave's first column (segment-relative)
   const int64_t rowoff = (int64_t)r * a.ld + c0;
+  const int gnv = SRC == kSrcBlocks ? (a.exp_nvis ? a.exp_nvis[r] : a.exp_limit) : 0;
 
   // ---- 0. load: register i of lane l is column wbase + 64 i + l ----
   constexpr int NP = SRC == kSrcScores ? 1 : EPL;   // positions are kept only when not implied
@@ -332,6 +337,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a, int seg_
         pos[i % NP] = a.cpos[rowoff + e];
       } else if (SRC == kSrcGather) {
         pos[i % NP] = a.map[rowoff + e];
+      } else if (SRC == kSrcBlocks) {
+        const int blk = a.blocks[e >> 3];
+        const int p = blk * 8 + (e & 7);
+        pos[i % NP] = blk >= 0 && p < gnv ? p : -1;
       } else {
         sv[i] = a.scores[rowoff + e];
         if (SRC == kSrcMapped) pos[i % NP] = a.map[rowoff + e];
@@ -350,7 +359,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a, int seg_
   }
   __syncthreads();
   if (lim > 0) {
-    if (SRC == kSrcGather) {
+    if (SRC == kSrcGather || SRC == kSrcBlocks) {
       // scores of the listed positions (clamped into the row: every load is in bounds)
 #pragma unroll
       for (int i = 0; i < EPL; ++i)
@@ -361,7 +370,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a, int seg_
       const int e = wbase + 64 * i + lane;
       bool ok = e < lim;
       if (SRC != kSrcScores) ok = ok && pos[i % NP] >= 0;
-      if (SRC == kSrcGather) ok = ok && pos[i % NP] < a.gld;
+      if (SRC == kSrcGather || SRC == kSrcBlocks) ok = ok && pos[i % NP] < a.gld;
       if (SRC != kSrcCand) key[i] = score_key(sv[i]);
       key[i] = ok ? key[i] : 0u;
     }
@@ -472,6 +481,27 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a, int seg_
     return;
   }
   topk_finish<SRC, DST, EPL, SRC != kSrcScores, true>(a, sm, key, pos, c0 + wbase, k, kk, sel, kmin, kmax, r, seg);
+}
+
+template <int SRC, int DST, int EPL>
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a, int seg_len, int k) {
+  __shared__ TopkSmem<(EPL > 4 ? kCompact : 1)> sm;
+  topk_segment<SRC, DST, EPL>(a, seg_len, k, sm, blockIdx.x, blockIdx.y);
+}
+
+// HSI Full layer in one workgroup per row: the pool (the k_blocks best blocks of the block
+// maxima, expanded to positions) and then the layer's Top-K over the pool's positions, whose
+// list stays in LDS between the two selections.
+constexpr int kSelMax = kSegMax / 8;        // pool blocks: up to 40960 positions
+template <int EPL_A, int EPL_B>
+__global__ __launch_bounds__(kTopkThreads) void pool_topk_kernel(TopkArgs pa, TopkArgs pb, int k_blocks, int k) {
+  __shared__ TopkSmem<kCompact> sm;
+  __shared__ int32_t sel[kSelMax];
+  pa.sel = sel;
+  topk_segment<kSrcScores, kDstExpand, EPL_A>(pa, pa.n_in, k_blocks, sm, blockIdx.x, 0);
+  __syncthreads();                            // the selected blocks are in LDS; sm is free again
+  pb.blocks = sel;
+  topk_segment<kSrcBlocks, kDstIdx, EPL_B>(pb, pb.n_in, k, sm, blockIdx.x, 0);
 }
 
 template <int SRC, int DST>
@@ -608,6 +638,53 @@ hipError_t launch_topk_gather(const float* scores, int n_max, int64_t rows, cons
                               int32_t* idx, void* ws, hipStream_t s) {
   if (n_max <= 0) return hipErrorInvalidValue;
   return run_topk(scores, rows, P, nullptr, 1, cand, n_max, k, idx, 0, nullptr, 0, ws, s);
+}
+
+template <int EPL_A>
+static hipError_t launch_pool_topk_b(int epl_b, dim3 grid, const TopkArgs& pa, const TopkArgs& pb, int kb, int k,
+                                     hipStream_t s) {
+  const dim3 blk(kTopkThreads);
+  switch (epl_b) {
+    case 4: hipLaunchKernelGGL((pool_topk_kernel<EPL_A, 4>), grid, blk, 0, s, pa, pb, kb, k); break;
+    case 8: hipLaunchKernelGGL((pool_topk_kernel<EPL_A, 8>), grid, blk, 0, s, pa, pb, kb, k); break;
+    default: hipLaunchKernelGGL((pool_topk_kernel<EPL_A, 16>), grid, blk, 0, s, pa, pb, kb, k); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_topk(const float* block_max, int64_t rows, int n_blocks, const int32_t* n_vis,
+                            int pool_blocks, int32_t* pool, const float* scores, int n_max, int k, int32_t* idx,
+                            hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int P = pool_blocks * 8;
+  const int epl_a = (n_blocks + kTopkThreads - 1) / kTopkThreads;
+  const int epl_b = (P + kTopkThreads - 1) / kTopkThreads;
+  if (epl_a <= 4 || epl_a > 40 || epl_b <= 2 || epl_b > 16 || pool_blocks > kSelMax || k > P)
+    return hipErrorNotSupported;
+  TopkArgs pa{};
+  pa.scores = block_max;
+  pa.n_valid = n_vis;
+  pa.valid_div = 8;
+  pa.n_in = n_blocks;
+  pa.ld = n_blocks;
+  pa.idx = pool;
+  pa.expand = 8;
+  pa.exp_nvis = n_vis;
+  pa.exp_limit = n_max;
+  TopkArgs pb{};
+  pb.gscores = scores;
+  pb.gld = n_max;
+  pb.n_in = P;
+  pb.ld = P;
+  pb.idx = idx;
+  pb.exp_nvis = n_vis;
+  pb.exp_limit = n_max;
+  const dim3 grid((unsigned)rows);
+  if (epl_a <= 8) return launch_pool_topk_b<8>(epl_b, grid, pa, pb, pool_blocks, k, s);
+  if (epl_a <= 16) return launch_pool_topk_b<16>(epl_b, grid, pa, pb, pool_blocks, k, s);
+  if (epl_a <= 24) return launch_pool_topk_b<24>(epl_b, grid, pa, pb, pool_blocks, k, s);
+  if (epl_a <= 32) return launch_pool_topk_b<32>(epl_b, grid, pa, pb, pool_blocks, k, s);
+  return launch_pool_topk_b<40>(epl_b, grid, pa, pb, pool_blocks, k, s);
 }
 
 }  // namespace csa2

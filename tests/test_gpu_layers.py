@@ -147,6 +147,8 @@ SMALL = {
     "stack": W.CONFIGS[3].scaled(B=3, N=3000, k=128),
     "hsi": W.CONFIGS[4].scaled(B=2, N=6000, k=128, pool_blocks=64),        # pool blocks < K: flat Top-K
     "hsi_pool_first": W.CONFIGS[4].scaled(B=3, N=7000, k=128, pool_blocks=200),  # Top-K taken from the pool
+    # pool and Top-K selected by one kernel (10000 blocks, 4800 pool positions)
+    "hsi_pool_fused": W.CONFIGS[4].scaled(B=2, N=80000, k=256, pool_blocks=600),
     "full_h16": W.CONFIGS[1].scaled(B=2, N=1001, k=64),
     "prefill": W.CONFIGS[5].scaled(T=160, N=2700, p0=10600, n_existing=2650, k=256),
 }
