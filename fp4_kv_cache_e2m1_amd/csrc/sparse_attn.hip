@@ -618,6 +618,288 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
   }
 }
 
+// Prefill form: many query rows, so one workgroup per (query row, 64 heads) keeps the chip busy
+// and each gathered entry is dequantized once for all 64 heads. Four waves; wave w owns channels
+// 128w .. 128w+127 throughout, as in the decode form, but every wave serves all 64 heads:
+//   - gather + dequantize: a lane fetches one entry's 64-channel slab (32 code bytes, 4 scale
+//     bytes) straight into registers, PF chunks ahead, and writes it as f16 (exact) into the
+//     wave's own slab of X[entry][channel], which only that wave reads;
+//   - partial scores S^T = X Q^T over the wave's 128 channels for 32 entries x 64 heads
+//     (16x16x32 f16 MFMA); each X fragment read from LDS feeds the four 16-head tiles;
+//   - the four partials meet in LDS (the chunk's first barrier); wave w then owns head tile w:
+//     it adds them, runs the online softmax of those 16 heads (fp32, exp2 domain, lazy rescale)
+//     and publishes their probabilities (f16, already in the B-operand layout of P.V) and
+//     rescale factors (the second barrier);
+//   - O^T += X^T P^T for the wave's channels and all 64 heads (16x16x16 f16 MFMA, the A operand
+//     from the transposing LDS read ds_read_b64_tr_b16), after applying the published factors.
+// At 256 registers per lane and ~76 KB of LDS two workgroups share a CU, so one's gathers and
+// softmax overlap the other's matrix work. Workgroups of consecutive query rows, whose selections
+// overlap, run on one XCD and share its L2.
+constexpr int kPKC = 32;                         // prefill entries per chunk
+
+template <int PF, int OCC>
+__global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ rows, int n_max,
+    const int32_t* __restrict__ idx, int T, int H, int K, float sm_scale, float* __restrict__ out,
+    float* __restrict__ lse, int n_rows, int per_xcd) {
+  constexpr int KC = kPKC, NS = KC / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[KC * kXPitch];     // X[entry][channel], f16
+  __shared__ __attribute__((aligned(16))) float4 sp4[4 * NS * 4 * 64];   // partial S: [wave][t][ht][lane]
+  __shared__ __attribute__((aligned(16))) f16x4_t pbuf[4 * NS * 64];     // P: [ht][s][lane]
+  __shared__ float abuf[64];                                             // rescale factor per head
+  __shared__ float amx[4 * 64];                                          // per-wave |q| max per head
+  __shared__ float mlb[2 * 64];                                          // final (max, sum) per head
+  __shared__ int sidx[kMaxKPS];
+
+  const int n_hg = H / 64;
+  const int u = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (u >= n_rows * n_hg) return;
+  const int qr = u / n_hg, hbase = (u % n_hg) * 64;
+  const int b = qr / T;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int nk = K;
+  const int32_t* irow = idx + (int64_t)qr * K;
+  const uint8_t* rbase = rows + (int64_t)b * n_max * kRowB;
+
+  // gather lane: entry gkey of a chunk, 64-channel slab gcs of this wave's 128 channels
+  const int gkey = lane & 31, gcs = 2 * w + (lane >> 5);
+  int pos0[PF];
+#pragma unroll
+  for (int v = 0; v < PF; ++v) {
+    const int ks = v * KC + gkey;
+    pos0[v] = ks < nk ? irow[ks] : -1;
+  }
+  // this wave's query fragments: head 16 ht + l16, channels 128 w + 32 kk + 8 g .. +7
+  uint4 rq[4][4];
+  {
+    const uint16_t* qrow = q + ((int64_t)qr * H + hbase) * kD + 128 * w + 8 * g;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        rq[ht][kk] = *reinterpret_cast<const uint4*>(qrow + (int64_t)(16 * ht + l16) * kD + 32 * kk);
+  }
+  constexpr int IPT = kMaxKPS / 256;
+  int ipos[IPT];
+#pragma unroll
+  for (int m = 0; m < IPT; ++m) {
+    const int i = tid + m * 256;
+    ipos[m] = i < nk ? irow[i] : -1;
+  }
+  struct Piece {
+    uint4 c01, c23;     // the slab's 64 E2M1 codes
+    uint32_t sc;        // its 4 E4M3 scales
+  };
+  Piece gr[PF];
+  auto gather_at = [&](Piece& d, int p) {   // p: position, or anything outside [0, n_max)
+    d.c01 = d.c23 = make_uint4(0, 0, 0, 0);
+    d.sc = 0u;
+    if (p >= 0 && p < n_max) {
+      const uint8_t* rp = rbase + (int64_t)p * kRowB;
+      d.c01 = *reinterpret_cast<const uint4*>(rp + 32 * gcs);
+      d.c23 = *reinterpret_cast<const uint4*>(rp + 32 * gcs + 16);
+      d.sc = *reinterpret_cast<const uint32_t*>(rp + 256 + 4 * gcs);
+    }
+  };
+#pragma unroll
+  for (int v = 0; v < PF; ++v) gather_at(gr[v], pos0[v]);
+#pragma unroll
+  for (int m = 0; m < IPT; ++m) {
+    const int i = tid + m * 256;
+    if (i < nk) sidx[i] = (ipos[m] >= 0 && ipos[m] < n_max) ? ipos[m] : -1;
+  }
+  // per-head |q| max over this wave's channels
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint32_t wq[4] = {rq[ht][kk].x, rq[ht][kk].y, rq[ht][kk].z, rq[ht][kk].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(wq[e] << 16)), fabsf(__uint_as_float(wq[e] & 0xFFFF0000u))));
+    }
+    amax = head_max(amax);
+    if (g == 0) amx[w * 64 + 16 * ht + l16] = amax;
+  }
+  __syncthreads();
+  // queries scaled per head by a power of two (the head's largest |q| into [2^14, 2^15)) and
+  // converted to f16 exactly; the factor is folded into the softmax scale of the owning wave
+  f16x8_t qb[4][4];
+  float qscale = 0.0f;
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+    const int hh = 16 * ht + l16;
+    const float amax = fmaxf(fmaxf(amx[hh], amx[64 + hh]), fmaxf(amx[128 + hh], amx[192 + hh]));
+    const int qe = amax > 0.0f ? 14 - ilogbf(amax) : 0;
+    const float sc = ldexpf(1.0f, qe);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint32_t wq[4] = {rq[ht][kk].x, rq[ht][kk].y, rq[ht][kk].z, rq[ht][kk].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qb[ht][kk][2 * e] = (_Float16)(__uint_as_float(wq[e] << 16) * sc);
+        qb[ht][kk][2 * e + 1] = (_Float16)(__uint_as_float(wq[e] & 0xFFFF0000u) * sc);
+      }
+    }
+    if (ht == w) qscale = sm_scale * kLog2e * ldexpf(1.0f, -qe);
+  }
+
+  // output tiles: acc[ht][j] holds channels 128 w + 16 j + (4 g + i) of head 16 ht + l16
+  f32x4_t acc[4][8];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[ht][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;    // softmax state of head 16 w + l16 (this wave owns it)
+  // transposing-read base for the P.V operand: entry 4 g + l16/4 (+16 s), channel 128 w + 4 (l16%4) (+16 j)
+  const uint16_t* xtr = xs + (4 * g + (l16 >> 2)) * kXPitch + 128 * w + 4 * (l16 & 3);
+  const uint16_t* xr = xs + l16 * kXPitch + 128 * w + 8 * g;
+
+  for (int cg = 0; cg < nk; cg += PF * KC)
+#pragma unroll
+  for (int v = 0; v < PF; ++v) {
+    const int c0 = cg + v * KC;
+    if (c0 >= nk) break;
+    {
+      // dequantize this lane's slab into X (read by this wave only; a wave's LDS operations
+      // complete in order, so the reads below see these writes)
+      const Piece& pc = gr[v];
+      const f16x2_t s01 = e4m3x2_to_f16(pc.sc), s23 = e4m3x2_to_f16(pc.sc >> 16);
+      const f16x2_t sgm[4] = {f16x2_t{s01[0], s01[0]}, f16x2_t{s01[1], s01[1]}, f16x2_t{s23[0], s23[0]},
+                              f16x2_t{s23[1], s23[1]}};
+      const uint32_t cw[8] = {pc.c01.x, pc.c01.y, pc.c01.z, pc.c01.w, pc.c23.x, pc.c23.y, pc.c23.z, pc.c23.w};
+      uint4* dst = reinterpret_cast<uint4*>(xs + gkey * kXPitch + 64 * gcs);
+#pragma unroll
+      for (int wi = 0; wi < 8; ++wi) {
+        uint32_t vv[4];
+        e2m1x8_to_f16(cw[wi], sgm[wi >> 1], vv);
+        dst[wi] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
+      }
+      const int ks = c0 + PF * KC + gkey;
+      if (c0 + PF * KC < nk) gather_at(gr[v], ks < nk ? sidx[ks] : -1);
+    }
+    __builtin_amdgcn_wave_barrier();
+    // partial S^T over this wave's channels: tile (t, ht), lane holds entries 16 t + 4 g + i of head 16 ht + l16
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      f16x8_t a[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) a[kk] = *reinterpret_cast<const f16x8_t*>(xr + 16 * t * kXPitch + 32 * kk);
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) {
+        f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;  // two chains halve the dependency latency
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], qb[ht][0], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[1], qb[ht][1], s1, 0, 0, 0);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[2], qb[ht][2], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[3], qb[ht][3], s1, 0, 0, 0);
+        const f32x4_t sv = s0 + s1;
+        sp4[((w * NS + t) * 4 + ht) * 64 + lane] = make_float4(sv[0], sv[1], sv[2], sv[3]);
+      }
+    }
+    __syncthreads();
+    // head tile w: complete scores, online softmax, publish P and the rescale factor
+    {
+      uint64_t vmask;              // bit e: entry c0 + e is a real entry
+      {
+        int pe = -1;
+        if (lane < KC && c0 + lane < nk) pe = sidx[c0 + lane];
+        vmask = __ballot(pe >= 0);
+      }
+      float tv[NS][4];
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
+        float4 a = sp4[((0 * NS + t) * 4 + w) * 64 + lane];
+#pragma unroll
+        for (int ww = 1; ww < 4; ++ww) {
+          const float4 x = sp4[((ww * NS + t) * 4 + w) * 64 + lane];
+          a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+        }
+        const float sv[4] = {a.x, a.y, a.z, a.w};
+        const uint32_t vb = (uint32_t)(vmask >> (16 * t + 4 * g)) & 15u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          tv[t][i] = ((vb >> i) & 1u) ? sv[i] * qscale : -INFINITY;
+          cmax = fmaxf(cmax, tv[t][i]);
+        }
+      }
+      cmax = head_max(cmax);
+      float alpha = 1.0f;
+      if (m_run == -INFINITY) {
+        m_run = cmax;              // first entries of this head: nothing accumulated yet
+      } else if (__builtin_expect(__ballot(cmax > m_run + kLazyRescale) != 0, 0)) {
+        const float mn = fmaxf(m_run, cmax);
+        alpha = exp2f(m_run - mn);
+        l_run *= alpha;
+        m_run = mn;
+      }
+      float psum = 0.0f;
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
+        f16x4_t pb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const _Float16 pv = m_run == -INFINITY ? (_Float16)0.0f : (_Float16)exp2f(tv[t][i] - m_run);
+          psum += (float)pv;       // normalize by the weights the f16 MFMA actually uses
+          pb[i] = pv;
+        }
+        pbuf[(w * NS + t) * 64 + lane] = pb;
+      }
+      l_run += head_sum(psum);
+      if (g == 0) abuf[16 * w + l16] = alpha;
+    }
+    __syncthreads();
+    // apply the owners' rescale factors, then O^T += X^T P^T over the chunk
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+      const float al = abuf[16 * ht + l16];
+      if (__ballot(al != 1.0f) != 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[ht][j] *= al;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      f16x4_t pb[4];
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) pb[ht] = pbuf[(ht * NS + t) * 64 + lane];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(xtr + 16 * t * kXPitch + 16 * j));
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+          acc[ht][j] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), pb[ht], acc[ht][j], 0, 0, 0);
+      }
+    }
+  }
+
+  // each head's (max, sum) from its owner, then every wave writes its channels of all 64 heads
+  if (g == 0) {
+    mlb[2 * (16 * w + l16)] = m_run;
+    mlb[2 * (16 * w + l16) + 1] = l_run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+    const int hh = 16 * ht + l16;
+    const float L = mlb[2 * hh + 1];
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    float* dst = out + ((int64_t)qr * H + hbase + hh) * kD + 128 * w + 4 * g;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const f32x4_t o = acc[ht][j] * inv;
+      *reinterpret_cast<float4*>(dst + 16 * j) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+  }
+  if (lse && g == 0) {
+    const float L = l_run;
+    lse[(int64_t)qr * H + hbase + 16 * w + l16] = L > 0.0f ? (m_run + log2f(L)) * kLn2 : -INFINITY;
+  }
+}
+
 // Merge of split results: one wave per (query row, head), lane owns 8 channels. The first 8
 // splits' partial rows are loaded together with all splits' (max, sum) pairs, so the common case
 // waits on memory once. Workgroups are placed on the XCD whose L2 holds the partials: the
@@ -696,6 +978,11 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
 // Decode form for few query rows (16 heads per workgroup), wide form otherwise (64 heads).
 static bool use_decode_form(int B, int T) { return (int64_t)B * T < 512; }
 
+// Prefill form: wide launches whose heads come in groups of 64 and whose selections fit one split.
+static bool use_prefill_form(int B, int T, int H, int K) {
+  return !use_decode_form(B, T) && H % 64 == 0 && K > 0 && K <= kMaxKPS;
+}
+
 static int attn_splits(int B, int T, int H, int K) {
   if (use_decode_form(B, T)) {
     const int64_t wgs = (int64_t)B * T * (H / 16);
@@ -703,6 +990,7 @@ static int attn_splits(int B, int T, int H, int K) {
     // at least one chunk per sub-group
     return std::max(1, std::min((K + kDKC * kDNG - 1) / (kDKC * kDNG), by_fill));
   }
+  if (use_prefill_form(B, T, H, K)) return 1;
   const int hpw = H >= 64 ? 64 : H;
   const int64_t wgs = (int64_t)B * T * (H / hpw);
   if (wgs >= 256 || K <= 2 * kKC) return 1;
@@ -742,6 +1030,13 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* rows, int n_max,
   if (n_splits > 1) {
     part_o = static_cast<float*>(ws);
     part_ml = part_o + (size_t)n_splits * nq * H * kD;
+  }
+  if (use_prefill_form(B, T, H, K)) {
+    const int64_t items = nq * (H / 64);
+    const int per_xcd = (int)((items + 7) / 8);
+    hipLaunchKernelGGL((sparse_attn_prefill_kernel<1, 2>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, q, rows, n_max,
+                       idx, T, H, K, sm_scale, out, lse, (int)nq, per_xcd);
+    return hipGetLastError();
   }
   if (use_decode_form(B, T)) {
     const int64_t items = nq * n_splits * (H / 16);

@@ -237,6 +237,27 @@ def test_sparse_attn(B, T, H, N, K):
     check_attn(out, ref, lse, lref, f"attn B={B} T={T} H={H} K={K}")
 
 
+@pytest.mark.parametrize("B,T,H,N,K,qmul", [(1, 512, 64, 1500, 1024, 1.0), (2, 300, 128, 400, 77, 1.0),
+                                             (1, 520, 64, 90, 33, 16.0), (1, 530, 32, 200, 40, 1.0)])
+def test_sparse_attn_many_rows(B, T, H, N, K, qmul):
+    """Launches with >= 512 query rows: the 64-head prefill form (H % 64 == 0, K <= 1024) and the
+    older wide form (H = 32). Checked against the oracle on a seeded sample of query rows (all
+    heads), including a row whose selection is empty; qmul = 16 widens the score range so the
+    lazy softmax rescale fires."""
+    rows, qb, idx = _attn_case(B, T, H, N, K, seed=7 * T + K, oob=True)
+    if qmul != 1.0:
+        qb = W.to_bf16_bits(W.bf16_bits_to_f32(qb) * np.float32(qmul))
+    idx[0, 1, :] = -1
+    scale = 1 / np.sqrt(512)
+    out, lse = P.sparse_attn(dev_bf16(qb), torch.from_numpy(rows).cuda(), torch.from_numpy(idx).cuda(), scale)
+    out, lse = _sync_np(out), _sync_np(lse)
+    g = np.random.default_rng(T + K)
+    ts = np.unique(np.concatenate([[0, 1, T - 1], g.choice(T, size=6, replace=False)]))
+    ref, lref = _attn_ref(rows, qb[:, ts], idx[:, ts], scale)
+    check_attn(out[:, ts], ref, lse[:, ts], lref, f"attn B={B} T={T} H={H} K={K} qmul={qmul}")
+    assert np.all(out[0, 1] == 0) and np.all(np.isneginf(lse[0, 1]))
+
+
 def test_sparse_attn_full_selection_and_empty():
     rows, qb, _ = _attn_case(1, 2, 64, 128, 1, seed=3)
     scale = 0.07
