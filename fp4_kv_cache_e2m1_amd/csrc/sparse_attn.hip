@@ -636,17 +636,18 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
 // softmax overlap the other's matrix work. Workgroups of consecutive query rows, whose selections
 // overlap, run on one XCD and share its L2.
 constexpr int kPKC = 32;                         // prefill entries per chunk
+constexpr int kPXPitch = kD + 24;                // f16 elements per X row of the prefill form (measured best)
 
-template <int PF, int OCC>
+template <int PF, int OCC, int XP>
 __global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ rows, int n_max,
     const int32_t* __restrict__ idx, int T, int H, int K, float sm_scale, float* __restrict__ out,
     float* __restrict__ lse, int n_rows, int per_xcd) {
   constexpr int KC = kPKC, NS = KC / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[KC * kXPitch];     // X[entry][channel], f16
+  __shared__ __attribute__((aligned(16))) uint16_t xs[KC * XP];     // X[entry][channel], f16
   __shared__ __attribute__((aligned(16))) float4 sp4[4 * NS * 4 * 64];   // partial S: [wave][t][ht][lane]
   __shared__ __attribute__((aligned(16))) f16x4_t pbuf[4 * NS * 64];     // P: [ht][s][lane]
-  __shared__ float abuf[64];                                             // rescale factor per head
+  __shared__ __attribute__((aligned(16))) float abuf[64];                // rescale factors: [l16][head tile]
   __shared__ float amx[4 * 64];                                          // per-wave |q| max per head
   __shared__ float mlb[2 * 64];                                          // final (max, sum) per head
   __shared__ int sidx[kMaxKPS];
@@ -755,8 +756,8 @@ __global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
     for (int j = 0; j < 8; ++j) acc[ht][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;    // softmax state of head 16 w + l16 (this wave owns it)
   // transposing-read base for the P.V operand: entry 4 g + l16/4 (+16 s), channel 128 w + 4 (l16%4) (+16 j)
-  const uint16_t* xtr = xs + (4 * g + (l16 >> 2)) * kXPitch + 128 * w + 4 * (l16 & 3);
-  const uint16_t* xr = xs + l16 * kXPitch + 128 * w + 8 * g;
+  const uint16_t* xtr = xs + (4 * g + (l16 >> 2)) * XP + 128 * w + 4 * (l16 & 3);
+  const uint16_t* xr = xs + l16 * XP + 128 * w + 8 * g;
 
   for (int cg = 0; cg < nk; cg += PF * KC)
 #pragma unroll
@@ -764,6 +765,10 @@ __global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
     const int c0 = cg + v * KC;
     if (c0 >= nk) break;
     {
+      // the next gather's position is read before this chunk's X writes, so waiting for it does
+      // not wait for them
+      const int ks = c0 + PF * KC + gkey;
+      const int pnext = (c0 + PF * KC < nk && ks < nk) ? sidx[ks] : -1;
       // dequantize this lane's slab into X (read by this wave only; a wave's LDS operations
       // complete in order, so the reads below see these writes)
       const Piece& pc = gr[v];
@@ -771,15 +776,14 @@ __global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
       const f16x2_t sgm[4] = {f16x2_t{s01[0], s01[0]}, f16x2_t{s01[1], s01[1]}, f16x2_t{s23[0], s23[0]},
                               f16x2_t{s23[1], s23[1]}};
       const uint32_t cw[8] = {pc.c01.x, pc.c01.y, pc.c01.z, pc.c01.w, pc.c23.x, pc.c23.y, pc.c23.z, pc.c23.w};
-      uint4* dst = reinterpret_cast<uint4*>(xs + gkey * kXPitch + 64 * gcs);
+      uint4* dst = reinterpret_cast<uint4*>(xs + gkey * XP + 64 * gcs);
 #pragma unroll
       for (int wi = 0; wi < 8; ++wi) {
         uint32_t vv[4];
         e2m1x8_to_f16(cw[wi], sgm[wi >> 1], vv);
         dst[wi] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
       }
-      const int ks = c0 + PF * KC + gkey;
-      if (c0 + PF * KC < nk) gather_at(gr[v], ks < nk ? sidx[ks] : -1);
+      if (c0 + PF * KC < nk) gather_at(gr[v], pnext);
     }
     __builtin_amdgcn_wave_barrier();
     // partial S^T over this wave's channels: tile (t, ht), lane holds entries 16 t + 4 g + i of head 16 ht + l16
@@ -787,7 +791,7 @@ __global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
     for (int t = 0; t < NS; ++t) {
       f16x8_t a[4];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) a[kk] = *reinterpret_cast<const f16x8_t*>(xr + 16 * t * kXPitch + 32 * kk);
+      for (int kk = 0; kk < 4; ++kk) a[kk] = *reinterpret_cast<const f16x8_t*>(xr + 16 * t * XP + 32 * kk);
 #pragma unroll
       for (int ht = 0; ht < 4; ++ht) {
         f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;  // two chains halve the dependency latency
@@ -849,16 +853,18 @@ __global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
         pbuf[(w * NS + t) * 64 + lane] = pb;
       }
       l_run += head_sum(psum);
-      if (g == 0) abuf[16 * w + l16] = alpha;
+      if (g == 0) abuf[4 * l16 + w] = alpha;
     }
     __syncthreads();
     // apply the owners' rescale factors, then O^T += X^T P^T over the chunk
+    {
+      const float4 al = *reinterpret_cast<const float4*>(&abuf[4 * l16]);  // head 16 ht + l16, ht = 0..3
+      if (__ballot(al.x != 1.0f || al.y != 1.0f || al.z != 1.0f || al.w != 1.0f) != 0) {
+        const float a4[4] = {al.x, al.y, al.z, al.w};
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
-      const float al = abuf[16 * ht + l16];
-      if (__ballot(al != 1.0f) != 0) {
+        for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[ht][j] *= al;
+          for (int j = 0; j < 8; ++j) acc[ht][j] *= a4[ht];
       }
     }
 #pragma unroll
@@ -868,7 +874,7 @@ __global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
       for (int ht = 0; ht < 4; ++ht) pb[ht] = pbuf[(ht * NS + t) * 64 + lane];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(xtr + 16 * t * kXPitch + 16 * j));
+        const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(xtr + 16 * t * XP + 16 * j));
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht)
           acc[ht][j] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), pb[ht], acc[ht][j], 0, 0, 0);
@@ -1034,7 +1040,7 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* rows, int n_max,
   if (use_prefill_form(B, T, H, K)) {
     const int64_t items = nq * (H / 64);
     const int per_xcd = (int)((items + 7) / 8);
-    hipLaunchKernelGGL((sparse_attn_prefill_kernel<1, 2>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, q, rows, n_max,
+    hipLaunchKernelGGL((sparse_attn_prefill_kernel<1, 2, kPXPitch>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, q, rows, n_max,
                        idx, T, H, K, sm_scale, out, lse, (int)nq, per_xcd);
     return hipGetLastError();
   }
