@@ -645,7 +645,8 @@ __global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
     float* __restrict__ lse, int n_rows, int per_xcd) {
   constexpr int KC = kPKC, NS = KC / 16;
   __shared__ __attribute__((aligned(16))) uint16_t xs[KC * XP];     // X[entry][channel], f16
-  __shared__ __attribute__((aligned(16))) float4 sp4[4 * NS * 4 * 64];   // partial S: [wave][t][ht][lane]
+  // partial S, component-major ([wave][t][ht][i][lane]) so every 4-byte access is lane-contiguous
+  __shared__ __attribute__((aligned(16))) float spf[4 * NS * 4 * 4 * 64];
   __shared__ __attribute__((aligned(16))) f16x4_t pbuf[4 * NS * 64];     // P: [ht][s][lane]
   __shared__ __attribute__((aligned(16))) float abuf[64];                // rescale factors: [l16][head tile]
   __shared__ float amx[4 * 64];                                          // per-wave |q| max per head
@@ -792,15 +793,21 @@ __global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
       f16x8_t a[4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) a[kk] = *reinterpret_cast<const f16x8_t*>(xr + 16 * t * XP + 32 * kk);
+      // head tiles in pairs: two independent chains interleaved step by step
 #pragma unroll
-      for (int ht = 0; ht < 4; ++ht) {
-        f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;  // two chains halve the dependency latency
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], qb[ht][0], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[1], qb[ht][1], s1, 0, 0, 0);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[2], qb[ht][2], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[3], qb[ht][3], s1, 0, 0, 0);
-        const f32x4_t sv = s0 + s1;
-        sp4[((w * NS + t) * 4 + ht) * 64 + lane] = make_float4(sv[0], sv[1], sv[2], sv[3]);
+      for (int hp = 0; hp < 4; hp += 2) {
+        f32x4_t sv[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2)
+            sv[h2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[kk], qb[hp + h2][kk], sv[h2], 0, 0, 0);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          float* dst = spf + ((w * NS + t) * 4 + hp + h2) * 256 + lane;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[64 * i] = sv[h2][i];
+        }
       }
     }
     __syncthreads();
@@ -816,13 +823,12 @@ __global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
       float cmax = -INFINITY;
 #pragma unroll
       for (int t = 0; t < NS; ++t) {
-        float4 a = sp4[((0 * NS + t) * 4 + w) * 64 + lane];
+        float sv[4];
 #pragma unroll
-        for (int ww = 1; ww < 4; ++ww) {
-          const float4 x = sp4[((ww * NS + t) * 4 + w) * 64 + lane];
-          a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+        for (int i = 0; i < 4; ++i) {
+          const float* src = spf + (t * 4 + w) * 256 + 64 * i + lane;
+          sv[i] = src[0] + src[NS * 4 * 256] + src[2 * NS * 4 * 256] + src[3 * NS * 4 * 256];
         }
-        const float sv[4] = {a.x, a.y, a.z, a.w};
         const uint32_t vb = (uint32_t)(vmask >> (16 * t + 4 * g)) & 15u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -836,7 +842,7 @@ __global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
         m_run = cmax;              // first entries of this head: nothing accumulated yet
       } else if (__builtin_expect(__ballot(cmax > m_run + kLazyRescale) != 0, 0)) {
         const float mn = fmaxf(m_run, cmax);
-        alpha = exp2f(m_run - mn);
+        alpha = __builtin_amdgcn_exp2f(m_run - mn);
         l_run *= alpha;
         m_run = mn;
       }
@@ -846,7 +852,8 @@ __global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
         f16x4_t pb;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const _Float16 pv = m_run == -INFINITY ? (_Float16)0.0f : (_Float16)exp2f(tv[t][i] - m_run);
+          // exponent <= 8 (lazy rescale); v_exp_f32 directly: the result is rounded to f16 anyway
+          const _Float16 pv = m_run == -INFINITY ? (_Float16)0.0f : (_Float16)__builtin_amdgcn_exp2f(tv[t][i] - m_run);
           psum += (float)pv;       // normalize by the weights the f16 MFMA actually uses
           pb[i] = pv;
         }
