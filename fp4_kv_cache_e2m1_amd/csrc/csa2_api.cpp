@@ -32,8 +32,10 @@ int pipeline_chunks() {
 csa2_status hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_E_HIP; }
 
 bool index_shape_ok(int32_t Hi, int32_t Hk, int32_t Di) {
+  // per-head keys: the query and the key row are Hi*Di channels, at most 1024; one shared key:
+  // the key row is Di channels (at most 1024) and the query heads are summed first (up to 8192)
   return Hi >= 1 && (Hk == Hi || Hk == 1) && Di > 0 && Di % 8 == 0 && (Hk * Di) % 64 == 0 &&
-         Hi * Di <= 1024 && (Hk == 1 ? Di <= 1024 : true);
+         (Hk == 1 ? Di <= 1024 && Hi * Di <= 8192 : Hi * Di <= 1024);
 }
 
 bool attn_shape_ok(int32_t H, int32_t D) { return D == 512 && H > 0 && H % 16 == 0 && (H <= 64 || H % 64 == 0); }

@@ -72,6 +72,13 @@ CONFIGS = {
                 modes=(FULL, REINDEX, REINDEX), pool_blocks=1024, planted_frac=0.01),
     5: Workload("prefill_t4096_n33792", 5, B=1, T=4096, N=33792, H=64, Hi=8, Hk=8, k=1024,
                 p0=131072, ratio=4, n_existing=32768),
+    # the decoder's layer schedule at the model's own shapes: one Full layer and three Reuse
+    # layers, then four times a Reindex layer and three Reuse layers, all on one shared cache;
+    # the Full layer builds a pool of 2048 blocks x 8 that every Reindex layer scores; indexer
+    # 32 query heads x 128 against one shared 128-channel key per entry; compression ratio 1
+    6: Workload("decoder20_hsi_b4_n262144_pool16384", 6, B=4, T=1, N=262144, H=64, Hi=32, Di=128,
+                Hk=1, k=512, modes=(FULL, REUSE, REUSE, REUSE) + (REINDEX, REUSE, REUSE, REUSE) * 4,
+                pool_blocks=2048, ratio=1),
 }
 
 

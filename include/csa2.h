@@ -101,7 +101,9 @@ csa2_status csa2_dequant_kv_fp4(const uint8_t* rows, int64_t n_rows, int32_t dim
  *           visible positions of each aligned block of `block` entries ([walkthrough]
  *           一(四)2, a block's score is the max index score inside it). Blocks with no visible
  *           position are left unwritten. block must be 8 when block_max is given.
- * Requires Hk in {1, Hi}, Di % 8 == 0, Hk*Di % 64 == 0, Hi*Di <= 1024.
+ * Requires Hk in {1, Hi}, Di % 8 == 0, Hk*Di % 64 == 0, and Hi*Di <= 1024 when Hk == Hi, or
+ * Di <= 1024 and Hi*Di <= 8192 when Hk == 1 (one shared key: the query heads are summed in fp32
+ * first, so the score is (sum_h q_idx[r, h]) . k_idx[n, 0]).
  * Decode-shaped calls (T small, or pool mode) stream the keys once per query row; prefill
  * calls (T >= 16, flat mode, Hk == Hi, Hi*Di % 64 == 0) run as MFMA tiles with causal tile
  * skipping.

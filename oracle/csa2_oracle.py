@@ -214,8 +214,12 @@ def index_scores(q_idx: np.ndarray, k_idx: np.ndarray, n_vis) -> np.ndarray:
     N, Hk, _ = k.shape
     assert Hk in (1, Hi)
     if Hk == 1:
-        k = np.repeat(k, Hi, axis=1)
-    s = q.reshape(R, Hi * Di) @ k.reshape(N, Hi * Di).T      # [R, N] fp64
+        # sum over the heads of each head's dot product with the one shared key
+        s = np.zeros((R, N), dtype=np.float64)
+        for h in range(Hi):
+            s += q[:, h, :] @ k[:, 0, :].T
+    else:
+        s = q.reshape(R, Hi * Di) @ k.reshape(N, Hi * Di).T  # [R, N] fp64
     out = s.astype(np.float32)
     n_vis = np.broadcast_to(np.asarray(n_vis), (R,))
     out[np.arange(N)[None, :] >= n_vis[:, None]] = -np.inf

@@ -67,6 +67,8 @@ def test_index_scores_validation(L):
     assert f(None, None, 1, 1, 8, 4, 64, 10, None, None, 0, None, None, 8, None) == E_SHAPE   # Hk not in {1, Hi}
     assert f(None, None, 1, 1, 8, 8, 12, 10, None, None, 0, None, None, 8, None) == E_SHAPE   # Di % 8
     assert f(None, None, 1, 1, 32, 32, 64, 10, None, None, 0, None, None, 8, None) == E_SHAPE  # Hi*Di > 1024
+    assert f(None, None, 0, 1, 32, 1, 128, 10, None, None, 0, None, None, 8, None) == OK       # shared key, 32 x 128
+    assert f(None, None, 1, 1, 128, 1, 128, 10, None, None, 0, None, None, 8, None) == E_SHAPE  # Hi*Di > 8192
     assert f(None, None, 1, 1, 8, 8, 64, 10, None, FAKE, 4, None, FAKE, 8, None) == E_UNSUP   # block max on pool
     assert f(None, None, 1, 1, 8, 8, 64, 10, None, None, 0, None, FAKE, 4, None) == E_UNSUP   # block != 8
     assert f(None, None, 1, 1, 8, 8, 64, 10, None, None, 0, None, None, 8, None) == E_ARG     # null tensors

@@ -151,6 +151,8 @@ SMALL = {
     "hsi_pool_fused": W.CONFIGS[4].scaled(B=2, N=80000, k=256, pool_blocks=600),
     "full_h16": W.CONFIGS[1].scaled(B=2, N=1001, k=64),
     "prefill": W.CONFIGS[5].scaled(T=160, N=2700, p0=10600, n_existing=2650, k=256),
+    # the 20-layer decoder schedule with a shared 32 x 128 indexer key, pool first (100 blocks)
+    "decoder20": W.CONFIGS[6].scaled(B=2, N=5000, k=128, pool_blocks=100),
 }
 
 
@@ -212,9 +214,9 @@ def test_hierarchical_equals_flat_when_pool_is_everything():
 
 
 # ---------------------------------------------------------------------------------------------
-# The five workloads at full size; the oracle checks sampled sequences (and query rows).
+# The workloads at full size; the oracle checks sampled sequences (and query rows).
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("cfg,sample", [(1, [0]), (2, [0, 17, 31]), (3, [0, 15]), (4, [0, 3]), (5, [0])])
+@pytest.mark.parametrize("cfg,sample", [(1, [0]), (2, [0, 17, 31]), (3, [0, 15]), (4, [0, 3]), (5, [0]), (6, [2])])
 def test_config_full_size(cfg, sample):
     wl = W.CONFIGS[cfg]
     print(f"[config {cfg}] {wl.name}: generating inputs", flush=True)
