@@ -15,10 +15,14 @@
 
 namespace csa2 {
 
-constexpr int kIdxThreads = 256;           // 4 waves, 32 rows per iteration
+constexpr int kIdxThreads = 256;           // 4 waves, 32 rows per row step
 constexpr int kRowsPerIter = kIdxThreads / 8;
+template <int NCH> constexpr int kRowsPerGroup = NCH >= 8 ? 1 : 8 / NCH;
 
-template <int NCH, bool kSharedKey, bool kPool, bool kBlockMax>
+// RPI rows per lane group and iteration (short key rows: 8 / NCH), so every lane keeps 8 loads in
+// flight whatever the row length; row u of an iteration is 32 u rows after row 0, so the 8 row
+// groups of a wave still cover one aligned 8-entry block for each u.
+template <int NCH, bool kSharedKey, bool kPool, bool kBlockMax, int RPI>
 __global__ __launch_bounds__(kIdxThreads) void index_stream_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int T, int Hi, int Di, int n_max,
     const int32_t* __restrict__ n_vis, const int32_t* __restrict__ cand, int P, int tile_rows,
@@ -70,62 +74,69 @@ __global__ __launch_bounds__(kIdxThreads) void index_stream_kernel(
   const int32_t* crow = kPool ? cand + (int64_t)r * P : nullptr;
   const int n_blocks = (n_max + 7) >> 3;
 
-  for (int it = 0; it < tile_rows; it += kRowsPerIter) {
-    const int col = tile0 + it + grp;
-    int pos = col;
-    bool valid;
-    if (kPool) {
-      pos = col < tile_end ? crow[col] : -1;
-      valid = pos >= 0 && pos < n_max;
-    } else {
-      valid = col < tile_end && col < nv;
-    }
-    u32x4_t kv[NCH];
-    if (valid) {
-      const u32x4_t* kp = kbase + (int64_t)pos * CH + j;
+  for (int it = 0; it < tile_rows; it += kRowsPerIter * RPI) {
+    int col[RPI];
+    bool valid[RPI];
+    u32x4_t kv[RPI][NCH];
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) kv[i] = __builtin_nontemporal_load(kp + 8 * i);
-    } else {
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) kv[i] = u32x4_t{0u, 0u, 0u, 0u};
-    }
-    float acc = 0.0f;
-    if (!kSharedKey) {
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const uint32_t w[4] = {kv[i].x, kv[i].y, kv[i].z, kv[i].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[i][e]),
-                                                __builtin_bit_cast(bf16x2_t, w[e]), acc, false);
+    for (int u = 0; u < RPI; ++u) {
+      col[u] = tile0 + it + kRowsPerIter * u + grp;
+      int pos = col[u];
+      if (kPool) {
+        pos = col[u] < tile_end ? crow[col[u]] : -1;
+        valid[u] = pos >= 0 && pos < n_max;
+      } else {
+        valid[u] = col[u] < tile_end && col[u] < nv;
       }
-    } else {
+      if (valid[u]) {
+        const u32x4_t* kp = kbase + (int64_t)pos * CH + j;
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const uint32_t w[4] = {kv[i].x, kv[i].y, kv[i].z, kv[i].w};
+        for (int i = 0; i < NCH; ++i) kv[u][i] = __builtin_nontemporal_load(kp + 8 * i);
+      } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc = fmaf(qf[kSharedKey ? i : 0][2 * e], __uint_as_float(w[e] << 16), acc);
-          acc = fmaf(qf[kSharedKey ? i : 0][2 * e + 1], __uint_as_float(w[e] & 0xFFFF0000u), acc);
+        for (int i = 0; i < NCH; ++i) kv[u][i] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < RPI; ++u) {
+      float acc = 0.0f;
+      if (!kSharedKey) {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          const uint32_t w[4] = {kv[u][i].x, kv[u][i].y, kv[u][i].z, kv[u][i].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[i][e]),
+                                                  __builtin_bit_cast(bf16x2_t, w[e]), acc, false);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          const uint32_t w[4] = {kv[u][i].x, kv[u][i].y, kv[u][i].z, kv[u][i].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc = fmaf(qf[kSharedKey ? i : 0][2 * e], __uint_as_float(w[e] << 16), acc);
+            acc = fmaf(qf[kSharedKey ? i : 0][2 * e + 1], __uint_as_float(w[e] & 0xFFFF0000u), acc);
+          }
         }
       }
-    }
-    acc = sum8(acc);
-    if (j == 0 && col < tile_end) {
-      if (kPool)
-        scores[(int64_t)r * ncols + col] = valid ? acc : -INFINITY;
-      else if (valid)
-        scores[(int64_t)r * ncols + col] = acc;
-    }
-    if (kBlockMax) {
-      // the wave's 8 row groups are one aligned block of 8 entries
-      float m = valid ? acc : -INFINITY;
-      m = fmaxf(m, shfl_xor_f(m, 8));
-      m = fmaxf(m, shfl_xor_f(m, 16));
-      m = fmaxf(m, shfl_xor_f(m, 32));
-      const int blk = (tile0 + it + (grp & ~7)) >> 3;  // first column of the wave / 8
-      if (lane == 0 && blk < n_blocks && blk * 8 < min(nv, tile_end))
-        block_max[(int64_t)r * n_blocks + blk] = m;
+      acc = sum8(acc);
+      if (j == 0 && col[u] < tile_end) {
+        if (kPool)
+          scores[(int64_t)r * ncols + col[u]] = valid[u] ? acc : -INFINITY;
+        else if (valid[u])
+          scores[(int64_t)r * ncols + col[u]] = acc;
+      }
+      if (kBlockMax) {
+        // the wave's 8 row groups are one aligned block of 8 entries
+        float m = valid[u] ? acc : -INFINITY;
+        m = fmaxf(m, shfl_xor_f(m, 8));
+        m = fmaxf(m, shfl_xor_f(m, 16));
+        m = fmaxf(m, shfl_xor_f(m, 32));
+        const int blk = (tile0 + it + kRowsPerIter * u + (grp & ~7)) >> 3;  // first column of the wave / 8
+        if (lane == 0 && blk < n_blocks && blk * 8 < min(nv, tile_end))
+          block_max[(int64_t)r * n_blocks + blk] = m;
+      }
     }
   }
 }
@@ -137,7 +148,7 @@ static hipError_t launch_nch(bool shared, bool pool, bool bmax, dim3 grid, hipSt
                              float* scores, float* block_max) {
   dim3 block(kIdxThreads);
 #define CSA2_IDX_LAUNCH(SK, PL, BM)                                                                  \
-  hipLaunchKernelGGL((index_stream_kernel<NCH, SK, PL, BM>), grid, block, 0, s, q, k, T, Hi, Di, n_max, \
+  hipLaunchKernelGGL((index_stream_kernel<NCH, SK, PL, BM, kRowsPerGroup<NCH>>), grid, block, 0, s, q, k, T, Hi, Di, n_max, \
                      n_vis, cand, P, tile_rows, scores, block_max)
   if (shared) {
     if (pool) CSA2_IDX_LAUNCH(true, true, false);
@@ -160,10 +171,17 @@ hipError_t launch_index_stream(const uint16_t* q, const uint16_t* k, int B, int 
   if (rows == 0 || ncols == 0) return hipSuccess;
   const int ch = Hk * Di * 2 / 16;  // 16-byte chunks per key row (multiple of 8)
   const int nch = ch / 8;
-  // Tile size: enough workgroups to cover the chip several times over.
-  int tile_rows = kRowsPerIter;
+  // Tile size: enough workgroups to cover the chip several times over, in whole iterations (short
+  // key rows take 8 / nch rows per lane group and iteration).
+  int tile_rows = kRowsPerIter * (nch >= 8 ? 1 : 8 / nch);
   while (tile_rows < 1024 && (int64_t)((ncols + 2 * tile_rows - 1) / (2 * tile_rows)) * rows >= 2048)
     tile_rows *= 2;
+  // short key rows: a workgroup streams as many bytes as it would with 1 KiB rows when the grid
+  // keeps at least 512 workgroups (measured: 256-byte rows, 4 x 262144 entries, 54 -> 47 us)
+  if (nch < 8) {
+    const int big = tile_rows * (8 / nch);
+    if ((int64_t)((ncols + big - 1) / big) * rows >= 512) tile_rows = big;
+  }
   while ((ncols + tile_rows - 1) / tile_rows > 65535) tile_rows *= 2;  // grid.y limit
   dim3 grid((unsigned)rows, (unsigned)((ncols + tile_rows - 1) / tile_rows));
   const bool shared = Hk == 1, pool = cand != nullptr, bmax = block_max != nullptr && !pool;
