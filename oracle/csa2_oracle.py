@@ -357,6 +357,73 @@ def sparse_attn(q: np.ndarray, kv: np.ndarray, idx: np.ndarray, sm_scale: float)
 
 
 # ---------------------------------------------------------------------------------------------
+# O12: the sliding-window branch, joined to the selected entries.
+# ---------------------------------------------------------------------------------------------
+SWA_EXP_MIN, SWA_EXP_MAX = -15, 7   # row exponents: every dequantized value stays exact in f16
+
+
+def quantize_swa_fp8(x: np.ndarray):
+    """O12a. FP8 storage of the layer's own sliding-window KV.
+
+    [walkthrough] 一(五)4: the SWA KV is more sensitive to quantization and keeps FP8 precision.
+    The pages give no FP8 layout; reading R-17: every channel is an OCP E4M3 code and every row
+    has one power-of-two scale 2^e, e the smallest integer with max|x| <= 448 * 2^e (clamped to
+    [SWA_EXP_MIN, SWA_EXP_MAX]; a zero row takes SWA_EXP_MIN). A code is the E4M3 value nearest to
+    x / 2^e (exact: a power-of-two scaling), ties to the even code, saturating at 448, with the
+    sign bit of x. Returns (codes uint8 [n, D], exps int8 [n]).
+    """
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    amax = np.abs(x).max(axis=1)
+    e = np.full(amax.shape, SWA_EXP_MIN, dtype=np.int64)
+    nz = amax > 0
+    est = np.ceil(np.log2(amax[nz] / 448.0)).astype(np.int64)
+    # correct the estimate so that 448 * 2^(e-1) < amax <= 448 * 2^e holds exactly
+    est = np.where(amax[nz] > 448.0 * np.ldexp(1.0, est), est + 1, est)
+    est = np.where(amax[nz] <= 448.0 * np.ldexp(1.0, est - 1), est - 1, est)
+    e[nz] = est
+    e = np.clip(e, SWA_EXP_MIN, SWA_EXP_MAX)
+    y = np.abs(x) * np.ldexp(1.0, -e)[:, None]
+    mag = _nearest_even(E4M3_POS, y)
+    codes = (mag | (np.signbit(x).astype(np.int64) << 7)).astype(np.uint8)
+    return codes, e.astype(np.int8)
+
+
+def dequant_swa_fp8(codes: np.ndarray, exps: np.ndarray) -> np.ndarray:
+    """O12b. x = E4M3(code) * 2^e per row (exact; R-17)."""
+    return e4m3_decode(codes) * np.ldexp(1.0, np.asarray(exps, dtype=np.int64))[..., None]
+
+
+def sparse_attn_swa(q: np.ndarray, kv: np.ndarray, idx: np.ndarray, win: np.ndarray, n_win, sm_scale: float):
+    """O12c. Attention of each query head over its selected entries and its window, as one softmax.
+
+    [walkthrough] 一(四): each query attends both to the selected entries and to its own layer's
+    sliding-window KV (reading R-18: one softmax over the union; the window rows are key and value
+    like the main entries, R-5). q: [R, H, D]; kv: [N, D] dequantized main entries; idx: [R, K]
+    (-1 = none); win: [R, W, D] dequantized window rows, of which the first n_win[r] belong to
+    row r. Returns (out fp32 [R, H, D], lse fp32 [R, H]); nothing to attend: 0 and -inf.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kv = np.asarray(kv, dtype=np.float64)
+    win = np.asarray(win, dtype=np.float64)
+    R, H, D = q.shape
+    n_win = np.broadcast_to(np.asarray(n_win), (R,))
+    out = np.zeros((R, H, D), dtype=np.float64)
+    lse = np.full((R, H), -np.inf, dtype=np.float64)
+    for r in range(R):
+        sel = idx[r][idx[r] >= 0]
+        x = np.concatenate([kv[sel], win[r, : int(n_win[r])]], axis=0)   # [S, D]
+        if len(x) == 0:
+            continue
+        logits = sm_scale * (q[r] @ x.T)
+        mx = logits.max(axis=1, keepdims=True)
+        w = np.exp(logits - mx)
+        den = w.sum(axis=1, keepdims=True)
+        out[r] = (w @ x) / den
+        lse[r] = mx[:, 0] + np.log(den[:, 0])
+    return out.astype(np.float32), lse.astype(np.float32)
+
+
+# ---------------------------------------------------------------------------------------------
 # O11: one CSA2 layer step for one sequence.
 # ---------------------------------------------------------------------------------------------
 FULL, REINDEX, REUSE = 0, 1, 2
