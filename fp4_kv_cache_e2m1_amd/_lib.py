@@ -33,6 +33,8 @@ EXPORTS = [
     "csa2_hier_pool",
     "csa2_sparse_attn_workspace_size",
     "csa2_sparse_attn",
+    "csa2_sparse_attn_swa_workspace_size",
+    "csa2_sparse_attn_swa",
     "csa2_layer_workspace_size",
     "csa2_layer_step",
 ]
@@ -79,6 +81,8 @@ def _declare(lib):
         "csa2_hier_pool": (i32, [vp, i64, i32, vp, i32, i32, vp, vp, sz, vp]),
         "csa2_sparse_attn_workspace_size": (sz, [i32, i32, i32, i32, i32]),
         "csa2_sparse_attn": (i32, [vp, vp, i32, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp, sz, vp]),
+        "csa2_sparse_attn_swa_workspace_size": (sz, [i32, i32, i32, i32]),
+        "csa2_sparse_attn_swa": (i32, [vp, vp, i32, vp, i32, i32, i32, i32, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
         "csa2_layer_workspace_size": (i32, [i32, C.POINTER(LayerArgs), C.POINTER(SharedKV),
                                             C.POINTER(SharedIdx), C.POINTER(sz)]),
         "csa2_layer_step": (i32, [i32, C.POINTER(LayerArgs), C.POINTER(SharedKV), C.POINTER(SharedIdx), vp]),

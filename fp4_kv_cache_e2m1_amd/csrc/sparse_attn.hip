@@ -618,6 +618,306 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
   }
 }
 
+// Sliding-window branch for decode (one query token per sequence): the layer's own window of
+// FP8 rows ([walkthrough] 一(四): each query also attends to its own layer's sliding-window KV;
+// 一(五)4: that KV stays in FP8). Same structure as the decode form above over the window rows
+// (positions 0 .. n_win-1 of the sequence's window), then the result is merged with the sparse
+// attention already written to out / lse_sparse, which makes it one softmax over the union.
+template <int KC, int PF, int NG>
+__global__ __launch_bounds__(256 * NG) void swa_attn_merge_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ swa_codes, const int8_t* __restrict__ swa_exp,
+    const int32_t* __restrict__ n_win, int W, int H, float sm_scale, float* __restrict__ out,
+    const float* __restrict__ lse_sparse, float* __restrict__ lse, int n_rows, int per_xcd) {
+  constexpr int T = 1;
+  using Sm = DecodeSmem<KC, NG>;
+  constexpr int NS = KC / 16;                  // NS entry steps of 16 per chunk
+  static_assert(KC == 32, "a wave's 64 lanes gather the chunk's 32 entries x 2 slabs of 64 channels");
+  static_assert(NG >= 1 && NG <= 4, "sub-groups");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[Sm::kTotal];
+  float* ml = reinterpret_cast<float*>(smem + NG * Sm::kGroup + Sm::kIdx);
+  uint16_t* qs = reinterpret_cast<uint16_t*>(smem + NG * Sm::kGroup + Sm::kIdx + Sm::kMl);
+
+  // Workgroup i runs on XCD i mod 8; each XCD takes a contiguous range of work items ordered
+  // (query row, split, head group), so all workgroups of a query row share one L2: the rows they
+  // gather and the query they load are fetched from HBM about once.
+  const int n_hg = H / 16;
+  const int u = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (u >= n_rows * n_hg) return;
+  const int qr = u / n_hg, hg = u % n_hg;
+  const int b = qr / T;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sg = wave >> 2, w4 = wave & 3;   // sub-group and wave within it
+  const int l16 = lane & 15, g = lane >> 4;
+  const int head = hg * 16 + l16;
+
+  unsigned char* gbase = smem + sg * Sm::kGroup;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(gbase);
+  float4* sp4b = reinterpret_cast<float4*>(gbase + Sm::kX);
+
+  const int nk = max(0, min(n_win[b], W));                           // window rows of this sequence
+  const int sub_len = ((nk + NG - 1) / NG + KC - 1) / KC * KC;          // entries per sub-group
+  const int sbeg = sg * sub_len;
+  const int snk = max(0, min(nk - sbeg, sub_len));                     // entries of this sub-group
+  const uint8_t* wbase = swa_codes + (int64_t)b * W * kD;           // [W][512] E4M3 codes
+  const int8_t* ebase = swa_exp + (int64_t)b * W;                    // [W] row exponents
+
+  // Lane: entry gkey of a chunk, channel slab gcs (64 channels) of this wave's 128. The
+  // positions of its entries in the first PF chunks are loaded first, so that those gathers can
+  // start without waiting for the LDS copy of the positions.
+  const int gkey = lane & 31, gcs = 2 * w4 + (lane >> 5);
+  int pos0[PF];
+#pragma unroll
+  for (int v = 0; v < PF; ++v) {
+    const int ks = v * KC + gkey;
+    pos0[v] = ks < snk ? sbeg + ks : -1;
+  }
+  // sub-group 0 loads the 16 heads' queries, wave w4 its channel blocks 4 w4 .. 4 w4 + 3
+  uint4 raw_q[4];
+  if (sg == 0) {
+    const uint4* qp = reinterpret_cast<const uint4*>(q + ((int64_t)qr * H + head) * kD);
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq) raw_q[kq] = qp[4 * (4 * w4 + kq) + g];
+  }
+
+  // gathers run PF chunks ahead: registers gr[v] hold chunk c0 + v KC of the current group
+  struct Piece {
+    uint4 c[4];         // the slab's 64 E4M3 codes
+    int e;              // the row's exponent
+  };
+  Piece gr[PF];
+  auto gather_at = [&](Piece& d, int p) {   // p: window row, or -1
+#pragma unroll
+    for (int m = 0; m < 4; ++m) d.c[m] = make_uint4(0, 0, 0, 0);
+    d.e = 0;
+    if (p >= 0 && p < nk) {
+      const uint4* rp = reinterpret_cast<const uint4*>(wbase + (int64_t)p * kD + 64 * gcs);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) d.c[m] = rp[m];
+      d.e = ebase[p];
+    }
+  };
+  auto gather = [&](Piece& d, int c0) {
+    const int ks = c0 + gkey;
+    gather_at(d, ks < snk ? sbeg + ks : -1);
+  };
+#pragma unroll
+  for (int v = 0; v < PF; ++v) gather_at(gr[v], pos0[v]);
+
+  if (sg == 0) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq) {
+      const uint32_t w[4] = {raw_q[kq].x, raw_q[kq].y, raw_q[kq].z, raw_q[kq].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w[e] << 16)), fabsf(__uint_as_float(w[e] & 0xFFFF0000u))));
+    }
+    amax = head_max(amax);
+    if (g == 0) ml[w4 * 16 + l16] = amax;
+  }
+  __syncthreads();
+  // the queries, scaled per head by a power of two and converted to f16 (exact), into LDS
+  float qscale;
+  {
+    const float amax = fmaxf(fmaxf(ml[l16], ml[16 + l16]), fmaxf(ml[32 + l16], ml[48 + l16]));
+    const int qe = amax > 0.0f ? 14 - ilogbf(amax) : 0;
+    if (sg == 0) {
+      const float sc = ldexpf(1.0f, qe);
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq) {
+        const int kk = 4 * w4 + kq;
+        const uint32_t w[4] = {raw_q[kq].x, raw_q[kq].y, raw_q[kq].z, raw_q[kq].w};
+        f16x8_t h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          h[2 * e] = (_Float16)(__uint_as_float(w[e] << 16) * sc);
+          h[2 * e + 1] = (_Float16)(__uint_as_float(w[e] & 0xFFFF0000u) * sc);
+        }
+        *reinterpret_cast<f16x8_t*>(qs + l16 * kXPitch + 32 * kk + 8 * g) = h;
+      }
+    }
+    qscale = sm_scale * kLog2e * ldexpf(1.0f, -qe);
+  }
+  __syncthreads();                                 // the scaled queries are in LDS
+  f16x8_t qb[4];                                   // this wave's query fragments, kept in registers
+  {
+    const uint16_t* qr16 = qs + l16 * kXPitch + 128 * w4 + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qb[kk] = *reinterpret_cast<const f16x8_t*>(qr16 + 32 * kk);
+  }
+
+  // output tiles of this wave: channels 128 w4 + 16 j + (4 g + i), head l16
+  f32x4_t acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;
+  // transposing-read base for the P.V operand: entry 4 g + l16/4 (+16 s), channel 128 w4 + 4 (l16%4) (+16 j)
+  const uint16_t* xtr = xs + (4 * g + (l16 >> 2)) * kXPitch + 128 * w4 + 4 * (l16 & 3);
+  // partial-score tile layout: [wave][entry / 4][head][entry % 4] (a lane's 4 entries are one float4)
+
+  // every sub-group runs the same number of chunk steps (barriers are shared); steps past its
+  // entries do no work
+  for (int cg = 0; cg < sub_len; cg += PF * KC)
+#pragma unroll
+  for (int v = 0; v < PF; ++v) {
+    const int c0 = cg + v * KC;
+    if (c0 >= sub_len) break;
+    const bool active = c0 < snk;
+    float4* sp4 = sp4b + ((c0 / KC) & 1) * (4 * (KC / 4) * 16);
+    if (active) {
+      // dequantize this lane's slab into X; the X slab of wave w4 is read by wave w4 only, and a
+      // wave's LDS operations complete in order, so the reads below see these writes
+      // E4M3 -> f16 is exact, and so is the product with the row's power of two for exponents
+      // in [-15, 7] (the results stay within f16's range and precision)
+      const Piece& pc = gr[v];
+      const _Float16 sc = (_Float16)ldexpf(1.0f, pc.e);
+      const f16x2_t s2 = f16x2_t{sc, sc};
+      uint4* dst = reinterpret_cast<uint4*>(xs + gkey * kXPitch + 64 * gcs);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t cw[4] = {pc.c[m].x, pc.c[m].y, pc.c[m].z, pc.c[m].w};
+        uint32_t vv[8];
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+          vv[2 * t4] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cw[t4], 1.0f, false) * s2);
+          vv[2 * t4 + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cw[t4] >> 16, 1.0f, false) * s2);
+        }
+        dst[2 * m] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
+        dst[2 * m + 1] = make_uint4(vv[4], vv[5], vv[6], vv[7]);
+      }
+      if (c0 + PF * KC < snk) gather(gr[v], c0 + PF * KC);
+      __builtin_amdgcn_wave_barrier();
+      // partial S^T over this wave's channels: entry tile t, lane holds entries 16 t + 4 g + i of head l16
+      const uint16_t* xr = xs + l16 * kXPitch + 128 * w4 + 8 * g;
+      float4* my_sp = sp4 + w4 * (KC / 4) * 16;
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
+        f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;  // two chains halve the dependency latency
+#pragma unroll
+        for (int kk = 0; kk < 4; kk += 2) {
+          const f16x8_t a0 = *reinterpret_cast<const f16x8_t*>(xr + 16 * t * kXPitch + 32 * kk);
+          const f16x8_t a1 = *reinterpret_cast<const f16x8_t*>(xr + 16 * t * kXPitch + 32 * kk + 32);
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qb[kk], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qb[kk + 1], s1, 0, 0, 0);
+        }
+        const f32x4_t sv = s0 + s1;
+        my_sp[(4 * t + g) * 16 + l16] = make_float4(sv[0], sv[1], sv[2], sv[3]);
+      }
+    }
+    __syncthreads();
+    if (!active) continue;
+    // complete scores and online softmax over the chunk: lane holds entries 16 s + 4 g + i of head l16
+    uint64_t vmask;                  // bit e: entry c0 + e of the sub-group is a real entry
+    {
+      vmask = __ballot(lane < KC && c0 + lane < snk);
+    }
+    float tv[NS][4];
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      float4 a = sp4[(4 * s + g) * 16 + l16];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        const float4 x = sp4[w * (KC / 4) * 16 + (4 * s + g) * 16 + l16];
+        a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+      }
+      const float sv[4] = {a.x, a.y, a.z, a.w};
+      const uint32_t vb = (uint32_t)(vmask >> (16 * s + 4 * g)) & 15u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        tv[s][i] = ((vb >> i) & 1u) ? sv[i] * qscale : -INFINITY;
+        cmax = fmaxf(cmax, tv[s][i]);
+      }
+    }
+    cmax = head_max(cmax);
+    if (m_run == -INFINITY) {
+      m_run = cmax;                 // first entries of this head: nothing accumulated yet
+    } else if (__builtin_expect(__ballot(cmax > m_run + kLazyRescale) != 0, 0)) {
+      const float mn = fmaxf(m_run, cmax);
+      const float alpha = exp2f(m_run - mn);
+      l_run *= alpha;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] *= alpha;
+      m_run = mn;
+    }
+    float psum = 0.0f;
+    f16x4_t pb[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const _Float16 pv = m_run == -INFINITY ? (_Float16)0.0f : (_Float16)exp2f(tv[s][i] - m_run);
+        psum += (float)pv;
+        pb[s][i] = pv;
+      }
+    l_run += head_sum(psum);
+    // O^T += X^T P^T: this wave's 8 channel tiles over the chunk's entry steps
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(xtr + 16 * s * kXPitch + 16 * j));
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), pb[s], acc[j], 0, 0, 0);
+      }
+  }
+
+  // merge the sub-groups: groups 1.. leave (max, sum) and their tiles in LDS, group 0 combines
+  float M = m_run, L = l_run;
+  if (NG > 1) {
+    __syncthreads();                               // every group is done with its buffers
+    if (sg > 0) {
+      float4* ob = reinterpret_cast<float4*>(smem + (sg - 1) * Sm::kOut);  // [w4][j][lane]
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ob[(w4 * 8 + j) * 64 + lane] = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+      if (w4 == 0 && g == 0) {
+        ml[(sg * 16 + l16) * 2] = m_run;
+        ml[(sg * 16 + l16) * 2 + 1] = l_run;
+      }
+    }
+    __syncthreads();
+    if (sg > 0) return;
+#pragma unroll
+    for (int k = 1; k < NG; ++k) M = fmaxf(M, ml[(k * 16 + l16) * 2]);
+    const float f0 = m_run == -INFINITY ? 0.0f : exp2f(m_run - M);
+    L = l_run * f0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= f0;
+#pragma unroll
+    for (int k = 1; k < NG; ++k) {
+      const float mk = ml[(k * 16 + l16) * 2];
+      const float fk = mk == -INFINITY ? 0.0f : exp2f(mk - M);
+      L += ml[(k * 16 + l16) * 2 + 1] * fk;
+      const float4* obk = reinterpret_cast<const float4*>(smem + (k - 1) * Sm::kOut);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float4 o = obk[(w4 * 8 + j) * 64 + lane];
+        acc[j] += f32x4_t{o.x, o.y, o.z, o.w} * fk;
+      }
+    }
+  }
+
+  // merge with the sparse result already in out (normalized) and lse_sparse (natural log): both
+  // are partial softmaxes over disjoint sets, so the union's output weights them by their sums
+  const int64_t orow = (int64_t)qr * H + head;
+  const float ls2 = lse_sparse ? lse_sparse[orow] * kLog2e : -INFINITY;
+  const float Mx = fmaxf(M, ls2);
+  float ws = 0.0f, ww = 0.0f, inv = 0.0f;
+  if (Mx != -INFINITY) {
+    ws = ls2 == -INFINITY ? 0.0f : exp2f(ls2 - Mx);
+    ww = M == -INFINITY ? 0.0f : exp2f(M - Mx);
+    inv = 1.0f / (ws + ww * L);
+  }
+  float* dst = out + orow * kD;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float4* p4 = reinterpret_cast<float4*>(dst + 128 * w4 + 16 * j + 4 * g);
+    const float4 os = lse_sparse ? *p4 : make_float4(0.f, 0.f, 0.f, 0.f);
+    const f32x4_t v = (f32x4_t{os.x, os.y, os.z, os.w} * ws + acc[j] * ww) * inv;
+    *p4 = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  if (lse && w4 == 0 && g == 0) lse[orow] = Mx == -INFINITY ? -INFINITY : (Mx + log2f(ws + ww * L)) * kLn2;
+}
+
 // Prefill form: many query rows, so one workgroup per (query row, 64 heads) keeps the chip busy
 // and each gathered entry is dequantized once for all 64 heads. Four waves; wave w owns channels
 // 128w .. 128w+127 throughout, as in the decode form, but every wave serves all 64 heads:
@@ -1073,6 +1373,31 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* rows, int n_max,
   const int per_xcd = (int)(((rows_h + 3) / 4 + 7) / 8);
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, part_o, part_ml,
                      n_splits, rows_h, out, lse, per_xcd);
+  return hipGetLastError();
+}
+
+size_t attn_swa_workspace(int B, int H, int D, int K) {
+  const size_t sparse = (attn_workspace(B, 1, H, D, K) + 255) & ~(size_t)255;
+  return sparse + (size_t)B * H * 4;            // the sparse part's lse, read by the merge
+}
+
+hipError_t launch_sparse_attn_swa(const uint16_t* q, const uint8_t* rows, int n_max, const int32_t* idx, int B,
+                                  int H, int D, int K, const uint8_t* swa_codes, const int8_t* swa_exp,
+                                  const int32_t* n_win, int W, float sm_scale, float* out, float* lse, void* ws,
+                                  hipStream_t s) {
+  if (B == 0 || H == 0) return hipSuccess;
+  const size_t sparse = (attn_workspace(B, 1, H, D, K) + 255) & ~(size_t)255;
+  // Separate from the caller's lse: the window kernel reads every (b, h) entry of this buffer from
+  // several waves while one of them writes the merged value.
+  float* lse_s = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + sparse);
+  if (K > 0) {
+    const hipError_t e = launch_sparse_attn(q, rows, n_max, idx, B, 1, H, D, K, sm_scale, out, lse_s, ws, s);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t items = (int64_t)B * (H / 16);
+  const int per_xcd = (int)((items + 7) / 8);
+  hipLaunchKernelGGL((swa_attn_merge_kernel<kDKC, kDPF, kDNG>), dim3((unsigned)(8 * per_xcd)), dim3(256 * kDNG), 0, s,
+                     q, swa_codes, swa_exp, n_win, W, H, sm_scale, out, K > 0 ? lse_s : nullptr, lse, B, per_xcd);
   return hipGetLastError();
 }
 

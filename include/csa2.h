@@ -176,6 +176,35 @@ csa2_status csa2_sparse_attn(const uint16_t* q, const uint8_t* rows, int32_t n_m
                              size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * csa2_sparse_attn_swa - decode attention over the selected FP4 entries joined with the
+ * layer's own sliding window of FP8 rows, as one softmax.
+ * [walkthrough] 一(四): each query attends to its selected entries and to its own layer's
+ * sliding-window KV; 一(五)4: that KV stays in FP8; 三(二)1: the window is 128 tokens.
+ *
+ * One query token per sequence (T = 1). For each (b, h) the softmax runs over the selected
+ * entries of idx[b] (as csa2_sparse_attn) and the window rows 0 .. n_win[b]-1 of sequence b:
+ *   window row value = E4M3(swa_codes[b, w, c]) * 2^swa_exp[b, w]   (exact in f16)
+ * out = sum over the union of softmax(l) * x, lse = ln sum exp(l); nothing to attend: 0, -inf.
+ * Computed as the sparse attention followed by a window kernel that merges the two partial
+ * softmaxes through their log-sum-exps.
+ *
+ * q         [B, H, D] bf16.          rows, n_max, idx [B, K], K: as csa2_sparse_attn with T = 1.
+ * swa_codes [B, W, D] uint8 OCP E4M3 codes (16-byte aligned base); swa_exp [B, W] int8 row
+ *           exponents in [-15, 7] (outside that range the f16 products are not exact).
+ * n_win     [B] int32 (device): window rows of each sequence, clamped to [0, W].
+ * W         rows reserved per sequence, W <= 128 (CSA2_E_SHAPE otherwise).
+ * out       [B, H, D] fp32.          lse [B, H] fp32 or NULL.
+ * ws        scratch of csa2_sparse_attn_swa_workspace_size() bytes (never NULL).
+ * Requires D == 512, H % 16 == 0.
+ * ------------------------------------------------------------------------------------------ */
+size_t csa2_sparse_attn_swa_workspace_size(int32_t B, int32_t H, int32_t D, int32_t K);
+csa2_status csa2_sparse_attn_swa(const uint16_t* q, const uint8_t* rows, int32_t n_max,
+                                 const int32_t* idx, int32_t B, int32_t H, int32_t D, int32_t K,
+                                 const uint8_t* swa_codes, const int8_t* swa_exp,
+                                 const int32_t* n_win, int32_t W, float sm_scale, float* out,
+                                 float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * csa2_layer_step - one CSA2 layer in its static mode.
  * [walkthrough] 一(四)1: every layer computes its own query. Full scores every visible entry
  * with its own indexer query and produces new Top-K; Reindex re-scores the latest shared keys

@@ -103,6 +103,29 @@ def test_sparse_attn_validation(L):
     assert f(FAKE, FAKE, 10, FAKE, 32, 1, 64, 512, 512, 1.0, FAKE, None, None, 0, None) == E_WS
 
 
+def test_sparse_attn_swa_validation(L):
+    f = L.csa2_sparse_attn_swa
+    # q, rows, n_max, idx, B, H, D, K, swa_codes, swa_exp, n_win, W, scale, out, lse, ws, ws_bytes, stream
+    assert f(None, None, 10, None, 1, 64, 256, 8, None, None, None, 128, 1.0, None, None, None, 0, None) == E_SHAPE
+    assert f(None, None, 10, None, 1, 24, 512, 8, None, None, None, 128, 1.0, None, None, None, 0, None) == E_SHAPE
+    assert f(FAKE, FAKE, 10, FAKE, 1, 64, 512, 8, FAKE, FAKE, FAKE, 129, 1.0, FAKE, None, FAKE, 1 << 30,
+             None) == E_SHAPE                                      # window above 128 rows
+    assert f(FAKE, FAKE, 10, FAKE, 1, 64, 512, 8, FAKE, FAKE, FAKE, -1, 1.0, FAKE, None, FAKE, 1 << 30,
+             None) == E_ARG
+    assert f(FAKE, FAKE, 10, FAKE, 1, 64, 512, 8, None, FAKE, FAKE, 128, 1.0, FAKE, None, FAKE, 1 << 30,
+             None) == E_ARG                                        # window rows missing
+    assert f(FAKE, FAKE, 10, FAKE, 1, 64, 512, 8, FAKE, FAKE, None, 128, 1.0, FAKE, None, FAKE, 1 << 30,
+             None) == E_ARG                                        # n_win missing
+    assert f(FAKE, FAKE, 10, FAKE, 1, 64, 512, 8, FAKE + 8, FAKE, FAKE, 128, 1.0, FAKE, None, FAKE, 1 << 30,
+             None) == E_ARG                                        # misaligned window rows
+    need = L.csa2_sparse_attn_swa_workspace_size(32, 64, 512, 512)
+    assert need >= L.csa2_sparse_attn_workspace_size(32, 1, 64, 512, 512) + 32 * 64 * 4
+    assert L.csa2_sparse_attn_swa_workspace_size(32, 64, 512, 0) > 0   # the sparse lse buffer
+    assert f(FAKE, FAKE, 10, FAKE, 32, 64, 512, 512, FAKE, FAKE, FAKE, 128, 1.0, FAKE, None, FAKE, need - 1,
+             None) == E_WS
+    assert f(FAKE, FAKE, 10, FAKE, 0, 64, 512, 512, None, None, None, 128, 1.0, None, None, None, 0, None) == 0
+
+
 def _layer(T=1, H=64, Hi=8, K=512, pool_blocks=0, use_pool=0, block=8):
     kv = SharedKV(rows=FAKE, k_idx=FAKE, n_vis=None, B=4, n_max=4096, D=512, Hk=8, Di=64, valid=0)
     idx = SharedIdx(topk=FAKE, K=K, pool=FAKE if pool_blocks else None, P=pool_blocks * block,

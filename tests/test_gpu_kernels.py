@@ -303,3 +303,92 @@ def test_split_merge_with_garbage_and_reused_workspace():
         out, lse = _sync_np(out), _sync_np(lse)
         ref, lref = _attn_ref(rows, qb, idx, scale)
         check_attn(out, ref, lse, lref, f"split merge B={B} K={K} seed={seed}")
+
+
+# ---------------------------------------------------------------------------------------------
+def _swa_case(B, H, N, K, Wn, n_win, seed, wide_exps=False):
+    rows, qb, idx = _attn_case(B, 1, H, N, K, seed=seed, oob=K > 0)
+    g = np.random.default_rng(seed + 1)
+    src = g.standard_normal((B * Wn, 512)).astype(np.float32)
+    if wide_exps:   # row magnitudes from 2^-24 to 2^14: row exponents across the whole range
+        src *= np.ldexp(1.0, g.integers(-24, 15, size=(B * Wn, 1))).astype(np.float32)
+    codes, exps = O.quantize_swa_fp8(src)
+    return rows, qb[:, 0], idx[:, 0], codes.reshape(B, Wn, 512), exps.reshape(B, Wn), np.asarray(n_win, np.int32)
+
+
+def _swa_ref(rows, qb, idx, codes, exps, n_win, scale):
+    N = rows.shape[1]
+    outs, lses = [], []
+    for b in range(len(qb)):
+        clean = np.where((idx[b] >= 0) & (idx[b] < N), idx[b], -1)
+        win = O.dequant_swa_fp8(codes[b], exps[b])[None]
+        o, l = O.sparse_attn_swa(f64(qb[b])[None], O.dequant_kv_fp4(rows[b]), clean[None], win,
+                                 [min(max(int(n_win[b]), 0), codes.shape[1])], scale)
+        outs.append(o[0])
+        lses.append(l[0])
+    return np.stack(outs), np.stack(lses)
+
+
+def _swa_run(rows, qb, idx, codes, exps, n_win, scale, with_lse=True, ws=None):
+    out, lse = P.sparse_attn_swa(dev_bf16(qb), torch.from_numpy(rows).cuda(), torch.from_numpy(idx).cuda(),
+                                 torch.from_numpy(codes).cuda(), torch.from_numpy(exps).cuda(),
+                                 torch.from_numpy(n_win).cuda(), scale, with_lse=with_lse, ws=ws)
+    return _sync_np(out), (_sync_np(lse) if lse is not None else None)
+
+
+@pytest.mark.parametrize("B,H,N,K,Wn,n_win", [(3, 64, 1000, 100, 128, [128, 1, 77]),
+                                              (2, 16, 200, 33, 64, [0, 50]),
+                                              (2, 32, 10, 0, 128, [128, 5]),
+                                              (32, 64, 800, 512, 128, list(range(0, 128, 4))),
+                                              (4, 128, 600, 1024, 100, [100, 99, 31, 33]),
+                                              (1, 48, 70, 31, 16, [200])])
+def test_sparse_attn_swa(B, H, N, K, Wn, n_win):
+    """Selected FP4 entries joined with the FP8 window as one softmax, against the oracle: one- and
+    several-chunk windows, a ragged last chunk, an empty window, no selected entries (K = 0), the
+    split sparse path (B = 32, K = 512) and n_win above the reserved rows (clamped)."""
+    case = _swa_case(B, H, N, K, Wn, n_win, seed=B * 100 + K + Wn)
+    scale = 1 / np.sqrt(512)
+    out, lse = _swa_run(*case, scale)
+    ref, lref = _swa_ref(*case, scale)
+    check_attn(out, ref, lse, lref, f"swa B={B} H={H} K={K} W={Wn}")
+
+
+def test_sparse_attn_swa_merge_extremes_and_empty():
+    """Row exponents over their whole range, with sm_scale chosen so the largest logit is ~300: in
+    sequence 0 the window dominates and the selected entries' merge weight underflows, in
+    sequence 1 (large FP4 rows, window rows near 2^-24) the reverse; a sequence with nothing to
+    attend (0, -inf); and the call without lse on a workspace of random bytes."""
+    B, H, N, K, Wn = 4, 64, 300, 64, 128
+    rows, qb, idx, codes, exps, _ = _swa_case(B, H, N, K, Wn, [0] * B, seed=77, wide_exps=True)
+    g = np.random.default_rng(78)
+    rows[1] = O.quantize_kv_fp4((400.0 * g.standard_normal((N, 512))).astype(np.float32))
+    tiny = np.ldexp(g.standard_normal((Wn, 512)), -22).astype(np.float32)
+    codes[1], exps[1] = O.quantize_swa_fp8(tiny)
+    qb[1] = W.to_bf16_bits(W.bf16_bits_to_f32(qb[1]) * np.float32(64.0))
+    idx[2, :] = -1
+    n_win = np.array([128, 100, 0, 64], np.int32)
+    qf = W.bf16_bits_to_f32(qb).astype(np.float64)
+    big = 0.0
+    for b in range(B):
+        sel = idx[b][(idx[b] >= 0) & (idx[b] < N)]
+        x = np.concatenate([O.dequant_kv_fp4(rows[b])[sel], O.dequant_swa_fp8(codes[b], exps[b])[:n_win[b]]])
+        if len(x):
+            big = max(big, float(np.abs(qf[b] @ x.T).max()))
+    scale = 300.0 / big
+    out, lse = _swa_run(rows, qb, idx, codes, exps, n_win, scale)
+    ref, lref = _swa_ref(rows, qb, idx, codes, exps, n_win, scale)
+    check_attn(out, ref, lse, lref, "swa extremes")
+    assert np.all(out[2] == 0) and np.all(np.isneginf(lse[2]))
+    gt = torch.Generator().manual_seed(11)
+    ws = torch.randint(0, 256, (8 << 20,), dtype=torch.uint8, generator=gt).cuda()
+    out2, none = _swa_run(rows, qb, idx, codes, exps, n_win, scale, with_lse=False, ws=ws)
+    assert none is None and np.array_equal(out2, out)
+
+
+def test_sparse_attn_swa_window_only_single_row_is_exact():
+    """One window row and no selected entries: the output is that row's dequantized value."""
+    rows, qb, idx, codes, exps, _ = _swa_case(1, 16, 20, 2, 8, [1], seed=5, wide_exps=True)
+    idx[:] = -1
+    out, lse = _swa_run(rows, qb, idx, codes, exps, np.array([1], np.int32), 0.1)
+    x = O.dequant_swa_fp8(codes[0, :1], exps[0, :1])[0].astype(np.float32)
+    assert np.array_equal(out[0], np.broadcast_to(x, (16, 512)))
