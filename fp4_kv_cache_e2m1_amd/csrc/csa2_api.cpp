@@ -167,7 +167,7 @@ csa2_status csa2_hier_pool(const float* block_max, int64_t rows, int32_t n_block
 }
 
 size_t csa2_sparse_attn_workspace_size(int32_t B, int32_t T, int32_t H, int32_t D, int32_t K) {
-  if (B <= 0 || T <= 0 || !attn_shape_ok(H, D) || K <= 0) return 0;
+  if (B <= 0 || T <= 0 || !attn_shape_ok(H, D) || K <= 0 || K > kMaxK) return 0;
   return attn_workspace(B, T, H, D, K);
 }
 
@@ -175,7 +175,8 @@ csa2_status csa2_sparse_attn(const uint16_t* q, const uint8_t* rows, int32_t n_m
                              int32_t T, int32_t H, int32_t D, int32_t K, float sm_scale, float* out, float* lse,
                              void* ws, size_t ws_bytes, void* stream) {
   if (B < 0 || T < 0 || n_max < 0 || K < 0 || H < 0) return CSA2_E_ARG;
-  if (!attn_shape_ok(H, D)) return CSA2_E_SHAPE;
+  // a split stages at most 1024 entry positions and the combine pass reads at most 64 splits
+  if (!attn_shape_ok(H, D) || K > kMaxK) return CSA2_E_SHAPE;
   if ((int64_t)B * T > INT32_MAX) return CSA2_E_SHAPE;
   if (B == 0 || T == 0) return CSA2_OK;
   if (!q || !out || (K > 0 && (!idx || (n_max > 0 && !rows)))) return CSA2_E_ARG;
@@ -189,7 +190,7 @@ csa2_status csa2_sparse_attn(const uint16_t* q, const uint8_t* rows, int32_t n_m
 }
 
 size_t csa2_sparse_attn_swa_workspace_size(int32_t B, int32_t H, int32_t D, int32_t K) {
-  if (B <= 0 || !attn_shape_ok(H, D) || K < 0) return 0;
+  if (B <= 0 || !attn_shape_ok(H, D) || K < 0 || K > kMaxK) return 0;
   return attn_swa_workspace(B, H, D, K);
 }
 
@@ -198,7 +199,7 @@ csa2_status csa2_sparse_attn_swa(const uint16_t* q, const uint8_t* rows, int32_t
                                  const int8_t* swa_exp, const int32_t* n_win, int32_t W, float sm_scale,
                                  float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   if (B < 0 || n_max < 0 || K < 0 || H < 0 || W < 0) return CSA2_E_ARG;
-  if (!attn_shape_ok(H, D) || W > kMaxSwaWindow) return CSA2_E_SHAPE;
+  if (!attn_shape_ok(H, D) || W > kMaxSwaWindow || K > kMaxK) return CSA2_E_SHAPE;
   if (B == 0) return CSA2_OK;
   if (!q || !out || !n_win || (W > 0 && (!swa_codes || !swa_exp)) || (K > 0 && (!idx || (n_max > 0 && !rows))))
     return CSA2_E_ARG;

@@ -320,7 +320,7 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ rows, int n_max,
     const int32_t* __restrict__ idx, int T, int H, int K, int keys_per_split, float sm_scale,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
-    float* __restrict__ part_ml, int n_rows, int n_splits, int per_xcd) {
+    float* __restrict__ part_ml, int n_rows, int n_splits, int final_out, int per_xcd) {
   using Sm = DecodeSmem<KC, NG>;
   constexpr int NT = 256 * NG, NS = KC / 16;    // NS entry steps of 16 per chunk
   static_assert(KC == 32, "a wave's 64 lanes gather the chunk's 32 entries x 2 slabs of 64 channels");
@@ -597,9 +597,9 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
     }
   }
 
-  // every wave holds the same (M, L) and disjoint channels: write directly
+  // every wave holds the same (M, L) and disjoint channels: write directly (final_out: the only
+  // split, normalized; else an unnormalized partial of split `split` for the combine pass)
   const int64_t orow = (int64_t)qr * H + head;
-  const bool final_out = n_splits == 1;
   const float scale = final_out ? (L > 0.0f ? 1.0f / L : 0.0f) : 1.0f;
   float* dst = final_out ? out + orow * kD : part_o + ((int64_t)split * n_rows * H + orow) * kD;
 #pragma unroll
@@ -620,14 +620,15 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
 
 // Sliding-window branch for decode (one query token per sequence): the layer's own window of
 // FP8 rows ([walkthrough] 一(四): each query also attends to its own layer's sliding-window KV;
-// 一(五)4: that KV stays in FP8). Same structure as the decode form above over the window rows
-// (positions 0 .. n_win-1 of the sequence's window), then the result is merged with the sparse
-// attention already written to out / lse_sparse, which makes it one softmax over the union.
+// 一(五)4: that KV stays in FP8). Same structure as the decode form above, over window rows
+// wsplit * rows_per_split .. of sequence b (rows 0 .. n_win[b]-1 are valid), written as
+// unnormalized partials into slots slot0 + wsplit of the decode form's split buffers, so that the
+// combine pass makes one softmax of the selected entries and the window.
 template <int KC, int PF, int NG>
-__global__ __launch_bounds__(256 * NG) void swa_attn_merge_kernel(
+__global__ __launch_bounds__(256 * NG) void swa_attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ swa_codes, const int8_t* __restrict__ swa_exp,
-    const int32_t* __restrict__ n_win, int W, int H, float sm_scale, float* __restrict__ out,
-    const float* __restrict__ lse_sparse, float* __restrict__ lse, int n_rows, int per_xcd) {
+    const int32_t* __restrict__ n_win, int W, int H, int rows_per_split, float sm_scale,
+    float* __restrict__ part_o, float* __restrict__ part_ml, int slot0, int n_rows, int n_wsplits, int per_xcd) {
   constexpr int T = 1;
   using Sm = DecodeSmem<KC, NG>;
   constexpr int NS = KC / 16;                  // NS entry steps of 16 per chunk
@@ -642,8 +643,8 @@ __global__ __launch_bounds__(256 * NG) void swa_attn_merge_kernel(
   // gather and the query they load are fetched from HBM about once.
   const int n_hg = H / 16;
   const int u = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  if (u >= n_rows * n_hg) return;
-  const int qr = u / n_hg, hg = u % n_hg;
+  if (u >= n_rows * n_wsplits * n_hg) return;
+  const int qr = u / (n_wsplits * n_hg), wsplit = (u / n_hg) % n_wsplits, hg = u % n_hg;
   const int b = qr / T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sg = wave >> 2, w4 = wave & 3;   // sub-group and wave within it
@@ -654,10 +655,12 @@ __global__ __launch_bounds__(256 * NG) void swa_attn_merge_kernel(
   uint16_t* xs = reinterpret_cast<uint16_t*>(gbase);
   float4* sp4b = reinterpret_cast<float4*>(gbase + Sm::kX);
 
-  const int nk = max(0, min(n_win[b], W));                           // window rows of this sequence
+  const int n_valid = max(0, min(n_win[b], W));                      // window rows of this sequence
+  const int kbeg = wsplit * rows_per_split;
+  const int nk = max(0, min(n_valid, kbeg + rows_per_split) - kbeg);  // rows of this workgroup
   const int sub_len = ((nk + NG - 1) / NG + KC - 1) / KC * KC;          // entries per sub-group
-  const int sbeg = sg * sub_len;
-  const int snk = max(0, min(nk - sbeg, sub_len));                     // entries of this sub-group
+  const int sbeg = kbeg + sg * sub_len;                                 // first window row of the sub-group
+  const int snk = max(0, min(nk - sg * sub_len, sub_len));             // entries of this sub-group
   const uint8_t* wbase = swa_codes + (int64_t)b * W * kD;           // [W][512] E4M3 codes
   const int8_t* ebase = swa_exp + (int64_t)b * W;                    // [W] row exponents
 
@@ -689,7 +692,7 @@ __global__ __launch_bounds__(256 * NG) void swa_attn_merge_kernel(
 #pragma unroll
     for (int m = 0; m < 4; ++m) d.c[m] = make_uint4(0, 0, 0, 0);
     d.e = 0;
-    if (p >= 0 && p < nk) {
+    if (p >= 0 && p < n_valid) {
       const uint4* rp = reinterpret_cast<const uint4*>(wbase + (int64_t)p * kD + 64 * gcs);
 #pragma unroll
       for (int m = 0; m < 4; ++m) d.c[m] = rp[m];
@@ -896,26 +899,16 @@ __global__ __launch_bounds__(256 * NG) void swa_attn_merge_kernel(
     }
   }
 
-  // merge with the sparse result already in out (normalized) and lse_sparse (natural log): both
-  // are partial softmaxes over disjoint sets, so the union's output weights them by their sums
-  const int64_t orow = (int64_t)qr * H + head;
-  const float ls2 = lse_sparse ? lse_sparse[orow] * kLog2e : -INFINITY;
-  const float Mx = fmaxf(M, ls2);
-  float ws = 0.0f, ww = 0.0f, inv = 0.0f;
-  if (Mx != -INFINITY) {
-    ws = ls2 == -INFINITY ? 0.0f : exp2f(ls2 - Mx);
-    ww = M == -INFINITY ? 0.0f : exp2f(M - Mx);
-    inv = 1.0f / (ws + ww * L);
-  }
-  float* dst = out + orow * kD;
+  // the workgroup's partial: unnormalized output and (max, sum) in the exp2 domain
+  const int64_t prow = (int64_t)(slot0 + wsplit) * n_rows * H + (int64_t)qr * H + head;
+  float* dst = part_o + prow * kD;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float4* p4 = reinterpret_cast<float4*>(dst + 128 * w4 + 16 * j + 4 * g);
-    const float4 os = lse_sparse ? *p4 : make_float4(0.f, 0.f, 0.f, 0.f);
-    const f32x4_t v = (f32x4_t{os.x, os.y, os.z, os.w} * ws + acc[j] * ww) * inv;
-    *p4 = make_float4(v[0], v[1], v[2], v[3]);
+  for (int j = 0; j < 8; ++j)
+    *reinterpret_cast<float4*>(dst + 128 * w4 + 16 * j + 4 * g) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+  if (w4 == 0 && g == 0) {
+    part_ml[2 * prow] = M;
+    part_ml[2 * prow + 1] = L;
   }
-  if (lse && w4 == 0 && g == 0) lse[orow] = Mx == -INFINITY ? -INFINITY : (Mx + log2f(ws + ww * L)) * kLn2;
 }
 
 // Prefill form: many query rows, so one workgroup per (query row, 64 heads) keeps the chip busy
@@ -1356,7 +1349,7 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* rows, int n_max,
     const int per_xcd = (int)((items + 7) / 8);
     hipLaunchKernelGGL((sparse_attn_decode_kernel<kDKC, kDPF, kDNG>), dim3((unsigned)(8 * per_xcd)), dim3(256 * kDNG), 0, s, q,
                        rows, n_max, idx, T, H, K, kps, sm_scale, out, lse, part_o, part_ml, (int)nq, n_splits,
-                       per_xcd);
+                       (int)(n_splits == 1), per_xcd);
   } else {
     const int hpw = H >= 64 ? 64 : H;
     dim3 grid((unsigned)nq, (unsigned)n_splits, (unsigned)(H / hpw));
@@ -1376,28 +1369,67 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* rows, int n_max,
   return hipGetLastError();
 }
 
+// The window's share of the combine pass: one slot per kDKC * kDNG window rows.
+constexpr int kSwaRowsPerSplit = kDKC * kDNG;
+constexpr int kMaxSwaSplits = 2;                 // windows of up to 128 rows
+
+// Splits of the selected entries when the window joins them (decode form at any batch): as the
+// decode form's own count, leaving kMaxSwaSplits slots of the combine pass to the window.
+static int swa_sparse_splits(int B, int H, int K, int* kps_out) {
+  if (K <= 0) {
+    if (kps_out) *kps_out = kDKC;
+    return 0;
+  }
+  const int64_t wgs = (int64_t)B * (H / 16);
+  const int by_fill = (int)std::max<int64_t>(1, (kDecodeFill + wgs - 1) / wgs);
+  int sp = std::max(1, std::min((K + kDKC * kDNG - 1) / (kDKC * kDNG), by_fill));
+  sp = std::max(sp, (K + kMaxKPS - 1) / kMaxKPS);
+  int kps = (K + sp - 1) / sp;
+  kps = std::min(kMaxKPS, std::max(kDKC, (kps + kDKC - 1) / kDKC * kDKC));
+  const int max_sp = kMaxSplits - kMaxSwaSplits;
+  const int min_kps = (K + max_sp - 1) / max_sp;
+  if (kps < min_kps) kps = (min_kps + kDKC - 1) / kDKC * kDKC;
+  if (kps_out) *kps_out = kps;
+  return (K + kps - 1) / kps;
+}
+
 size_t attn_swa_workspace(int B, int H, int D, int K) {
-  const size_t sparse = (attn_workspace(B, 1, H, D, K) + 255) & ~(size_t)255;
-  return sparse + (size_t)B * H * 4;            // the sparse part's lse, read by the merge
+  const size_t slots = (size_t)swa_sparse_splits(B, H, K, nullptr) + kMaxSwaSplits;
+  const size_t rows_h = (size_t)B * H;
+  return slots * rows_h * (size_t)D * 4 + slots * rows_h * 8 + 256;
 }
 
 hipError_t launch_sparse_attn_swa(const uint16_t* q, const uint8_t* rows, int n_max, const int32_t* idx, int B,
                                   int H, int D, int K, const uint8_t* swa_codes, const int8_t* swa_exp,
                                   const int32_t* n_win, int W, float sm_scale, float* out, float* lse, void* ws,
                                   hipStream_t s) {
+  (void)D;
   if (B == 0 || H == 0) return hipSuccess;
-  const size_t sparse = (attn_workspace(B, 1, H, D, K) + 255) & ~(size_t)255;
-  // Separate from the caller's lse: the window kernel reads every (b, h) entry of this buffer from
-  // several waves while one of them writes the merged value.
-  float* lse_s = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + sparse);
-  if (K > 0) {
-    const hipError_t e = launch_sparse_attn(q, rows, n_max, idx, B, 1, H, D, K, sm_scale, out, lse_s, ws, s);
+  int kps = kDKC;
+  const int n_sp = swa_sparse_splits(B, H, K, &kps);
+  const int n_ws = (W + kSwaRowsPerSplit - 1) / kSwaRowsPerSplit;     // 0 .. kMaxSwaSplits
+  const int64_t rows_h = (int64_t)B * H;
+  float* part_o = static_cast<float*>(ws);
+  float* part_ml = part_o + (size_t)(n_sp + kMaxSwaSplits) * rows_h * kD;
+  const int n_hg = H / 16;
+  if (n_sp > 0) {
+    const int per_xcd = (int)(((int64_t)B * n_sp * n_hg + 7) / 8);
+    hipLaunchKernelGGL((sparse_attn_decode_kernel<kDKC, kDPF, kDNG>), dim3((unsigned)(8 * per_xcd)), dim3(256 * kDNG), 0, s,
+                       q, rows, n_max, idx, 1, H, K, kps, sm_scale, out, lse, part_o, part_ml, B, n_sp, 0, per_xcd);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t items = (int64_t)B * (H / 16);
-  const int per_xcd = (int)((items + 7) / 8);
-  hipLaunchKernelGGL((swa_attn_merge_kernel<kDKC, kDPF, kDNG>), dim3((unsigned)(8 * per_xcd)), dim3(256 * kDNG), 0, s,
-                     q, swa_codes, swa_exp, n_win, W, H, sm_scale, out, K > 0 ? lse_s : nullptr, lse, B, per_xcd);
+  if (n_ws > 0) {
+    const int per_xcd = (int)(((int64_t)B * n_ws * n_hg + 7) / 8);
+    hipLaunchKernelGGL((swa_attn_kernel<kDKC, kDPF, kDNG>), dim3((unsigned)(8 * per_xcd)), dim3(256 * kDNG), 0, s,
+                       q, swa_codes, swa_exp, n_win, W, H, kSwaRowsPerSplit, sm_scale, part_o, part_ml, n_sp, B, n_ws,
+                       per_xcd);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int per_xcd = (int)(((rows_h + 3) / 4 + 7) / 8);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, part_o, part_ml,
+                     n_sp + n_ws, rows_h, out, lse, per_xcd);
   return hipGetLastError();
 }
 

@@ -166,7 +166,7 @@ csa2_status csa2_hier_pool(const float* block_max, int64_t rows, int32_t n_block
  *
  * q     [B, T, H, D] bf16.        rows [B, n_max, D/2 + D/16] bytes (16-byte aligned base).
  * idx   [B, T, K] int32.          out  [B, T, H, D] fp32.   lse [B, T, H] fp32 or NULL.
- * Requires D == 512, H % 16 == 0.
+ * Requires D == 512, H % 16 == 0, K <= 4096 (the Top-K limit; CSA2_E_SHAPE otherwise).
  * ws    scratch of csa2_sparse_attn_workspace_size() bytes (split-K partial results).
  * ------------------------------------------------------------------------------------------ */
 size_t csa2_sparse_attn_workspace_size(int32_t B, int32_t T, int32_t H, int32_t D, int32_t K);
@@ -185,8 +185,8 @@ csa2_status csa2_sparse_attn(const uint16_t* q, const uint8_t* rows, int32_t n_m
  * entries of idx[b] (as csa2_sparse_attn) and the window rows 0 .. n_win[b]-1 of sequence b:
  *   window row value = E4M3(swa_codes[b, w, c]) * 2^swa_exp[b, w]   (exact in f16)
  * out = sum over the union of softmax(l) * x, lse = ln sum exp(l); nothing to attend: 0, -inf.
- * Computed as the sparse attention followed by a window kernel that merges the two partial
- * softmaxes through their log-sum-exps.
+ * The selected entries are split over workgroups as in the decode form of csa2_sparse_attn,
+ * the window over up to two more; their partial softmaxes meet in one combine pass.
  *
  * q         [B, H, D] bf16.          rows, n_max, idx [B, K], K: as csa2_sparse_attn with T = 1.
  * swa_codes [B, W, D] uint8 OCP E4M3 codes (16-byte aligned base); swa_exp [B, W] int8 row
@@ -194,8 +194,9 @@ csa2_status csa2_sparse_attn(const uint16_t* q, const uint8_t* rows, int32_t n_m
  * n_win     [B] int32 (device): window rows of each sequence, clamped to [0, W].
  * W         rows reserved per sequence, W <= 128 (CSA2_E_SHAPE otherwise).
  * out       [B, H, D] fp32.          lse [B, H] fp32 or NULL.
- * ws        scratch of csa2_sparse_attn_swa_workspace_size() bytes (never NULL).
- * Requires D == 512, H % 16 == 0.
+ * ws        scratch of csa2_sparse_attn_swa_workspace_size() bytes (never NULL; partial
+ *           results of every split, independent of W).
+ * Requires D == 512, H % 16 == 0, K <= 4096.
  * ------------------------------------------------------------------------------------------ */
 size_t csa2_sparse_attn_swa_workspace_size(int32_t B, int32_t H, int32_t D, int32_t K);
 csa2_status csa2_sparse_attn_swa(const uint16_t* q, const uint8_t* rows, int32_t n_max,

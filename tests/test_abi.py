@@ -98,6 +98,8 @@ def test_sparse_attn_validation(L):
     assert f(None, None, 10, None, 1, 1, 96, 512, 8, 1.0, None, None, None, 0, None) == E_SHAPE
     assert f(None, None, 10, None, 1, 1, 64, 512, 8, 1.0, None, None, None, 0, None) == E_ARG
     assert f(FAKE, FAKE + 8, 10, FAKE, 1, 1, 64, 512, 8, 1.0, FAKE, None, None, 0, None) == E_ARG  # misaligned
+    assert f(FAKE, FAKE, 10, FAKE, 1, 1, 64, 512, 4097, 1.0, FAKE, None, FAKE, 1 << 30, None) == E_SHAPE
+    assert L.csa2_sparse_attn_workspace_size(1, 1, 64, 512, 4097) == 0
     need = L.csa2_sparse_attn_workspace_size(32, 1, 64, 512, 512)
     assert need > 0                                                # decode is split over the entries
     assert f(FAKE, FAKE, 10, FAKE, 32, 1, 64, 512, 512, 1.0, FAKE, None, None, 0, None) == E_WS
@@ -112,6 +114,8 @@ def test_sparse_attn_swa_validation(L):
              None) == E_SHAPE                                      # window above 128 rows
     assert f(FAKE, FAKE, 10, FAKE, 1, 64, 512, 8, FAKE, FAKE, FAKE, -1, 1.0, FAKE, None, FAKE, 1 << 30,
              None) == E_ARG
+    assert f(FAKE, FAKE, 10, FAKE, 1, 64, 512, 4097, FAKE, FAKE, FAKE, 128, 1.0, FAKE, None, FAKE, 1 << 30,
+             None) == E_SHAPE                                      # K above the Top-K limit
     assert f(FAKE, FAKE, 10, FAKE, 1, 64, 512, 8, None, FAKE, FAKE, 128, 1.0, FAKE, None, FAKE, 1 << 30,
              None) == E_ARG                                        # window rows missing
     assert f(FAKE, FAKE, 10, FAKE, 1, 64, 512, 8, FAKE, FAKE, None, 128, 1.0, FAKE, None, FAKE, 1 << 30,
@@ -119,8 +123,8 @@ def test_sparse_attn_swa_validation(L):
     assert f(FAKE, FAKE, 10, FAKE, 1, 64, 512, 8, FAKE + 8, FAKE, FAKE, 128, 1.0, FAKE, None, FAKE, 1 << 30,
              None) == E_ARG                                        # misaligned window rows
     need = L.csa2_sparse_attn_swa_workspace_size(32, 64, 512, 512)
-    assert need >= L.csa2_sparse_attn_workspace_size(32, 1, 64, 512, 512) + 32 * 64 * 4
-    assert L.csa2_sparse_attn_swa_workspace_size(32, 64, 512, 0) > 0   # the sparse lse buffer
+    assert need >= L.csa2_sparse_attn_workspace_size(32, 1, 64, 512, 512) + 2 * 32 * 64 * (512 * 4 + 8)
+    assert L.csa2_sparse_attn_swa_workspace_size(32, 64, 512, 0) > 0   # the window's partials
     assert f(FAKE, FAKE, 10, FAKE, 32, 64, 512, 512, FAKE, FAKE, FAKE, 128, 1.0, FAKE, None, FAKE, need - 1,
              None) == E_WS
     assert f(FAKE, FAKE, 10, FAKE, 0, 64, 512, 512, None, None, None, 128, 1.0, None, None, None, 0, None) == 0
