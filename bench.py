@@ -140,6 +140,50 @@ def cpu_baseline(wl, n_seq, min_seconds):
                       f"{dt:.1f} s"}
 
 
+def window_leg(wl, sets, state, n_rows, steps, dev, stream):
+    """Decode attention over the last step's Top-K joined with a full window of n_rows FP8 rows per
+    sequence (csa2_sparse_attn_swa), timed beside the same attention without the window."""
+    import torch
+    import fp4_kv_cache_e2m1_amd as P
+    from fp4_kv_cache_e2m1_amd import workloads as W
+    B = wl.B
+    wins = [W.swa_window(wl, b, n_rows) for b in range(B)]
+    codes = torch.from_numpy(np.stack([c for c, _ in wins])).to(dev)
+    exps = torch.from_numpy(np.stack([e for _, e in wins])).to(dev)
+    n_win = torch.full((B,), n_rows, dtype=torch.int32, device=dev)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+    calls = []
+    for s, kv, idx, _ in state:
+        q = s["q"][0].view(B, wl.H, wl.D)
+        calls.append((q, s["rows"], idx.topk.view(B, wl.k)))
+
+    def timed(fn):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(steps):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps * 1e3
+
+    def with_window(i):
+        q, rows, topk = calls[i % len(calls)]
+        P.sparse_attn_swa(q, rows, topk, codes, exps, n_win, wl.sm_scale, with_lse=False, ws=ws)
+
+    def without(i):
+        q, rows, topk = calls[i % len(calls)]
+        P.sparse_attn(q.view(B, 1, wl.H, wl.D), rows, topk.view(B, 1, wl.k), wl.sm_scale, with_lse=False, ws=ws)
+
+    us_w, us_s = timed(with_window), timed(without)
+    row_b = wl.D // 2 + wl.D // 16
+    nbytes = B * (wl.k * (4 + row_b) + n_rows * (wl.D + 1) + wl.H * wl.D * 2 + wl.H * wl.D * 4)
+    return {"window_rows": n_rows, "us_per_call": round(us_w, 2), "sparse_only_us_per_call": round(us_s, 2),
+            "algorithmic_bytes": nbytes, "hbm_gbs": round(nbytes / (us_w * 1e-6) / 1e9, 1)}
+
+
 def calibrate_copy(dev):
     import torch
     n = 1 << 30
@@ -163,6 +207,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay each step from a captured HIP graph")
+    ap.add_argument("--window", type=int, default=0,
+                    help="also time decode attention with each sequence's window of this many FP8 rows")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path has no "
@@ -297,6 +343,8 @@ def main():
         "step_algorithmic_bytes": step_bytes,
         "roofline": roofline,
     }
+    if args.window > 0 and wl.T == 1:
+        line["window_attention"] = window_leg(wl, sets, state, args.window, args.steps, dev, stream)
     if not args.no_cpu_baseline and args.config == 2:
         log(f"[bench] CPU oracle on {args.cpu_sample} sequences, >= {args.cpu_seconds} s")
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample, args.cpu_seconds)

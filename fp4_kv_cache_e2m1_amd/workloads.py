@@ -23,7 +23,7 @@ import torch
 FULL, REINDEX, REUSE = 0, 1, 2
 
 # tensor ids inside a config's seed space
-TID_KV, TID_KIDX, TID_QIDX, TID_Q, TID_PLANT = 1, 2, 3, 4, 5
+TID_KV, TID_KIDX, TID_QIDX, TID_Q, TID_PLANT, TID_SWA = 1, 2, 3, 4, 5, 6
 
 
 @dataclasses.dataclass(frozen=True)
@@ -128,6 +128,16 @@ def k_idx(wl: Workload, b: int) -> np.ndarray:
         planted = _rng(wl, TID_PLANT, b).choice(wl.N, size=n_plant, replace=False)
         x[planted] += (3.0 * direction[: wl.Hk]).astype(np.float32)
     return to_bf16_bits(x)
+
+
+def swa_window(wl: Workload, b: int, rows: int) -> Tuple[np.ndarray, np.ndarray]:
+    """A sliding window of FP8 rows of sequence b: uint8 [rows, D] E4M3 codes, uniform over the
+    non-NaN codes, and int8 [rows] row exponents, uniform over [-8, 0]."""
+    g = _rng(wl, TID_SWA, b)
+    codes = g.integers(0, 256, size=(rows, wl.D), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0
+    exps = g.integers(-8, 1, size=rows).astype(np.int8)
+    return codes, exps
 
 
 def sequence(wl: Workload, b: int, layers: Optional[int] = None) -> dict:
