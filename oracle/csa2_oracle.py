@@ -226,6 +226,72 @@ def index_scores(q_idx: np.ndarray, k_idx: np.ndarray, n_vis) -> np.ndarray:
     return out
 
 
+# ---------------------------------------------------------------------------------------------
+# O13: FP4 (OCP MXFP4) indexer query and key.
+# ---------------------------------------------------------------------------------------------
+MX_BLOCK = 32         # channels per E8M0 scale (OCP MX)
+MX_EMAX_E2M1 = 2      # exponent of E2M1's largest power of two (6 = 1.5 * 2^2)
+
+
+def e8m0_decode(codes) -> np.ndarray:
+    """OCP E8M0 scale: code c is 2^(c - 127); c = 255 is NaN."""
+    c = np.asarray(codes, dtype=np.int64)
+    return np.where(c == 255, np.nan, np.ldexp(1.0, c - 127))
+
+
+def mxfp4_row_bytes(channels: int) -> int:
+    return channels // 2 + channels // MX_BLOCK
+
+
+def quantize_mxfp4(x: np.ndarray) -> np.ndarray:
+    """O13a. Quantize rows [n, C] to MXFP4 rows [n, C/2 + C/32] bytes.
+
+    [walkthrough] 一(五)4: the indexer query and key are FP4 in the OCP MXFP4 format (E2M1
+    elements, one E8M0 power-of-two scale per 32). Conversion as the OCP MX rule states it
+    (reading R-19): the block's shared exponent is X = floor(log2(max |x|)) - 2 (the largest
+    E2M1 power of two is 2^2), clamped to the E8M0 range [-127, 127]; each element is the E2M1
+    value nearest to x / 2^X (ties to the even code, saturating at 6) with the sign bit of x.
+    A block of zeros takes X = -127. Layout (R-20, as the main KV rows): bytes 0 .. C/2-1 hold
+    the codes (channel 2i in the low nibble of byte i), bytes C/2 .. C/2 + C/32 - 1 the E8M0
+    codes X + 127 of blocks 0, 1, ...
+    """
+    x = np.asarray(x).astype(np.float64)
+    n, C = x.shape
+    assert C % (2 * MX_BLOCK) == 0
+    xb = x.reshape(n, C // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(xb).max(axis=-1)
+    X = np.full(amax.shape, -127, dtype=np.int64)
+    nz = amax > 0
+    X[nz] = np.frexp(amax[nz])[1] - 1 - MX_EMAX_E2M1      # frexp: amax = m 2^e, m in [0.5, 1)
+    X = np.clip(X, -127, 127)
+    mj = _nearest_even_scaled(np.abs(xb), np.ldexp(1.0, X)[..., None])
+    codes = ((np.signbit(xb).astype(np.int64) << 3) | mj).reshape(n, C).astype(np.uint16)
+    out = np.empty((n, mxfp4_row_bytes(C)), dtype=np.uint8)
+    out[:, : C // 2] = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    out[:, C // 2:] = (X + 127).astype(np.uint8)
+    return out
+
+
+def dequant_mxfp4(rows: np.ndarray, channels: int) -> np.ndarray:
+    """O13b. MXFP4 rows [n, C/2 + C/32] -> exact fp64 values [n, C]: E2M1(code) * 2^(scale - 127)."""
+    rows = np.asarray(rows, dtype=np.uint8)
+    n = rows.shape[0]
+    assert rows.shape[1] == mxfp4_row_bytes(channels)
+    codes = np.empty((n, channels), dtype=np.uint8)
+    codes[:, 0::2] = rows[:, : channels // 2] & 0xF
+    codes[:, 1::2] = rows[:, : channels // 2] >> 4
+    return e2m1_decode(codes) * np.repeat(e8m0_decode(rows[:, channels // 2:]), MX_BLOCK, axis=1)
+
+
+def index_scores_mxfp4(q_rows: np.ndarray, k_rows: np.ndarray, channels: int, n_vis) -> np.ndarray:
+    """O13c. The indexer score (O6) of MXFP4 query rows [R, .] against MXFP4 key rows [N, .], each
+    row holding all Hi x Di channels of one query or one entry (one key head per index head, R-4):
+    s[r, n] = sum_c q[r, c] * k[n, c] over the dequantized values, fp64, rounded once to fp32."""
+    q = dequant_mxfp4(q_rows, channels)
+    k = dequant_mxfp4(k_rows, channels)
+    return index_scores(q[:, None, :], k[:, None, :], n_vis)
+
+
 def prefill_n_vis(p0: int, T: int, ratio: int) -> np.ndarray:
     """Causal visibility for query tokens at absolute positions p0 .. p0+T-1 (reading R-6).
 
