@@ -122,6 +122,34 @@ def index_scores(q_idx: torch.Tensor, k_idx: torch.Tensor, n_vis: Optional[torch
     return (out, bm) if block_max else out
 
 
+def mxfp4_row_bytes(channels: int) -> int:
+    return channels // 2 + channels // 32
+
+
+def index_scores_mxfp4(q_rows: torch.Tensor, k_rows: torch.Tensor, channels: int,
+                       n_vis: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """Indexer scores over MXFP4 rows. q_rows [B, T, C/2 + C/32] uint8, k_rows [B, N, C/2 + C/32]
+    uint8 -> scores [B*T, N] fp32 (entries >= n_vis unwritten)."""
+    _need(q_rows, "q_rows", torch.uint8)
+    dev = q_rows.device
+    _need(k_rows, "k_rows", torch.uint8, dev)
+    B, T, RB = q_rows.shape
+    B2, N, RB2 = k_rows.shape
+    if B2 != B or RB != mxfp4_row_bytes(channels) or RB2 != RB:
+        raise ValueError("q_rows / k_rows disagree with B or the row size of C channels")
+    if n_vis is not None:
+        _need(n_vis, "n_vis", torch.int32, dev)
+        if n_vis.numel() != B * T:
+            raise ValueError("n_vis must have B*T entries")
+    if out is None:
+        out = torch.empty(B * T, N, dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, dev)
+    code = _lib.lib().csa2_index_scores_mxfp4(_ptr(q_rows), _ptr(k_rows), B, T, channels, N, _ptr(n_vis),
+                                              _ptr(out), _stream(dev))
+    check("csa2_index_scores_mxfp4", code)
+    return out
+
+
 def topk(scores: torch.Tensor, k: int, n_valid: Optional[torch.Tensor] = None,
          col_to_pos: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """k best columns per row as ascending positions, -1 padded. scores [rows, n] fp32."""

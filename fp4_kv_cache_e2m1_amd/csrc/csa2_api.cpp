@@ -131,6 +131,20 @@ csa2_status csa2_index_scores(const uint16_t* q_idx, const uint16_t* k_idx, int3
                                         block_max, s));
 }
 
+csa2_status csa2_index_scores_mxfp4(const uint8_t* q_rows, const uint8_t* k_rows, int32_t B, int32_t T,
+                                    int32_t C, int32_t n_max, const int32_t* n_vis, float* scores, void* stream) {
+  if (B < 0 || T < 0 || n_max < 0 || C < 0) return CSA2_E_ARG;
+  if (C != 256 && C != 512) return CSA2_E_SHAPE;
+  const int64_t rows = (int64_t)B * T;
+  if (rows == 0 || n_max == 0) return CSA2_OK;
+  if (!q_rows || !k_rows || !scores) return CSA2_E_ARG;
+  if (rows > INT32_MAX || n_max > kMaxCols) return CSA2_E_SHAPE;
+  if (reinterpret_cast<uintptr_t>(q_rows) % 8 || reinterpret_cast<uintptr_t>(k_rows) % 8 ||
+      reinterpret_cast<uintptr_t>(scores) % 4)
+    return CSA2_E_ARG;
+  return hip_status(launch_index_mxfp4(q_rows, k_rows, B, T, C, n_max, n_vis, scores, as_stream(stream)));
+}
+
 size_t csa2_topk_workspace_size(int64_t rows, int32_t n_cols, int32_t k) {
   if (rows <= 0 || n_cols <= 0 || k <= 0 || k > kMaxK || n_cols > kMaxCols) return 0;
   return topk_workspace(rows, n_cols, k);

@@ -1,0 +1,116 @@
+// Lightweight indexer over FP4 query and key rows (OCP MXFP4), streaming form.
+// Source: DeepSeek-V4.1-Flash walkthrough (wkq9411.github.io), 一(五)4 "FP4 Main KV Cache": the
+// indexer query and key are FP4 in the OCP MXFP4 format (E2M1 elements, one power-of-two E8M0
+// scale per 32 channels); 一(四): the indexer scores every main-KV entry.
+//
+// A row (one query's or one entry's Hi x Di channels, C = Hi*Di) is C/2 code bytes (channel 2i
+// in the low nibble of byte i) followed by C/32 E8M0 bytes. score[r, n] = sum_c q[r,c] k[n,c].
+// HBM-bound: every key row is read once (C = 512: 272 bytes instead of 1024 in bf16). L = C/32
+// lanes own one key row, lane j its 32-channel block j: 16 code bytes and one scale byte. The
+// block's E2M1 values of query and key are converted to f16 (exact) and multiplied with v_dot2
+// into an fp32 sum that is exact (products are multiples of 1/4 below 36, 32 of them), which is
+// then scaled by 2^(eq + ek - 254) (one rounding) and the L block sums meet in a butterfly.
+#include "common.h"
+#include "launch.h"
+
+namespace csa2 {
+
+typedef _Float16 f16x2_mx_t __attribute__((ext_vector_type(2)));
+
+constexpr int kMxThreads = 256;
+constexpr int kMxInFlight = 8;          // row steps whose loads a lane issues before using them
+
+// 8 E2M1 codes (one 32-bit word, channel 2i in the low nibble of byte i) -> 4 f16 pairs, exact.
+__device__ __forceinline__ void mx_e2m1x8(uint32_t w, f16x2_mx_t* out) {
+  out[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+  out[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+  out[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+  out[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+}
+
+template <int L>
+__global__ __launch_bounds__(kMxThreads) void index_mxfp4_kernel(const uint8_t* __restrict__ q,
+                                                                 const uint8_t* __restrict__ k, int T,
+                                                                 int n_max, const int32_t* __restrict__ n_vis,
+                                                                 int tile_rows, float* __restrict__ scores) {
+  static_assert(L == 8 || L == 16, "rows of 256 or 512 channels");
+  constexpr int C = 32 * L;
+  constexpr int RB = C / 2 + C / 32;            // bytes per row
+  constexpr int ROWS = kMxThreads / L;          // rows per workgroup step
+  const int r = blockIdx.x;                     // query row = b * T + t
+  const int b = r / T;
+  const int tid = threadIdx.x;
+  const int j = tid % L;                        // the lane's 32-channel block
+  const int grp = tid / L;                      // the lane group's row within a step
+  const int nv = n_vis ? min(n_vis[r], n_max) : n_max;
+  const int tile0 = blockIdx.y * tile_rows;
+  const int tile_end = min(tile0 + tile_rows, nv);
+  if (tile0 >= tile_end) return;
+
+  // the query's block j as 16 f16 pairs and its exponent
+  f16x2_mx_t qv[16];
+  int eq;
+  {
+    const uint8_t* qp = q + (int64_t)r * RB;
+    const uint2 a = *reinterpret_cast<const uint2*>(qp + 16 * j);
+    const uint2 c = *reinterpret_cast<const uint2*>(qp + 16 * j + 8);
+    mx_e2m1x8(a.x, qv);
+    mx_e2m1x8(a.y, qv + 4);
+    mx_e2m1x8(c.x, qv + 8);
+    mx_e2m1x8(c.y, qv + 12);
+    eq = qp[C / 2 + j];
+  }
+  const uint8_t* kb = k + (int64_t)b * n_max * RB;
+  float* srow = scores + (int64_t)r * n_max;
+
+  for (int base = tile0; base < tile_end; base += ROWS * kMxInFlight) {
+    uint2 ca[kMxInFlight], cb[kMxInFlight];
+    int ek[kMxInFlight];
+#pragma unroll
+    for (int u = 0; u < kMxInFlight; ++u) {
+      const int n = base + u * ROWS + grp;
+      ca[u] = cb[u] = make_uint2(0, 0);
+      ek[u] = 127;
+      if (n < tile_end) {
+        const uint8_t* p = kb + (int64_t)n * RB;
+        ca[u] = *reinterpret_cast<const uint2*>(p + 16 * j);
+        cb[u] = *reinterpret_cast<const uint2*>(p + 16 * j + 8);
+        ek[u] = p[C / 2 + j];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kMxInFlight; ++u) {
+      f16x2_mx_t kv[16];
+      mx_e2m1x8(ca[u].x, kv);
+      mx_e2m1x8(ca[u].y, kv + 4);
+      mx_e2m1x8(cb[u].x, kv + 8);
+      mx_e2m1x8(cb[u].y, kv + 12);
+      float part = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) part = __builtin_amdgcn_fdot2(qv[i], kv[i], part, false);
+      float v = ldexpf(part, eq + ek[u] - 254);
+#pragma unroll
+      for (int m = L / 2; m >= 1; m /= 2) v += shfl_xor_f(v, m);
+      const int n = base + u * ROWS + grp;
+      if (j == 0 && n < tile_end) srow[n] = v;
+    }
+  }
+}
+
+hipError_t launch_index_mxfp4(const uint8_t* q, const uint8_t* k, int B, int T, int C, int n_max,
+                              const int32_t* n_vis, float* scores, hipStream_t s) {
+  const int64_t rows = (int64_t)B * T;
+  if (rows == 0 || n_max == 0) return hipSuccess;
+  // tiles of rows per workgroup: enough workgroups to fill the chip several times over
+  const int step = (kMxThreads / (C / 32)) * kMxInFlight;
+  int tile = step;
+  while (tile < 8192 && rows * ((n_max + 2 * tile - 1) / (2 * tile)) >= 2048) tile *= 2;
+  dim3 grid((unsigned)rows, (unsigned)((n_max + tile - 1) / tile));
+  if (C == 256)
+    hipLaunchKernelGGL(index_mxfp4_kernel<8>, grid, dim3(kMxThreads), 0, s, q, k, T, n_max, n_vis, tile, scores);
+  else
+    hipLaunchKernelGGL(index_mxfp4_kernel<16>, grid, dim3(kMxThreads), 0, s, q, k, T, n_max, n_vis, tile, scores);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

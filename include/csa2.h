@@ -114,6 +114,28 @@ csa2_status csa2_index_scores(const uint16_t* q_idx, const uint16_t* k_idx, int3
                               float* scores, float* block_max, int32_t block, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * csa2_index_scores_mxfp4 - the lightweight indexer over FP4 query and key rows.
+ * [walkthrough] 一(五)4: the indexer query and key are FP4 in the OCP MXFP4 format (E2M1
+ * elements, one E8M0 power-of-two scale per 32 channels); 一(四): the indexer scores every
+ * main-KV entry.
+ *
+ * A row holds the C = Hi * Di channels of one query row or one entry (one key head per index
+ * head): bytes 0 .. C/2-1 are E2M1 codes (channel 2i in the low nibble of byte i), bytes
+ * C/2 .. C/2 + C/32 - 1 the E8M0 scale codes (value 2^(code - 127)) of channels 32j .. 32j+31.
+ * score[r, n] = sum_c q[r, c] * k[b(r), n, c] over the dequantized values, r = b*T + t. Each
+ * 32-channel block's sum is exact; the blocks' scaled sums are added in fp32.
+ *
+ * q_rows  [B*T, C/2 + C/32] bytes, k_rows [B, n_max, C/2 + C/32] bytes (8-byte aligned bases).
+ * n_vis   [B*T] int32 visible entries per query row (device), or NULL for all n_max; entries
+ *         n >= n_vis[r] are not scored and their slots are left unwritten.
+ * scores  [B*T, n_max] fp32.
+ * Requires C in {256, 512} (CSA2_E_SHAPE otherwise) and finite scales (code 255 is NaN).
+ * ------------------------------------------------------------------------------------------ */
+csa2_status csa2_index_scores_mxfp4(const uint8_t* q_rows, const uint8_t* k_rows, int32_t B,
+                                    int32_t T, int32_t C, int32_t n_max, const int32_t* n_vis,
+                                    float* scores, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * csa2_topk - Top-K selection per row.
  * [walkthrough] 一(四): each query keeps its Top-K entries (512 in the model, 三(二)1).
  *

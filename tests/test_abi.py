@@ -105,6 +105,18 @@ def test_sparse_attn_validation(L):
     assert f(FAKE, FAKE, 10, FAKE, 32, 1, 64, 512, 512, 1.0, FAKE, None, None, 0, None) == E_WS
 
 
+def test_index_scores_mxfp4_validation(L):
+    f = L.csa2_index_scores_mxfp4
+    # q_rows, k_rows, B, T, C, n_max, n_vis, scores, stream
+    assert f(FAKE, FAKE, 1, 1, 128, 10, None, FAKE, None) == E_SHAPE
+    assert f(FAKE, FAKE, 1, 1, 1024, 10, None, FAKE, None) == E_SHAPE
+    assert f(FAKE, FAKE, -1, 1, 512, 10, None, FAKE, None) == E_ARG
+    assert f(None, FAKE, 1, 1, 512, 10, None, FAKE, None) == E_ARG
+    assert f(FAKE + 4, FAKE, 1, 1, 512, 10, None, FAKE, None) == E_ARG       # misaligned rows
+    assert f(None, None, 0, 1, 512, 10, None, None, None) == 0                # nothing to do
+    assert f(None, None, 1, 1, 512, 0, None, None, None) == 0
+
+
 def test_sparse_attn_swa_validation(L):
     f = L.csa2_sparse_attn_swa
     # q, rows, n_max, idx, B, H, D, K, swa_codes, swa_exp, n_win, W, scale, out, lse, ws, ws_bytes, stream

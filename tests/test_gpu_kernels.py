@@ -392,3 +392,53 @@ def test_sparse_attn_swa_window_only_single_row_is_exact():
     out, lse = _swa_run(rows, qb, idx, codes, exps, np.array([1], np.int32), 0.1)
     x = O.dequant_swa_fp8(codes[0, :1], exps[0, :1])[0].astype(np.float32)
     assert np.array_equal(out[0], np.broadcast_to(x, (16, 512)))
+
+
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("B,T,N,C,spread", [(3, 1, 1000, 512, 0), (2, 1, 777, 256, 0), (1, 1, 1, 512, 0),
+                                            (32, 1, 1100, 512, 0), (2, 3, 2049, 256, 6), (2, 1, 20000, 512, 0)])
+def test_index_scores_mxfp4(B, T, N, C, spread):
+    """FP4 (MXFP4) indexer against the oracle on MXFP4 rows the oracle quantized: ragged tiles,
+    one entry, several query rows per sequence with n_vis cutting tiles, block magnitudes spread
+    over 2^-spread .. 2^spread (different scales per block), and long rows over many tiles.
+    Slots past n_vis stay as they were."""
+    g = np.random.default_rng(N + C + T)
+    xq = g.standard_normal((B * T, C)).astype(np.float32)
+    xk = g.standard_normal((B * N, C)).astype(np.float32)
+    if spread:
+        xq *= np.ldexp(1.0, g.integers(-spread, spread + 1, size=(B * T, C // 32))).repeat(32, 1).astype(np.float32)
+        xk *= np.ldexp(1.0, g.integers(-spread, spread + 1, size=(B * N, C // 32))).repeat(32, 1).astype(np.float32)
+    q_rows = O.quantize_mxfp4(xq).reshape(B, T, -1)
+    k_rows = O.quantize_mxfp4(xk).reshape(B, N, -1)
+    n_vis = np.array([[max(1, N - 7 * (b * T + t) - 300 * t) for t in range(T)] for b in range(B)], np.int32).reshape(-1)
+    n_vis[0] = N
+    out = torch.full((B * T, N), 7.0, dtype=torch.float32).cuda()
+    s = _sync_np(P.index_scores_mxfp4(torch.from_numpy(q_rows).cuda(), torch.from_numpy(k_rows).cuda(), C,
+                                      n_vis=torch.from_numpy(n_vis).cuda(), out=out))
+    for b in range(B):
+        kd = O.dequant_mxfp4(k_rows[b], C)
+        rows = range(b * T, b * T + T) if B <= 4 else [b * T]
+        for r in rows:
+            ref = O.index_scores_mxfp4(q_rows.reshape(B * T, -1)[r:r + 1], k_rows[b], C, [n_vis[r]])[0]
+            qd = O.dequant_mxfp4(q_rows.reshape(B * T, -1)[r:r + 1], C)
+            mask = np.arange(N) < n_vis[r]
+            check_scores(s[r], ref, (np.abs(qd) @ np.abs(kd).T)[0], mask, f"mxfp4 r={r}")
+            assert np.all(s[r][~mask] == 7.0)
+
+
+def test_index_scores_mxfp4_exact_blocks():
+    """Keys equal to the query on one 32-channel block and zero elsewhere: every score is that
+    block's exact sum of squares times its scale squared (one exact block, no rounding)."""
+    C, N = 512, 300
+    g = np.random.default_rng(3)
+    xq = g.standard_normal((1, C)).astype(np.float32)
+    q_rows = O.quantize_mxfp4(xq)
+    k_src = np.zeros((N, C), np.float32)
+    qd = O.dequant_mxfp4(q_rows, C)[0]
+    for n in range(N):
+        blk = n % 16
+        k_src[n, 32 * blk: 32 * blk + 32] = qd[32 * blk: 32 * blk + 32]
+    k_rows = O.quantize_mxfp4(k_src)
+    s = _sync_np(P.index_scores_mxfp4(torch.from_numpy(q_rows[None]).cuda(), torch.from_numpy(k_rows[None]).cuda(), C))
+    want = np.array([np.sum(qd[32 * (n % 16): 32 * (n % 16) + 32] ** 2) for n in range(N)], np.float32)
+    assert np.array_equal(s[0], want)
