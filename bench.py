@@ -140,6 +140,36 @@ def cpu_baseline(wl, n_seq, min_seconds):
                       f"{dt:.1f} s"}
 
 
+def fp4_indexer_leg(wl, steps, dev, stream):
+    """csa2_index_scores_mxfp4 over the workload's B x N entries with their Hi x Di indexer
+    channels stored as MXFP4 rows (seeded synthetic codes and scales), two alternating copies;
+    achieved bytes per launch against the HBM peak."""
+    import torch
+    import fp4_kv_cache_e2m1_amd as P
+    from fp4_kv_cache_e2m1_amd import workloads as W
+    C = wl.Hi * wl.Di
+    keys = [torch.from_numpy(np.stack([W.mxfp4_rows(wl, b, wl.N, C, copy=c) for b in range(wl.B)])).to(dev)
+            for c in range(2)]
+    q = torch.from_numpy(np.stack([W.mxfp4_rows(wl, b, wl.T, C, copy=2) for b in range(wl.B)])).to(dev)
+    out = torch.empty(wl.B * wl.T, wl.N, dtype=torch.float32, device=dev)
+    for i in range(3):
+        P.index_scores_mxfp4(q, keys[i % 2], C, out=out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(steps):
+        P.index_scores_mxfp4(q, keys[i % 2], C, out=out)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / steps * 1e3
+    rb = C // 2 + C // 32
+    nbytes = wl.B * wl.N * rb + wl.B * wl.T * rb
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"kernel": "index_mxfp4_kernel (MXFP4 indexer scores)", "bound": "hbm", "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": round(us, 2), "row_bytes": rb}
+
+
 def window_leg(wl, sets, state, n_rows, steps, dev, stream):
     """Decode attention over the last step's Top-K joined with a full window of n_rows FP8 rows per
     sequence (csa2_sparse_attn_swa), timed beside the same attention without the window."""
@@ -207,6 +237,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay each step from a captured HIP graph")
+    ap.add_argument("--fp4-indexer", action="store_true",
+                    help="also time the FP4 (MXFP4) indexer on the workload's keys, stored as MXFP4 rows")
     ap.add_argument("--window", type=int, default=0,
                     help="also time decode attention with each sequence's window of this many FP8 rows")
     args = ap.parse_args()
@@ -343,6 +375,8 @@ def main():
         "step_algorithmic_bytes": step_bytes,
         "roofline": roofline,
     }
+    if args.fp4_indexer and wl.T == 1 and wl.Hk == wl.Hi and wl.Hi * wl.Di in (256, 512):
+        line["fp4_indexer"] = fp4_indexer_leg(wl, args.steps, dev, stream)
     if args.window > 0 and wl.T == 1:
         line["window_attention"] = window_leg(wl, sets, state, args.window, args.steps, dev, stream)
     if not args.no_cpu_baseline and args.config == 2:

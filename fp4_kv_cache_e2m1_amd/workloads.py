@@ -23,7 +23,7 @@ import torch
 FULL, REINDEX, REUSE = 0, 1, 2
 
 # tensor ids inside a config's seed space
-TID_KV, TID_KIDX, TID_QIDX, TID_Q, TID_PLANT, TID_SWA = 1, 2, 3, 4, 5, 6
+TID_KV, TID_KIDX, TID_QIDX, TID_Q, TID_PLANT, TID_SWA, TID_MXFP4 = 1, 2, 3, 4, 5, 6, 7
 
 
 @dataclasses.dataclass(frozen=True)
@@ -128,6 +128,15 @@ def k_idx(wl: Workload, b: int) -> np.ndarray:
         planted = _rng(wl, TID_PLANT, b).choice(wl.N, size=n_plant, replace=False)
         x[planted] += (3.0 * direction[: wl.Hk]).astype(np.float32)
     return to_bf16_bits(x)
+
+
+def mxfp4_rows(wl: Workload, b: int, rows: int, channels: int, copy: int = 0) -> np.ndarray:
+    """MXFP4 rows of sequence b: uint8 [rows, C/2 + C/32], codes uniform over all 16 E2M1 codes,
+    scale codes uniform over 2^-4 .. 2^2 (E8M0 123 .. 129)."""
+    g = _rng(wl, TID_MXFP4, b, copy)
+    out = g.integers(0, 256, size=(rows, channels // 2 + channels // 32), dtype=np.uint8)
+    out[:, channels // 2:] = g.integers(123, 130, size=(rows, channels // 32), dtype=np.uint8)
+    return out
 
 
 def swa_window(wl: Workload, b: int, rows: int) -> Tuple[np.ndarray, np.ndarray]:
