@@ -62,7 +62,8 @@ class LayerArgs(C.Structure):
     _fields_ = [("q", C.c_void_p), ("q_idx", C.c_void_p), ("T", C.c_int32), ("H", C.c_int32),
                 ("Hi", C.c_int32), ("sm_scale", C.c_float), ("use_pool", C.c_int32),
                 ("pool_blocks", C.c_int32), ("block", C.c_int32), ("out", C.c_void_p),
-                ("lse", C.c_void_p), ("ws", C.c_void_p), ("ws_bytes", C.c_size_t)]
+                ("lse", C.c_void_p), ("ws", C.c_void_p), ("ws_bytes", C.c_size_t),
+                ("swa_codes", C.c_void_p), ("swa_exp", C.c_void_p), ("swa_n", C.c_void_p), ("swa_W", C.c_int32)]
 
 
 _lib = None

@@ -311,8 +311,13 @@ def layer_workspace_size(mode: int, args: LayerArgs, kv: KVState, idx: IdxState)
 def layer_step(mode: int, q: torch.Tensor, kv: KVState, idx: IdxState, q_idx: Optional[torch.Tensor] = None,
                sm_scale: Optional[float] = None, use_pool: bool = False, pool_blocks: int = 0, block: int = 8,
                with_lse: bool = True, ws: Optional[torch.Tensor] = None,
-               out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """One CSA2 layer (FULL / REINDEX / REUSE) over caller-owned shared state; returns (out, lse)."""
+               out: Optional[torch.Tensor] = None,
+               window: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None
+               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """One CSA2 layer (FULL / REINDEX / REUSE) over caller-owned shared state; returns (out, lse).
+
+    window: (swa_codes [B, W, D] uint8, swa_exp [B, W] int8, n_win [B] int32), decode only: the
+    layer's sliding window joined to the selected entries as one softmax."""
     _need(q, "q", torch.bfloat16, kv.rows.device)
     dev = q.device
     B, T, H, D = q.shape
@@ -324,6 +329,14 @@ def layer_step(mode: int, q: torch.Tensor, kv: KVState, idx: IdxState, q_idx: Op
         a.q_idx, a.Hi = _ptr(q_idx), q_idx.shape[2]
     a.sm_scale = float(sm_scale if sm_scale is not None else D ** -0.5)
     a.use_pool, a.pool_blocks, a.block = int(use_pool), pool_blocks, block
+    if window is not None:
+        codes, exps, n_win = window
+        _need(codes, "swa_codes", torch.uint8, dev)
+        _need(exps, "swa_exp", torch.int8, dev)
+        _need(n_win, "n_win", torch.int32, dev)
+        if codes.shape[0] != B or codes.shape[2] != D or exps.shape != codes.shape[:2] or n_win.shape != (B,):
+            raise ValueError("window shapes must be [B, W, D], [B, W], [B]")
+        a.swa_codes, a.swa_exp, a.swa_n, a.swa_W = _ptr(codes), _ptr(exps), _ptr(n_win), codes.shape[1]
     if out is None:
         out = torch.empty(B, T, H, D, dtype=torch.float32, device=dev)
     lse = torch.empty(B, T, H, dtype=torch.float32, device=dev) if with_lse else None

@@ -249,6 +249,9 @@ csa2_status plan_layer(csa2_mode mode, const csa2_layer_args* a, const csa2_shar
   if (kv->B < 0 || kv->n_max < 0 || a->T < 0 || idx->K < 0) return CSA2_E_ARG;
   if (!attn_shape_ok(a->H, kv->D)) return CSA2_E_SHAPE;
   if (idx->K > kMaxK) return CSA2_E_SHAPE;
+  const bool window = a->swa_codes != nullptr;
+  if (window && a->T != 1) return CSA2_E_UNSUPPORTED;            // the window branch is decode-only
+  if (window && (a->swa_W < 0 || a->swa_W > kMaxSwaWindow)) return CSA2_E_SHAPE;
   *p = LayerPlan{};
   p->rows = (int64_t)kv->B * a->T;
   p->score = mode != CSA2_REUSE;
@@ -286,7 +289,10 @@ csa2_status plan_layer(csa2_mode mode, const csa2_layer_args* a, const csa2_shar
       sel = std::max(sel, csa2_hier_pool_workspace_size(rows_c, p->n_blocks, a->pool_blocks));
     if (p->build_pool && idx->P > 0 && idx->K > 0)  // Top-K taken from the pool's positions
       sel = std::max(sel, csa2_topk_workspace_size(rows_c, idx->P, idx->K));
-    if (idx->K > 0) attn = std::max(attn, csa2_sparse_attn_workspace_size(b1 - b0, a->T, a->H, kv->D, idx->K));
+    if (window)
+      attn = std::max(attn, csa2_sparse_attn_swa_workspace_size(b1 - b0, a->H, kv->D, idx->K));
+    else if (idx->K > 0)
+      attn = std::max(attn, csa2_sparse_attn_workspace_size(b1 - b0, a->T, a->H, kv->D, idx->K));
   }
   off = align_up(off + sel);
   p->off_attn = off;
@@ -316,6 +322,7 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_share
   if (mode == CSA2_REUSE && !idx->topk_valid) return CSA2_E_STATE;
   if (!a->out || !idx->topk || !kv->rows || !a->q) return CSA2_E_ARG;
   if (p.score && (!a->q_idx || !kv->k_idx)) return CSA2_E_ARG;
+  if (a->swa_codes && (!a->swa_exp || !a->swa_n)) return CSA2_E_ARG;
   if (p.total > 0 && (!a->ws || a->ws_bytes < p.total)) return CSA2_E_WORKSPACE;
 
   uint8_t* ws = static_cast<uint8_t*>(a->ws);
@@ -373,6 +380,12 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_share
         }
       }
     }
+    if (a->swa_codes)
+      return csa2_sparse_attn_swa(a->q + r0 * a->H * kv->D, kv->rows + (int64_t)b0 * kv->n_max * rb, kv->n_max,
+                                  idx->topk + r0 * idx->K, nb, a->H, kv->D, idx->K,
+                                  a->swa_codes + (int64_t)b0 * a->swa_W * kv->D, a->swa_exp + (int64_t)b0 * a->swa_W,
+                                  a->swa_n + b0, a->swa_W, a->sm_scale, a->out + r0 * a->H * kv->D,
+                                  a->lse ? a->lse + r0 * a->H : nullptr, attn_ws, attn_bytes, s_sel);
     return csa2_sparse_attn(a->q + r0 * a->H * kv->D, kv->rows + (int64_t)b0 * kv->n_max * rb, kv->n_max,
                             idx->topk + r0 * idx->K, nb, T, a->H, kv->D, idx->K, a->sm_scale,
                             a->out + r0 * a->H * kv->D, a->lse ? a->lse + r0 * a->H : nullptr, attn_ws, attn_bytes,

@@ -276,6 +276,12 @@ typedef struct {
   float* lse;              /* [B, T, H] fp32 or NULL */
   void* ws;
   size_t ws_bytes;
+  /* The layer's sliding window (decode, T = 1), joined to the selected entries as one softmax
+   * as in csa2_sparse_attn_swa. swa_codes NULL: no window (a zero-initialized struct has none). */
+  const uint8_t* swa_codes; /* [B, swa_W, D] OCP E4M3 codes (16-byte aligned) */
+  const int8_t* swa_exp;    /* [B, swa_W] row exponents in [-15, 7] */
+  const int32_t* swa_n;     /* [B] window rows per sequence (device), clamped to [0, swa_W] */
+  int32_t swa_W;            /* rows reserved per sequence, <= 128 */
 } csa2_layer_args;
 
 csa2_status csa2_layer_workspace_size(csa2_mode mode, const csa2_layer_args* a,

@@ -497,7 +497,7 @@ FULL, REINDEX, REUSE = 0, 1, 2
 
 def layer_step(mode: int, *, q, kv_deq, k_idx=None, q_idx=None, n_vis=None, k=None,
                shared_topk=None, pool=None, pool_blocks: int = 0, block: int = 8,
-               sm_scale: float = 1.0 / np.sqrt(512.0)):
+               sm_scale: float = 1.0 / np.sqrt(512.0), win=None, n_win=None):
     """O11. One layer of one sequence in the given static mode.
 
     [walkthrough] 一(四)1: every layer computes its own query; Full scores all visible entries
@@ -506,7 +506,8 @@ def layer_step(mode: int, *, q, kv_deq, k_idx=None, q_idx=None, n_vis=None, k=No
     latest index-producing layer and computes no indexer query and no score. 一(四)2: with the
     hierarchical indexer the Full layer also builds the candidate pool (pool_blocks > 0) and a
     Reindex layer given a pool scores only the pool (reading R-9: the Full layer itself attends
-    over its flat Top-K).
+    over its flat Top-K). With a window (win [R, W, D] dequantized rows, n_win [R]) the attention
+    is O12c's, over the selected entries and the window as one softmax (一(四), reading R-18).
     Returns dict(out, lse, topk, pool, scores).
     """
     res = {"pool": pool, "scores": None}
@@ -522,6 +523,9 @@ def layer_step(mode: int, *, q, kv_deq, k_idx=None, q_idx=None, n_vis=None, k=No
         s = pool_scores(q_idx, k_idx, pool)
         sel = topk(s, k, col_to_pos=pool)
         res["scores"] = s
-    out, lse = sparse_attn(q, kv_deq, sel, sm_scale)
+    if win is None:
+        out, lse = sparse_attn(q, kv_deq, sel, sm_scale)
+    else:
+        out, lse = sparse_attn_swa(q, kv_deq, sel, win, n_win, sm_scale)
     res.update(out=out, lse=lse, topk=sel)
     return res

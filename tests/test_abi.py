@@ -179,3 +179,22 @@ def test_layer_step_pool_rules(L):
     assert L.csa2_layer_workspace_size(0, C.byref(a3), C.byref(kv3), C.byref(idx3), C.byref(n)) == E_UNSUP
     idx.P = 100                                                      # capacity must equal blocks * 8
     assert L.csa2_layer_workspace_size(0, C.byref(a), C.byref(kv), C.byref(idx), C.byref(n)) == E_SHAPE
+
+
+def test_layer_step_window_rules(L):
+    n = C.c_size_t(0)
+    a, kv, idx = _layer()
+    assert L.csa2_layer_workspace_size(0, C.byref(a), C.byref(kv), C.byref(idx), C.byref(n)) == OK
+    plain = n.value
+    a.swa_codes, a.swa_exp, a.swa_n, a.swa_W = FAKE, FAKE, FAKE, 128
+    assert L.csa2_layer_workspace_size(0, C.byref(a), C.byref(kv), C.byref(idx), C.byref(n)) == OK
+    assert n.value > plain                                          # the window's partial slots
+    a.swa_W = 129
+    assert L.csa2_layer_workspace_size(0, C.byref(a), C.byref(kv), C.byref(idx), C.byref(n)) == E_SHAPE
+    a.swa_W = 128
+    a.swa_exp = None                                                # exponents missing
+    kv.valid, idx.topk_valid = 1, 1
+    assert L.csa2_layer_step(2, C.byref(a), C.byref(kv), C.byref(idx), None) == E_ARG
+    a2, kv2, idx2 = _layer(T=2)
+    a2.swa_codes, a2.swa_exp, a2.swa_n, a2.swa_W = FAKE, FAKE, FAKE, 128
+    assert L.csa2_layer_workspace_size(0, C.byref(a2), C.byref(kv2), C.byref(idx2), C.byref(n)) == E_UNSUP

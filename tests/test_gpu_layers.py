@@ -241,3 +241,55 @@ def test_config_full_size(cfg, sample):
         pool = res[0][3]
         for r in range(wl.B):
             assert set(t[r][t[r] >= 0].tolist()) <= set(pool[r].tolist())
+
+
+def test_layer_stack_with_window():
+    """Full -> Reindex -> Reuse in decode, each layer with its own FP8 window (full, partial and
+    empty windows across the batch): the selections are the same as without the window, the
+    output equals csa2_sparse_attn_swa on the layer's Top-K, and it matches the oracle's union
+    attention on the oracle's own selection."""
+    wl = SMALL["stack"]
+    Wn = 128
+    n_win = np.array([128, 50, 0], np.int32)[: wl.B]
+    rows, kidx = kv_rows_device(wl), k_idx_device(wl)
+    g = np.random.default_rng(41)
+    wins = []
+    for layer in range(len(wl.modes)):
+        c, e = O.quantize_swa_fp8(g.standard_normal((wl.B * Wn, wl.D)).astype(np.float32))
+        wins.append((c.reshape(wl.B, Wn, wl.D), e.reshape(wl.B, Wn)))
+    n_win_d = torch.from_numpy(n_win).cuda()
+    kv = P.KVState(rows, kidx)
+    idx = P.IdxState.empty(wl.B, wl.k, "cuda")
+    kv0 = P.KVState(rows, kidx)
+    idx0 = P.IdxState.empty(wl.B, wl.k, "cuda")
+    gpu = []
+    for layer, mode in enumerate(wl.modes):
+        q = q_device(wl, layer, "q")
+        qi = q_device(wl, layer, "q_idx") if mode != P.REUSE else None
+        cd, ed = torch.from_numpy(wins[layer][0]).cuda(), torch.from_numpy(wins[layer][1]).cuda()
+        out, lse = P.layer_step(mode, q, kv, idx, q_idx=qi, window=(cd, ed, n_win_d))
+        P.layer_step(mode, q, kv0, idx0, q_idx=qi)
+        topk = _np(idx.topk).copy()
+        assert np.array_equal(topk, _np(idx0.topk))
+        o2, l2 = P.sparse_attn_swa(q.view(wl.B, wl.H, wl.D), rows, idx.topk, cd, ed, n_win_d, wl.sm_scale)
+        assert torch.equal(out.view(wl.B, wl.H, wl.D), o2) and torch.equal(lse.view(wl.B, wl.H), l2)
+        gpu.append((_np(out), _np(lse), topk))
+    for b in range(wl.B):
+        ores, src = oracle_sequence(wl, b, np.arange(1))
+        kvd = O.dequant_kv_fp4(O.quantize_kv_fp4(src))
+        scores = None                      # the newest index layer's oracle scores (Reuse keeps them)
+        for layer, lay in enumerate(ores):
+            if lay["scores"] is not None:
+                scores = lay["scores"][0]
+            win = O.dequant_swa_fp8(*wins[layer])[b:b + 1]
+            ref, lref = O.sparse_attn_swa(lay["q"], kvd, lay["topk"], win, n_win[b:b + 1], wl.sm_scale)
+            what = f"window layer {layer} b={b}"
+            if compare_topk(gpu[layer][2][b], lay["topk"][0], lambda p, s=scores: s[p], what):
+                check_attn(gpu[layer][0][b], ref[0], gpu[layer][1][b], lref[0], what)
+            else:
+                o, l = P.sparse_attn_swa(q_device(wl, layer, "q").view(wl.B, wl.H, wl.D)[b:b + 1], rows[b:b + 1],
+                                         torch.from_numpy(lay["topk"].astype(np.int32)).cuda(),
+                                         torch.from_numpy(wins[layer][0][b:b + 1]).cuda(),
+                                         torch.from_numpy(wins[layer][1][b:b + 1]).cuda(),
+                                         torch.from_numpy(n_win[b:b + 1]).cuda(), wl.sm_scale)
+                check_attn(_np(o)[0], ref[0], _np(l)[0], lref[0], what + " (oracle indices)")

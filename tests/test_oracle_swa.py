@@ -86,3 +86,22 @@ def test_swa_attention_empty_union():
     q = np.ones((1, 16, 512))
     out, lse = O.sparse_attn_swa(q, np.zeros((4, 512)), np.full((1, 8), -1), np.zeros((1, 128, 512)), [0], 0.1)
     assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_layer_step_with_window_is_union_attention():
+    """O11 with a window attends over the layer's own selection joined with the window (O12c);
+    an empty window gives the plain layer."""
+    g = np.random.default_rng(21)
+    N, H, D, Wn = 200, 4, 512, 16
+    kv = O.dequant_kv_fp4(O.quantize_kv_fp4(g.standard_normal((N, D)).astype(np.float32)))
+    win = O.dequant_swa_fp8(*O.quantize_swa_fp8(g.standard_normal((Wn, D)).astype(np.float32)))[None]
+    q = g.standard_normal((1, H, D))
+    qi = g.standard_normal((1, 2, 64))
+    ki = g.standard_normal((N, 2, 64))
+    base = O.layer_step(O.FULL, q=q, kv_deq=kv, k_idx=ki, q_idx=qi, n_vis=[N], k=32)
+    with_w = O.layer_step(O.FULL, q=q, kv_deq=kv, k_idx=ki, q_idx=qi, n_vis=[N], k=32, win=win, n_win=[Wn])
+    assert np.array_equal(with_w["topk"], base["topk"])
+    o, l = O.sparse_attn_swa(q, kv, base["topk"], win, [Wn], 1.0 / np.sqrt(512.0))
+    assert np.array_equal(with_w["out"], o) and np.array_equal(with_w["lse"], l)
+    empty = O.layer_step(O.FULL, q=q, kv_deq=kv, k_idx=ki, q_idx=qi, n_vis=[N], k=32, win=win, n_win=[0])
+    assert np.allclose(empty["out"], base["out"], rtol=1e-6, atol=1e-6)
