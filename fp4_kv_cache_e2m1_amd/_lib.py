@@ -50,7 +50,7 @@ class Csa2Error(RuntimeError):
 class SharedKV(C.Structure):
     _fields_ = [("rows", C.c_void_p), ("k_idx", C.c_void_p), ("n_vis", C.c_void_p),
                 ("B", C.c_int32), ("n_max", C.c_int32), ("D", C.c_int32), ("Hk", C.c_int32),
-                ("Di", C.c_int32), ("valid", C.c_int32)]
+                ("Di", C.c_int32), ("valid", C.c_int32), ("k_mx", C.c_void_p)]
 
 
 class SharedIdx(C.Structure):
@@ -63,7 +63,8 @@ class LayerArgs(C.Structure):
                 ("Hi", C.c_int32), ("sm_scale", C.c_float), ("use_pool", C.c_int32),
                 ("pool_blocks", C.c_int32), ("block", C.c_int32), ("out", C.c_void_p),
                 ("lse", C.c_void_p), ("ws", C.c_void_p), ("ws_bytes", C.c_size_t),
-                ("swa_codes", C.c_void_p), ("swa_exp", C.c_void_p), ("swa_n", C.c_void_p), ("swa_W", C.c_int32)]
+                ("swa_codes", C.c_void_p), ("swa_exp", C.c_void_p), ("swa_n", C.c_void_p), ("swa_W", C.c_int32),
+                ("q_idx_mx", C.c_void_p)]
 
 
 _lib = None

@@ -256,20 +256,33 @@ def prefill_n_vis(p0: int, T: int, ratio: int, device) -> torch.Tensor:
 # ---------------------------------------------------------------------------------------------
 @dataclass
 class KVState:
-    """The cache of the most recent Full layer: FP4 rows and indexer keys (device tensors)."""
+    """The cache of the most recent Full layer: FP4 rows and indexer keys (device tensors).
+
+    The indexer keys are bf16 (k_idx), or FP4 (k_mx: MXFP4 rows [B, N, C/2 + C/32] of
+    C = Hk * Di channels, with k_idx None and mx_heads = (Hk, Di))."""
     rows: torch.Tensor                 # [B, N, 288] uint8
-    k_idx: torch.Tensor                # [B, N, Hk, Di] bf16
+    k_idx: Optional[torch.Tensor]      # [B, N, Hk, Di] bf16, or None with k_mx
     n_vis: Optional[torch.Tensor] = None  # [B*T] int32
+    k_mx: Optional[torch.Tensor] = None   # [B, N, C/2 + C/32] uint8
+    mx_heads: Tuple[int, int] = (0, 0)
     c: SharedKV = field(default_factory=SharedKV)
 
     def __post_init__(self):
         _need(self.rows, "rows", torch.uint8)
-        _need(self.k_idx, "k_idx", torch.bfloat16, self.rows.device)
         B, N, rb = self.rows.shape
-        _, N2, Hk, Di = self.k_idx.shape
-        if N2 != N:
-            raise ValueError("rows and k_idx disagree on N")
+        if self.k_mx is not None:
+            _need(self.k_mx, "k_mx", torch.uint8, self.rows.device)
+            Hk, Di = self.mx_heads
+            C = Hk * Di
+            if self.k_mx.shape != (B, N, mxfp4_row_bytes(C)):
+                raise ValueError("k_mx must be [B, N, C/2 + C/32] with C = Hk * Di")
+        else:
+            _need(self.k_idx, "k_idx", torch.bfloat16, self.rows.device)
+            _, N2, Hk, Di = self.k_idx.shape
+            if N2 != N:
+                raise ValueError("rows and k_idx disagree on N")
         self.c.rows, self.c.k_idx, self.c.n_vis = _ptr(self.rows), _ptr(self.k_idx), _ptr(self.n_vis)
+        self.c.k_mx = _ptr(self.k_mx)
         self.c.B, self.c.n_max, self.c.D, self.c.Hk, self.c.Di = B, N, (rb * 16) // 9, Hk, Di
         self.c.valid = 0
 
@@ -312,12 +325,14 @@ def layer_step(mode: int, q: torch.Tensor, kv: KVState, idx: IdxState, q_idx: Op
                sm_scale: Optional[float] = None, use_pool: bool = False, pool_blocks: int = 0, block: int = 8,
                with_lse: bool = True, ws: Optional[torch.Tensor] = None,
                out: Optional[torch.Tensor] = None,
-               window: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None
-               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+               window: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+               q_idx_mx: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """One CSA2 layer (FULL / REINDEX / REUSE) over caller-owned shared state; returns (out, lse).
 
     window: (swa_codes [B, W, D] uint8, swa_exp [B, W] int8, n_win [B] int32), decode only: the
-    layer's sliding window joined to the selected entries as one softmax."""
+    layer's sliding window joined to the selected entries as one softmax.
+    q_idx_mx: [B, T, C/2 + C/32] uint8 MXFP4 indexer query, for a KVState with FP4 keys (then
+    q_idx only gives Hi and may be None with Hi taken from the state)."""
     _need(q, "q", torch.bfloat16, kv.rows.device)
     dev = q.device
     B, T, H, D = q.shape
@@ -327,6 +342,11 @@ def layer_step(mode: int, q: torch.Tensor, kv: KVState, idx: IdxState, q_idx: Op
     if q_idx is not None:
         _need(q_idx, "q_idx", torch.bfloat16, dev)
         a.q_idx, a.Hi = _ptr(q_idx), q_idx.shape[2]
+    if q_idx_mx is not None:
+        _need(q_idx_mx, "q_idx_mx", torch.uint8, dev)
+        if q_idx_mx.shape[:2] != (B, T):
+            raise ValueError("q_idx_mx must be [B, T, C/2 + C/32]")
+        a.q_idx_mx, a.Hi = _ptr(q_idx_mx), kv.c.Hk
     a.sm_scale = float(sm_scale if sm_scale is not None else D ** -0.5)
     a.use_pool, a.pool_blocks, a.block = int(use_pool), pool_blocks, block
     if window is not None:

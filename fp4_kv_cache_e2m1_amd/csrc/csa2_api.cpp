@@ -258,7 +258,14 @@ csa2_status plan_layer(csa2_mode mode, const csa2_layer_args* a, const csa2_shar
   p->build_pool = mode == CSA2_FULL && a->use_pool;
   p->on_pool = mode == CSA2_REINDEX && a->use_pool && idx->pool_valid;
   if (p->score) {
-    if (!index_shape_ok(a->Hi, kv->Hk, kv->Di)) return CSA2_E_SHAPE;
+    if (kv->k_mx) {
+      // FP4 (MXFP4) indexer keys: flat scoring only, one key head per index head
+      if (a->use_pool) return CSA2_E_UNSUPPORTED;
+      const int32_t C = kv->Hk * kv->Di;
+      if (kv->Hk != a->Hi || kv->Hk <= 0 || kv->Di <= 0 || (C != 256 && C != 512)) return CSA2_E_SHAPE;
+    } else if (!index_shape_ok(a->Hi, kv->Hk, kv->Di)) {
+      return CSA2_E_SHAPE;
+    }
     p->ncols = p->on_pool ? idx->P : kv->n_max;
   }
   if (p->build_pool) {
@@ -321,7 +328,7 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_share
   if (mode != CSA2_FULL && !kv->valid) return CSA2_E_STATE;
   if (mode == CSA2_REUSE && !idx->topk_valid) return CSA2_E_STATE;
   if (!a->out || !idx->topk || !kv->rows || !a->q) return CSA2_E_ARG;
-  if (p.score && (!a->q_idx || !kv->k_idx)) return CSA2_E_ARG;
+  if (p.score && (kv->k_mx ? !a->q_idx_mx : (!a->q_idx || !kv->k_idx))) return CSA2_E_ARG;
   if (a->swa_codes && (!a->swa_exp || !a->swa_n)) return CSA2_E_ARG;
   if (p.total > 0 && (!a->ws || a->ws_bytes < p.total)) return CSA2_E_WORKSPACE;
 
@@ -346,9 +353,16 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_share
     float* scores_c = scores + r0 * p.ncols;
     csa2_status s2 = CSA2_OK;
     if (p.score) {
-      s2 = csa2_index_scores(a->q_idx + r0 * a->Hi * kv->Di, kv->k_idx + (int64_t)b0 * kv->n_max * kbytes_row, nb,
-                             T, a->Hi, kv->Hk, kv->Di, kv->n_max, n_vis_c, p.on_pool ? pool_c : nullptr,
-                             p.on_pool ? idx->P : 0, scores_c, bmax ? bmax + r0 * p.n_blocks : nullptr, 8, s_idx);
+      if (kv->k_mx) {
+        const int32_t C = kv->Hk * kv->Di;
+        const int64_t mrb = C / 2 + C / 32;                        // bytes per MXFP4 row
+        s2 = csa2_index_scores_mxfp4(a->q_idx_mx + r0 * mrb, kv->k_mx + (int64_t)b0 * kv->n_max * mrb, nb, T, C,
+                                     kv->n_max, n_vis_c, scores_c, s_idx);
+      } else {
+        s2 = csa2_index_scores(a->q_idx + r0 * a->Hi * kv->Di, kv->k_idx + (int64_t)b0 * kv->n_max * kbytes_row,
+                               nb, T, a->Hi, kv->Hk, kv->Di, kv->n_max, n_vis_c, p.on_pool ? pool_c : nullptr,
+                               p.on_pool ? idx->P : 0, scores_c, bmax ? bmax + r0 * p.n_blocks : nullptr, 8, s_idx);
+      }
       if (s2 != CSA2_OK) return s2;
       if (ev) {
         if (hipEventRecord(ev, as_stream(s_idx)) != hipSuccess) return CSA2_E_HIP;

@@ -254,6 +254,11 @@ typedef struct {
   const int32_t* n_vis;    /* [B*T] visible entries per query row, or NULL (= n_max) */
   int32_t B, n_max, D, Hk, Di;
   int32_t valid;           /* set by FULL */
+  /* FP4 indexer keys ([walkthrough] 一(五)4, OCP MXFP4): [B, n_max, C/2 + C/32] rows of
+   * C = Hk * Di channels (layout of csa2_index_scores_mxfp4), or NULL. When given, Full and
+   * flat Reindex layers score them against the layer's q_idx_mx instead of k_idx / q_idx
+   * (Hk == Hi, C in {256, 512}; the hierarchical pool is not supported with them). */
+  const uint8_t* k_mx;
 } csa2_shared_kv;
 
 typedef struct {
@@ -282,6 +287,7 @@ typedef struct {
   const int8_t* swa_exp;    /* [B, swa_W] row exponents in [-15, 7] */
   const int32_t* swa_n;     /* [B] window rows per sequence (device), clamped to [0, swa_W] */
   int32_t swa_W;            /* rows reserved per sequence, <= 128 */
+  const uint8_t* q_idx_mx;  /* [B*T, C/2 + C/32] MXFP4 indexer query, used with shared_kv.k_mx */
 } csa2_layer_args;
 
 csa2_status csa2_layer_workspace_size(csa2_mode mode, const csa2_layer_args* a,

@@ -198,3 +198,16 @@ def test_layer_step_window_rules(L):
     a2, kv2, idx2 = _layer(T=2)
     a2.swa_codes, a2.swa_exp, a2.swa_n, a2.swa_W = FAKE, FAKE, FAKE, 128
     assert L.csa2_layer_workspace_size(0, C.byref(a2), C.byref(kv2), C.byref(idx2), C.byref(n)) == E_UNSUP
+
+
+def test_layer_step_fp4_indexer_rules(L):
+    n = C.c_size_t(0)
+    a, kv, idx = _layer()
+    kv.k_mx = FAKE
+    assert L.csa2_layer_workspace_size(0, C.byref(a), C.byref(kv), C.byref(idx), C.byref(n)) == OK
+    assert L.csa2_layer_step(0, C.byref(a), C.byref(kv), C.byref(idx), None) == E_ARG   # no q_idx_mx
+    a.Hi = 4                                                        # one key head per index head
+    assert L.csa2_layer_workspace_size(0, C.byref(a), C.byref(kv), C.byref(idx), C.byref(n)) == E_SHAPE
+    a2, kv2, idx2 = _layer(pool_blocks=128, use_pool=1)
+    kv2.k_mx = FAKE
+    assert L.csa2_layer_workspace_size(0, C.byref(a2), C.byref(kv2), C.byref(idx2), C.byref(n)) == E_UNSUP

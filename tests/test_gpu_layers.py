@@ -293,3 +293,41 @@ def test_layer_stack_with_window():
                                          torch.from_numpy(wins[layer][1][b:b + 1]).cuda(),
                                          torch.from_numpy(n_win[b:b + 1]).cuda(), wl.sm_scale)
                 check_attn(_np(o)[0], ref[0], _np(l)[0], lref[0], what + " (oracle indices)")
+
+
+def test_layer_stack_fp4_indexer():
+    """Full -> Reindex -> Reuse with FP4 (MXFP4) indexer keys and queries: each index layer's
+    Top-K against the oracle's Top-K of the MXFP4 scores, attention against the oracle's on its
+    own selection."""
+    wl = SMALL["stack"]
+    C = wl.Hi * wl.Di
+    rows = kv_rows_device(wl)
+    k_rows = np.stack([O.quantize_mxfp4(W.bf16_bits_to_f32(W.k_idx(wl, b)).reshape(wl.N, C)) for b in range(wl.B)])
+    q_rows = [np.stack([O.quantize_mxfp4(W.bf16_bits_to_f32(W.q_idx(wl, b, layer)).reshape(wl.T, C))
+                        for b in range(wl.B)]) for layer in range(len(wl.modes))]
+    kv = P.KVState(rows, None, k_mx=torch.from_numpy(k_rows).cuda(), mx_heads=(wl.Hk, wl.Di))
+    idx = P.IdxState.empty(wl.B, wl.k, "cuda")
+    gpu = []
+    for layer, mode in enumerate(wl.modes):
+        q = q_device(wl, layer, "q")
+        qm = torch.from_numpy(q_rows[layer]).cuda() if mode != P.REUSE else None
+        out, lse = P.layer_step(mode, q, kv, idx, q_idx_mx=qm)
+        gpu.append((_np(out), _np(lse), _np(idx.topk).copy()))
+    assert kv.valid
+    for b in range(wl.B):
+        seq = W.sequence(wl, b)
+        kvd = O.dequant_kv_fp4(O.quantize_kv_fp4(seq["kv_src"]))
+        sel, scores = None, None
+        for layer, mode in enumerate(wl.modes):
+            if mode != W.REUSE:
+                scores = O.index_scores_mxfp4(q_rows[layer][b], k_rows[b], C, [wl.N])[0]
+                sel = O.topk(scores[None], wl.k)
+            q = f64(seq["q"][layer])
+            ref, lref = O.sparse_attn(q, kvd, sel, wl.sm_scale)
+            what = f"fp4 indexer layer {layer} b={b}"
+            if compare_topk(gpu[layer][2][b], sel[0], lambda p, s=scores: s[p], what):
+                check_attn(gpu[layer][0][b], ref, gpu[layer][1][b], lref, what)
+            else:
+                o, l = P.sparse_attn(q_device(wl, layer, "q")[b:b + 1], rows[b:b + 1],
+                                     torch.from_numpy(sel.astype(np.int32)[None]).cuda(), wl.sm_scale)
+                check_attn(_np(o)[0], ref, _np(l)[0], lref, what + " (oracle indices)")
