@@ -140,10 +140,11 @@ def cpu_baseline(wl, n_seq, min_seconds):
                       f"{dt:.1f} s"}
 
 
-def fp4_indexer_leg(wl, steps, dev, stream):
+def fp4_indexer_leg(wl, sets, steps, dev, stream):
     """csa2_index_scores_mxfp4 over the workload's B x N entries with their Hi x Di indexer
     channels stored as MXFP4 rows (seeded synthetic codes and scales), two alternating copies;
-    achieved bytes per launch against the HBM peak."""
+    achieved bytes per launch against the HBM peak. Then the whole Full layer step with those
+    keys (indexer, Top-K, attention over the same FP4 main-KV rows), timed the same way."""
     import torch
     import fp4_kv_cache_e2m1_amd as P
     from fp4_kv_cache_e2m1_amd import workloads as W
@@ -165,9 +166,38 @@ def fp4_indexer_leg(wl, steps, dev, stream):
     rb = C // 2 + C // 32
     nbytes = wl.B * wl.N * rb + wl.B * wl.T * rb
     gbs = nbytes / (us * 1e-6) / 1e9
+    # the Full layer step with FP4 indexer keys
+    ws = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    layer = []
+    for c in range(2):
+        s = sets[c % len(sets)]
+        kv = P.KVState(s["rows"], None, k_mx=keys[c], mx_heads=(wl.Hk, wl.Di))
+        idx = P.IdxState.empty(wl.B * wl.T, wl.k, dev)
+        o = torch.empty(wl.B, wl.T, wl.H, wl.D, dtype=torch.float32, device=dev)
+        layer.append((s["q"][0], kv, idx, o))
+
+    def full_step(i):
+        qm, kv, idx, o = layer[i % 2]
+        P.layer_step(P.FULL, qm, kv, idx, q_idx_mx=q, sm_scale=wl.sm_scale, with_lse=False, ws=ws, out=o)
+
+    for i in range(3):
+        full_step(i)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(steps):
+        full_step(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    step_us = a.elapsed_time(b) / steps * 1e3
+    row_b = wl.D // 2 + wl.D // 16
+    R = wl.B * wl.T
+    step_bytes = nbytes + R * wl.k * 4 * 2 + R * wl.k * row_b + R * wl.H * wl.D * 2 + R * wl.H * wl.D * 4
     return {"kernel": "index_mxfp4_kernel (MXFP4 indexer scores)", "bound": "hbm", "achieved": round(gbs, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": round(us, 2), "row_bytes": rb}
+            "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": round(us, 2), "row_bytes": rb,
+            "full_step_us": round(step_us, 2), "full_step_query_tokens_per_s": round(R / (step_us * 1e-6), 1),
+            "full_step_algorithmic_bytes": step_bytes,
+            "full_step_hbm_frac": round(step_bytes / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def window_leg(wl, sets, state, n_rows, steps, dev, stream):
@@ -376,7 +406,7 @@ def main():
         "roofline": roofline,
     }
     if args.fp4_indexer and wl.T == 1 and wl.Hk == wl.Hi and wl.Hi * wl.Di in (256, 512):
-        line["fp4_indexer"] = fp4_indexer_leg(wl, args.steps, dev, stream)
+        line["fp4_indexer"] = fp4_indexer_leg(wl, sets, args.steps, dev, stream)
     if args.window > 0 and wl.T == 1:
         line["window_attention"] = window_leg(wl, sets, state, args.window, args.steps, dev, stream)
     if not args.no_cpu_baseline and args.config == 2:
