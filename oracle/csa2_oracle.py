@@ -283,12 +283,20 @@ def dequant_mxfp4(rows: np.ndarray, channels: int) -> np.ndarray:
     return e2m1_decode(codes) * np.repeat(e8m0_decode(rows[:, channels // 2:]), MX_BLOCK, axis=1)
 
 
-def index_scores_mxfp4(q_rows: np.ndarray, k_rows: np.ndarray, channels: int, n_vis) -> np.ndarray:
-    """O13c. The indexer score (O6) of MXFP4 query rows [R, .] against MXFP4 key rows [N, .], each
-    row holding all Hi x Di channels of one query or one entry (one key head per index head, R-4):
-    s[r, n] = sum_c q[r, c] * k[n, c] over the dequantized values, fp64, rounded once to fp32."""
-    q = dequant_mxfp4(q_rows, channels)
+def index_scores_mxfp4(q_rows: np.ndarray, k_rows: np.ndarray, channels: int, n_vis,
+                       q_heads: int = 0) -> np.ndarray:
+    """O13c. The indexer score (O6) of MXFP4 query rows [R, .] against MXFP4 key rows [N, .].
+
+    q_heads = 0: each row holds all Hi x Di channels of one query or one entry (one key head per
+    index head, R-4): s[r, n] = sum_c q[r, c] * k[n, c]. q_heads = Hi: one shared key of
+    `channels` channels per entry, query rows of Hi x `channels` (head h = channels
+    h*channels .. ), s[r, n] = sum_h q[r, h] . k[n] (R-4, R-16). Over the dequantized values,
+    fp64, rounded once to fp32."""
     k = dequant_mxfp4(k_rows, channels)
+    if q_heads:
+        q = dequant_mxfp4(q_rows, q_heads * channels).reshape(-1, q_heads, channels)
+        return index_scores(q, k[:, None, :], n_vis)
+    q = dequant_mxfp4(q_rows, channels)
     return index_scores(q[:, None, :], k[:, None, :], n_vis)
 
 

@@ -138,3 +138,26 @@ def test_index_score_is_the_exact_dot_product(golden_dir):
                 continue
             exact = sum(val(q[r], c) * val(k[n], c) for c in range(C))
             assert got[r, n] == np.float32(float(exact)), (r, n)
+
+
+def test_index_score_shared_key_is_the_exact_sum_over_heads(golden_dir):
+    """One 128-channel key per entry, four query heads: the exact sum over heads of each head's
+    dot product with the key."""
+    e2m1 = _e2m1_golden(golden_dir)
+    g = np.random.default_rng(8)
+    Dk, Hq = 128, 4
+    q = O.quantize_mxfp4(g.standard_normal((2, Hq * Dk)).astype(np.float32))
+    k = O.quantize_mxfp4((g.standard_normal((7, Dk)) * 3).astype(np.float32))
+
+    def val(row, c, C):
+        nib = (row[c // 2] >> (4 * (c % 2))) & 0xF
+        return Fraction(e2m1[int(nib)]) * Fraction(2) ** (int(row[C // 2 + c // 32]) - 127)
+
+    got = O.index_scores_mxfp4(q, k, Dk, [7, 5], q_heads=Hq)
+    for r in range(2):
+        for n in range(7):
+            if n >= [7, 5][r]:
+                assert got[r, n] == -np.inf
+                continue
+            exact = sum(val(q[r], h * Dk + c, Hq * Dk) * val(k[n], c, Dk) for h in range(Hq) for c in range(Dk))
+            assert got[r, n] == np.float32(float(exact)), (r, n)
