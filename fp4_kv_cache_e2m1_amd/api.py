@@ -127,16 +127,21 @@ def mxfp4_row_bytes(channels: int) -> int:
 
 
 def index_scores_mxfp4(q_rows: torch.Tensor, k_rows: torch.Tensor, channels: int,
-                       n_vis: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
-    """Indexer scores over MXFP4 rows. q_rows [B, T, C/2 + C/32] uint8, k_rows [B, N, C/2 + C/32]
-    uint8 -> scores [B*T, N] fp32 (entries >= n_vis unwritten)."""
+                       n_vis: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                       q_heads: int = 0):
+    """Indexer scores over MXFP4 rows -> scores [B*T, N] fp32 (entries >= n_vis unwritten).
+
+    q_heads = 0: q_rows [B, T, C/2 + C/32] and k_rows [B, N, C/2 + C/32] hold C = `channels`
+    channels each (one key head per index head). q_heads = Hi: one shared key of `channels` = 128
+    channels per entry, q_rows [B, T, Hi*C/2 + Hi*C/32]."""
     _need(q_rows, "q_rows", torch.uint8)
     dev = q_rows.device
     _need(k_rows, "k_rows", torch.uint8, dev)
     B, T, RB = q_rows.shape
     B2, N, RB2 = k_rows.shape
-    if B2 != B or RB != mxfp4_row_bytes(channels) or RB2 != RB:
-        raise ValueError("q_rows / k_rows disagree with B or the row size of C channels")
+    Hi = q_heads if q_heads else 1
+    if B2 != B or RB2 != mxfp4_row_bytes(channels) or RB != mxfp4_row_bytes(Hi * channels):
+        raise ValueError("q_rows / k_rows disagree with B or the row sizes")
     if n_vis is not None:
         _need(n_vis, "n_vis", torch.int32, dev)
         if n_vis.numel() != B * T:
@@ -144,8 +149,8 @@ def index_scores_mxfp4(q_rows: torch.Tensor, k_rows: torch.Tensor, channels: int
     if out is None:
         out = torch.empty(B * T, N, dtype=torch.float32, device=dev)
     _need(out, "out", torch.float32, dev)
-    code = _lib.lib().csa2_index_scores_mxfp4(_ptr(q_rows), _ptr(k_rows), B, T, channels, N, _ptr(n_vis),
-                                              _ptr(out), _stream(dev))
+    code = _lib.lib().csa2_index_scores_mxfp4(_ptr(q_rows), _ptr(k_rows), B, T, Hi, 1, channels,
+                                              N, _ptr(n_vis), _ptr(out), _stream(dev))
     check("csa2_index_scores_mxfp4", code)
     return out
 
@@ -346,7 +351,8 @@ def layer_step(mode: int, q: torch.Tensor, kv: KVState, idx: IdxState, q_idx: Op
         _need(q_idx_mx, "q_idx_mx", torch.uint8, dev)
         if q_idx_mx.shape[:2] != (B, T):
             raise ValueError("q_idx_mx must be [B, T, C/2 + C/32]")
-        a.q_idx_mx, a.Hi = _ptr(q_idx_mx), kv.c.Hk
+        qc = q_idx_mx.shape[2] * 32 // 17                           # channels of a query row
+        a.q_idx_mx, a.Hi = _ptr(q_idx_mx), qc // kv.c.Di
     a.sm_scale = float(sm_scale if sm_scale is not None else D ** -0.5)
     a.use_pool, a.pool_blocks, a.block = int(use_pool), pool_blocks, block
     if window is not None:

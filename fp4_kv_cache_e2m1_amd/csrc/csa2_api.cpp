@@ -131,10 +131,17 @@ csa2_status csa2_index_scores(const uint16_t* q_idx, const uint16_t* k_idx, int3
                                         block_max, s));
 }
 
+static bool mxfp4_shape_ok(int32_t Hi, int32_t Hk, int32_t Di) {
+  if (Hi <= 0 || Hk <= 0 || Di <= 0) return false;
+  if (Hk == 1 && Di == 128) return Hi <= 64;                       // one shared 128-channel key
+  return Hk == Hi && (Hi * Di == 256 || Hi * Di == 512);
+}
+
 csa2_status csa2_index_scores_mxfp4(const uint8_t* q_rows, const uint8_t* k_rows, int32_t B, int32_t T,
-                                    int32_t C, int32_t n_max, const int32_t* n_vis, float* scores, void* stream) {
-  if (B < 0 || T < 0 || n_max < 0 || C < 0) return CSA2_E_ARG;
-  if (C != 256 && C != 512) return CSA2_E_SHAPE;
+                                    int32_t Hi, int32_t Hk, int32_t Di, int32_t n_max, const int32_t* n_vis,
+                                    float* scores, void* stream) {
+  if (B < 0 || T < 0 || n_max < 0) return CSA2_E_ARG;
+  if (!mxfp4_shape_ok(Hi, Hk, Di)) return CSA2_E_SHAPE;
   const int64_t rows = (int64_t)B * T;
   if (rows == 0 || n_max == 0) return CSA2_OK;
   if (!q_rows || !k_rows || !scores) return CSA2_E_ARG;
@@ -142,7 +149,7 @@ csa2_status csa2_index_scores_mxfp4(const uint8_t* q_rows, const uint8_t* k_rows
   if (reinterpret_cast<uintptr_t>(q_rows) % 8 || reinterpret_cast<uintptr_t>(k_rows) % 8 ||
       reinterpret_cast<uintptr_t>(scores) % 4)
     return CSA2_E_ARG;
-  return hip_status(launch_index_mxfp4(q_rows, k_rows, B, T, C, n_max, n_vis, scores, as_stream(stream)));
+  return hip_status(launch_index_mxfp4(q_rows, k_rows, B, T, Hi, Hk, Di, n_max, n_vis, scores, as_stream(stream)));
 }
 
 size_t csa2_topk_workspace_size(int64_t rows, int32_t n_cols, int32_t k) {
@@ -261,8 +268,7 @@ csa2_status plan_layer(csa2_mode mode, const csa2_layer_args* a, const csa2_shar
     if (kv->k_mx) {
       // FP4 (MXFP4) indexer keys: flat scoring only, one key head per index head
       if (a->use_pool) return CSA2_E_UNSUPPORTED;
-      const int32_t C = kv->Hk * kv->Di;
-      if (kv->Hk != a->Hi || kv->Hk <= 0 || kv->Di <= 0 || (C != 256 && C != 512)) return CSA2_E_SHAPE;
+      if (!mxfp4_shape_ok(a->Hi, kv->Hk, kv->Di)) return CSA2_E_SHAPE;
     } else if (!index_shape_ok(a->Hi, kv->Hk, kv->Di)) {
       return CSA2_E_SHAPE;
     }
@@ -354,10 +360,10 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_share
     csa2_status s2 = CSA2_OK;
     if (p.score) {
       if (kv->k_mx) {
-        const int32_t C = kv->Hk * kv->Di;
-        const int64_t mrb = C / 2 + C / 32;                        // bytes per MXFP4 row
-        s2 = csa2_index_scores_mxfp4(a->q_idx_mx + r0 * mrb, kv->k_mx + (int64_t)b0 * kv->n_max * mrb, nb, T, C,
-                                     kv->n_max, n_vis_c, scores_c, s_idx);
+        const int64_t kc = (int64_t)kv->Hk * kv->Di, qc = (int64_t)a->Hi * kv->Di;   // channels per row
+        const int64_t krb = kc / 2 + kc / 32, qrb = qc / 2 + qc / 32;                // bytes per MXFP4 row
+        s2 = csa2_index_scores_mxfp4(a->q_idx_mx + r0 * qrb, kv->k_mx + (int64_t)b0 * kv->n_max * krb, nb, T, a->Hi,
+                                     kv->Hk, kv->Di, kv->n_max, n_vis_c, scores_c, s_idx);
       } else {
         s2 = csa2_index_scores(a->q_idx + r0 * a->Hi * kv->Di, kv->k_idx + (int64_t)b0 * kv->n_max * kbytes_row,
                                nb, T, a->Hi, kv->Hk, kv->Di, kv->n_max, n_vis_c, p.on_pool ? pool_c : nullptr,

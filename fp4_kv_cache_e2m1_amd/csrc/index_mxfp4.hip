@@ -97,10 +97,106 @@ __global__ __launch_bounds__(kMxThreads) void index_mxfp4_kernel(const uint8_t* 
   }
 }
 
-hipError_t launch_index_mxfp4(const uint8_t* q, const uint8_t* k, int B, int T, int C, int n_max,
-                              const int32_t* n_vis, float* scores, hipStream_t s) {
+// One shared key of 128 channels per entry (68-byte rows, 4 lanes per row) and Hi query heads:
+// score = (sum_h q_h) . k. Lane j first sums the heads' dequantized values of its block j in
+// fp32 (once per workgroup), then each entry's block is 32 fp32 products with the key's E2M1
+// values, scaled by the key's exponent; the 4 block sums meet in a butterfly.
+__global__ __launch_bounds__(kMxThreads) void index_mxfp4_shared_kernel(const uint8_t* __restrict__ q,
+                                                                        const uint8_t* __restrict__ k, int T,
+                                                                        int Hi, int n_max,
+                                                                        const int32_t* __restrict__ n_vis,
+                                                                        int tile_rows, float* __restrict__ scores) {
+  constexpr int L = 4, RB = 68;                 // 128 channels: 64 code bytes + 4 scale bytes
+  constexpr int ROWS = kMxThreads / L;
+  const int r = blockIdx.x;
+  const int b = r / T;
+  const int tid = threadIdx.x;
+  const int j = tid % L;
+  const int grp = tid / L;
+  const int nv = n_vis ? min(n_vis[r], n_max) : n_max;
+  const int tile0 = blockIdx.y * tile_rows;
+  const int tile_end = min(tile0 + tile_rows, nv);
+  if (tile0 >= tile_end) return;
+
+  // block j of the query summed over its heads; the query row is Hi*64 code bytes (head h at
+  // 64 h) followed by Hi*4 scale bytes (head h at 4 h)
+  float qs[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) qs[i] = 0.0f;
+  {
+    const uint8_t* qp = q + (int64_t)r * Hi * RB;
+    for (int h = 0; h < Hi; ++h) {
+      const uint32_t* cw = reinterpret_cast<const uint32_t*>(qp + 64 * h + 16 * j);
+      const float sc = ldexpf(1.0f, (int)qp[Hi * 64 + 4 * h + j] - 127);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t word = cw[w];
+        f16x2_mx_t v[4];
+        mx_e2m1x8(word, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qs[8 * w + 2 * e] = fmaf((float)v[e][0], sc, qs[8 * w + 2 * e]);
+          qs[8 * w + 2 * e + 1] = fmaf((float)v[e][1], sc, qs[8 * w + 2 * e + 1]);
+        }
+      }
+    }
+  }
+  const uint8_t* kb = k + (int64_t)b * n_max * RB;
+  float* srow = scores + (int64_t)r * n_max;
+
+  for (int base = tile0; base < tile_end; base += ROWS * kMxInFlight) {
+    uint32_t cw[kMxInFlight][4];
+    int ek[kMxInFlight];
+#pragma unroll
+    for (int u = 0; u < kMxInFlight; ++u) {
+      const int n = base + u * ROWS + grp;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) cw[u][w] = 0u;
+      ek[u] = 127;
+      if (n < tile_end) {
+        const uint8_t* p = kb + (int64_t)n * RB;
+        const uint32_t* pw = reinterpret_cast<const uint32_t*>(p + 16 * j);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) cw[u][w] = pw[w];
+        ek[u] = p[64 + j];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kMxInFlight; ++u) {
+      float part = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        f16x2_mx_t v[4];
+        mx_e2m1x8(cw[u][w], v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          part = fmaf(qs[8 * w + 2 * e], (float)v[e][0], part);
+          part = fmaf(qs[8 * w + 2 * e + 1], (float)v[e][1], part);
+        }
+      }
+      float v = ldexpf(part, ek[u] - 127);
+      v += shfl_xor_f(v, 2);
+      v += shfl_xor_f(v, 1);
+      const int n = base + u * ROWS + grp;
+      if (j == 0 && n < tile_end) srow[n] = v;
+    }
+  }
+}
+
+hipError_t launch_index_mxfp4(const uint8_t* q, const uint8_t* k, int B, int T, int Hi, int Hk, int Di,
+                              int n_max, const int32_t* n_vis, float* scores, hipStream_t s) {
   const int64_t rows = (int64_t)B * T;
   if (rows == 0 || n_max == 0) return hipSuccess;
+  if (Hk == 1 && Di == 128) {                   // one shared key per entry
+    const int step = (kMxThreads / 4) * kMxInFlight;
+    int tile = step;
+    while (tile < 8192 && rows * ((n_max + 2 * tile - 1) / (2 * tile)) >= 4096) tile *= 2;
+    dim3 grid((unsigned)rows, (unsigned)((n_max + tile - 1) / tile));
+    hipLaunchKernelGGL(index_mxfp4_shared_kernel, grid, dim3(kMxThreads), 0, s, q, k, T, Hi, n_max, n_vis, tile,
+                       scores);
+    return hipGetLastError();
+  }
+  const int C = Hi * Di;
   // tiles of rows per workgroup: about 4096 workgroups or more (16 per CU; measured best against
   // 512 .. 2048 at 32 x 16384 entries), each tile at least one step of rows in flight
   const int step = (kMxThreads / (C / 32)) * kMxInFlight;

@@ -119,21 +119,25 @@ csa2_status csa2_index_scores(const uint16_t* q_idx, const uint16_t* k_idx, int3
  * elements, one E8M0 power-of-two scale per 32 channels); 一(四): the indexer scores every
  * main-KV entry.
  *
- * A row holds the C = Hi * Di channels of one query row or one entry (one key head per index
- * head): bytes 0 .. C/2-1 are E2M1 codes (channel 2i in the low nibble of byte i), bytes
- * C/2 .. C/2 + C/32 - 1 the E8M0 scale codes (value 2^(code - 127)) of channels 32j .. 32j+31.
- * score[r, n] = sum_c q[r, c] * k[b(r), n, c] over the dequantized values, r = b*T + t. Each
- * 32-channel block's sum is exact; the blocks' scaled sums are added in fp32.
+ * An MXFP4 row of C channels is C/2 code bytes (channel 2i in the low nibble of byte i)
+ * followed by C/32 E8M0 scale codes (value 2^(code - 127)) of channels 32j .. 32j+31.
+ * Key rows hold an entry's Hk * Di channels, query rows a query's Hi * Di channels (head h at
+ * channels h*Di ..). score[r, n] = sum_h q[r, h] . k[b(r), n, h'] over the dequantized values,
+ * h' = h (Hk == Hi) or 0 (Hk == 1, one shared key), r = b*T + t. With Hk == Hi each 32-channel
+ * block's sum is exact and the blocks' scaled sums are added in fp32; with a shared key the
+ * heads are summed in fp32 first.
  *
- * q_rows  [B*T, C/2 + C/32] bytes, k_rows [B, n_max, C/2 + C/32] bytes (8-byte aligned bases).
+ * q_rows  [B*T, Hi*Di/2 + Hi*Di/32] bytes, k_rows [B, n_max, Hk*Di/2 + Hk*Di/32] bytes (8-byte
+ *         aligned bases).
  * n_vis   [B*T] int32 visible entries per query row (device), or NULL for all n_max; entries
  *         n >= n_vis[r] are not scored and their slots are left unwritten.
  * scores  [B*T, n_max] fp32.
- * Requires C in {256, 512} (CSA2_E_SHAPE otherwise) and finite scales (code 255 is NaN).
+ * Requires Hk == Hi with Hi * Di in {256, 512}, or Hk == 1, Di == 128 and Hi <= 64
+ * (CSA2_E_SHAPE otherwise); finite scales (code 255 is NaN).
  * ------------------------------------------------------------------------------------------ */
 csa2_status csa2_index_scores_mxfp4(const uint8_t* q_rows, const uint8_t* k_rows, int32_t B,
-                                    int32_t T, int32_t C, int32_t n_max, const int32_t* n_vis,
-                                    float* scores, void* stream);
+                                    int32_t T, int32_t Hi, int32_t Hk, int32_t Di, int32_t n_max,
+                                    const int32_t* n_vis, float* scores, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * csa2_topk - Top-K selection per row.
@@ -257,7 +261,7 @@ typedef struct {
   /* FP4 indexer keys ([walkthrough] 一(五)4, OCP MXFP4): [B, n_max, C/2 + C/32] rows of
    * C = Hk * Di channels (layout of csa2_index_scores_mxfp4), or NULL. When given, Full and
    * flat Reindex layers score them against the layer's q_idx_mx instead of k_idx / q_idx
-   * (Hk == Hi, C in {256, 512}; the hierarchical pool is not supported with them). */
+   * (shapes as csa2_index_scores_mxfp4; the hierarchical pool is not supported with them). */
   const uint8_t* k_mx;
 } csa2_shared_kv;
 
@@ -287,7 +291,7 @@ typedef struct {
   const int8_t* swa_exp;    /* [B, swa_W] row exponents in [-15, 7] */
   const int32_t* swa_n;     /* [B] window rows per sequence (device), clamped to [0, swa_W] */
   int32_t swa_W;            /* rows reserved per sequence, <= 128 */
-  const uint8_t* q_idx_mx;  /* [B*T, C/2 + C/32] MXFP4 indexer query, used with shared_kv.k_mx */
+  const uint8_t* q_idx_mx;  /* [B*T, Hi*Di/2 + Hi*Di/32] MXFP4 indexer query, with shared_kv.k_mx */
 } csa2_layer_args;
 
 csa2_status csa2_layer_workspace_size(csa2_mode mode, const csa2_layer_args* a,

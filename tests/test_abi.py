@@ -107,14 +107,17 @@ def test_sparse_attn_validation(L):
 
 def test_index_scores_mxfp4_validation(L):
     f = L.csa2_index_scores_mxfp4
-    # q_rows, k_rows, B, T, C, n_max, n_vis, scores, stream
-    assert f(FAKE, FAKE, 1, 1, 128, 10, None, FAKE, None) == E_SHAPE
-    assert f(FAKE, FAKE, 1, 1, 1024, 10, None, FAKE, None) == E_SHAPE
-    assert f(FAKE, FAKE, -1, 1, 512, 10, None, FAKE, None) == E_ARG
-    assert f(None, FAKE, 1, 1, 512, 10, None, FAKE, None) == E_ARG
-    assert f(FAKE + 4, FAKE, 1, 1, 512, 10, None, FAKE, None) == E_ARG       # misaligned rows
-    assert f(None, None, 0, 1, 512, 10, None, None, None) == 0                # nothing to do
-    assert f(None, None, 1, 1, 512, 0, None, None, None) == 0
+    # q_rows, k_rows, B, T, Hi, Hk, Di, n_max, n_vis, scores, stream
+    assert f(FAKE, FAKE, 1, 1, 2, 2, 64, 10, None, FAKE, None) == E_SHAPE      # 128 channels per head pair
+    assert f(FAKE, FAKE, 1, 1, 8, 8, 128, 10, None, FAKE, None) == E_SHAPE     # 1024 channels
+    assert f(FAKE, FAKE, 1, 1, 8, 4, 64, 10, None, FAKE, None) == E_SHAPE      # Hk neither Hi nor 1
+    assert f(FAKE, FAKE, 1, 1, 65, 1, 128, 10, None, FAKE, None) == E_SHAPE    # too many query heads
+    assert f(FAKE, FAKE, 1, 1, 8, 1, 64, 10, None, FAKE, None) == E_SHAPE      # shared keys are 128 wide
+    assert f(FAKE, FAKE, -1, 1, 8, 8, 64, 10, None, FAKE, None) == E_ARG
+    assert f(None, FAKE, 1, 1, 8, 8, 64, 10, None, FAKE, None) == E_ARG
+    assert f(FAKE + 4, FAKE, 1, 1, 8, 8, 64, 10, None, FAKE, None) == E_ARG    # misaligned rows
+    assert f(None, None, 0, 1, 8, 8, 64, 10, None, None, None) == 0            # nothing to do
+    assert f(None, None, 1, 1, 32, 1, 128, 0, None, None, None) == 0
 
 
 def test_sparse_attn_swa_validation(L):

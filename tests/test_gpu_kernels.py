@@ -426,6 +426,31 @@ def test_index_scores_mxfp4(B, T, N, C, spread):
             assert np.all(s[r][~mask] == 7.0)
 
 
+@pytest.mark.parametrize("B,T,N,Hi", [(2, 1, 3001, 32), (3, 2, 500, 1), (1, 1, 70000, 32), (4, 1, 1, 16)])
+def test_index_scores_mxfp4_shared_key(B, T, N, Hi):
+    """FP4 indexer with one shared 128-channel key per entry and Hi query heads (the paper-scale
+    indexer shape) against the oracle: ragged tiles, several query rows with n_vis cuts, long
+    rows, one entry."""
+    g = np.random.default_rng(N + Hi)
+    q_rows = O.quantize_mxfp4(g.standard_normal((B * T, Hi * 128)).astype(np.float32)).reshape(B, T, -1)
+    k_rows = O.quantize_mxfp4(g.standard_normal((B * N, 128)).astype(np.float32)).reshape(B, N, -1)
+    n_vis = np.array([max(1, N - 13 * r) for r in range(B * T)], np.int32)
+    out = torch.full((B * T, N), 7.0, dtype=torch.float32).cuda()
+    s = _sync_np(P.index_scores_mxfp4(torch.from_numpy(q_rows).cuda(), torch.from_numpy(k_rows).cuda(), 128,
+                                      n_vis=torch.from_numpy(n_vis).cuda(), out=out, q_heads=Hi))
+    for b in range(B):
+        kd = O.dequant_mxfp4(k_rows[b], 128)
+        for t in range(T):
+            r = b * T + t
+            qr = q_rows.reshape(B * T, -1)[r:r + 1]
+            ref = O.index_scores_mxfp4(qr, k_rows[b], 128, [n_vis[r]], q_heads=Hi)[0]
+            qd = O.dequant_mxfp4(qr, Hi * 128).reshape(Hi, 128)
+            abs_dot = np.abs(qd).sum(axis=0) @ np.abs(kd).T
+            mask = np.arange(N) < n_vis[r]
+            check_scores(s[r], ref, abs_dot, mask, f"mxfp4 shared r={r}")
+            assert np.all(s[r][~mask] == 7.0)
+
+
 def test_index_scores_mxfp4_exact_blocks():
     """Keys equal to the query on one 32-channel block and zero elsewhere: every score is that
     block's exact sum of squares times its scale squared (one exact block, no rounding)."""

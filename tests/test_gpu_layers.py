@@ -295,15 +295,18 @@ def test_layer_stack_with_window():
                 check_attn(_np(o)[0], ref[0], _np(l)[0], lref[0], what + " (oracle indices)")
 
 
-def test_layer_stack_fp4_indexer():
-    """Full -> Reindex -> Reuse with FP4 (MXFP4) indexer keys and queries: each index layer's
-    Top-K against the oracle's Top-K of the MXFP4 scores, attention against the oracle's on its
-    own selection."""
-    wl = SMALL["stack"]
-    C = wl.Hi * wl.Di
+@pytest.mark.parametrize("name", ["stack", "decoder20_flat"])
+def test_layer_stack_fp4_indexer(name):
+    """Layer stacks with FP4 (MXFP4) indexer keys and queries: Full -> Reindex -> Reuse with one
+    key head per index head (8 x 64), and the 20-layer schedule with one shared 128-channel key
+    and 32 query heads (flat Reindex). Each index layer's Top-K against the oracle's Top-K of the
+    MXFP4 scores, attention against the oracle's on its own selection."""
+    wl = SMALL["stack"] if name == "stack" else W.CONFIGS[6].scaled(B=2, N=3000, k=128, pool_blocks=0)
+    shared = wl.Hk == 1
+    kc, qc = wl.Hk * wl.Di, wl.Hi * wl.Di
     rows = kv_rows_device(wl)
-    k_rows = np.stack([O.quantize_mxfp4(W.bf16_bits_to_f32(W.k_idx(wl, b)).reshape(wl.N, C)) for b in range(wl.B)])
-    q_rows = [np.stack([O.quantize_mxfp4(W.bf16_bits_to_f32(W.q_idx(wl, b, layer)).reshape(wl.T, C))
+    k_rows = np.stack([O.quantize_mxfp4(W.bf16_bits_to_f32(W.k_idx(wl, b)).reshape(wl.N, kc)) for b in range(wl.B)])
+    q_rows = [np.stack([O.quantize_mxfp4(W.bf16_bits_to_f32(W.q_idx(wl, b, layer)).reshape(wl.T, qc))
                         for b in range(wl.B)]) for layer in range(len(wl.modes))]
     kv = P.KVState(rows, None, k_mx=torch.from_numpy(k_rows).cuda(), mx_heads=(wl.Hk, wl.Di))
     idx = P.IdxState.empty(wl.B, wl.k, "cuda")
@@ -320,11 +323,14 @@ def test_layer_stack_fp4_indexer():
         sel, scores = None, None
         for layer, mode in enumerate(wl.modes):
             if mode != W.REUSE:
-                scores = O.index_scores_mxfp4(q_rows[layer][b], k_rows[b], C, [wl.N])[0]
+                if shared:
+                    scores = O.index_scores_mxfp4(q_rows[layer][b], k_rows[b], wl.Di, [wl.N], q_heads=wl.Hi)[0]
+                else:
+                    scores = O.index_scores_mxfp4(q_rows[layer][b], k_rows[b], kc, [wl.N])[0]
                 sel = O.topk(scores[None], wl.k)
             q = f64(seq["q"][layer])
             ref, lref = O.sparse_attn(q, kvd, sel, wl.sm_scale)
-            what = f"fp4 indexer layer {layer} b={b}"
+            what = f"fp4 indexer {name} layer {layer} b={b}"
             if compare_topk(gpu[layer][2][b], sel[0], lambda p, s=scores: s[p], what):
                 check_attn(gpu[layer][0][b], ref, gpu[layer][1][b], lref, what)
             else:
