@@ -148,23 +148,25 @@ def fp4_indexer_leg(wl, sets, steps, dev, stream):
     import torch
     import fp4_kv_cache_e2m1_amd as P
     from fp4_kv_cache_e2m1_amd import workloads as W
-    C = wl.Hi * wl.Di
-    keys = [torch.from_numpy(np.stack([W.mxfp4_rows(wl, b, wl.N, C, copy=c) for b in range(wl.B)])).to(dev)
+    kc, qc = wl.Hk * wl.Di, wl.Hi * wl.Di          # channels of a key row and of a query row
+    shared = wl.Hk == 1 and wl.Di == 128
+    keys = [torch.from_numpy(np.stack([W.mxfp4_rows(wl, b, wl.N, kc, copy=c) for b in range(wl.B)])).to(dev)
             for c in range(2)]
-    q = torch.from_numpy(np.stack([W.mxfp4_rows(wl, b, wl.T, C, copy=2) for b in range(wl.B)])).to(dev)
+    q = torch.from_numpy(np.stack([W.mxfp4_rows(wl, b, wl.T, qc, copy=2) for b in range(wl.B)])).to(dev)
+    C, qh = (wl.Di, wl.Hi) if shared else (kc, 0)
     out = torch.empty(wl.B * wl.T, wl.N, dtype=torch.float32, device=dev)
     for i in range(3):
-        P.index_scores_mxfp4(q, keys[i % 2], C, out=out)
+        P.index_scores_mxfp4(q, keys[i % 2], C, out=out, q_heads=qh)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
     for i in range(steps):
-        P.index_scores_mxfp4(q, keys[i % 2], C, out=out)
+        P.index_scores_mxfp4(q, keys[i % 2], C, out=out, q_heads=qh)
     b.record(stream)
     torch.cuda.synchronize()
     us = a.elapsed_time(b) / steps * 1e3
-    rb = C // 2 + C // 32
-    nbytes = wl.B * wl.N * rb + wl.B * wl.T * rb
+    rb, qrb = kc // 2 + kc // 32, qc // 2 + qc // 32
+    nbytes = wl.B * wl.N * rb + wl.B * wl.T * qrb
     gbs = nbytes / (us * 1e-6) / 1e9
     # the Full layer step with FP4 indexer keys
     ws = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -405,7 +407,8 @@ def main():
         "step_algorithmic_bytes": step_bytes,
         "roofline": roofline,
     }
-    if args.fp4_indexer and wl.T == 1 and wl.Hk == wl.Hi and wl.Hi * wl.Di in (256, 512):
+    fp4_shape = (wl.Hk == wl.Hi and wl.Hi * wl.Di in (256, 512)) or (wl.Hk == 1 and wl.Di == 128)
+    if args.fp4_indexer and wl.T == 1 and fp4_shape:
         line["fp4_indexer"] = fp4_indexer_leg(wl, sets, args.steps, dev, stream)
     if args.window > 0 and wl.T == 1:
         line["window_attention"] = window_leg(wl, sets, state, args.window, args.steps, dev, stream)

@@ -16,6 +16,7 @@
 namespace csa2 {
 
 typedef _Float16 f16x2_mx_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_mx_t __attribute__((ext_vector_type(2)));
 
 constexpr int kMxThreads = 256;
 constexpr int kMxInFlight = 8;          // row steps whose loads a lane issues before using them
@@ -98,9 +99,10 @@ __global__ __launch_bounds__(kMxThreads) void index_mxfp4_kernel(const uint8_t* 
 }
 
 // One shared key of 128 channels per entry (68-byte rows, 4 lanes per row) and Hi query heads:
-// score = (sum_h q_h) . k. Lane j first sums the heads' dequantized values of its block j in
-// fp32 (once per workgroup), then each entry's block is 32 fp32 products with the key's E2M1
-// values, scaled by the key's exponent; the 4 block sums meet in a butterfly.
+// score = (sum_h q_h) . k. The workgroup first sums the heads' dequantized query values in fp32,
+// then each entry's 32-channel block j (lane j) is 32 fp32 products with the key's E2M1 values,
+// scaled by the key's exponent; the 4 block sums meet in a butterfly.
+constexpr int kMaxSharedHeads = 64;      // query heads of the shared-key form
 __global__ __launch_bounds__(kMxThreads) void index_mxfp4_shared_kernel(const uint8_t* __restrict__ q,
                                                                         const uint8_t* __restrict__ k, int T,
                                                                         int Hi, int n_max,
@@ -118,29 +120,35 @@ __global__ __launch_bounds__(kMxThreads) void index_mxfp4_shared_kernel(const ui
   const int tile_end = min(tile0 + tile_rows, nv);
   if (tile0 >= tile_end) return;
 
-  // block j of the query summed over its heads; the query row is Hi*64 code bytes (head h at
-  // 64 h) followed by Hi*4 scale bytes (head h at 4 h)
+  // The query summed over its heads, (sum_h q_h)[c] for the 128 channels. The query row is
+  // Hi*64 code bytes (head h at 64 h) followed by Hi*4 scale bytes (head h at 4 h); it is staged
+  // in LDS with one load per thread (at most 64 x 68 bytes), then thread t sums channel t % 128
+  // over every other head and the two halves meet in LDS, so each workgroup spends a few hundred
+  // instructions per thread on it instead of every lane summing all heads of its block.
+  __shared__ uint32_t qsm[kMaxSharedHeads * RB / 4];
+  __shared__ float qsum[2][128];
+  {
+    const uint32_t* qw = reinterpret_cast<const uint32_t*>(q + (int64_t)r * Hi * RB);
+    for (int i = tid; i < Hi * (RB / 4); i += kMxThreads) qsm[i] = qw[i];
+  }
+  __syncthreads();
+  {
+    const uint8_t* qp = reinterpret_cast<const uint8_t*>(qsm);
+    const int c = tid & 127, half = tid >> 7;
+    float acc = 0.0f;
+    for (int h = half; h < Hi; h += 2) {
+      const uint32_t nib = (qp[64 * h + (c >> 1)] >> (4 * (c & 1))) & 0xFu;
+      const uint32_t e = (nib >> 1) & 3u, m = nib & 1u;
+      const float mag = e ? ldexpf(1.0f + 0.5f * (float)m, (int)e - 1) : 0.5f * (float)m;   // E2M1
+      const float sc = ldexpf(1.0f, (int)qp[Hi * 64 + 4 * h + (c >> 5)] - 127);
+      acc = fmaf((nib & 8u) ? -mag : mag, sc, acc);
+    }
+    qsum[half][c] = acc;
+  }
+  __syncthreads();
   float qs[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) qs[i] = 0.0f;
-  {
-    const uint8_t* qp = q + (int64_t)r * Hi * RB;
-    for (int h = 0; h < Hi; ++h) {
-      const uint32_t* cw = reinterpret_cast<const uint32_t*>(qp + 64 * h + 16 * j);
-      const float sc = ldexpf(1.0f, (int)qp[Hi * 64 + 4 * h + j] - 127);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t word = cw[w];
-        f16x2_mx_t v[4];
-        mx_e2m1x8(word, v);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          qs[8 * w + 2 * e] = fmaf((float)v[e][0], sc, qs[8 * w + 2 * e]);
-          qs[8 * w + 2 * e + 1] = fmaf((float)v[e][1], sc, qs[8 * w + 2 * e + 1]);
-        }
-      }
-    }
-  }
+  for (int i = 0; i < 32; ++i) qs[i] = qsum[0][32 * j + i] + qsum[1][32 * j + i];
   const uint8_t* kb = k + (int64_t)b * n_max * RB;
   float* srow = scores + (int64_t)r * n_max;
 
@@ -166,12 +174,14 @@ __global__ __launch_bounds__(kMxThreads) void index_mxfp4_shared_kernel(const ui
       float part = 0.0f;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        f16x2_mx_t v[4];
-        mx_e2m1x8(cw[u][w], v);
+        const f32x2_mx_t v[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[u][w], 1.0f, 0),
+                                 __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[u][w], 1.0f, 1),
+                                 __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[u][w], 1.0f, 2),
+                                 __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[u][w], 1.0f, 3)};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          part = fmaf(qs[8 * w + 2 * e], (float)v[e][0], part);
-          part = fmaf(qs[8 * w + 2 * e + 1], (float)v[e][1], part);
+          part = fmaf(qs[8 * w + 2 * e], v[e][0], part);
+          part = fmaf(qs[8 * w + 2 * e + 1], v[e][1], part);
         }
       }
       float v = ldexpf(part, ek[u] - 127);
@@ -188,9 +198,10 @@ hipError_t launch_index_mxfp4(const uint8_t* q, const uint8_t* k, int B, int T, 
   const int64_t rows = (int64_t)B * T;
   if (rows == 0 || n_max == 0) return hipSuccess;
   if (Hk == 1 && Di == 128) {                   // one shared key per entry
+    // larger tiles than the per-head form: each workgroup first sums the query heads
     const int step = (kMxThreads / 4) * kMxInFlight;
     int tile = step;
-    while (tile < 8192 && rows * ((n_max + 2 * tile - 1) / (2 * tile)) >= 4096) tile *= 2;
+    while (tile < 8192 && rows * ((n_max + 2 * tile - 1) / (2 * tile)) >= 1024) tile *= 2;
     dim3 grid((unsigned)rows, (unsigned)((n_max + tile - 1) / tile));
     hipLaunchKernelGGL(index_mxfp4_shared_kernel, grid, dim3(kMxThreads), 0, s, q, k, T, Hi, n_max, n_vis, tile,
                        scores);
