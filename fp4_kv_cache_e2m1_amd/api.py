@@ -128,12 +128,13 @@ def mxfp4_row_bytes(channels: int) -> int:
 
 def index_scores_mxfp4(q_rows: torch.Tensor, k_rows: torch.Tensor, channels: int,
                        n_vis: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                       q_heads: int = 0):
+                       q_heads: int = 0, cand: Optional[torch.Tensor] = None, block_max: bool = False):
     """Indexer scores over MXFP4 rows -> scores [B*T, N] fp32 (entries >= n_vis unwritten).
 
     q_heads = 0: q_rows [B, T, C/2 + C/32] and k_rows [B, N, C/2 + C/32] hold C = `channels`
     channels each (one key head per index head). q_heads = Hi: one shared key of `channels` = 128
-    channels per entry, q_rows [B, T, Hi*C/2 + Hi*C/32]."""
+    channels per entry, q_rows [B, T, Hi*C/2 + Hi*C/32]. With the shared key, cand [B*T, P] int32
+    scores the pool (-> [B*T, P]) and block_max=True also returns the 8-entry block maxima."""
     _need(q_rows, "q_rows", torch.uint8)
     dev = q_rows.device
     _need(k_rows, "k_rows", torch.uint8, dev)
@@ -146,13 +147,20 @@ def index_scores_mxfp4(q_rows: torch.Tensor, k_rows: torch.Tensor, channels: int
         _need(n_vis, "n_vis", torch.int32, dev)
         if n_vis.numel() != B * T:
             raise ValueError("n_vis must have B*T entries")
+    P = 0
+    if cand is not None:
+        _need(cand, "cand", torch.int32, dev)
+        P = cand.shape[-1]
+        if cand.numel() != B * T * P:
+            raise ValueError("cand must be [B*T, P]")
     if out is None:
-        out = torch.empty(B * T, N, dtype=torch.float32, device=dev)
+        out = torch.empty(B * T, P if cand is not None else N, dtype=torch.float32, device=dev)
     _need(out, "out", torch.float32, dev)
+    bm = torch.empty(B * T, (N + 7) // 8, dtype=torch.float32, device=dev) if block_max else None
     code = _lib.lib().csa2_index_scores_mxfp4(_ptr(q_rows), _ptr(k_rows), B, T, Hi, 1, channels,
-                                              N, _ptr(n_vis), _ptr(out), _stream(dev))
+                                              N, _ptr(n_vis), _ptr(cand), P, _ptr(out), _ptr(bm), 8, _stream(dev))
     check("csa2_index_scores_mxfp4", code)
-    return out
+    return (out, bm) if block_max else out
 
 
 def topk(scores: torch.Tensor, k: int, n_valid: Optional[torch.Tensor] = None,

@@ -139,17 +139,23 @@ static bool mxfp4_shape_ok(int32_t Hi, int32_t Hk, int32_t Di) {
 
 csa2_status csa2_index_scores_mxfp4(const uint8_t* q_rows, const uint8_t* k_rows, int32_t B, int32_t T,
                                     int32_t Hi, int32_t Hk, int32_t Di, int32_t n_max, const int32_t* n_vis,
-                                    float* scores, void* stream) {
-  if (B < 0 || T < 0 || n_max < 0) return CSA2_E_ARG;
+                                    const int32_t* cand, int32_t P, float* scores, float* block_max,
+                                    int32_t block, void* stream) {
+  if (B < 0 || T < 0 || n_max < 0 || (cand && P < 0)) return CSA2_E_ARG;
   if (!mxfp4_shape_ok(Hi, Hk, Di)) return CSA2_E_SHAPE;
+  const bool shared = Hk == 1 && Di == 128;
+  if ((cand || block_max) && !shared) return CSA2_E_UNSUPPORTED;   // pool modes: shared-key form only
+  if (block_max && (cand || block != 8)) return CSA2_E_UNSUPPORTED;
   const int64_t rows = (int64_t)B * T;
-  if (rows == 0 || n_max == 0) return CSA2_OK;
+  const int32_t ncols = cand ? P : n_max;
+  if (rows == 0 || ncols == 0) return CSA2_OK;
   if (!q_rows || !k_rows || !scores) return CSA2_E_ARG;
-  if (rows > INT32_MAX || n_max > kMaxCols) return CSA2_E_SHAPE;
+  if (rows > INT32_MAX || ncols > kMaxCols || n_max > kMaxCols) return CSA2_E_SHAPE;
   if (reinterpret_cast<uintptr_t>(q_rows) % 8 || reinterpret_cast<uintptr_t>(k_rows) % 8 ||
       reinterpret_cast<uintptr_t>(scores) % 4)
     return CSA2_E_ARG;
-  return hip_status(launch_index_mxfp4(q_rows, k_rows, B, T, Hi, Hk, Di, n_max, n_vis, scores, as_stream(stream)));
+  return hip_status(launch_index_mxfp4(q_rows, k_rows, B, T, Hi, Hk, Di, n_max, n_vis, cand, P, scores, block_max,
+                                       as_stream(stream)));
 }
 
 size_t csa2_topk_workspace_size(int64_t rows, int32_t n_cols, int32_t k) {
@@ -266,9 +272,9 @@ csa2_status plan_layer(csa2_mode mode, const csa2_layer_args* a, const csa2_shar
   p->on_pool = mode == CSA2_REINDEX && a->use_pool && idx->pool_valid;
   if (p->score) {
     if (kv->k_mx) {
-      // FP4 (MXFP4) indexer keys: flat scoring only, one key head per index head
-      if (a->use_pool) return CSA2_E_UNSUPPORTED;
+      // FP4 (MXFP4) indexer keys; the hierarchical pool needs the shared-key form
       if (!mxfp4_shape_ok(a->Hi, kv->Hk, kv->Di)) return CSA2_E_SHAPE;
+      if (a->use_pool && !(kv->Hk == 1 && kv->Di == 128)) return CSA2_E_UNSUPPORTED;
     } else if (!index_shape_ok(a->Hi, kv->Hk, kv->Di)) {
       return CSA2_E_SHAPE;
     }
@@ -363,7 +369,9 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_share
         const int64_t kc = (int64_t)kv->Hk * kv->Di, qc = (int64_t)a->Hi * kv->Di;   // channels per row
         const int64_t krb = kc / 2 + kc / 32, qrb = qc / 2 + qc / 32;                // bytes per MXFP4 row
         s2 = csa2_index_scores_mxfp4(a->q_idx_mx + r0 * qrb, kv->k_mx + (int64_t)b0 * kv->n_max * krb, nb, T, a->Hi,
-                                     kv->Hk, kv->Di, kv->n_max, n_vis_c, scores_c, s_idx);
+                                     kv->Hk, kv->Di, kv->n_max, n_vis_c, p.on_pool ? pool_c : nullptr,
+                                     p.on_pool ? idx->P : 0, scores_c, bmax ? bmax + r0 * p.n_blocks : nullptr, 8,
+                                     s_idx);
       } else {
         s2 = csa2_index_scores(a->q_idx + r0 * a->Hi * kv->Di, kv->k_idx + (int64_t)b0 * kv->n_max * kbytes_row,
                                nb, T, a->Hi, kv->Hk, kv->Di, kv->n_max, n_vis_c, p.on_pool ? pool_c : nullptr,

@@ -102,12 +102,15 @@ __global__ __launch_bounds__(kMxThreads) void index_mxfp4_kernel(const uint8_t* 
 // score = (sum_h q_h) . k. The workgroup first sums the heads' dequantized query values in fp32,
 // then each entry's 32-channel block j (lane j) is 32 fp32 products with the key's E2M1 values,
 // scaled by the key's exponent; the 4 block sums meet in a butterfly.
+// kPool: column c of a query row scores position cand[r, c] (-inf for an empty slot or a position
+// outside [0, n_max)); kBlockMax: the max score of each aligned block of 8 visible entries (the 8
+// row groups of a half-wave are one block) goes to block_max ([walkthrough] 一(四)2).
 constexpr int kMaxSharedHeads = 64;      // query heads of the shared-key form
-__global__ __launch_bounds__(kMxThreads) void index_mxfp4_shared_kernel(const uint8_t* __restrict__ q,
-                                                                        const uint8_t* __restrict__ k, int T,
-                                                                        int Hi, int n_max,
-                                                                        const int32_t* __restrict__ n_vis,
-                                                                        int tile_rows, float* __restrict__ scores) {
+template <bool kPool, bool kBlockMax>
+__global__ __launch_bounds__(kMxThreads) void index_mxfp4_shared_kernel(
+    const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, int T, int Hi, int n_max,
+    const int32_t* __restrict__ n_vis, const int32_t* __restrict__ cand, int P, int tile_rows,
+    float* __restrict__ scores, float* __restrict__ block_max) {
   constexpr int L = 4, RB = 68;                 // 128 channels: 64 code bytes + 4 scale bytes
   constexpr int ROWS = kMxThreads / L;
   const int r = blockIdx.x;
@@ -115,9 +118,11 @@ __global__ __launch_bounds__(kMxThreads) void index_mxfp4_shared_kernel(const ui
   const int tid = threadIdx.x;
   const int j = tid % L;
   const int grp = tid / L;
-  const int nv = n_vis ? min(n_vis[r], n_max) : n_max;
+  const int lane = tid & 63;
+  const int ncols = kPool ? P : n_max;
+  const int nv = (!kPool && n_vis) ? min(n_vis[r], n_max) : n_max;
   const int tile0 = blockIdx.y * tile_rows;
-  const int tile_end = min(tile0 + tile_rows, nv);
+  const int tile_end = min(tile0 + tile_rows, kPool ? ncols : nv);
   if (tile0 >= tile_end) return;
 
   // The query summed over its heads, (sum_h q_h)[c] for the 128 channels. The query row is
@@ -150,18 +155,28 @@ __global__ __launch_bounds__(kMxThreads) void index_mxfp4_shared_kernel(const ui
 #pragma unroll
   for (int i = 0; i < 32; ++i) qs[i] = qsum[0][32 * j + i] + qsum[1][32 * j + i];
   const uint8_t* kb = k + (int64_t)b * n_max * RB;
-  float* srow = scores + (int64_t)r * n_max;
+  float* srow = scores + (int64_t)r * ncols;
+  const int32_t* crow = kPool ? cand + (int64_t)r * P : nullptr;
+  const int n_blocks = (n_max + 7) >> 3;
 
   for (int base = tile0; base < tile_end; base += ROWS * kMxInFlight) {
     uint32_t cw[kMxInFlight][4];
     int ek[kMxInFlight];
+    bool valid[kMxInFlight];
 #pragma unroll
     for (int u = 0; u < kMxInFlight; ++u) {
-      const int n = base + u * ROWS + grp;
+      const int col = base + u * ROWS + grp;
+      int n = col;
+      if (kPool) {
+        n = col < tile_end ? crow[col] : -1;
+        valid[u] = n >= 0 && n < n_max;
+      } else {
+        valid[u] = col < tile_end;
+      }
 #pragma unroll
       for (int w = 0; w < 4; ++w) cw[u][w] = 0u;
       ek[u] = 127;
-      if (n < tile_end) {
+      if (valid[u]) {
         const uint8_t* p = kb + (int64_t)n * RB;
         const uint32_t* pw = reinterpret_cast<const uint32_t*>(p + 16 * j);
 #pragma unroll
@@ -187,26 +202,46 @@ __global__ __launch_bounds__(kMxThreads) void index_mxfp4_shared_kernel(const ui
       float v = ldexpf(part, ek[u] - 127);
       v += shfl_xor_f(v, 2);
       v += shfl_xor_f(v, 1);
-      const int n = base + u * ROWS + grp;
-      if (j == 0 && n < tile_end) srow[n] = v;
+      const int col = base + u * ROWS + grp;
+      if (j == 0 && col < tile_end) srow[col] = valid[u] ? v : -INFINITY;
+      if (kBlockMax) {
+        // the 8 row groups of a half-wave are one aligned block of 8 entries (tiles and steps are
+        // multiples of 8 rows)
+        float m = valid[u] ? v : -INFINITY;
+        m = fmaxf(m, shfl_xor_f(m, 4));
+        m = fmaxf(m, shfl_xor_f(m, 8));
+        m = fmaxf(m, shfl_xor_f(m, 16));
+        const int blk = (base + u * ROWS + (grp & ~7)) >> 3;
+        if ((lane & 31) == 0 && blk < n_blocks && blk * 8 < tile_end) block_max[(int64_t)r * n_blocks + blk] = m;
+      }
     }
   }
 }
 
 hipError_t launch_index_mxfp4(const uint8_t* q, const uint8_t* k, int B, int T, int Hi, int Hk, int Di,
-                              int n_max, const int32_t* n_vis, float* scores, hipStream_t s) {
+                              int n_max, const int32_t* n_vis, const int32_t* cand, int P, float* scores,
+                              float* block_max, hipStream_t s) {
   const int64_t rows = (int64_t)B * T;
-  if (rows == 0 || n_max == 0) return hipSuccess;
+  const int ncols = cand ? P : n_max;
+  if (rows == 0 || ncols == 0) return hipSuccess;
   if (Hk == 1 && Di == 128) {                   // one shared key per entry
     // larger tiles than the per-head form: each workgroup first sums the query heads
     const int step = (kMxThreads / 4) * kMxInFlight;
     int tile = step;
-    while (tile < 8192 && rows * ((n_max + 2 * tile - 1) / (2 * tile)) >= 1024) tile *= 2;
-    dim3 grid((unsigned)rows, (unsigned)((n_max + tile - 1) / tile));
-    hipLaunchKernelGGL(index_mxfp4_shared_kernel, grid, dim3(kMxThreads), 0, s, q, k, T, Hi, n_max, n_vis, tile,
-                       scores);
+    while (tile < 8192 && rows * ((ncols + 2 * tile - 1) / (2 * tile)) >= 1024) tile *= 2;
+    dim3 grid((unsigned)rows, (unsigned)((ncols + tile - 1) / tile));
+    if (cand)
+      hipLaunchKernelGGL((index_mxfp4_shared_kernel<true, false>), grid, dim3(kMxThreads), 0, s, q, k, T, Hi, n_max,
+                         n_vis, cand, P, tile, scores, block_max);
+    else if (block_max)
+      hipLaunchKernelGGL((index_mxfp4_shared_kernel<false, true>), grid, dim3(kMxThreads), 0, s, q, k, T, Hi, n_max,
+                         n_vis, cand, P, tile, scores, block_max);
+    else
+      hipLaunchKernelGGL((index_mxfp4_shared_kernel<false, false>), grid, dim3(kMxThreads), 0, s, q, k, T, Hi, n_max,
+                         n_vis, cand, P, tile, scores, block_max);
     return hipGetLastError();
   }
+  if (cand || block_max) return hipErrorNotSupported;
   const int C = Hi * Di;
   // tiles of rows per workgroup: about 4096 workgroups or more (16 per CU; measured best against
   // 512 .. 2048 at 32 x 16384 entries), each tile at least one step of rows in flight

@@ -22,8 +22,10 @@ hipError_t launch_index_stream(const uint16_t* q, const uint16_t* k, int B, int 
 
 // index_mxfp4.hip: streaming indexer over MXFP4 query and key rows: Hk == Hi with Hi*Di = 256
 // or 512, or one shared key of Di = 128 channels (Hk == 1) and Hi query heads
+// (the shared-key form also scores a candidate pool, or writes the 8-entry block max)
 hipError_t launch_index_mxfp4(const uint8_t* q, const uint8_t* k, int B, int T, int Hi, int Hk, int Di,
-                              int n_max, const int32_t* n_vis, float* scores, hipStream_t s);
+                              int n_max, const int32_t* n_vis, const int32_t* cand, int P, float* scores,
+                              float* block_max, hipStream_t s);
 
 // index_prefill.hip: MFMA tiles for many query rows, causal tile skipping
 bool index_prefill_supported(int T, int Hi, int Hk, int Di);

@@ -130,14 +130,19 @@ csa2_status csa2_index_scores(const uint16_t* q_idx, const uint16_t* k_idx, int3
  * q_rows  [B*T, Hi*Di/2 + Hi*Di/32] bytes, k_rows [B, n_max, Hk*Di/2 + Hk*Di/32] bytes (8-byte
  *         aligned bases).
  * n_vis   [B*T] int32 visible entries per query row (device), or NULL for all n_max; entries
- *         n >= n_vis[r] are not scored and their slots are left unwritten.
- * scores  [B*T, n_max] fp32.
+ *         n >= n_vis[r] are not scored and their slots are left unwritten (flat mode).
+ * cand, P, block_max, block: as csa2_index_scores (pool mode: scores [B*T, P], slot p holds the
+ *         score of position cand[r, p] or -inf; flat mode: the max of every aligned block of 8
+ *         visible entries, block == 8). Both need the shared-key form (CSA2_E_UNSUPPORTED
+ *         otherwise).
+ * scores  [B*T, n_max] fp32 (flat) or [B*T, P] (pool).
  * Requires Hk == Hi with Hi * Di in {256, 512}, or Hk == 1, Di == 128 and Hi <= 64
  * (CSA2_E_SHAPE otherwise); finite scales (code 255 is NaN).
  * ------------------------------------------------------------------------------------------ */
 csa2_status csa2_index_scores_mxfp4(const uint8_t* q_rows, const uint8_t* k_rows, int32_t B,
                                     int32_t T, int32_t Hi, int32_t Hk, int32_t Di, int32_t n_max,
-                                    const int32_t* n_vis, float* scores, void* stream);
+                                    const int32_t* n_vis, const int32_t* cand, int32_t P,
+                                    float* scores, float* block_max, int32_t block, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * csa2_topk - Top-K selection per row.
@@ -260,8 +265,8 @@ typedef struct {
   int32_t valid;           /* set by FULL */
   /* FP4 indexer keys ([walkthrough] 一(五)4, OCP MXFP4): [B, n_max, C/2 + C/32] rows of
    * C = Hk * Di channels (layout of csa2_index_scores_mxfp4), or NULL. When given, Full and
-   * flat Reindex layers score them against the layer's q_idx_mx instead of k_idx / q_idx
-   * (shapes as csa2_index_scores_mxfp4; the hierarchical pool is not supported with them). */
+   * Reindex layers score them against the layer's q_idx_mx instead of k_idx / q_idx (shapes as
+   * csa2_index_scores_mxfp4; the hierarchical pool needs the shared-key form). */
   const uint8_t* k_mx;
 } csa2_shared_kv;
 

@@ -105,19 +105,29 @@ def test_sparse_attn_validation(L):
     assert f(FAKE, FAKE, 10, FAKE, 32, 1, 64, 512, 512, 1.0, FAKE, None, None, 0, None) == E_WS
 
 
+def test_index_scores_mxfp4_pool_modes(L):
+    f = L.csa2_index_scores_mxfp4
+    # pool scoring and block max need the shared-key form; block max only in flat mode, 8 wide
+    assert f(FAKE, FAKE, 1, 1, 8, 8, 64, 10, None, FAKE, 4, FAKE, None, 8, None) == E_UNSUP
+    assert f(FAKE, FAKE, 1, 1, 8, 8, 64, 10, None, None, 0, FAKE, FAKE, 8, None) == E_UNSUP
+    assert f(FAKE, FAKE, 1, 1, 32, 1, 128, 10, None, FAKE, 4, FAKE, FAKE, 8, None) == E_UNSUP
+    assert f(FAKE, FAKE, 1, 1, 32, 1, 128, 10, None, None, 0, FAKE, FAKE, 4, None) == E_UNSUP
+    assert f(FAKE, FAKE, 1, 1, 32, 1, 128, 10, None, FAKE, -1, FAKE, None, 8, None) == E_ARG
+
+
 def test_index_scores_mxfp4_validation(L):
     f = L.csa2_index_scores_mxfp4
-    # q_rows, k_rows, B, T, Hi, Hk, Di, n_max, n_vis, scores, stream
-    assert f(FAKE, FAKE, 1, 1, 2, 2, 64, 10, None, FAKE, None) == E_SHAPE      # 128 channels per head pair
-    assert f(FAKE, FAKE, 1, 1, 8, 8, 128, 10, None, FAKE, None) == E_SHAPE     # 1024 channels
-    assert f(FAKE, FAKE, 1, 1, 8, 4, 64, 10, None, FAKE, None) == E_SHAPE      # Hk neither Hi nor 1
-    assert f(FAKE, FAKE, 1, 1, 65, 1, 128, 10, None, FAKE, None) == E_SHAPE    # too many query heads
-    assert f(FAKE, FAKE, 1, 1, 8, 1, 64, 10, None, FAKE, None) == E_SHAPE      # shared keys are 128 wide
-    assert f(FAKE, FAKE, -1, 1, 8, 8, 64, 10, None, FAKE, None) == E_ARG
-    assert f(None, FAKE, 1, 1, 8, 8, 64, 10, None, FAKE, None) == E_ARG
-    assert f(FAKE + 4, FAKE, 1, 1, 8, 8, 64, 10, None, FAKE, None) == E_ARG    # misaligned rows
-    assert f(None, None, 0, 1, 8, 8, 64, 10, None, None, None) == 0            # nothing to do
-    assert f(None, None, 1, 1, 32, 1, 128, 0, None, None, None) == 0
+    # q_rows, k_rows, B, T, Hi, Hk, Di, n_max, n_vis, cand, P, scores, block_max, block, stream
+    assert f(FAKE, FAKE, 1, 1, 2, 2, 64, 10, None, None, 0, FAKE, None, 8, None) == E_SHAPE      # 128 channels per head pair
+    assert f(FAKE, FAKE, 1, 1, 8, 8, 128, 10, None, None, 0, FAKE, None, 8, None) == E_SHAPE     # 1024 channels
+    assert f(FAKE, FAKE, 1, 1, 8, 4, 64, 10, None, None, 0, FAKE, None, 8, None) == E_SHAPE      # Hk neither Hi nor 1
+    assert f(FAKE, FAKE, 1, 1, 65, 1, 128, 10, None, None, 0, FAKE, None, 8, None) == E_SHAPE    # too many query heads
+    assert f(FAKE, FAKE, 1, 1, 8, 1, 64, 10, None, None, 0, FAKE, None, 8, None) == E_SHAPE      # shared keys are 128 wide
+    assert f(FAKE, FAKE, -1, 1, 8, 8, 64, 10, None, None, 0, FAKE, None, 8, None) == E_ARG
+    assert f(None, FAKE, 1, 1, 8, 8, 64, 10, None, None, 0, FAKE, None, 8, None) == E_ARG
+    assert f(FAKE + 4, FAKE, 1, 1, 8, 8, 64, 10, None, None, 0, FAKE, None, 8, None) == E_ARG    # misaligned rows
+    assert f(None, None, 0, 1, 8, 8, 64, 10, None, None, 0, None, None, 8, None) == 0            # nothing to do
+    assert f(None, None, 1, 1, 32, 1, 128, 0, None, None, 0, None, None, 8, None) == 0
 
 
 def test_sparse_attn_swa_validation(L):
@@ -214,3 +224,5 @@ def test_layer_step_fp4_indexer_rules(L):
     a2, kv2, idx2 = _layer(pool_blocks=128, use_pool=1)
     kv2.k_mx = FAKE
     assert L.csa2_layer_workspace_size(0, C.byref(a2), C.byref(kv2), C.byref(idx2), C.byref(n)) == E_UNSUP
+    kv2.Hk, kv2.Di, a2.Hi = 1, 128, 32                              # the shared-key form takes the pool
+    assert L.csa2_layer_workspace_size(0, C.byref(a2), C.byref(kv2), C.byref(idx2), C.byref(n)) == OK

@@ -24,25 +24,44 @@ def _np(t):
     return t.cpu().numpy()
 
 
-def run_stack_gpu(wl, rows, kidx, n_vis=None):
-    """Run the workload's layer stack through csa2_layer_step; returns per-layer (out, lse, topk, pool)."""
-    kv = P.KVState(rows, kidx, n_vis)
+def mx_inputs(wl):
+    """FP4 (MXFP4) indexer rows of the workload, quantized by the oracle from its bf16 indexer
+    keys and queries: (per-layer query rows [B, T, .], key rows [B, N, .])."""
+    kc, qc = wl.Hk * wl.Di, wl.Hi * wl.Di
+    k_rows = np.stack([O.quantize_mxfp4(W.bf16_bits_to_f32(W.k_idx(wl, b)).reshape(wl.N, kc)) for b in range(wl.B)])
+    q_rows = [np.stack([O.quantize_mxfp4(W.bf16_bits_to_f32(W.q_idx(wl, b, layer)).reshape(wl.T, qc))
+                        for b in range(wl.B)]) for layer in range(len(wl.modes))]
+    return q_rows, k_rows
+
+
+def run_stack_gpu(wl, rows, kidx, n_vis=None, mx=None):
+    """Run the workload's layer stack through csa2_layer_step; returns per-layer (out, lse, topk, pool).
+    mx: FP4 indexer rows from mx_inputs (then kidx is unused)."""
+    if mx is None:
+        kv = P.KVState(rows, kidx, n_vis)
+    else:
+        kv = P.KVState(rows, None, n_vis, k_mx=torch.from_numpy(mx[1]).cuda(), mx_heads=(wl.Hk, wl.Di))
     pool_size = wl.pool_blocks * wl.block
     idx = P.IdxState.empty(wl.B * wl.T, wl.k, "cuda", pool_size=pool_size)
     res = []
     for layer, mode in enumerate(wl.modes):
         q = q_device(wl, layer, "q")
-        qi = q_device(wl, layer, "q_idx") if mode != P.REUSE else None
+        qi = q_device(wl, layer, "q_idx") if mode != P.REUSE and mx is None else None
+        qm = torch.from_numpy(mx[0][layer]).cuda() if mode != P.REUSE and mx is not None else None
         use_pool = wl.pool_blocks > 0
-        out, lse = P.layer_step(mode, q, kv, idx, q_idx=qi, use_pool=use_pool, pool_blocks=wl.pool_blocks)
+        out, lse = P.layer_step(mode, q, kv, idx, q_idx=qi, q_idx_mx=qm, use_pool=use_pool,
+                                pool_blocks=wl.pool_blocks)
         res.append((_np(out), _np(lse), _np(idx.topk).copy(), _np(idx.pool).copy() if idx.pool is not None else None))
     return res, kv, idx
 
 
-def oracle_sequence(wl, b, tr):
-    """Oracle layer stack for sequence b, query rows tr (indices into the T query tokens)."""
+def oracle_sequence(wl, b, tr, mx=None):
+    """Oracle layer stack for sequence b, query rows tr (indices into the T query tokens). mx: FP4
+    indexer rows from mx_inputs, scored over their dequantized values (O13)."""
     seq = W.sequence(wl, b)
     kq = f64(seq["k_idx"])
+    if mx is not None:
+        kq = O.dequant_mxfp4(mx[1][b], wl.Hk * wl.Di).reshape(wl.N, wl.Hk, wl.Di)
     N = wl.N
     n_vis = np.full(wl.T, N) if wl.T == 1 else np.minimum(O.prefill_n_vis(wl.p0, wl.T, wl.ratio), N)
     n_vis = n_vis[tr]
@@ -51,6 +70,8 @@ def oracle_sequence(wl, b, tr):
     for layer, mode in enumerate(wl.modes):
         q = f64(seq["q"][layer])[tr]
         qi = f64(seq["q_idx"][layer])[tr]
+        if mx is not None:
+            qi = O.dequant_mxfp4(mx[0][layer][b], wl.Hi * wl.Di).reshape(wl.T, wl.Hi, wl.Di)[tr]
         bmax = None
         if mode == W.REUSE:
             sel, scores = shared_topk, None
@@ -86,14 +107,14 @@ def _blocks(pool_row):
     return np.concatenate([bl, -np.ones(0, np.int64)])
 
 
-def verify(wl, gpu_res, bs, rows_gpu, sample_rows=None):
+def verify(wl, gpu_res, bs, rows_gpu, sample_rows=None, mx=None):
     """Compare GPU layer results for sequences bs (query rows sample_rows) against the oracle.
     Returns (rows with identical index sets, rows with an allowed near-tie swap)."""
     scale = wl.sm_scale
     tr = np.arange(wl.T) if sample_rows is None else np.asarray(sample_rows)
     n_same = n_swap = 0
     for b in bs:
-        ora, src = oracle_sequence(wl, b, tr)
+        ora, src = oracle_sequence(wl, b, tr, mx)
         rows_b = rows_gpu[b].cpu().numpy()
         row_ok = np.ones(len(tr), bool)      # GPU and oracle agree on everything upstream
         for layer, o in enumerate(ora):
@@ -295,45 +316,16 @@ def test_layer_stack_with_window():
                 check_attn(_np(o)[0], ref[0], _np(l)[0], lref[0], what + " (oracle indices)")
 
 
-@pytest.mark.parametrize("name", ["stack", "decoder20_flat"])
+@pytest.mark.parametrize("name", ["stack", "decoder20_flat", "decoder20"])
 def test_layer_stack_fp4_indexer(name):
-    """Layer stacks with FP4 (MXFP4) indexer keys and queries: Full -> Reindex -> Reuse with one
-    key head per index head (8 x 64), and the 20-layer schedule with one shared 128-channel key
-    and 32 query heads (flat Reindex). Each index layer's Top-K against the oracle's Top-K of the
-    MXFP4 scores, attention against the oracle's on its own selection."""
-    wl = SMALL["stack"] if name == "stack" else W.CONFIGS[6].scaled(B=2, N=3000, k=128, pool_blocks=0)
-    shared = wl.Hk == 1
-    kc, qc = wl.Hk * wl.Di, wl.Hi * wl.Di
+    """Layer stacks with FP4 (MXFP4) indexer keys and queries against the oracle on the same
+    MXFP4 rows: Full -> Reindex -> Reuse with one key head per index head (8 x 64); the 20-layer
+    schedule with one shared 128-channel key and 32 query heads, flat and with the hierarchical
+    pool (Full builds it from the fused block max, Reindex scores it)."""
+    wl = {"stack": SMALL["stack"], "decoder20": SMALL["decoder20"],
+          "decoder20_flat": W.CONFIGS[6].scaled(B=2, N=3000, k=128, pool_blocks=0)}[name]
     rows = kv_rows_device(wl)
-    k_rows = np.stack([O.quantize_mxfp4(W.bf16_bits_to_f32(W.k_idx(wl, b)).reshape(wl.N, kc)) for b in range(wl.B)])
-    q_rows = [np.stack([O.quantize_mxfp4(W.bf16_bits_to_f32(W.q_idx(wl, b, layer)).reshape(wl.T, qc))
-                        for b in range(wl.B)]) for layer in range(len(wl.modes))]
-    kv = P.KVState(rows, None, k_mx=torch.from_numpy(k_rows).cuda(), mx_heads=(wl.Hk, wl.Di))
-    idx = P.IdxState.empty(wl.B, wl.k, "cuda")
-    gpu = []
-    for layer, mode in enumerate(wl.modes):
-        q = q_device(wl, layer, "q")
-        qm = torch.from_numpy(q_rows[layer]).cuda() if mode != P.REUSE else None
-        out, lse = P.layer_step(mode, q, kv, idx, q_idx_mx=qm)
-        gpu.append((_np(out), _np(lse), _np(idx.topk).copy()))
-    assert kv.valid
-    for b in range(wl.B):
-        seq = W.sequence(wl, b)
-        kvd = O.dequant_kv_fp4(O.quantize_kv_fp4(seq["kv_src"]))
-        sel, scores = None, None
-        for layer, mode in enumerate(wl.modes):
-            if mode != W.REUSE:
-                if shared:
-                    scores = O.index_scores_mxfp4(q_rows[layer][b], k_rows[b], wl.Di, [wl.N], q_heads=wl.Hi)[0]
-                else:
-                    scores = O.index_scores_mxfp4(q_rows[layer][b], k_rows[b], kc, [wl.N])[0]
-                sel = O.topk(scores[None], wl.k)
-            q = f64(seq["q"][layer])
-            ref, lref = O.sparse_attn(q, kvd, sel, wl.sm_scale)
-            what = f"fp4 indexer {name} layer {layer} b={b}"
-            if compare_topk(gpu[layer][2][b], sel[0], lambda p, s=scores: s[p], what):
-                check_attn(gpu[layer][0][b], ref, gpu[layer][1][b], lref, what)
-            else:
-                o, l = P.sparse_attn(q_device(wl, layer, "q")[b:b + 1], rows[b:b + 1],
-                                     torch.from_numpy(sel.astype(np.int32)[None]).cuda(), wl.sm_scale)
-                check_attn(_np(o)[0], ref, _np(l)[0], lref, what + " (oracle indices)")
+    mx = mx_inputs(wl)
+    res, kv, idx = run_stack_gpu(wl, rows, None, mx=mx)
+    assert kv.valid and idx.c.topk_valid
+    verify(wl, res, range(wl.B), rows, mx=mx)
