@@ -194,7 +194,37 @@ def fp4_indexer_leg(wl, sets, steps, dev, stream):
     row_b = wl.D // 2 + wl.D // 16
     R = wl.B * wl.T
     step_bytes = nbytes + R * wl.k * 4 * 2 + R * wl.k * row_b + R * wl.H * wl.D * 2 + R * wl.H * wl.D * 4
-    return {"kernel": "index_mxfp4_kernel (MXFP4 indexer scores)", "bound": "hbm", "achieved": round(gbs, 1),
+    extra = {}
+    if len(wl.modes) > 1:
+        # the workload's whole layer schedule with FP4 indexer keys (and its pool, shared-key form)
+        use_pool = wl.pool_blocks > 0 and shared
+        stacks = []
+        for c in range(2):
+            s = sets[c % len(sets)]
+            kv = P.KVState(s["rows"], None, k_mx=keys[c], mx_heads=(wl.Hk, wl.Di))
+            idx = P.IdxState.empty(R, wl.k, dev, pool_size=wl.pool_blocks * wl.block if use_pool else 0)
+            outs = [torch.empty(wl.B, wl.T, wl.H, wl.D, dtype=torch.float32, device=dev) for _ in wl.modes]
+            stacks.append((s, kv, idx, outs))
+
+        def schedule(i):
+            s, kv, idx, outs = stacks[i % 2]
+            for l, mode in enumerate(wl.modes):
+                P.layer_step(mode, s["q"][l], kv, idx, q_idx_mx=q if mode != 2 else None, sm_scale=wl.sm_scale,
+                             use_pool=use_pool, pool_blocks=wl.pool_blocks if use_pool else 0, with_lse=False,
+                             ws=ws, out=outs[l])
+
+        for i in range(3):
+            schedule(i)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(steps):
+            schedule(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        sched_us = a.elapsed_time(b) / steps * 1e3
+        extra = {"schedule_us": round(sched_us, 2), "schedule_query_tokens_per_s": round(R / (sched_us * 1e-6), 1),
+                 "schedule_pool": use_pool}
+    return {**extra, "kernel": "index_mxfp4_kernel (MXFP4 indexer scores)", "bound": "hbm", "achieved": round(gbs, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
             "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": round(us, 2), "row_bytes": rb,
             "full_step_us": round(step_us, 2), "full_step_query_tokens_per_s": round(R / (step_us * 1e-6), 1),
