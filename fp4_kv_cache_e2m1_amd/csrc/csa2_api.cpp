@@ -143,8 +143,6 @@ csa2_status csa2_index_scores_mxfp4(const uint8_t* q_rows, const uint8_t* k_rows
                                     int32_t block, void* stream) {
   if (B < 0 || T < 0 || n_max < 0 || (cand && P < 0)) return CSA2_E_ARG;
   if (!mxfp4_shape_ok(Hi, Hk, Di)) return CSA2_E_SHAPE;
-  const bool shared = Hk == 1 && Di == 128;
-  if ((cand || block_max) && !shared) return CSA2_E_UNSUPPORTED;   // pool modes: shared-key form only
   if (block_max && (cand || block != 8)) return CSA2_E_UNSUPPORTED;
   const int64_t rows = (int64_t)B * T;
   const int32_t ncols = cand ? P : n_max;
@@ -272,9 +270,8 @@ csa2_status plan_layer(csa2_mode mode, const csa2_layer_args* a, const csa2_shar
   p->on_pool = mode == CSA2_REINDEX && a->use_pool && idx->pool_valid;
   if (p->score) {
     if (kv->k_mx) {
-      // FP4 (MXFP4) indexer keys; the hierarchical pool needs the shared-key form
+      // FP4 (MXFP4) indexer keys
       if (!mxfp4_shape_ok(a->Hi, kv->Hk, kv->Di)) return CSA2_E_SHAPE;
-      if (a->use_pool && !(kv->Hk == 1 && kv->Di == 128)) return CSA2_E_UNSUPPORTED;
     } else if (!index_shape_ok(a->Hi, kv->Hk, kv->Di)) {
       return CSA2_E_SHAPE;
     }

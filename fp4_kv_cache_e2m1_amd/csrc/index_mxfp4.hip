@@ -29,11 +29,14 @@ __device__ __forceinline__ void mx_e2m1x8(uint32_t w, f16x2_mx_t* out) {
   out[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
 }
 
-template <int L>
-__global__ __launch_bounds__(kMxThreads) void index_mxfp4_kernel(const uint8_t* __restrict__ q,
-                                                                 const uint8_t* __restrict__ k, int T,
-                                                                 int n_max, const int32_t* __restrict__ n_vis,
-                                                                 int tile_rows, float* __restrict__ scores) {
+// kPool: column c of a query row scores position cand[r, c] (-inf for an empty slot or a position
+// outside [0, n_max)); kBlockMax: the max score of each aligned block of 8 visible entries goes to
+// block_max (a block spans two waves here, so an iteration's scores meet in LDS).
+template <int L, bool kPool, bool kBlockMax>
+__global__ __launch_bounds__(kMxThreads) void index_mxfp4_kernel(
+    const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, int T, int n_max,
+    const int32_t* __restrict__ n_vis, const int32_t* __restrict__ cand, int P, int tile_rows,
+    float* __restrict__ scores, float* __restrict__ block_max) {
   static_assert(L == 8 || L == 16, "rows of 256 or 512 channels");
   constexpr int C = 32 * L;
   constexpr int RB = C / 2 + C / 32;            // bytes per row
@@ -43,10 +46,14 @@ __global__ __launch_bounds__(kMxThreads) void index_mxfp4_kernel(const uint8_t* 
   const int tid = threadIdx.x;
   const int j = tid % L;                        // the lane's 32-channel block
   const int grp = tid / L;                      // the lane group's row within a step
-  const int nv = n_vis ? min(n_vis[r], n_max) : n_max;
+  const int ncols = kPool ? P : n_max;
+  const int nv = (!kPool && n_vis) ? min(n_vis[r], n_max) : n_max;
   const int tile0 = blockIdx.y * tile_rows;
-  const int tile_end = min(tile0 + tile_rows, nv);
-  if (tile0 >= tile_end) return;
+  const int tile_end = min(tile0 + tile_rows, kPool ? ncols : nv);
+  if (tile0 >= tile_end) return;               // uniform over the workgroup
+  __shared__ float sbm[kBlockMax ? ROWS * kMxInFlight : 1];
+  const int32_t* crow = kPool ? cand + (int64_t)r * P : nullptr;
+  const int n_blocks = (n_max + 7) >> 3;
 
   // the query's block j as 16 f16 pairs and its exponent
   f16x2_mx_t qv[16];
@@ -62,17 +69,25 @@ __global__ __launch_bounds__(kMxThreads) void index_mxfp4_kernel(const uint8_t* 
     eq = qp[C / 2 + j];
   }
   const uint8_t* kb = k + (int64_t)b * n_max * RB;
-  float* srow = scores + (int64_t)r * n_max;
+  float* srow = scores + (int64_t)r * ncols;
 
   for (int base = tile0; base < tile_end; base += ROWS * kMxInFlight) {
     uint2 ca[kMxInFlight], cb[kMxInFlight];
     int ek[kMxInFlight];
+    bool valid[kMxInFlight];
 #pragma unroll
     for (int u = 0; u < kMxInFlight; ++u) {
-      const int n = base + u * ROWS + grp;
+      const int col = base + u * ROWS + grp;
+      int n = col;
+      if (kPool) {
+        n = col < tile_end ? crow[col] : -1;
+        valid[u] = n >= 0 && n < n_max;
+      } else {
+        valid[u] = col < tile_end;
+      }
       ca[u] = cb[u] = make_uint2(0, 0);
       ek[u] = 127;
-      if (n < tile_end) {
+      if (valid[u]) {
         const uint8_t* p = kb + (int64_t)n * RB;
         ca[u] = *reinterpret_cast<const uint2*>(p + 16 * j);
         cb[u] = *reinterpret_cast<const uint2*>(p + 16 * j + 8);
@@ -92,8 +107,21 @@ __global__ __launch_bounds__(kMxThreads) void index_mxfp4_kernel(const uint8_t* 
       float v = ldexpf(part, eq + ek[u] - 254);
 #pragma unroll
       for (int m = L / 2; m >= 1; m /= 2) v += shfl_xor_f(v, m);
-      const int n = base + u * ROWS + grp;
-      if (j == 0 && n < tile_end) srow[n] = v;
+      const int col = base + u * ROWS + grp;
+      if (j == 0 && col < tile_end) srow[col] = valid[u] ? v : -INFINITY;
+      if (kBlockMax && j == 0) sbm[u * ROWS + grp] = valid[u] ? v : -INFINITY;
+    }
+    if (kBlockMax) {
+      // sbm[i] is the score of row base + i (base and the tile are multiples of 8 rows)
+      __syncthreads();
+      if (tid < ROWS * kMxInFlight / 8) {
+        float m = sbm[8 * tid];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) m = fmaxf(m, sbm[8 * tid + e]);
+        const int blk = (base >> 3) + tid;
+        if (blk < n_blocks && blk * 8 < tile_end) block_max[(int64_t)r * n_blocks + blk] = m;
+      }
+      __syncthreads();                          // sbm is rewritten by the next iteration
     }
   }
 }
@@ -218,6 +246,22 @@ __global__ __launch_bounds__(kMxThreads) void index_mxfp4_shared_kernel(
   }
 }
 
+template <int L>
+static hipError_t launch_mx_modes(dim3 grid, hipStream_t s, const uint8_t* q, const uint8_t* k, int T, int n_max,
+                                  const int32_t* n_vis, const int32_t* cand, int P, int tile, float* scores,
+                                  float* block_max) {
+  if (cand)
+    hipLaunchKernelGGL((index_mxfp4_kernel<L, true, false>), grid, dim3(kMxThreads), 0, s, q, k, T, n_max, n_vis,
+                       cand, P, tile, scores, block_max);
+  else if (block_max)
+    hipLaunchKernelGGL((index_mxfp4_kernel<L, false, true>), grid, dim3(kMxThreads), 0, s, q, k, T, n_max, n_vis,
+                       cand, P, tile, scores, block_max);
+  else
+    hipLaunchKernelGGL((index_mxfp4_kernel<L, false, false>), grid, dim3(kMxThreads), 0, s, q, k, T, n_max, n_vis,
+                       cand, P, tile, scores, block_max);
+  return hipGetLastError();
+}
+
 hipError_t launch_index_mxfp4(const uint8_t* q, const uint8_t* k, int B, int T, int Hi, int Hk, int Di,
                               int n_max, const int32_t* n_vis, const int32_t* cand, int P, float* scores,
                               float* block_max, hipStream_t s) {
@@ -241,19 +285,16 @@ hipError_t launch_index_mxfp4(const uint8_t* q, const uint8_t* k, int B, int T, 
                          n_vis, cand, P, tile, scores, block_max);
     return hipGetLastError();
   }
-  if (cand || block_max) return hipErrorNotSupported;
+
   const int C = Hi * Di;
   // tiles of rows per workgroup: about 4096 workgroups or more (16 per CU; measured best against
   // 512 .. 2048 at 32 x 16384 entries), each tile at least one step of rows in flight
   const int step = (kMxThreads / (C / 32)) * kMxInFlight;
   int tile = step;
-  while (tile < 8192 && rows * ((n_max + 2 * tile - 1) / (2 * tile)) >= 4096) tile *= 2;
-  dim3 grid((unsigned)rows, (unsigned)((n_max + tile - 1) / tile));
-  if (C == 256)
-    hipLaunchKernelGGL(index_mxfp4_kernel<8>, grid, dim3(kMxThreads), 0, s, q, k, T, n_max, n_vis, tile, scores);
-  else
-    hipLaunchKernelGGL(index_mxfp4_kernel<16>, grid, dim3(kMxThreads), 0, s, q, k, T, n_max, n_vis, tile, scores);
-  return hipGetLastError();
+  while (tile < 8192 && rows * ((ncols + 2 * tile - 1) / (2 * tile)) >= 4096) tile *= 2;
+  dim3 grid((unsigned)rows, (unsigned)((ncols + tile - 1) / tile));
+  if (C == 256) return launch_mx_modes<8>(grid, s, q, k, T, n_max, n_vis, cand, P, tile, scores, block_max);
+  return launch_mx_modes<16>(grid, s, q, k, T, n_max, n_vis, cand, P, tile, scores, block_max);
 }
 
 }  // namespace csa2

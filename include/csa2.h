@@ -133,8 +133,8 @@ csa2_status csa2_index_scores(const uint16_t* q_idx, const uint16_t* k_idx, int3
  *         n >= n_vis[r] are not scored and their slots are left unwritten (flat mode).
  * cand, P, block_max, block: as csa2_index_scores (pool mode: scores [B*T, P], slot p holds the
  *         score of position cand[r, p] or -inf; flat mode: the max of every aligned block of 8
- *         visible entries, block == 8). Both need the shared-key form (CSA2_E_UNSUPPORTED
- *         otherwise).
+ *         visible entries, block == 8; CSA2_E_UNSUPPORTED for block_max with cand or another
+ *         block).
  * scores  [B*T, n_max] fp32 (flat) or [B*T, P] (pool).
  * Requires Hk == Hi with Hi * Di in {256, 512}, or Hk == 1, Di == 128 and Hi <= 64
  * (CSA2_E_SHAPE otherwise); finite scales (code 255 is NaN).
@@ -266,7 +266,7 @@ typedef struct {
   /* FP4 indexer keys ([walkthrough] 一(五)4, OCP MXFP4): [B, n_max, C/2 + C/32] rows of
    * C = Hk * Di channels (layout of csa2_index_scores_mxfp4), or NULL. When given, Full and
    * Reindex layers score them against the layer's q_idx_mx instead of k_idx / q_idx (shapes as
-   * csa2_index_scores_mxfp4; the hierarchical pool needs the shared-key form). */
+   * csa2_index_scores_mxfp4, with or without the hierarchical pool). */
   const uint8_t* k_mx;
 } csa2_shared_kv;
 

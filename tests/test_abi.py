@@ -107,9 +107,8 @@ def test_sparse_attn_validation(L):
 
 def test_index_scores_mxfp4_pool_modes(L):
     f = L.csa2_index_scores_mxfp4
-    # pool scoring and block max need the shared-key form; block max only in flat mode, 8 wide
-    assert f(FAKE, FAKE, 1, 1, 8, 8, 64, 10, None, FAKE, 4, FAKE, None, 8, None) == E_UNSUP
-    assert f(FAKE, FAKE, 1, 1, 8, 8, 64, 10, None, None, 0, FAKE, FAKE, 8, None) == E_UNSUP
+    # block max only in flat mode, 8 wide
+    assert f(FAKE, FAKE, 1, 1, 8, 8, 64, 10, None, FAKE, 4, FAKE, FAKE, 8, None) == E_UNSUP
     assert f(FAKE, FAKE, 1, 1, 32, 1, 128, 10, None, FAKE, 4, FAKE, FAKE, 8, None) == E_UNSUP
     assert f(FAKE, FAKE, 1, 1, 32, 1, 128, 10, None, None, 0, FAKE, FAKE, 4, None) == E_UNSUP
     assert f(FAKE, FAKE, 1, 1, 32, 1, 128, 10, None, FAKE, -1, FAKE, None, 8, None) == E_ARG
@@ -223,6 +222,6 @@ def test_layer_step_fp4_indexer_rules(L):
     assert L.csa2_layer_workspace_size(0, C.byref(a), C.byref(kv), C.byref(idx), C.byref(n)) == E_SHAPE
     a2, kv2, idx2 = _layer(pool_blocks=128, use_pool=1)
     kv2.k_mx = FAKE
-    assert L.csa2_layer_workspace_size(0, C.byref(a2), C.byref(kv2), C.byref(idx2), C.byref(n)) == E_UNSUP
-    kv2.Hk, kv2.Di, a2.Hi = 1, 128, 32                              # the shared-key form takes the pool
+    assert L.csa2_layer_workspace_size(0, C.byref(a2), C.byref(kv2), C.byref(idx2), C.byref(n)) == OK
+    kv2.Hk, kv2.Di, a2.Hi = 1, 128, 32                              # the shared-key form too
     assert L.csa2_layer_workspace_size(0, C.byref(a2), C.byref(kv2), C.byref(idx2), C.byref(n)) == OK

@@ -451,26 +451,28 @@ def test_index_scores_mxfp4_shared_key(B, T, N, Hi):
             assert np.all(s[r][~mask] == 7.0)
 
 
-def test_index_scores_mxfp4_shared_pool_and_block_max():
-    """Shared-key FP4 indexer in its pool modes: the fused 8-entry block max equals the max of the
-    kernel's own scores over visible block members (ragged n_vis), and candidate scoring (empty
-    slots and out-of-range positions give -inf) matches the oracle's pool scores."""
-    B, N, Hi, n_pool = 2, 3001, 32, 1000
-    g = np.random.default_rng(12)
-    q_rows = O.quantize_mxfp4(g.standard_normal((B, Hi * 128)).astype(np.float32)).reshape(B, 1, -1)
-    k_rows = O.quantize_mxfp4(g.standard_normal((B * N, 128)).astype(np.float32)).reshape(B, N, -1)
+@pytest.mark.parametrize("Hi,Hk,Di", [(32, 1, 128), (8, 8, 64), (4, 4, 64)])
+def test_index_scores_mxfp4_pool_and_block_max(Hi, Hk, Di):
+    """FP4 indexer pool modes, shared-key and per-head forms: the fused 8-entry block max equals
+    the max of the kernel's own scores over visible block members (ragged n_vis), and candidate
+    scoring (empty slots and out-of-range positions give -inf) matches the oracle's pool scores."""
+    B, N, n_pool = 2, 3001, 1000
+    kc, qc = Hk * Di, Hi * Di
+    g = np.random.default_rng(12 + Hi)
+    q_rows = O.quantize_mxfp4(g.standard_normal((B, qc)).astype(np.float32)).reshape(B, 1, -1)
+    k_rows = O.quantize_mxfp4(g.standard_normal((B * N, kc)).astype(np.float32)).reshape(B, N, -1)
     n_vis = np.array([N, 1237], np.int32)
     qd, kq = torch.from_numpy(q_rows).cuda(), torch.from_numpy(k_rows).cuda()
-    s, bm = P.index_scores_mxfp4(qd, kq, 128, n_vis=torch.from_numpy(n_vis).cuda(), q_heads=Hi, block_max=True)
+    C, qh = (Di, Hi) if Hk == 1 else (kc, 0)
+    s, bm = P.index_scores_mxfp4(qd, kq, C, n_vis=torch.from_numpy(n_vis).cuda(), q_heads=qh, block_max=True)
     s, bm = _sync_np(s), _sync_np(bm)
     cand = np.sort(g.choice(N + 40, size=(B, n_pool), replace=True), axis=1).astype(np.int32)
     cand[:, -37:] = -1
-    sp = _sync_np(P.index_scores_mxfp4(qd, kq, 128, q_heads=Hi, cand=torch.from_numpy(cand).cuda()))
+    sp = _sync_np(P.index_scores_mxfp4(qd, kq, C, q_heads=qh, cand=torch.from_numpy(cand).cuda()))
     for b in range(B):
-        qv = O.dequant_mxfp4(q_rows[b], Hi * 128).reshape(1, Hi, 128)
-        kv = O.dequant_mxfp4(k_rows[b], 128).reshape(N, 1, 128)
-        abs_k = np.abs(kv[:, 0])
-        abs_dot = (np.abs(qv[0]).sum(axis=0) @ abs_k.T)
+        qv = O.dequant_mxfp4(q_rows[b], qc).reshape(1, Hi, Di)
+        kv = O.dequant_mxfp4(k_rows[b], kc).reshape(N, Hk, Di)
+        abs_dot = _abs_dot(qv, kv)[0]
         ref = O.index_scores(qv, kv, [n_vis[b]])[0]
         mask = np.arange(N) < n_vis[b]
         check_scores(s[b], ref, abs_dot, mask, f"mxfp4 flat b={b}")

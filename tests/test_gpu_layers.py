@@ -316,14 +316,14 @@ def test_layer_stack_with_window():
                 check_attn(_np(o)[0], ref[0], _np(l)[0], lref[0], what + " (oracle indices)")
 
 
-@pytest.mark.parametrize("name", ["stack", "decoder20_flat", "decoder20"])
+@pytest.mark.parametrize("name", ["stack", "decoder20_flat", "decoder20", "hsi_pool_first", "hsi_pool_fused"])
 def test_layer_stack_fp4_indexer(name):
     """Layer stacks with FP4 (MXFP4) indexer keys and queries against the oracle on the same
     MXFP4 rows: Full -> Reindex -> Reuse with one key head per index head (8 x 64); the 20-layer
     schedule with one shared 128-channel key and 32 query heads, flat and with the hierarchical
-    pool (Full builds it from the fused block max, Reindex scores it)."""
-    wl = {"stack": SMALL["stack"], "decoder20": SMALL["decoder20"],
-          "decoder20_flat": W.CONFIGS[6].scaled(B=2, N=3000, k=128, pool_blocks=0)}[name]
+    pool (Full builds it from the fused block max, Reindex scores it); the HSI stacks with
+    per-head keys, pool first and pool with Top-K in one kernel."""
+    wl = W.CONFIGS[6].scaled(B=2, N=3000, k=128, pool_blocks=0) if name == "decoder20_flat" else SMALL[name]
     rows = kv_rows_device(wl)
     mx = mx_inputs(wl)
     res, kv, idx = run_stack_gpu(wl, rows, None, mx=mx)
