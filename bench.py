@@ -196,8 +196,8 @@ def fp4_indexer_leg(wl, sets, steps, dev, stream):
     step_bytes = nbytes + R * wl.k * 4 * 2 + R * wl.k * row_b + R * wl.H * wl.D * 2 + R * wl.H * wl.D * 4
     extra = {}
     if len(wl.modes) > 1:
-        # the workload's whole layer schedule with FP4 indexer keys (and its pool, shared-key form)
-        use_pool = wl.pool_blocks > 0 and shared
+        # the workload's whole layer schedule with FP4 indexer keys (and its pool)
+        use_pool = wl.pool_blocks > 0
         stacks = []
         for c in range(2):
             s = sets[c % len(sets)]
