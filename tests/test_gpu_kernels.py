@@ -341,11 +341,13 @@ def _swa_run(rows, qb, idx, codes, exps, n_win, scale, with_lse=True, ws=None):
                                               (2, 32, 10, 0, 128, [128, 5]),
                                               (32, 64, 800, 512, 128, list(range(0, 128, 4))),
                                               (4, 128, 600, 1024, 100, [100, 99, 31, 33]),
-                                              (1, 48, 70, 31, 16, [200])])
+                                              (1, 48, 70, 31, 16, [200]),
+                                              (600, 16, 40, 24, 64, [(7 * b) % 70 for b in range(600)])])
 def test_sparse_attn_swa(B, H, N, K, Wn, n_win):
     """Selected FP4 entries joined with the FP8 window as one softmax, against the oracle: one- and
     several-chunk windows, a ragged last chunk, an empty window, no selected entries (K = 0), the
-    split sparse path (B = 32, K = 512) and n_win above the reserved rows (clamped)."""
+    split sparse path (B = 32, K = 512), n_win above the reserved rows (clamped), and 600
+    sequences (beyond the plain sparse attention's decode-form limit)."""
     case = _swa_case(B, H, N, K, Wn, n_win, seed=B * 100 + K + Wn)
     scale = 1 / np.sqrt(512)
     out, lse = _swa_run(*case, scale)
