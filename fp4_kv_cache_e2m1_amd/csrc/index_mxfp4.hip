@@ -19,7 +19,8 @@ typedef _Float16 f16x2_mx_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_mx_t __attribute__((ext_vector_type(2)));
 
 constexpr int kMxThreads = 256;
-constexpr int kMxInFlight = 8;          // row steps whose loads a lane issues before using them
+constexpr int kMxInFlight = 4;          // row steps whose loads a lane issues before using them
+constexpr int kMxSharedInFlight = 8;    // the same for the shared-key form (68-byte rows)
 
 // 8 E2M1 codes (one 32-bit word, channel 2i in the low nibble of byte i) -> 4 f16 pairs, exact.
 __device__ __forceinline__ void mx_e2m1x8(uint32_t w, f16x2_mx_t* out) {
@@ -187,12 +188,12 @@ __global__ __launch_bounds__(kMxThreads) void index_mxfp4_shared_kernel(
   const int32_t* crow = kPool ? cand + (int64_t)r * P : nullptr;
   const int n_blocks = (n_max + 7) >> 3;
 
-  for (int base = tile0; base < tile_end; base += ROWS * kMxInFlight) {
-    uint32_t cw[kMxInFlight][4];
-    int ek[kMxInFlight];
-    bool valid[kMxInFlight];
+  for (int base = tile0; base < tile_end; base += ROWS * kMxSharedInFlight) {
+    uint32_t cw[kMxSharedInFlight][4];
+    int ek[kMxSharedInFlight];
+    bool valid[kMxSharedInFlight];
 #pragma unroll
-    for (int u = 0; u < kMxInFlight; ++u) {
+    for (int u = 0; u < kMxSharedInFlight; ++u) {
       const int col = base + u * ROWS + grp;
       int n = col;
       if (kPool) {
@@ -213,7 +214,7 @@ __global__ __launch_bounds__(kMxThreads) void index_mxfp4_shared_kernel(
       }
     }
 #pragma unroll
-    for (int u = 0; u < kMxInFlight; ++u) {
+    for (int u = 0; u < kMxSharedInFlight; ++u) {
       float part = 0.0f;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -270,7 +271,7 @@ hipError_t launch_index_mxfp4(const uint8_t* q, const uint8_t* k, int B, int T, 
   if (rows == 0 || ncols == 0) return hipSuccess;
   if (Hk == 1 && Di == 128) {                   // one shared key per entry
     // larger tiles than the per-head form: each workgroup first sums the query heads
-    const int step = (kMxThreads / 4) * kMxInFlight;
+    const int step = (kMxThreads / 4) * kMxSharedInFlight;
     int tile = step;
     while (tile < 8192 && rows * ((ncols + 2 * tile - 1) / (2 * tile)) >= 1024) tile *= 2;
     dim3 grid((unsigned)rows, (unsigned)((ncols + tile - 1) / tile));
@@ -287,11 +288,12 @@ hipError_t launch_index_mxfp4(const uint8_t* q, const uint8_t* k, int B, int T, 
   }
 
   const int C = Hi * Di;
-  // tiles of rows per workgroup: about 4096 workgroups or more (16 per CU; measured best against
-  // 512 .. 2048 at 32 x 16384 entries), each tile at least one step of rows in flight
+  // tiles of rows per workgroup: about 16384 workgroups or more, each at least one step of rows in
+  // flight (four steps of 8-byte loads per lane and this target measured best against 8 or 16
+  // steps and 4096 / 8192 workgroups at 4 x 262144, 16 x 65536 and 32 x 16384 entries)
   const int step = (kMxThreads / (C / 32)) * kMxInFlight;
   int tile = step;
-  while (tile < 8192 && rows * ((ncols + 2 * tile - 1) / (2 * tile)) >= 4096) tile *= 2;
+  while (tile < 8192 && rows * ((ncols + 2 * tile - 1) / (2 * tile)) >= 16384) tile *= 2;
   dim3 grid((unsigned)rows, (unsigned)((ncols + tile - 1) / tile));
   if (C == 256) return launch_mx_modes<8>(grid, s, q, k, T, n_max, n_vis, cand, P, tile, scores, block_max);
   return launch_mx_modes<16>(grid, s, q, k, T, n_max, n_vis, cand, P, tile, scores, block_max);
