@@ -306,7 +306,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path has no "
-              "multi-GPU mode in this build.", file=sys.stderr)
+              "multi-GPU mode.", file=sys.stderr)
         sys.exit(2)
 
     import torch

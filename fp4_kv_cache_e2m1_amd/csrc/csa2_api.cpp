@@ -87,7 +87,7 @@ const char* csa2_status_string(csa2_status s) {
     case CSA2_E_SHAPE: return "unsupported or inconsistent shape";
     case CSA2_E_STATE: return "shared state needed by this mode is not valid";
     case CSA2_E_WORKSPACE: return "workspace missing or too small";
-    case CSA2_E_UNSUPPORTED: return "not supported by this build";
+    case CSA2_E_UNSUPPORTED: return "not supported by this library";
     case CSA2_E_HIP: return "HIP launch failed";
   }
   return "unknown status";

@@ -43,7 +43,7 @@ typedef enum {
   CSA2_E_SHAPE = 2,        /* unsupported or inconsistent shape */
   CSA2_E_STATE = 3,        /* Reindex/Reuse without the shared state they need */
   CSA2_E_WORKSPACE = 4,    /* workspace missing or smaller than required */
-  CSA2_E_UNSUPPORTED = 5,  /* valid request this build does not implement */
+  CSA2_E_UNSUPPORTED = 5,  /* valid request the library does not implement */
   CSA2_E_HIP = 6           /* a HIP launch failed */
 } csa2_status;
 
