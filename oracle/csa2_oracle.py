@@ -467,6 +467,25 @@ def dequant_swa_fp8(codes: np.ndarray, exps: np.ndarray) -> np.ndarray:
     return e4m3_decode(codes) * np.ldexp(1.0, np.asarray(exps, dtype=np.int64))[..., None]
 
 
+def prefill_windows(buf: np.ndarray, n_win, W: int) -> np.ndarray:
+    """O12d. The window rows of each query token of one sequence in prefill.
+
+    [walkthrough] 一(四): each query attends to its own layer's sliding window, which ends at the
+    query's own token. Reading R-21: the sequence's window buffer holds T + W - 1 rows, row i
+    being token p0 - W + 1 + i (p0 = the first query's position); query t takes its last
+    n = min(n_win[t], W) tokens up to its own, buffer rows t + W - n .. t + W - 1 (n < W only near
+    the start of the sequence). buf: [T + W - 1, D]; returns win [T, W, D] with those rows first
+    (the layout sparse_attn_swa takes)."""
+    buf = np.asarray(buf)
+    T = buf.shape[0] - W + 1
+    win = np.zeros((T, W) + buf.shape[1:], dtype=buf.dtype)
+    for t in range(T):
+        n = min(int(n_win[t]), W)
+        if n > 0:
+            win[t, :n] = buf[t + W - n: t + W]
+    return win
+
+
 def sparse_attn_swa(q: np.ndarray, kv: np.ndarray, idx: np.ndarray, win: np.ndarray, n_win, sm_scale: float):
     """O12c. Attention of each query head over its selected entries and its window, as one softmax.
 

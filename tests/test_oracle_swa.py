@@ -105,3 +105,18 @@ def test_layer_step_with_window_is_union_attention():
     assert np.array_equal(with_w["out"], o) and np.array_equal(with_w["lse"], l)
     empty = O.layer_step(O.FULL, q=q, kv_deq=kv, k_idx=ki, q_idx=qi, n_vis=[N], k=32, win=win, n_win=[0])
     assert np.allclose(empty["out"], base["out"], rtol=1e-6, atol=1e-6)
+
+
+def test_prefill_windows_end_at_the_query_token():
+    """Each query's window is its last n tokens up to and including its own (buffer row i holds
+    token p0 - W + 1 + i); tokens before the sequence start are never taken."""
+    W, T, p0 = 8, 12, 3
+    tokens = np.arange(p0 - W + 1, p0 + T)[:, None].astype(np.float64)   # buffer rows = token ids
+    n_win = [min(W, p0 + t + 1) for t in range(T)]
+    win = O.prefill_windows(tokens, n_win, W)
+    for t in range(T):
+        p = p0 + t
+        n = n_win[t]
+        assert list(win[t, :n, 0]) == list(range(p - n + 1, p + 1))
+        assert min(win[t, :n, 0]) >= 0
+        assert np.all(win[t, n:] == 0)
