@@ -6,8 +6,8 @@ the first call does, and fails loudly if it has not been built.
 """
 from .api import (FULL, REINDEX, REUSE, IdxState, KVState, dequant_kv_fp4, hier_pool, index_scores,
                   index_scores_mxfp4, layer_step, prefill_n_vis, quantize_kv_fp4, row_bytes, sparse_attn,
-                  sparse_attn_swa, topk)
+                  sparse_attn_swa, sparse_attn_swa_prefill, topk)
 
 __all__ = ["FULL", "REINDEX", "REUSE", "IdxState", "KVState", "dequant_kv_fp4", "hier_pool", "index_scores",
            "index_scores_mxfp4", "layer_step", "prefill_n_vis", "quantize_kv_fp4", "row_bytes", "sparse_attn",
-           "sparse_attn_swa", "topk"]
+           "sparse_attn_swa", "sparse_attn_swa_prefill", "topk"]

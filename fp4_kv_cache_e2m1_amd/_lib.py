@@ -35,6 +35,8 @@ EXPORTS = [
     "csa2_sparse_attn",
     "csa2_sparse_attn_swa_workspace_size",
     "csa2_sparse_attn_swa",
+    "csa2_sparse_attn_swa_prefill_workspace_size",
+    "csa2_sparse_attn_swa_prefill",
     "csa2_index_scores_mxfp4",
     "csa2_layer_workspace_size",
     "csa2_layer_step",
@@ -86,6 +88,9 @@ def _declare(lib):
         "csa2_sparse_attn": (i32, [vp, vp, i32, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp, sz, vp]),
         "csa2_sparse_attn_swa_workspace_size": (sz, [i32, i32, i32, i32]),
         "csa2_sparse_attn_swa": (i32, [vp, vp, i32, vp, i32, i32, i32, i32, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
+        "csa2_sparse_attn_swa_prefill_workspace_size": (sz, [i32, i32, i32, i32, i32]),
+        "csa2_sparse_attn_swa_prefill": (i32, [vp, vp, i32, vp, i32, i32, i32, i32, i32, vp, vp, vp, i32, f32, vp, vp,
+                                               vp, sz, vp]),
         "csa2_index_scores_mxfp4": (i32, [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, i32, vp, vp, i32, vp]),
         "csa2_layer_workspace_size": (i32, [i32, C.POINTER(LayerArgs), C.POINTER(SharedKV),
                                             C.POINTER(SharedIdx), C.POINTER(sz)]),

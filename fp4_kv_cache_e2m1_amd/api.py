@@ -258,6 +258,38 @@ def sparse_attn_swa(q: torch.Tensor, rows: torch.Tensor, idx: torch.Tensor, swa_
     return out, lse
 
 
+def sparse_attn_swa_prefill(q: torch.Tensor, rows: torch.Tensor, idx: torch.Tensor, swa_codes: torch.Tensor,
+                            swa_exp: torch.Tensor, n_win: torch.Tensor, sm_scale: float, with_lse: bool = True,
+                            ws: Optional[torch.Tensor] = None):
+    """Many query tokens over their selected entries joined with each token's window (its last
+    n_win tokens up to its own). q [B, T, H, 512] bf16, rows [B, N, 288] uint8, idx [B, T, K]
+    int32, swa_codes [B, T + W - 1, 512] uint8, swa_exp [B, T + W - 1] int8, n_win [B, T] int32
+    -> out fp32 [B, T, H, 512], lse fp32 [B, T, H]."""
+    _need(q, "q", torch.bfloat16)
+    dev = q.device
+    _need(rows, "rows", torch.uint8, dev)
+    _need(idx, "idx", torch.int32, dev)
+    _need(swa_codes, "swa_codes", torch.uint8, dev)
+    _need(swa_exp, "swa_exp", torch.int8, dev)
+    _need(n_win, "n_win", torch.int32, dev)
+    B, T, H, D = q.shape
+    N, K = rows.shape[1], idx.shape[-1]
+    W = swa_codes.shape[1] - T + 1
+    if (rows.shape[0] != B or rows.shape[2] != row_bytes(D) or idx.shape[:2] != (B, T) or W < 0
+            or swa_codes.shape != (B, T + W - 1, D) or swa_exp.shape != (B, T + W - 1) or n_win.numel() != B * T):
+        raise ValueError("inconsistent shapes for q / rows / idx / window")
+    out = torch.empty(B, T, H, D, dtype=torch.float32, device=dev)
+    lse = torch.empty(B, T, H, dtype=torch.float32, device=dev) if with_lse else None
+    L = _lib.lib()
+    nbytes = L.csa2_sparse_attn_swa_prefill_workspace_size(B, T, H, D, K)
+    ws = _ws(max(nbytes, 1), dev, ws)
+    code = L.csa2_sparse_attn_swa_prefill(_ptr(q), _ptr(rows), N, _ptr(idx), B, T, H, D, K, _ptr(swa_codes),
+                                          _ptr(swa_exp), _ptr(n_win), W, float(sm_scale), _ptr(out), _ptr(lse),
+                                          _ptr(ws), nbytes, _stream(dev))
+    check("csa2_sparse_attn_swa_prefill", code)
+    return out, lse
+
+
 def prefill_n_vis(p0: int, T: int, ratio: int, device) -> torch.Tensor:
     """Visible compressed entries for query tokens at positions p0..p0+T-1: floor((p+1)/ratio)."""
     p = torch.arange(p0 + 1, p0 + T + 1, dtype=torch.int64)

@@ -237,6 +237,31 @@ csa2_status csa2_sparse_attn_swa(const uint16_t* q, const uint8_t* rows, int32_t
                                            out, lse, ws, as_stream(stream)));
 }
 
+size_t csa2_sparse_attn_swa_prefill_workspace_size(int32_t B, int32_t T, int32_t H, int32_t D, int32_t K) {
+  if (B <= 0 || T <= 0 || !attn_shape_ok(H, D) || K < 0 || K > kMaxK) return 0;
+  return attn_swa_prefill_workspace(B, T, H, D, K);
+}
+
+csa2_status csa2_sparse_attn_swa_prefill(const uint16_t* q, const uint8_t* rows, int32_t n_max, const int32_t* idx,
+                                         int32_t B, int32_t T, int32_t H, int32_t D, int32_t K,
+                                         const uint8_t* swa_codes, const int8_t* swa_exp, const int32_t* n_win,
+                                         int32_t W, float sm_scale, float* out, float* lse, void* ws,
+                                         size_t ws_bytes, void* stream) {
+  if (B < 0 || T < 0 || n_max < 0 || K < 0 || H < 0 || W < 0) return CSA2_E_ARG;
+  if (!attn_shape_ok(H, D) || W > kMaxSwaWindow || K > kMaxK) return CSA2_E_SHAPE;
+  if ((int64_t)B * T > INT32_MAX) return CSA2_E_SHAPE;
+  if (B == 0 || T == 0) return CSA2_OK;
+  if (!q || !out || !n_win || (W > 0 && (!swa_codes || !swa_exp)) || (K > 0 && (!idx || (n_max > 0 && !rows))))
+    return CSA2_E_ARG;
+  if (reinterpret_cast<uintptr_t>(q) % 16 || reinterpret_cast<uintptr_t>(rows) % 16 ||
+      reinterpret_cast<uintptr_t>(out) % 16 || reinterpret_cast<uintptr_t>(swa_codes) % 16)
+    return CSA2_E_ARG;
+  const size_t need = csa2_sparse_attn_swa_prefill_workspace_size(B, T, H, D, K);
+  if (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 256) return CSA2_E_WORKSPACE;
+  return hip_status(launch_sparse_attn_swa_prefill(q, rows, n_max, idx, B, T, H, D, K, swa_codes, swa_exp, n_win, W,
+                                                   sm_scale, out, lse, ws, as_stream(stream)));
+}
+
 // ---------------------------------------------------------------------------------------------
 // Layer step. Workspace layout: [scores][block_max][top-k / pool scratch][attention partials].
 // ---------------------------------------------------------------------------------------------

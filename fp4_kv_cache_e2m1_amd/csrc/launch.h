@@ -57,6 +57,11 @@ hipError_t launch_pool_topk(const float* block_max, int64_t rows, int n_blocks, 
 // sparse_attn.hip
 size_t attn_workspace(int B, int T, int H, int D, int K);
 size_t attn_swa_workspace(int B, int H, int D, int K);
+size_t attn_swa_prefill_workspace(int B, int T, int H, int D, int K);
+hipError_t launch_sparse_attn_swa_prefill(const uint16_t* q, const uint8_t* rows, int n_max, const int32_t* idx,
+                                          int B, int T, int H, int D, int K, const uint8_t* swa_codes,
+                                          const int8_t* swa_exp, const int32_t* n_win, int W, float sm_scale,
+                                          float* out, float* lse, void* ws, hipStream_t s);
 hipError_t launch_sparse_attn_swa(const uint16_t* q, const uint8_t* rows, int n_max, const int32_t* idx, int B,
                                   int H, int D, int K, const uint8_t* swa_codes, const int8_t* swa_exp,
                                   const int32_t* n_win, int W, float sm_scale, float* out, float* lse, void* ws,

@@ -627,9 +627,8 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
 template <int KC, int PF, int NG>
 __global__ __launch_bounds__(256 * NG) void swa_attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ swa_codes, const int8_t* __restrict__ swa_exp,
-    const int32_t* __restrict__ n_win, int W, int H, int rows_per_split, float sm_scale,
+    const int32_t* __restrict__ n_win, int T, int W, int H, int rows_per_split, float sm_scale,
     float* __restrict__ part_o, float* __restrict__ part_ml, int slot0, int n_rows, int n_wsplits, int per_xcd) {
-  constexpr int T = 1;
   using Sm = DecodeSmem<KC, NG>;
   constexpr int NS = KC / 16;                  // NS entry steps of 16 per chunk
   static_assert(KC == 32, "a wave's 64 lanes gather the chunk's 32 entries x 2 slabs of 64 channels");
@@ -655,14 +654,18 @@ __global__ __launch_bounds__(256 * NG) void swa_attn_kernel(
   uint16_t* xs = reinterpret_cast<uint16_t*>(gbase);
   float4* sp4b = reinterpret_cast<float4*>(gbase + Sm::kX);
 
-  const int n_valid = max(0, min(n_win[b], W));                      // window rows of this sequence
+  // decode (T == 1): rows 0 .. n-1 of the sequence's W-row window, n = n_win[b]; prefill (T > 1):
+  // the sequence's buffer holds T + W - 1 rows and query t takes rows t + W - n .. t + W - 1,
+  // n = n_win[query row] (its last n tokens up to its own)
+  const int n_valid = max(0, min(n_win[T == 1 ? b : qr], W));        // window rows of this query
+  const int64_t row0 = T == 1 ? (int64_t)b * W : (int64_t)b * (T + W - 1) + (qr - b * T) + (W - n_valid);
   const int kbeg = wsplit * rows_per_split;
   const int nk = max(0, min(n_valid, kbeg + rows_per_split) - kbeg);  // rows of this workgroup
   const int sub_len = ((nk + NG - 1) / NG + KC - 1) / KC * KC;          // entries per sub-group
   const int sbeg = kbeg + sg * sub_len;                                 // first window row of the sub-group
   const int snk = max(0, min(nk - sg * sub_len, sub_len));             // entries of this sub-group
-  const uint8_t* wbase = swa_codes + (int64_t)b * W * kD;           // [W][512] E4M3 codes
-  const int8_t* ebase = swa_exp + (int64_t)b * W;                    // [W] row exponents
+  const uint8_t* wbase = swa_codes + row0 * kD;                     // this query's window rows
+  const int8_t* ebase = swa_exp + row0;                              // their exponents
 
   // Lane: entry gkey of a chunk, channel slab gcs (64 channels) of this wave's 128. The
   // positions of its entries in the first PF chunks are loaded first, so that those gathers can
@@ -1233,11 +1236,14 @@ CSA2_DEV float wave_fsum(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// lse0: NULL, or slot 0 holds a normalized output whose natural log-sum-exp is lse0[row]: it
+// enters as a partial with m = lse0 * log2(e) and l = 1 (l = 0 when nothing was attended).
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
                                                            int n_splits, int64_t n_rows_h,
                                                            float* __restrict__ out,
-                                                           float* __restrict__ lse, int per_xcd) {
+                                                           float* __restrict__ lse, int per_xcd,
+                                                           const float* __restrict__ lse0) {
   const int lane = threadIdx.x & 63;
   const int64_t u = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   const int64_t rh = u * 4 + (threadIdx.x >> 6);
@@ -1254,8 +1260,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   // lane s < n_splits holds split s's (m, l)
   float ms = -INFINITY, ls = 0.0f;
   if (lane < n_splits) {
-    ms = part_ml[2 * (lane * n_rows_h + rh)];
-    ls = part_ml[2 * (lane * n_rows_h + rh) + 1];
+    if (lse0 && lane == 0) {
+      const float l0 = lse0[rh];
+      ms = l0 == -INFINITY ? -INFINITY : l0 * kLog2e;
+      ls = l0 == -INFINITY ? 0.0f : 1.0f;
+    } else {
+      ms = part_ml[2 * (lane * n_rows_h + rh)];
+      ls = part_ml[2 * (lane * n_rows_h + rh) + 1];
+    }
   }
   const float M = wave_fmax(ms);
   const float w_lane = (ms == -INFINITY) ? 0.0f : exp2f(ms - M);
@@ -1365,7 +1377,7 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* rows, int n_max,
   const int64_t rows_h = nq * H;
   const int per_xcd = (int)(((rows_h + 3) / 4 + 7) / 8);
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, part_o, part_ml,
-                     n_splits, rows_h, out, lse, per_xcd);
+                     n_splits, rows_h, out, lse, per_xcd, nullptr);
   return hipGetLastError();
 }
 
@@ -1422,14 +1434,56 @@ hipError_t launch_sparse_attn_swa(const uint16_t* q, const uint8_t* rows, int n_
   if (n_ws > 0) {
     const int per_xcd = (int)(((int64_t)B * n_ws * n_hg + 7) / 8);
     hipLaunchKernelGGL((swa_attn_kernel<kDKC, kDPF, kDNG>), dim3((unsigned)(8 * per_xcd)), dim3(256 * kDNG), 0, s,
-                       q, swa_codes, swa_exp, n_win, W, H, kSwaRowsPerSplit, sm_scale, part_o, part_ml, n_sp, B, n_ws,
+                       q, swa_codes, swa_exp, n_win, 1, W, H, kSwaRowsPerSplit, sm_scale, part_o, part_ml, n_sp, B, n_ws,
                        per_xcd);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int per_xcd = (int)(((rows_h + 3) / 4 + 7) / 8);
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, part_o, part_ml,
-                     n_sp + n_ws, rows_h, out, lse, per_xcd);
+                     n_sp + n_ws, rows_h, out, lse, per_xcd, nullptr);
+  return hipGetLastError();
+}
+
+// Prefill with the window: slot 0 of the split buffers takes the sparse attention's normalized
+// output (its log-sum-exp alongside), slots 1 .. the window's partials; one combine pass.
+size_t attn_swa_prefill_workspace(int B, int T, int H, int D, int K) {
+  const size_t rows_h = (size_t)B * T * H;
+  const size_t slots = 1 + kMaxSwaSplits;
+  const size_t parts = ((slots * rows_h * (size_t)D * 4 + slots * rows_h * 8 + rows_h * 4) + 255) & ~(size_t)255;
+  return parts + (K > 0 ? attn_workspace(B, T, H, D, K) : 0) + 256;
+}
+
+hipError_t launch_sparse_attn_swa_prefill(const uint16_t* q, const uint8_t* rows, int n_max, const int32_t* idx,
+                                          int B, int T, int H, int D, int K, const uint8_t* swa_codes,
+                                          const int8_t* swa_exp, const int32_t* n_win, int W, float sm_scale,
+                                          float* out, float* lse, void* ws, hipStream_t s) {
+  if (B == 0 || T == 0 || H == 0) return hipSuccess;
+  const int64_t nq = (int64_t)B * T, rows_h = nq * H;
+  const size_t slots = 1 + kMaxSwaSplits;
+  float* part_o = static_cast<float*>(ws);
+  float* part_ml = part_o + slots * (size_t)rows_h * kD;
+  float* lse_s = part_ml + 2 * slots * (size_t)rows_h;
+  const size_t parts = ((slots * rows_h * (size_t)D * 4 + slots * rows_h * 8 + rows_h * 4) + 255) & ~(size_t)255;
+  void* attn_ws = static_cast<uint8_t*>(ws) + parts;
+  const int n_sp = K > 0 ? 1 : 0;
+  if (n_sp) {
+    const hipError_t e = launch_sparse_attn(q, rows, n_max, idx, B, T, H, D, K, sm_scale, part_o, lse_s, attn_ws, s);
+    if (e != hipSuccess) return e;
+  }
+  const int n_ws = (W + kSwaRowsPerSplit - 1) / kSwaRowsPerSplit;
+  const int n_hg = H / 16;
+  if (n_ws > 0) {
+    const int per_xcd = (int)((nq * n_ws * n_hg + 7) / 8);
+    hipLaunchKernelGGL((swa_attn_kernel<kDKC, kDPF, kDNG>), dim3((unsigned)(8 * per_xcd)), dim3(256 * kDNG), 0, s,
+                       q, swa_codes, swa_exp, n_win, T, W, H, kSwaRowsPerSplit, sm_scale, part_o, part_ml, n_sp,
+                       (int)nq, n_ws, per_xcd);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int per_xcd = (int)(((rows_h + 3) / 4 + 7) / 8);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, part_o, part_ml,
+                     n_sp + n_ws, rows_h, out, lse, per_xcd, n_sp ? lse_s : nullptr);
   return hipGetLastError();
 }
 

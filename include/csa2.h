@@ -237,6 +237,34 @@ csa2_status csa2_sparse_attn_swa(const uint16_t* q, const uint8_t* rows, int32_t
                                  float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * csa2_sparse_attn_swa_prefill - attention of many query tokens over their selected FP4
+ * entries joined with each token's own sliding window of FP8 rows, as one softmax.
+ * [walkthrough] 一(四): each query attends to its selected entries and to its own layer's
+ * sliding-window KV, which ends at the query's own token; 一(五)4: that KV is FP8.
+ *
+ * For each (b, t, h) the softmax runs over the selected entries of idx[b, t] (as
+ * csa2_sparse_attn) and the window of query t: the sequence's buffer holds T + W - 1 rows (row i
+ * = token p0 - W + 1 + i, p0 = position of query 0), and query t takes its last
+ * n = min(n_win[b, t], W) tokens up to its own, rows t + W - n .. t + W - 1 (n < W near the start
+ * of the sequence). Row values as csa2_sparse_attn_swa. out / lse as csa2_sparse_attn.
+ *
+ * q [B, T, H, D] bf16; rows, n_max, idx [B, T, K], K <= 4096: as csa2_sparse_attn.
+ * swa_codes [B, T + W - 1, D] uint8 E4M3 codes (16-byte aligned); swa_exp [B, T + W - 1] int8
+ *           exponents in [-15, 7]; n_win [B, T] int32 (device); W <= 128.
+ * out [B, T, H, D] fp32; lse [B, T, H] fp32 or NULL.
+ * ws        scratch of csa2_sparse_attn_swa_prefill_workspace_size() bytes, 256-byte aligned.
+ * Requires D == 512, H % 16 == 0.
+ * ------------------------------------------------------------------------------------------ */
+size_t csa2_sparse_attn_swa_prefill_workspace_size(int32_t B, int32_t T, int32_t H, int32_t D,
+                                                   int32_t K);
+csa2_status csa2_sparse_attn_swa_prefill(const uint16_t* q, const uint8_t* rows, int32_t n_max,
+                                         const int32_t* idx, int32_t B, int32_t T, int32_t H,
+                                         int32_t D, int32_t K, const uint8_t* swa_codes,
+                                         const int8_t* swa_exp, const int32_t* n_win, int32_t W,
+                                         float sm_scale, float* out, float* lse, void* ws,
+                                         size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * csa2_layer_step - one CSA2 layer in its static mode.
  * [walkthrough] 一(四)1: every layer computes its own query. Full scores every visible entry
  * with its own indexer query and produces new Top-K; Reindex re-scores the latest shared keys

@@ -225,3 +225,21 @@ def test_layer_step_fp4_indexer_rules(L):
     assert L.csa2_layer_workspace_size(0, C.byref(a2), C.byref(kv2), C.byref(idx2), C.byref(n)) == OK
     kv2.Hk, kv2.Di, a2.Hi = 1, 128, 32                              # the shared-key form too
     assert L.csa2_layer_workspace_size(0, C.byref(a2), C.byref(kv2), C.byref(idx2), C.byref(n)) == OK
+
+
+def test_sparse_attn_swa_prefill_validation(L):
+    f = L.csa2_sparse_attn_swa_prefill
+    # q, rows, n_max, idx, B, T, H, D, K, swa_codes, swa_exp, n_win, W, scale, out, lse, ws, ws_bytes, stream
+    assert f(FAKE, FAKE, 10, FAKE, 1, 4, 64, 256, 8, FAKE, FAKE, FAKE, 128, 1.0, FAKE, None, FAKE, 1 << 30,
+             None) == E_SHAPE
+    assert f(FAKE, FAKE, 10, FAKE, 1, 4, 64, 512, 8, FAKE, FAKE, FAKE, 129, 1.0, FAKE, None, FAKE, 1 << 30,
+             None) == E_SHAPE
+    assert f(FAKE, FAKE, 10, FAKE, 1, 4, 64, 512, 8, FAKE, FAKE, None, 128, 1.0, FAKE, None, FAKE, 1 << 30,
+             None) == E_ARG
+    need = L.csa2_sparse_attn_swa_prefill_workspace_size(1, 600, 64, 512, 64)
+    assert need >= 3 * 600 * 64 * 512 * 4
+    assert f(FAKE, FAKE, 10, FAKE, 1, 600, 64, 512, 64, FAKE, FAKE, FAKE, 128, 1.0, FAKE, None, FAKE, need - 1,
+             None) == E_WS
+    assert f(FAKE, FAKE, 10, FAKE, 1, 600, 64, 512, 64, FAKE, FAKE, FAKE, 128, 1.0, FAKE, None, FAKE + 16, need,
+             None) == E_WS                                          # workspace not 256-byte aligned
+    assert f(None, None, 10, None, 1, 0, 64, 512, 8, None, None, None, 128, 1.0, None, None, None, 0, None) == 0

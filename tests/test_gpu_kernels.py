@@ -502,3 +502,29 @@ def test_index_scores_mxfp4_exact_blocks():
     s = _sync_np(P.index_scores_mxfp4(torch.from_numpy(q_rows[None]).cuda(), torch.from_numpy(k_rows[None]).cuda(), C))
     want = np.array([np.sum(qd[32 * (n % 16): 32 * (n % 16) + 32] ** 2) for n in range(N)], np.float32)
     assert np.array_equal(s[0], want)
+
+
+@pytest.mark.parametrize("B,T,H,N,K,Wn,p0", [(1, 600, 64, 700, 64, 128, 50), (2, 40, 16, 300, 33, 64, 10),
+                                             (1, 520, 32, 200, 40, 100, 500), (1, 3, 16, 20, 0, 8, 0)])
+def test_sparse_attn_swa_prefill(B, T, H, N, K, Wn, p0):
+    """Prefill with each query token's own window (its last n tokens up to its own, n < W near the
+    start of the sequence) joined to its selected entries, against the oracle: the 64-head prefill
+    form underneath (600 rows), the decode form with several query tokens (split path), the wide
+    32-head form, and no selected entries."""
+    rows, qb, idx = _attn_case(B, T, H, N, K, seed=T + K + Wn, oob=K > 0) if K > 0 else _attn_case(B, T, H, N, 1, seed=5)
+    if K == 0:
+        idx = np.zeros((B, T, 0), np.int32)
+    g = np.random.default_rng(T + Wn)
+    codes, exps = O.quantize_swa_fp8(g.standard_normal((B * (T + Wn - 1), 512)).astype(np.float32))
+    codes, exps = codes.reshape(B, T + Wn - 1, 512), exps.reshape(B, T + Wn - 1)
+    n_win = np.array([[min(Wn, p0 + t + 1) for t in range(T)] for _ in range(B)], np.int32)
+    scale = 1 / np.sqrt(512)
+    out, lse = P.sparse_attn_swa_prefill(dev_bf16(qb), torch.from_numpy(rows).cuda(), torch.from_numpy(idx).cuda(),
+                                         torch.from_numpy(codes).cuda(), torch.from_numpy(exps).cuda(),
+                                         torch.from_numpy(n_win).cuda(), scale)
+    out, lse = _sync_np(out), _sync_np(lse)
+    for b in range(B):
+        win = O.prefill_windows(O.dequant_swa_fp8(codes[b], exps[b]), n_win[b], Wn)
+        clean = np.where((idx[b] >= 0) & (idx[b] < N), idx[b], -1)
+        ref, lref = O.sparse_attn_swa(f64(qb[b]), O.dequant_kv_fp4(rows[b]), clean, win, n_win[b], scale)
+        check_attn(out[b], ref, lse[b], lref, f"swa prefill B={B} T={T} H={H} K={K} b={b}")
