@@ -233,21 +233,24 @@ def fp4_indexer_leg(wl, sets, steps, dev, stream):
 
 
 def window_leg(wl, sets, state, n_rows, steps, dev, stream):
-    """Decode attention over the last step's Top-K joined with a full window of n_rows FP8 rows per
-    sequence (csa2_sparse_attn_swa), timed beside the same attention without the window."""
+    """Attention over the last step's Top-K joined with full windows of n_rows FP8 rows
+    (csa2_sparse_attn_swa in decode, csa2_sparse_attn_swa_prefill for many query tokens, each
+    token's window ending at its own), timed beside the same attention without the window."""
     import torch
     import fp4_kv_cache_e2m1_amd as P
-    from fp4_kv_cache_e2m1_amd import workloads as W
-    B = wl.B
-    wins = [W.swa_window(wl, b, n_rows) for b in range(B)]
+    from fp4_kv_cache_e2m1_amd import _lib, workloads as W
+    B, T = wl.B, wl.T
+    buf_rows = n_rows if T == 1 else T + n_rows - 1
+    wins = [W.swa_window(wl, b, buf_rows) for b in range(B)]
     codes = torch.from_numpy(np.stack([c for c, _ in wins])).to(dev)
     exps = torch.from_numpy(np.stack([e for _, e in wins])).to(dev)
-    n_win = torch.full((B,), n_rows, dtype=torch.int32, device=dev)
-    ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+    n_win = torch.full((B,) if T == 1 else (B, T), n_rows, dtype=torch.int32, device=dev)
+    need = _lib.lib().csa2_sparse_attn_swa_prefill_workspace_size(B, T, wl.H, wl.D, wl.k) if T > 1 else 0
+    ws = torch.empty(max(64 << 20, need), dtype=torch.uint8, device=dev)
     calls = []
     for s, kv, idx, _ in state:
-        q = s["q"][0].view(B, wl.H, wl.D)
-        calls.append((q, s["rows"], idx.topk.view(B, wl.k)))
+        q = s["q"][0] if T > 1 else s["q"][0].view(B, wl.H, wl.D)
+        calls.append((q, s["rows"], idx.topk.view(B, T, wl.k) if T > 1 else idx.topk.view(B, wl.k)))
 
     def timed(fn):
         for i in range(3):
@@ -263,15 +266,18 @@ def window_leg(wl, sets, state, n_rows, steps, dev, stream):
 
     def with_window(i):
         q, rows, topk = calls[i % len(calls)]
-        P.sparse_attn_swa(q, rows, topk, codes, exps, n_win, wl.sm_scale, with_lse=False, ws=ws)
+        if T == 1:
+            P.sparse_attn_swa(q, rows, topk, codes, exps, n_win, wl.sm_scale, with_lse=False, ws=ws)
+        else:
+            P.sparse_attn_swa_prefill(q, rows, topk, codes, exps, n_win, wl.sm_scale, with_lse=False, ws=ws)
 
     def without(i):
         q, rows, topk = calls[i % len(calls)]
-        P.sparse_attn(q.view(B, 1, wl.H, wl.D), rows, topk.view(B, 1, wl.k), wl.sm_scale, with_lse=False, ws=ws)
+        P.sparse_attn(q.view(B, T, wl.H, wl.D), rows, topk.view(B, T, wl.k), wl.sm_scale, with_lse=False, ws=ws)
 
     us_w, us_s = timed(with_window), timed(without)
     row_b = wl.D // 2 + wl.D // 16
-    nbytes = B * (wl.k * (4 + row_b) + n_rows * (wl.D + 1) + wl.H * wl.D * 2 + wl.H * wl.D * 4)
+    nbytes = B * (T * wl.k * (4 + row_b) + buf_rows * (wl.D + 1) + T * wl.H * wl.D * 2 + T * wl.H * wl.D * 4)
     return {"window_rows": n_rows, "us_per_call": round(us_w, 2), "sparse_only_us_per_call": round(us_s, 2),
             "algorithmic_bytes": nbytes, "hbm_gbs": round(nbytes / (us_w * 1e-6) / 1e9, 1)}
 
@@ -440,7 +446,7 @@ def main():
     fp4_shape = (wl.Hk == wl.Hi and wl.Hi * wl.Di in (256, 512)) or (wl.Hk == 1 and wl.Di == 128)
     if args.fp4_indexer and wl.T == 1 and fp4_shape:
         line["fp4_indexer"] = fp4_indexer_leg(wl, sets, args.steps, dev, stream)
-    if args.window > 0 and wl.T == 1:
+    if args.window > 0:
         line["window_attention"] = window_leg(wl, sets, state, args.window, args.steps, dev, stream)
     if not args.no_cpu_baseline and args.config == 2:
         log(f"[bench] CPU oracle on {args.cpu_sample} sequences, >= {args.cpu_seconds} s")
