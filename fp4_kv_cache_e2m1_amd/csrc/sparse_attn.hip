@@ -1471,12 +1471,15 @@ hipError_t launch_sparse_attn_swa_prefill(const uint16_t* q, const uint8_t* rows
     const hipError_t e = launch_sparse_attn(q, rows, n_max, idx, B, T, H, D, K, sm_scale, part_o, lse_s, attn_ws, s);
     if (e != hipSuccess) return e;
   }
-  const int n_ws = (W + kSwaRowsPerSplit - 1) / kSwaRowsPerSplit;
+  // many query rows keep the chip busy: one slot holds a token's whole window (each sub-group
+  // takes half of it), which halves the window workgroups and the partials the combine reads
+  const int n_ws = W > 0 ? 1 : 0;
+  const int rps = (W + kSwaRowsPerSplit - 1) / kSwaRowsPerSplit * kSwaRowsPerSplit;
   const int n_hg = H / 16;
   if (n_ws > 0) {
     const int per_xcd = (int)((nq * n_ws * n_hg + 7) / 8);
     hipLaunchKernelGGL((swa_attn_kernel<kDKC, kDPF, kDNG>), dim3((unsigned)(8 * per_xcd)), dim3(256 * kDNG), 0, s,
-                       q, swa_codes, swa_exp, n_win, T, W, H, kSwaRowsPerSplit, sm_scale, part_o, part_ml, n_sp,
+                       q, swa_codes, swa_exp, n_win, T, W, H, rps, sm_scale, part_o, part_ml, n_sp,
                        (int)nq, n_ws, per_xcd);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
