@@ -374,8 +374,9 @@ def layer_step(mode: int, q: torch.Tensor, kv: KVState, idx: IdxState, q_idx: Op
                q_idx_mx: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """One CSA2 layer (FULL / REINDEX / REUSE) over caller-owned shared state; returns (out, lse).
 
-    window: (swa_codes [B, W, D] uint8, swa_exp [B, W] int8, n_win [B] int32), decode only: the
-    layer's sliding window joined to the selected entries as one softmax.
+    window: the layer's sliding window joined to the selected entries as one softmax: decode
+    (swa_codes [B, W, D] uint8, swa_exp [B, W] int8, n_win [B] int32), or prefill (swa_codes
+    [B, T + W - 1, D], swa_exp [B, T + W - 1], n_win [B, T]: each token's last n tokens).
     q_idx_mx: [B, T, C/2 + C/32] uint8 MXFP4 indexer query, for a KVState with FP4 keys (then
     q_idx only gives Hi and may be None with Hi taken from the state)."""
     _need(q, "q", torch.bfloat16, kv.rows.device)
@@ -400,9 +401,11 @@ def layer_step(mode: int, q: torch.Tensor, kv: KVState, idx: IdxState, q_idx: Op
         _need(codes, "swa_codes", torch.uint8, dev)
         _need(exps, "swa_exp", torch.int8, dev)
         _need(n_win, "n_win", torch.int32, dev)
-        if codes.shape[0] != B or codes.shape[2] != D or exps.shape != codes.shape[:2] or n_win.shape != (B,):
-            raise ValueError("window shapes must be [B, W, D], [B, W], [B]")
-        a.swa_codes, a.swa_exp, a.swa_n, a.swa_W = _ptr(codes), _ptr(exps), _ptr(n_win), codes.shape[1]
+        Wn = codes.shape[1] - T + 1
+        if (codes.shape[0] != B or codes.shape[2] != D or exps.shape != codes.shape[:2] or Wn < 0
+                or n_win.numel() != (B if T == 1 else B * T)):
+            raise ValueError("window shapes must be [B, T + W - 1, D], [B, T + W - 1], [B] or [B, T]")
+        a.swa_codes, a.swa_exp, a.swa_n, a.swa_W = _ptr(codes), _ptr(exps), _ptr(n_win), Wn
     if out is None:
         out = torch.empty(B, T, H, D, dtype=torch.float32, device=dev)
     lse = torch.empty(B, T, H, dtype=torch.float32, device=dev) if with_lse else None

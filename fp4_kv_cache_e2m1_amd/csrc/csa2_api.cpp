@@ -286,7 +286,6 @@ csa2_status plan_layer(csa2_mode mode, const csa2_layer_args* a, const csa2_shar
   if (!attn_shape_ok(a->H, kv->D)) return CSA2_E_SHAPE;
   if (idx->K > kMaxK) return CSA2_E_SHAPE;
   const bool window = a->swa_codes != nullptr;
-  if (window && a->T != 1) return CSA2_E_UNSUPPORTED;            // the window branch is decode-only
   if (window && (a->swa_W < 0 || a->swa_W > kMaxSwaWindow)) return CSA2_E_SHAPE;
   *p = LayerPlan{};
   p->rows = (int64_t)kv->B * a->T;
@@ -330,8 +329,10 @@ csa2_status plan_layer(csa2_mode mode, const csa2_layer_args* a, const csa2_shar
       sel = std::max(sel, csa2_hier_pool_workspace_size(rows_c, p->n_blocks, a->pool_blocks));
     if (p->build_pool && idx->P > 0 && idx->K > 0)  // Top-K taken from the pool's positions
       sel = std::max(sel, csa2_topk_workspace_size(rows_c, idx->P, idx->K));
-    if (window)
+    if (window && a->T == 1)
       attn = std::max(attn, csa2_sparse_attn_swa_workspace_size(b1 - b0, a->H, kv->D, idx->K));
+    else if (window)
+      attn = std::max(attn, csa2_sparse_attn_swa_prefill_workspace_size(b1 - b0, a->T, a->H, kv->D, idx->K));
     else if (idx->K > 0)
       attn = std::max(attn, csa2_sparse_attn_workspace_size(b1 - b0, a->T, a->H, kv->D, idx->K));
   }
@@ -429,6 +430,14 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_share
           if (e != hipSuccess) return CSA2_E_HIP;
         }
       }
+    }
+    if (a->swa_codes && T > 1) {
+      const int64_t wrows = (int64_t)T + a->swa_W - 1;               // window buffer rows per sequence
+      return csa2_sparse_attn_swa_prefill(a->q + r0 * a->H * kv->D, kv->rows + (int64_t)b0 * kv->n_max * rb,
+                                          kv->n_max, idx->topk + r0 * idx->K, nb, T, a->H, kv->D, idx->K,
+                                          a->swa_codes + (int64_t)b0 * wrows * kv->D, a->swa_exp + (int64_t)b0 * wrows,
+                                          a->swa_n + r0, a->swa_W, a->sm_scale, a->out + r0 * a->H * kv->D,
+                                          a->lse ? a->lse + r0 * a->H : nullptr, attn_ws, attn_bytes, s_sel);
     }
     if (a->swa_codes)
       return csa2_sparse_attn_swa(a->q + r0 * a->H * kv->D, kv->rows + (int64_t)b0 * kv->n_max * rb, kv->n_max,

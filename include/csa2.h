@@ -318,11 +318,13 @@ typedef struct {
   float* lse;              /* [B, T, H] fp32 or NULL */
   void* ws;
   size_t ws_bytes;
-  /* The layer's sliding window (decode, T = 1), joined to the selected entries as one softmax
-   * as in csa2_sparse_attn_swa. swa_codes NULL: no window (a zero-initialized struct has none). */
-  const uint8_t* swa_codes; /* [B, swa_W, D] OCP E4M3 codes (16-byte aligned) */
-  const int8_t* swa_exp;    /* [B, swa_W] row exponents in [-15, 7] */
-  const int32_t* swa_n;     /* [B] window rows per sequence (device), clamped to [0, swa_W] */
+  /* The layer's sliding window, joined to the selected entries as one softmax: as
+   * csa2_sparse_attn_swa when T == 1, as csa2_sparse_attn_swa_prefill when T > 1 (the buffer then
+   * holds T + swa_W - 1 rows per sequence and swa_n one count per query row).
+   * swa_codes NULL: no window (a zero-initialized struct has none). */
+  const uint8_t* swa_codes; /* [B, swa_W, D] (T == 1) or [B, T + swa_W - 1, D] E4M3 codes */
+  const int8_t* swa_exp;    /* [B, swa_W] or [B, T + swa_W - 1] row exponents in [-15, 7] */
+  const int32_t* swa_n;     /* [B] or [B*T] window rows (device), clamped to [0, swa_W] */
   int32_t swa_W;            /* rows reserved per sequence, <= 128 */
   const uint8_t* q_idx_mx;  /* [B*T, Hi*Di/2 + Hi*Di/32] MXFP4 indexer query, with shared_kv.k_mx */
 } csa2_layer_args;

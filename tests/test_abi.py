@@ -207,9 +207,12 @@ def test_layer_step_window_rules(L):
     a.swa_exp = None                                                # exponents missing
     kv.valid, idx.topk_valid = 1, 1
     assert L.csa2_layer_step(2, C.byref(a), C.byref(kv), C.byref(idx), None) == E_ARG
-    a2, kv2, idx2 = _layer(T=2)
+    a2, kv2, idx2 = _layer(T=2)                                     # prefill: the prefill window sizing
+    assert L.csa2_layer_workspace_size(0, C.byref(a2), C.byref(kv2), C.byref(idx2), C.byref(n)) == OK
+    plain2 = n.value
     a2.swa_codes, a2.swa_exp, a2.swa_n, a2.swa_W = FAKE, FAKE, FAKE, 128
-    assert L.csa2_layer_workspace_size(0, C.byref(a2), C.byref(kv2), C.byref(idx2), C.byref(n)) == E_UNSUP
+    assert L.csa2_layer_workspace_size(0, C.byref(a2), C.byref(kv2), C.byref(idx2), C.byref(n)) == OK
+    assert n.value > plain2
 
 
 def test_layer_step_fp4_indexer_rules(L):

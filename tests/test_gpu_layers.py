@@ -329,3 +329,38 @@ def test_layer_stack_fp4_indexer(name):
     res, kv, idx = run_stack_gpu(wl, rows, None, mx=mx)
     assert kv.valid and idx.c.topk_valid
     verify(wl, res, range(wl.B), rows, mx=mx)
+
+
+def test_prefill_layer_with_window():
+    """A prefill Full layer with each token's window (partial windows at the sequence start): the
+    selection equals the windowless layer's, the output is the prefill window entry point's on
+    that selection, and sampled query rows match the oracle on its own selection."""
+    wl = SMALL["prefill"]
+    Wn = 128
+    rows, kidx = kv_rows_device(wl), k_idx_device(wl)
+    n_vis = torch.clamp(P.prefill_n_vis(wl.p0, wl.T, wl.ratio, "cuda"), max=wl.N).repeat(wl.B)
+    g = np.random.default_rng(43)
+    codes, exps = O.quantize_swa_fp8(g.standard_normal((wl.B * (wl.T + Wn - 1), wl.D)).astype(np.float32))
+    codes, exps = codes.reshape(wl.B, wl.T + Wn - 1, wl.D), exps.reshape(wl.B, wl.T + Wn - 1)
+    p_start = 40                                   # the window buffer starts at the sequence start
+    n_win = np.array([[min(Wn, p_start + t + 1) for t in range(wl.T)] for _ in range(wl.B)], np.int32)
+    cd, ed, nd = (torch.from_numpy(x).cuda() for x in (codes, exps, n_win))
+    q, qi = q_device(wl, 0, "q"), q_device(wl, 0, "q_idx")
+    kv, idx = P.KVState(rows, kidx, n_vis), P.IdxState.empty(wl.B * wl.T, wl.k, "cuda")
+    out, lse = P.layer_step(P.FULL, q, kv, idx, q_idx=qi, window=(cd, ed, nd))
+    kv0, idx0 = P.KVState(rows, kidx, n_vis), P.IdxState.empty(wl.B * wl.T, wl.k, "cuda")
+    P.layer_step(P.FULL, q, kv0, idx0, q_idx=qi)
+    topk = _np(idx.topk).copy()
+    assert np.array_equal(topk, _np(idx0.topk))
+    o2, l2 = P.sparse_attn_swa_prefill(q, rows, idx.topk.view(wl.B, wl.T, wl.k), cd, ed, nd, wl.sm_scale)
+    assert torch.equal(out, o2) and torch.equal(lse, l2)
+    out, lse = _np(out), _np(lse)
+    tr = np.array([0, 1, 77, wl.T - 1])
+    ora, src = oracle_sequence(wl, 0, tr)
+    kvd = O.dequant_kv_fp4(O.quantize_kv_fp4(src))
+    win = O.prefill_windows(O.dequant_swa_fp8(codes[0], exps[0]), n_win[0], Wn)[tr]
+    lay = ora[0]
+    ref, lref = O.sparse_attn_swa(lay["q"], kvd, lay["topk"], win, n_win[0][tr], wl.sm_scale)
+    for i, t in enumerate(tr):
+        if compare_topk(topk[t], lay["topk"][i], lambda p, i=i: lay["scores"][i, p], f"prefill window t={t}"):
+            check_attn(out[0, t], ref[i], lse[0, t], lref[i], f"prefill window t={t}")
