@@ -1381,9 +1381,11 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* rows, int n_max,
   return hipGetLastError();
 }
 
-// The window's share of the combine pass: one slot per kDKC * kDNG window rows.
+// The window's share of the combine pass: one slot per kDKC * kDNG window rows, or, when that
+// grid would leave CUs idle (few sequences), one slot per kDKC rows for a one-sub-group form of
+// the window kernel (256 lanes, half the LDS, so two workgroups share a CU).
 constexpr int kSwaRowsPerSplit = kDKC * kDNG;
-constexpr int kMaxSwaSplits = 2;                 // windows of up to 128 rows
+constexpr int kMaxSwaSplits = 4;                 // windows of up to 128 rows, 32 rows per slot
 
 // Splits of the selected entries when the window joins them (decode form at any batch): as the
 // decode form's own count, leaving kMaxSwaSplits slots of the combine pass to the window.
@@ -1419,7 +1421,8 @@ hipError_t launch_sparse_attn_swa(const uint16_t* q, const uint8_t* rows, int n_
   if (B == 0 || H == 0) return hipSuccess;
   int kps = kDKC;
   const int n_sp = swa_sparse_splits(B, H, K, &kps);
-  const int n_ws = (W + kSwaRowsPerSplit - 1) / kSwaRowsPerSplit;     // 0 .. kMaxSwaSplits
+  const int n_ws = (W + kSwaRowsPerSplit - 1) / kSwaRowsPerSplit;     // 0 .. 2 with 64-row slots
+  int n_used = 0;                                                       // window slots written
   const int64_t rows_h = (int64_t)B * H;
   float* part_o = static_cast<float*>(ws);
   float* part_ml = part_o + (size_t)(n_sp + kMaxSwaSplits) * rows_h * kD;
@@ -1432,24 +1435,35 @@ hipError_t launch_sparse_attn_swa(const uint16_t* q, const uint8_t* rows, int n_
     if (e != hipSuccess) return e;
   }
   if (n_ws > 0) {
-    const int per_xcd = (int)(((int64_t)B * n_ws * n_hg + 7) / 8);
-    hipLaunchKernelGGL((swa_attn_kernel<kDKC, kDPF, kDNG>), dim3((unsigned)(8 * per_xcd)), dim3(256 * kDNG), 0, s,
-                       q, swa_codes, swa_exp, n_win, 1, W, H, kSwaRowsPerSplit, sm_scale, part_o, part_ml, n_sp, B, n_ws,
-                       per_xcd);
+    // few sequences: 32-row slots and the one-sub-group kernel (19.2 -> 17.6 us per call at 4
+    // sequences x 64 heads x 128 rows; at 32 sequences the two-sub-group form is faster)
+    const bool small = (int64_t)B * n_ws * n_hg < 256;
+    const int ws_n = small ? (W + kDKC - 1) / kDKC : n_ws;
+    const int per_xcd = (int)(((int64_t)B * ws_n * n_hg + 7) / 8);
+    if (small)
+      hipLaunchKernelGGL((swa_attn_kernel<kDKC, kDPF, 1>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s,
+                         q, swa_codes, swa_exp, n_win, 1, W, H, kDKC, sm_scale, part_o, part_ml, n_sp, B, ws_n,
+                         per_xcd);
+    else
+      hipLaunchKernelGGL((swa_attn_kernel<kDKC, kDPF, kDNG>), dim3((unsigned)(8 * per_xcd)), dim3(256 * kDNG), 0, s,
+                         q, swa_codes, swa_exp, n_win, 1, W, H, kSwaRowsPerSplit, sm_scale, part_o, part_ml, n_sp, B,
+                         n_ws, per_xcd);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    n_used = ws_n;
   }
   const int per_xcd = (int)(((rows_h + 3) / 4 + 7) / 8);
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, part_o, part_ml,
-                     n_sp + n_ws, rows_h, out, lse, per_xcd, nullptr);
+                     n_sp + n_used, rows_h, out, lse, per_xcd, nullptr);
   return hipGetLastError();
 }
 
 // Prefill with the window: slot 0 of the split buffers takes the sparse attention's normalized
-// output (its log-sum-exp alongside), slots 1 .. the window's partials; one combine pass.
+// output (its log-sum-exp alongside), slot 1 the window's partials; one combine pass.
+constexpr int kSwaPrefillSlots = 2;
 size_t attn_swa_prefill_workspace(int B, int T, int H, int D, int K) {
   const size_t rows_h = (size_t)B * T * H;
-  const size_t slots = 1 + kMaxSwaSplits;
+  const size_t slots = kSwaPrefillSlots;
   const size_t parts = ((slots * rows_h * (size_t)D * 4 + slots * rows_h * 8 + rows_h * 4) + 255) & ~(size_t)255;
   return parts + (K > 0 ? attn_workspace(B, T, H, D, K) : 0) + 256;
 }
@@ -1460,7 +1474,7 @@ hipError_t launch_sparse_attn_swa_prefill(const uint16_t* q, const uint8_t* rows
                                           float* out, float* lse, void* ws, hipStream_t s) {
   if (B == 0 || T == 0 || H == 0) return hipSuccess;
   const int64_t nq = (int64_t)B * T, rows_h = nq * H;
-  const size_t slots = 1 + kMaxSwaSplits;
+  const size_t slots = kSwaPrefillSlots;
   float* part_o = static_cast<float*>(ws);
   float* part_ml = part_o + slots * (size_t)rows_h * kD;
   float* lse_s = part_ml + 2 * slots * (size_t)rows_h;

@@ -240,7 +240,7 @@ def test_sparse_attn_swa_prefill_validation(L):
     assert f(FAKE, FAKE, 10, FAKE, 1, 4, 64, 512, 8, FAKE, FAKE, None, 128, 1.0, FAKE, None, FAKE, 1 << 30,
              None) == E_ARG
     need = L.csa2_sparse_attn_swa_prefill_workspace_size(1, 600, 64, 512, 64)
-    assert need >= 3 * 600 * 64 * 512 * 4
+    assert need >= 2 * 600 * 64 * 512 * 4                          # the sparse slot and one window slot
     assert f(FAKE, FAKE, 10, FAKE, 1, 600, 64, 512, 64, FAKE, FAKE, FAKE, 128, 1.0, FAKE, None, FAKE, need - 1,
              None) == E_WS
     assert f(FAKE, FAKE, 10, FAKE, 1, 600, 64, 512, 64, FAKE, FAKE, FAKE, 128, 1.0, FAKE, None, FAKE + 16, need,
