@@ -27,6 +27,7 @@ EXPORTS = [
     "csa2_quantize_kv_fp4",
     "csa2_dequant_kv_fp4",
     "csa2_index_scores",
+    "csa2_prefill_visibility",
     "csa2_topk_workspace_size",
     "csa2_topk",
     "csa2_hier_pool_workspace_size",
@@ -80,6 +81,7 @@ def _declare(lib):
         "csa2_quantize_kv_fp4": (i32, [vp, i32, i64, i32, vp, vp]),
         "csa2_dequant_kv_fp4": (i32, [vp, i64, i32, vp, vp]),
         "csa2_index_scores": (i32, [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, i32, vp, vp, i32, vp]),
+        "csa2_prefill_visibility": (i32, [vp, i32, i32, i32, i32, vp, vp]),
         "csa2_topk_workspace_size": (sz, [i64, i32, i32]),
         "csa2_topk": (i32, [vp, i64, i32, vp, vp, i32, vp, vp, sz, vp]),
         "csa2_hier_pool_workspace_size": (sz, [i64, i32, i32]),

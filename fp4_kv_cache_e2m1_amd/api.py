@@ -290,10 +290,16 @@ def sparse_attn_swa_prefill(q: torch.Tensor, rows: torch.Tensor, idx: torch.Tens
     return out, lse
 
 
-def prefill_n_vis(p0: int, T: int, ratio: int, device) -> torch.Tensor:
-    """Visible compressed entries for query tokens at positions p0..p0+T-1: floor((p+1)/ratio)."""
-    p = torch.arange(p0 + 1, p0 + T + 1, dtype=torch.int64)
-    return torch.div(p, ratio, rounding_mode="floor").to(torch.int32).to(device)
+def prefill_n_vis(p0, T: int, ratio: int, device, n_max: int = 2 ** 31 - 1) -> torch.Tensor:
+    """Visible compressed entries of query tokens at positions p0[b] .. p0[b]+T-1, from
+    csa2_prefill_visibility: int32 [B*T]. p0 is one start position or one per sequence."""
+    dev = torch.device(device)
+    starts = torch.as_tensor([p0] if isinstance(p0, int) else list(p0), dtype=torch.int64).to(dev)
+    B = starts.numel()
+    out = torch.empty(B * T, dtype=torch.int32, device=dev)
+    code = _lib.lib().csa2_prefill_visibility(_ptr(starts), B, T, ratio, n_max, _ptr(out), _stream(dev))
+    check("csa2_prefill_visibility", code)
+    return out
 
 
 # ---------------------------------------------------------------------------------------------

@@ -5,8 +5,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <cstdlib>
-#include <mutex>
 
 #include "../../include/csa2.h"
 #include "launch.h"
@@ -16,19 +14,10 @@ using namespace csa2;
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kPipelineChunks = 8;   // most chunks the pipeline may use
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
-int pipeline_chunks() {
-  static const int n = [] {
-    const char* e = std::getenv("CSA2_PIPELINE_CHUNKS");
-    const int v = e ? std::atoi(e) : 1;
-    return v < 1 ? 1 : (v > kPipelineChunks ? kPipelineChunks : v);
-  }();
-  return n;
-}
 csa2_status hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_E_HIP; }
 
 bool index_shape_ok(int32_t Hi, int32_t Hk, int32_t Di) {
@@ -38,43 +27,21 @@ bool index_shape_ok(int32_t Hi, int32_t Hk, int32_t Di) {
          (Hk == 1 ? Di <= 1024 && Hi * Di <= 8192 : Hi * Di <= 1024);
 }
 
+// The streaming kernel is instantiated for key rows of 64, 128, 256, 512 and 1024 channels; the
+// MFMA prefill kernel takes any per-head channel count that index_shape_ok admits.
+bool index_call_ok(int32_t T, int32_t Hi, int32_t Hk, int32_t Di, bool pool, bool bmax) {
+  if (!index_shape_ok(Hi, Hk, Di)) return false;
+  if (!pool && !bmax && index_prefill_supported(T, Hi, Hk, Di)) return true;
+  const int32_t c = Hk * Di;
+  return c == 64 || c == 128 || c == 256 || c == 512 || c == 1024;
+}
+
 constexpr int32_t kMaxSwaWindow = 128;   // window rows per sequence (n_win of the model)
 
 bool attn_shape_ok(int32_t H, int32_t D) { return D == 512 && H > 0 && H % 16 == 0 && (H <= 64 || H % 64 == 0); }
 
 constexpr int kMaxK = 4096;
 constexpr int64_t kMaxCols = 1 << 26;
-
-// Per-device auxiliary stream and events for the chunk pipeline of csa2_layer_step. Created on
-// first use and kept for the life of the process; a mutex serializes the enqueue sequences that
-// share them (the enqueue itself is short; the work runs asynchronously).
-struct AuxDevice {
-  bool ready = false;
-  hipStream_t aux = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  hipEvent_t chunk[kPipelineChunks] = {};
-};
-constexpr int kMaxDevices = 64;
-AuxDevice g_aux[kMaxDevices];
-std::mutex g_aux_mu;
-
-hipError_t aux_for_current_device(AuxDevice** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  AuxDevice& a = g_aux[dev];
-  if (!a.ready) {
-    if ((e = hipStreamCreateWithFlags(&a.aux, hipStreamNonBlocking)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&a.fork, hipEventDisableTiming)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&a.join, hipEventDisableTiming)) != hipSuccess) return e;
-    for (auto& ev : a.chunk)
-      if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return e;
-    a.ready = true;
-  }
-  *out = &a;
-  return hipSuccess;
-}
 
 }  // namespace
 
@@ -86,7 +53,7 @@ const char* csa2_status_string(csa2_status s) {
     case CSA2_E_ARG: return "invalid argument (null pointer, negative size or bad enum)";
     case CSA2_E_SHAPE: return "unsupported or inconsistent shape";
     case CSA2_E_STATE: return "shared state needed by this mode is not valid";
-    case CSA2_E_WORKSPACE: return "workspace missing or too small";
+    case CSA2_E_WORKSPACE: return "workspace missing, too small or misaligned";
     case CSA2_E_UNSUPPORTED: return "not supported by this library";
     case CSA2_E_HIP: return "HIP launch failed";
   }
@@ -116,7 +83,7 @@ csa2_status csa2_index_scores(const uint16_t* q_idx, const uint16_t* k_idx, int3
                               int32_t Hk, int32_t Di, int32_t n_max, const int32_t* n_vis, const int32_t* cand,
                               int32_t P, float* scores, float* block_max, int32_t block, void* stream) {
   if (B < 0 || T < 0 || n_max < 0 || (cand && P < 0)) return CSA2_E_ARG;
-  if (!index_shape_ok(Hi, Hk, Di)) return CSA2_E_SHAPE;
+  if (!index_call_ok(T, Hi, Hk, Di, cand != nullptr, block_max != nullptr)) return CSA2_E_SHAPE;
   if (block_max && (cand || block != 8)) return CSA2_E_UNSUPPORTED;
   const int64_t rows = (int64_t)B * T;
   const int32_t ncols = cand ? P : n_max;
@@ -129,6 +96,15 @@ csa2_status csa2_index_scores(const uint16_t* q_idx, const uint16_t* k_idx, int3
     return hip_status(launch_index_prefill(q_idx, k_idx, B, T, Hi, Di, n_max, n_vis, scores, s));
   return hip_status(launch_index_stream(q_idx, k_idx, B, T, Hi, Hk, Di, n_max, n_vis, cand, P, scores,
                                         block_max, s));
+}
+
+csa2_status csa2_prefill_visibility(const int64_t* p0, int32_t B, int32_t T, int32_t ratio, int32_t n_max,
+                                    int32_t* n_vis, void* stream) {
+  if (B < 0 || T < 0 || n_max < 0 || ratio <= 0) return CSA2_E_ARG;
+  if ((int64_t)B * T > INT32_MAX) return CSA2_E_SHAPE;
+  if (B == 0 || T == 0) return CSA2_OK;
+  if (!p0 || !n_vis) return CSA2_E_ARG;
+  return hip_status(launch_prefill_visibility(p0, B, T, ratio, n_max, n_vis, as_stream(stream)));
 }
 
 static bool mxfp4_shape_ok(int32_t Hi, int32_t Hk, int32_t Di) {
@@ -268,7 +244,6 @@ csa2_status csa2_sparse_attn_swa_prefill(const uint16_t* q, const uint8_t* rows,
 namespace {
 
 struct LayerPlan {
-  int nch;              // batch chunks pipelined across the caller's stream and the aux stream
   bool score;           // runs the indexer (Full / Reindex)
   bool on_pool;         // Reindex restricted to the candidate pool
   bool build_pool;      // Full with the hierarchical indexer
@@ -296,7 +271,7 @@ csa2_status plan_layer(csa2_mode mode, const csa2_layer_args* a, const csa2_shar
     if (kv->k_mx) {
       // FP4 (MXFP4) indexer keys
       if (!mxfp4_shape_ok(a->Hi, kv->Hk, kv->Di)) return CSA2_E_SHAPE;
-    } else if (!index_shape_ok(a->Hi, kv->Hk, kv->Di)) {
+    } else if (!index_call_ok(a->T, a->Hi, kv->Hk, kv->Di, p->on_pool, p->build_pool)) {
       return CSA2_E_SHAPE;
     }
     p->ncols = p->on_pool ? idx->P : kv->n_max;
@@ -309,32 +284,27 @@ csa2_status plan_layer(csa2_mode mode, const csa2_layer_args* a, const csa2_shar
     p->n_blocks = (kv->n_max + 7) / 8;
   }
   if (p->on_pool && (!idx->pool || idx->P <= 0)) return CSA2_E_SHAPE;
-  // Index-producing layers with several sequences may be pipelined over chunks of the batch
-  // (CSA2_PIPELINE_CHUNKS, default 1 = off: in eager mode a cross-stream wait costs ~11 us).
-  p->nch = (p->score && kv->B >= 2) ? std::min(kv->B, pipeline_chunks()) : 1;
   size_t off = 0;
   p->off_scores = off;
   if (p->score) off = align_up(off + (size_t)p->rows * p->ncols * 4);
   p->off_bmax = off;
   if (p->build_pool) off = align_up(off + (size_t)p->rows * p->n_blocks * 4);
   p->off_sel = off;
-  // scratch of the chunk-wise Top-K / pool / attention calls (they run one after another)
+  // scratch of the Top-K / pool / attention calls (they run one after another)
   size_t sel = 0, attn = 0;
-  for (int c = 0; c < p->nch; ++c) {
-    const int b0 = (int)((int64_t)kv->B * c / p->nch), b1 = (int)((int64_t)kv->B * (c + 1) / p->nch);
-    const int64_t rows_c = (int64_t)(b1 - b0) * a->T;
-    if (rows_c == 0) continue;
-    if (p->score && p->ncols > 0 && idx->K > 0) sel = std::max(sel, csa2_topk_workspace_size(rows_c, p->ncols, idx->K));
+  const int64_t rows = p->rows;
+  if (rows > 0) {
+    if (p->score && p->ncols > 0 && idx->K > 0) sel = std::max(sel, csa2_topk_workspace_size(rows, p->ncols, idx->K));
     if (p->build_pool && p->n_blocks > 0)
-      sel = std::max(sel, csa2_hier_pool_workspace_size(rows_c, p->n_blocks, a->pool_blocks));
+      sel = std::max(sel, csa2_hier_pool_workspace_size(rows, p->n_blocks, a->pool_blocks));
     if (p->build_pool && idx->P > 0 && idx->K > 0)  // Top-K taken from the pool's positions
-      sel = std::max(sel, csa2_topk_workspace_size(rows_c, idx->P, idx->K));
+      sel = std::max(sel, csa2_topk_workspace_size(rows, idx->P, idx->K));
     if (window && a->T == 1)
-      attn = std::max(attn, csa2_sparse_attn_swa_workspace_size(b1 - b0, a->H, kv->D, idx->K));
+      attn = csa2_sparse_attn_swa_workspace_size(kv->B, a->H, kv->D, idx->K);
     else if (window)
-      attn = std::max(attn, csa2_sparse_attn_swa_prefill_workspace_size(b1 - b0, a->T, a->H, kv->D, idx->K));
+      attn = csa2_sparse_attn_swa_prefill_workspace_size(kv->B, a->T, a->H, kv->D, idx->K);
     else if (idx->K > 0)
-      attn = std::max(attn, csa2_sparse_attn_workspace_size(b1 - b0, a->T, a->H, kv->D, idx->K));
+      attn = csa2_sparse_attn_workspace_size(kv->B, a->T, a->H, kv->D, idx->K);
   }
   off = align_up(off + sel);
   p->off_attn = off;
@@ -365,7 +335,8 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_share
   if (!a->out || !idx->topk || !kv->rows || !a->q) return CSA2_E_ARG;
   if (p.score && (kv->k_mx ? !a->q_idx_mx : (!a->q_idx || !kv->k_idx))) return CSA2_E_ARG;
   if (a->swa_codes && (!a->swa_exp || !a->swa_n)) return CSA2_E_ARG;
-  if (p.total > 0 && (!a->ws || a->ws_bytes < p.total)) return CSA2_E_WORKSPACE;
+  if (p.total > 0 && (!a->ws || a->ws_bytes < p.total || reinterpret_cast<uintptr_t>(a->ws) % kAlign))
+    return CSA2_E_WORKSPACE;
 
   uint8_t* ws = static_cast<uint8_t*>(a->ws);
   float* scores = reinterpret_cast<float*>(ws + p.off_scores);
@@ -375,100 +346,56 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_share
   const size_t sel_bytes = p.off_attn - p.off_sel;
   const size_t attn_bytes = p.total - p.off_attn;
   const int T = a->T;
-  const int64_t kbytes_row = (int64_t)kv->Hk * kv->Di;          // bf16 elements per key row
-  const int64_t rb = CSA2_ROW_BYTES(kv->D);
 
-  // One chunk of whole sequences [b0, b1): scores on `s_idx`, then (after the event) Top-K,
-  // pool and attention on `s_sel`.
-  auto run_chunk = [&](int b0, int b1, void* s_idx, void* s_sel, hipEvent_t ev, hipStream_t aux) -> csa2_status {
-    const int nb = b1 - b0;
-    const int64_t r0 = (int64_t)b0 * T, rows_c = (int64_t)nb * T;
-    const int32_t* n_vis_c = kv->n_vis ? kv->n_vis + r0 : nullptr;
-    int32_t* pool_c = idx->pool ? idx->pool + r0 * idx->P : nullptr;
-    float* scores_c = scores + r0 * p.ncols;
-    csa2_status s2 = CSA2_OK;
-    if (p.score) {
-      if (kv->k_mx) {
-        const int64_t kc = (int64_t)kv->Hk * kv->Di, qc = (int64_t)a->Hi * kv->Di;   // channels per row
-        const int64_t krb = kc / 2 + kc / 32, qrb = qc / 2 + qc / 32;                // bytes per MXFP4 row
-        s2 = csa2_index_scores_mxfp4(a->q_idx_mx + r0 * qrb, kv->k_mx + (int64_t)b0 * kv->n_max * krb, nb, T, a->Hi,
-                                     kv->Hk, kv->Di, kv->n_max, n_vis_c, p.on_pool ? pool_c : nullptr,
-                                     p.on_pool ? idx->P : 0, scores_c, bmax ? bmax + r0 * p.n_blocks : nullptr, 8,
-                                     s_idx);
-      } else {
-        s2 = csa2_index_scores(a->q_idx + r0 * a->Hi * kv->Di, kv->k_idx + (int64_t)b0 * kv->n_max * kbytes_row,
-                               nb, T, a->Hi, kv->Hk, kv->Di, kv->n_max, n_vis_c, p.on_pool ? pool_c : nullptr,
-                               p.on_pool ? idx->P : 0, scores_c, bmax ? bmax + r0 * p.n_blocks : nullptr, 8, s_idx);
-      }
-      if (s2 != CSA2_OK) return s2;
-      if (ev) {
-        if (hipEventRecord(ev, as_stream(s_idx)) != hipSuccess) return CSA2_E_HIP;
-        if (hipStreamWaitEvent(aux, ev, 0) != hipSuccess) return CSA2_E_HIP;
-      }
-      if (p.build_pool && a->pool_blocks >= idx->K) {
-        // The pool of the best pool_blocks >= K blocks holds the layer's own flat Top-K: each Top-K
-        // position's block max is at least its score, so a block left out would be outranked by
-        // >= K block maxima. The pool is chosen first and the Top-K taken from its positions.
-        hipError_t e = launch_pool_topk(bmax + r0 * p.n_blocks, rows_c, p.n_blocks, n_vis_c, a->pool_blocks, pool_c,
-                                        scores_c, p.ncols, idx->K, idx->topk + r0 * idx->K, as_stream(s_sel));
-        if (e == hipErrorNotSupported) {
-          (void)hipGetLastError();
-          e = launch_topk(bmax + r0 * p.n_blocks, rows_c, p.n_blocks, n_vis_c, 8, nullptr, a->pool_blocks, pool_c, 8,
-                          n_vis_c, kv->n_max, sel_ws, as_stream(s_sel));
-          if (e != hipSuccess) return CSA2_E_HIP;
-          e = launch_topk_gather(scores_c, p.ncols, rows_c, pool_c, idx->P, idx->K, idx->topk + r0 * idx->K, sel_ws,
-                                 as_stream(s_sel));
-        }
+  hipStream_t hs = as_stream(stream);
+  const int B = kv->B;
+  const int64_t rows = p.rows;
+  const int32_t* n_vis = kv->n_vis;
+  int32_t* pool = idx->pool;
+  if (p.score) {
+    if (kv->k_mx) {
+      st = csa2_index_scores_mxfp4(a->q_idx_mx, kv->k_mx, B, T, a->Hi, kv->Hk, kv->Di, kv->n_max, n_vis,
+                                   p.on_pool ? pool : nullptr, p.on_pool ? idx->P : 0, scores, bmax, 8, stream);
+    } else {
+      st = csa2_index_scores(a->q_idx, kv->k_idx, B, T, a->Hi, kv->Hk, kv->Di, kv->n_max, n_vis,
+                             p.on_pool ? pool : nullptr, p.on_pool ? idx->P : 0, scores, bmax, 8, stream);
+    }
+    if (st != CSA2_OK) return st;
+    if (p.build_pool && a->pool_blocks >= idx->K) {
+      // The pool of the best pool_blocks >= K blocks holds the layer's own flat Top-K: each Top-K
+      // position's block max is at least its score, so a block left out would be outranked by
+      // >= K block maxima. The pool is chosen first and the Top-K taken from its positions.
+      hipError_t e = launch_pool_topk(bmax, rows, p.n_blocks, n_vis, a->pool_blocks, pool, scores, p.ncols, idx->K,
+                                      idx->topk, hs);
+      if (e == hipErrorNotSupported) {
+        (void)hipGetLastError();
+        e = launch_topk(bmax, rows, p.n_blocks, n_vis, 8, nullptr, a->pool_blocks, pool, 8, n_vis, kv->n_max, sel_ws,
+                        hs);
         if (e != hipSuccess) return CSA2_E_HIP;
-      } else {
-        s2 = csa2_topk(scores_c, rows_c, p.ncols, p.on_pool ? nullptr : n_vis_c, p.on_pool ? pool_c : nullptr,
-                       idx->K, idx->topk + r0 * idx->K, sel_ws, sel_bytes, s_sel);
-        if (s2 != CSA2_OK) return s2;
-        if (p.build_pool && a->pool_blocks > 0) {
-          const hipError_t e = launch_topk(bmax + r0 * p.n_blocks, rows_c, p.n_blocks, n_vis_c, 8, nullptr,
-                                           a->pool_blocks, pool_c, 8, n_vis_c, kv->n_max, sel_ws, as_stream(s_sel));
-          if (e != hipSuccess) return CSA2_E_HIP;
-        }
+        e = launch_topk_gather(scores, p.ncols, rows, pool, idx->P, idx->K, idx->topk, sel_ws, hs);
+      }
+      if (e != hipSuccess) return CSA2_E_HIP;
+    } else {
+      st = csa2_topk(scores, rows, p.ncols, p.on_pool ? nullptr : n_vis, p.on_pool ? pool : nullptr, idx->K, idx->topk,
+                     sel_ws, sel_bytes, stream);
+      if (st != CSA2_OK) return st;
+      if (p.build_pool && a->pool_blocks > 0) {
+        const hipError_t e = launch_topk(bmax, rows, p.n_blocks, n_vis, 8, nullptr, a->pool_blocks, pool, 8, n_vis,
+                                         kv->n_max, sel_ws, hs);
+        if (e != hipSuccess) return CSA2_E_HIP;
       }
     }
-    if (a->swa_codes && T > 1) {
-      const int64_t wrows = (int64_t)T + a->swa_W - 1;               // window buffer rows per sequence
-      return csa2_sparse_attn_swa_prefill(a->q + r0 * a->H * kv->D, kv->rows + (int64_t)b0 * kv->n_max * rb,
-                                          kv->n_max, idx->topk + r0 * idx->K, nb, T, a->H, kv->D, idx->K,
-                                          a->swa_codes + (int64_t)b0 * wrows * kv->D, a->swa_exp + (int64_t)b0 * wrows,
-                                          a->swa_n + r0, a->swa_W, a->sm_scale, a->out + r0 * a->H * kv->D,
-                                          a->lse ? a->lse + r0 * a->H : nullptr, attn_ws, attn_bytes, s_sel);
-    }
-    if (a->swa_codes)
-      return csa2_sparse_attn_swa(a->q + r0 * a->H * kv->D, kv->rows + (int64_t)b0 * kv->n_max * rb, kv->n_max,
-                                  idx->topk + r0 * idx->K, nb, a->H, kv->D, idx->K,
-                                  a->swa_codes + (int64_t)b0 * a->swa_W * kv->D, a->swa_exp + (int64_t)b0 * a->swa_W,
-                                  a->swa_n + b0, a->swa_W, a->sm_scale, a->out + r0 * a->H * kv->D,
-                                  a->lse ? a->lse + r0 * a->H : nullptr, attn_ws, attn_bytes, s_sel);
-    return csa2_sparse_attn(a->q + r0 * a->H * kv->D, kv->rows + (int64_t)b0 * kv->n_max * rb, kv->n_max,
-                            idx->topk + r0 * idx->K, nb, T, a->H, kv->D, idx->K, a->sm_scale,
-                            a->out + r0 * a->H * kv->D, a->lse ? a->lse + r0 * a->H : nullptr, attn_ws, attn_bytes,
-                            s_sel);
-  };
-
-  if (p.nch <= 1) {
-    st = run_chunk(0, kv->B, stream, stream, nullptr, nullptr);
-  } else {
-    std::lock_guard<std::mutex> lock(g_aux_mu);
-    AuxDevice* ad = nullptr;
-    if (aux_for_current_device(&ad) != hipSuccess) return CSA2_E_HIP;
-    hipStream_t s = as_stream(stream);
-    // the aux stream starts after everything already queued on the caller's stream
-    if (hipEventRecord(ad->fork, s) != hipSuccess || hipStreamWaitEvent(ad->aux, ad->fork, 0) != hipSuccess)
-      return CSA2_E_HIP;
-    for (int c = 0; c < p.nch && st == CSA2_OK; ++c) {
-      const int b0 = (int)((int64_t)kv->B * c / p.nch), b1 = (int)((int64_t)kv->B * (c + 1) / p.nch);
-      if (b1 > b0) st = run_chunk(b0, b1, stream, ad->aux, ad->chunk[c], ad->aux);
-    }
-    // join: the caller's stream continues after the last chunk's attention
-    if (hipEventRecord(ad->join, ad->aux) != hipSuccess || hipStreamWaitEvent(s, ad->join, 0) != hipSuccess)
-      return CSA2_E_HIP;
   }
+  if (a->swa_codes && T > 1)
+    st = csa2_sparse_attn_swa_prefill(a->q, kv->rows, kv->n_max, idx->topk, B, T, a->H, kv->D, idx->K, a->swa_codes,
+                                      a->swa_exp, a->swa_n, a->swa_W, a->sm_scale, a->out, a->lse, attn_ws, attn_bytes,
+                                      stream);
+  else if (a->swa_codes)
+    st = csa2_sparse_attn_swa(a->q, kv->rows, kv->n_max, idx->topk, B, a->H, kv->D, idx->K, a->swa_codes, a->swa_exp,
+                              a->swa_n, a->swa_W, a->sm_scale, a->out, a->lse, attn_ws, attn_bytes, stream);
+  else
+    st = csa2_sparse_attn(a->q, kv->rows, kv->n_max, idx->topk, B, T, a->H, kv->D, idx->K, a->sm_scale, a->out,
+                          a->lse, attn_ws, attn_bytes, stream);
   if (st != CSA2_OK) return st;
   if (p.score) idx->topk_valid = 1;
   if (p.build_pool) idx->pool_valid = 1;

@@ -338,6 +338,27 @@ hipError_t launch_prefill_qs(const uint16_t* q, const uint16_t* k, int B, int T,
 }
 }  // namespace
 
+// Causal visibility of the compressed entries for a chunk of query tokens: the query at absolute
+// position p sees entry n once the entry's last source token is at or before p, i.e. n < (p+1) / ratio
+// (floor), capped at n_max. One thread per query row.
+__global__ void prefill_visibility_kernel(const int64_t* __restrict__ p0, int T, int ratio, int n_max,
+                                          int64_t rows, int32_t* __restrict__ n_vis) {
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= rows) return;
+  const int64_t pos = p0[r / T] + r % T;
+  const int64_t v = (pos + 1) / ratio;
+  n_vis[r] = (int32_t)(v < 0 ? 0 : (v > n_max ? n_max : v));
+}
+
+hipError_t launch_prefill_visibility(const int64_t* p0, int B, int T, int ratio, int n_max, int32_t* n_vis,
+                                     hipStream_t s) {
+  const int64_t rows = (int64_t)B * T;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(prefill_visibility_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, p0, T, ratio,
+                     n_max, rows, n_vis);
+  return hipGetLastError();
+}
+
 bool index_prefill_supported(int T, int Hi, int Hk, int Di) {
   return T >= 16 && Hk == Hi && (Hi * Di) % 64 == 0;
 }

@@ -31,6 +31,8 @@ hipError_t launch_index_mxfp4(const uint8_t* q, const uint8_t* k, int B, int T, 
 bool index_prefill_supported(int T, int Hi, int Hk, int Di);
 hipError_t launch_index_prefill(const uint16_t* q, const uint16_t* k, int B, int T, int Hi, int Di,
                                 int n_max, const int32_t* n_vis, float* scores, hipStream_t s);
+hipError_t launch_prefill_visibility(const int64_t* p0, int B, int T, int ratio, int n_max, int32_t* n_vis,
+                                     hipStream_t s);
 
 // topk.hip
 size_t topk_workspace(int64_t rows, int n_cols, int k);

@@ -627,7 +627,7 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
 template <int KC, int PF, int NG>
 __global__ __launch_bounds__(256 * NG) void swa_attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ swa_codes, const int8_t* __restrict__ swa_exp,
-    const int32_t* __restrict__ n_win, int T, int W, int H, int rows_per_split, float sm_scale,
+    const int32_t* __restrict__ n_win, int T, int prefill, int W, int H, int rows_per_split, float sm_scale,
     float* __restrict__ part_o, float* __restrict__ part_ml, int slot0, int n_rows, int n_wsplits, int per_xcd) {
   using Sm = DecodeSmem<KC, NG>;
   constexpr int NS = KC / 16;                  // NS entry steps of 16 per chunk
@@ -654,11 +654,12 @@ __global__ __launch_bounds__(256 * NG) void swa_attn_kernel(
   uint16_t* xs = reinterpret_cast<uint16_t*>(gbase);
   float4* sp4b = reinterpret_cast<float4*>(gbase + Sm::kX);
 
-  // decode (T == 1): rows 0 .. n-1 of the sequence's W-row window, n = n_win[b]; prefill (T > 1):
-  // the sequence's buffer holds T + W - 1 rows and query t takes rows t + W - n .. t + W - 1,
-  // n = n_win[query row] (its last n tokens up to its own)
-  const int n_valid = max(0, min(n_win[T == 1 ? b : qr], W));        // window rows of this query
-  const int64_t row0 = T == 1 ? (int64_t)b * W : (int64_t)b * (T + W - 1) + (qr - b * T) + (W - n_valid);
+  // decode layout (prefill == 0, T == 1): rows 0 .. n-1 of the sequence's W-row window,
+  // n = n_win[b]; prefill layout (any T, including 1): the sequence's buffer holds T + W - 1 rows
+  // and query t takes rows t + W - n .. t + W - 1, n = n_win[query row] (its last n tokens up to
+  // its own)
+  const int n_valid = max(0, min(n_win[prefill ? qr : b], W));        // window rows of this query
+  const int64_t row0 = prefill ? (int64_t)b * (T + W - 1) + (qr - b * T) + (W - n_valid) : (int64_t)b * W;
   const int kbeg = wsplit * rows_per_split;
   const int nk = max(0, min(n_valid, kbeg + rows_per_split) - kbeg);  // rows of this workgroup
   const int sub_len = ((nk + NG - 1) / NG + KC - 1) / KC * KC;          // entries per sub-group
@@ -1442,11 +1443,11 @@ hipError_t launch_sparse_attn_swa(const uint16_t* q, const uint8_t* rows, int n_
     const int per_xcd = (int)(((int64_t)B * ws_n * n_hg + 7) / 8);
     if (small)
       hipLaunchKernelGGL((swa_attn_kernel<kDKC, kDPF, 1>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s,
-                         q, swa_codes, swa_exp, n_win, 1, W, H, kDKC, sm_scale, part_o, part_ml, n_sp, B, ws_n,
+                         q, swa_codes, swa_exp, n_win, 1, 0, W, H, kDKC, sm_scale, part_o, part_ml, n_sp, B, ws_n,
                          per_xcd);
     else
       hipLaunchKernelGGL((swa_attn_kernel<kDKC, kDPF, kDNG>), dim3((unsigned)(8 * per_xcd)), dim3(256 * kDNG), 0, s,
-                         q, swa_codes, swa_exp, n_win, 1, W, H, kSwaRowsPerSplit, sm_scale, part_o, part_ml, n_sp, B,
+                         q, swa_codes, swa_exp, n_win, 1, 0, W, H, kSwaRowsPerSplit, sm_scale, part_o, part_ml, n_sp, B,
                          n_ws, per_xcd);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1493,7 +1494,7 @@ hipError_t launch_sparse_attn_swa_prefill(const uint16_t* q, const uint8_t* rows
   if (n_ws > 0) {
     const int per_xcd = (int)((nq * n_ws * n_hg + 7) / 8);
     hipLaunchKernelGGL((swa_attn_kernel<kDKC, kDPF, kDNG>), dim3((unsigned)(8 * per_xcd)), dim3(256 * kDNG), 0, s,
-                       q, swa_codes, swa_exp, n_win, T, W, H, rps, sm_scale, part_o, part_ml, n_sp,
+                       q, swa_codes, swa_exp, n_win, T, 1, W, H, rps, sm_scale, part_o, part_ml, n_sp,
                        (int)nq, n_ws, per_xcd);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

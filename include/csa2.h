@@ -42,7 +42,7 @@ typedef enum {
   CSA2_E_ARG = 1,          /* null pointer, negative size, bad enum */
   CSA2_E_SHAPE = 2,        /* unsupported or inconsistent shape */
   CSA2_E_STATE = 3,        /* Reindex/Reuse without the shared state they need */
-  CSA2_E_WORKSPACE = 4,    /* workspace missing or smaller than required */
+  CSA2_E_WORKSPACE = 4,    /* workspace missing, smaller than required or misaligned */
   CSA2_E_UNSUPPORTED = 5,  /* valid request the library does not implement */
   CSA2_E_HIP = 6           /* a HIP launch failed */
 } csa2_status;
@@ -101,17 +101,31 @@ csa2_status csa2_dequant_kv_fp4(const uint8_t* rows, int64_t n_rows, int32_t dim
  *           visible positions of each aligned block of `block` entries ([walkthrough]
  *           一(四)2, a block's score is the max index score inside it). Blocks with no visible
  *           position are left unwritten. block must be 8 when block_max is given.
- * Requires Hk in {1, Hi}, Di % 8 == 0, Hk*Di % 64 == 0, and Hi*Di <= 1024 when Hk == Hi, or
- * Di <= 1024 and Hi*Di <= 8192 when Hk == 1 (one shared key: the query heads are summed in fp32
- * first, so the score is (sum_h q_idx[r, h]) . k_idx[n, 0]).
- * Decode-shaped calls (T small, or pool mode) stream the keys once per query row; prefill
- * calls (T >= 16, flat mode, Hk == Hi, Hi*Di % 64 == 0) run as MFMA tiles with causal tile
- * skipping.
+ * Requires Hk in {1, Hi}, Di % 8 == 0, and Hi*Di <= 1024 when Hk == Hi, or Di <= 1024 and
+ * Hi*Di <= 8192 when Hk == 1 (one shared key: the query heads are summed in fp32 first, so the
+ * score is (sum_h q_idx[r, h]) . k_idx[n, 0]).
+ * Prefill calls (T >= 16, flat mode without block_max, Hk == Hi, Hi*Di % 64 == 0) run as MFMA
+ * tiles with causal tile skipping. Every other call streams the keys once per query row and
+ * needs a key row of Hk*Di in {64, 128, 256, 512, 1024} channels. Other shapes: CSA2_E_SHAPE.
  * ------------------------------------------------------------------------------------------ */
 csa2_status csa2_index_scores(const uint16_t* q_idx, const uint16_t* k_idx, int32_t B, int32_t T,
                               int32_t Hi, int32_t Hk, int32_t Di, int32_t n_max,
                               const int32_t* n_vis, const int32_t* cand, int32_t P,
                               float* scores, float* block_max, int32_t block, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * csa2_prefill_visibility - causal visibility of the compressed entries for a prefill chunk.
+ * [walkthrough] 一(四): a query scores only the compressed entries it may see. An entry
+ * compresses `ratio` consecutive tokens and becomes visible once its last source token is at or
+ * before the query's own position p, so the query sees entries n < floor((p + 1) / ratio).
+ *
+ * p0     [B] int64 (device): absolute position of the first query token of each sequence.
+ * n_vis  [B*T] int32 (device), written: n_vis[b*T + t] = min(n_max, floor((p0[b] + t + 1) / ratio)),
+ *        and 0 where that is negative. Feeds the n_vis argument of the indexer, Top-K and layer calls.
+ * ratio > 0; B, T, n_max >= 0 (B*T == 0 enqueues nothing).
+ * ------------------------------------------------------------------------------------------ */
+csa2_status csa2_prefill_visibility(const int64_t* p0, int32_t B, int32_t T, int32_t ratio, int32_t n_max,
+                                    int32_t* n_vis, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * csa2_index_scores_mxfp4 - the lightweight indexer over FP4 query and key rows.
@@ -192,8 +206,12 @@ csa2_status csa2_hier_pool(const float* block_max, int64_t rows, int32_t n_block
  * For each (b, t, h): l_j = sm_scale * q[b,t,h,:] . x_j over selected j, out = sum softmax(l)_j
  * x_j, lse = ln sum_j exp(l_j), with x_j the dequantized entry idx[b,t,j] of sequence b.
  * Indices < 0 or >= n_max are skipped; with nothing selected out = 0 and lse = -inf.
- * q K^T runs on bf16 MFMA (dequantized values are exact in bf16), softmax in fp32, P V on f16
- * MFMA (values exact in f16, probabilities rounded to f16), fp32 accumulation.
+ * q K^T and P V run on f16 MFMA with fp32 accumulation: dequantized entries are exact in f16
+ * (at most 6 significant bits, magnitudes 2^-10 .. 2688); each head's bf16 query is scaled by a
+ * power of two that puts its largest |q| in [2^14, 2^15) and then converted to f16, which is exact
+ * for every component within 2^31 of that largest one (smaller ones round to f16 subnormals, an
+ * error below 2^-24 of the head's largest |q|); the power of two is folded back into the softmax
+ * scale. Softmax in fp32; probabilities are rounded to f16 for P V.
  *
  * q     [B, T, H, D] bf16.        rows [B, n_max, D/2 + D/16] bytes (16-byte aligned base).
  * idx   [B, T, K] int32.          out  [B, T, H, D] fp32.   lse [B, T, H] fp32 or NULL.
@@ -217,7 +235,8 @@ csa2_status csa2_sparse_attn(const uint16_t* q, const uint8_t* rows, int32_t n_m
  *   window row value = E4M3(swa_codes[b, w, c]) * 2^swa_exp[b, w]   (exact in f16)
  * out = sum over the union of softmax(l) * x, lse = ln sum exp(l); nothing to attend: 0, -inf.
  * The selected entries are split over workgroups as in the decode form of csa2_sparse_attn,
- * the window over up to two more; their partial softmaxes meet in one combine pass.
+ * the window over up to two more slots of 64 rows, or up to four of 32 rows when fewer than 256
+ * workgroups would run otherwise; their partial softmaxes meet in one combine pass.
  *
  * q         [B, H, D] bf16.          rows, n_max, idx [B, K], K: as csa2_sparse_attn with T = 1.
  * swa_codes [B, W, D] uint8 OCP E4M3 codes (16-byte aligned base); swa_exp [B, W] int8 row
@@ -316,7 +335,7 @@ typedef struct {
   int32_t block;           /* positions per block (8) */
   float* out;              /* [B, T, H, D] fp32 */
   float* lse;              /* [B, T, H] fp32 or NULL */
-  void* ws;
+  void* ws;                /* scratch of csa2_layer_workspace_size() bytes, 256-byte aligned */
   size_t ws_bytes;
   /* The layer's sliding window, joined to the selected entries as one softmax: as
    * csa2_sparse_attn_swa when T == 1, as csa2_sparse_attn_swa_prefill when T > 1 (the buffer then
@@ -329,6 +348,11 @@ typedef struct {
   const uint8_t* q_idx_mx;  /* [B*T, Hi*Di/2 + Hi*Di/32] MXFP4 indexer query, with shared_kv.k_mx */
 } csa2_layer_args;
 
+/* csa2_layer_workspace_size - scratch bytes csa2_layer_step needs for this layer (index scores,
+ * block maxima, Top-K scratch, attention partials). It takes the shared index state too, since the
+ * sizes depend on its Top-K and pool capacity. The workspace passed in a->ws must be 256-byte
+ * aligned (hipMalloc and torch allocations are); csa2_layer_step returns CSA2_E_WORKSPACE for a
+ * NULL, short or misaligned one. */
 csa2_status csa2_layer_workspace_size(csa2_mode mode, const csa2_layer_args* a,
                                       const csa2_shared_kv* kv, const csa2_shared_idx* idx,
                                       size_t* bytes);

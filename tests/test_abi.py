@@ -73,6 +73,22 @@ def test_index_scores_validation(L):
     assert f(None, None, 1, 1, 8, 8, 64, 10, None, None, 0, None, FAKE, 4, None) == E_UNSUP   # block != 8
     assert f(None, None, 1, 1, 8, 8, 64, 10, None, None, 0, None, None, 8, None) == E_ARG     # null tensors
     assert f(None, None, 0, 1, 8, 8, 64, 10, None, None, 0, None, None, 8, None) == OK        # empty
+    # 192-channel key rows: the streaming kernel has no such instantiation (decode, pool, block max)
+    assert f(FAKE, FAKE, 1, 1, 3, 3, 64, 10, None, None, 0, FAKE, None, 8, None) == E_SHAPE
+    assert f(FAKE, FAKE, 1, 64, 3, 3, 64, 10, None, FAKE, 4, FAKE, None, 8, None) == E_SHAPE
+    assert f(FAKE, FAKE, 1, 64, 3, 3, 64, 10, None, None, 0, FAKE, FAKE, 8, None) == E_SHAPE
+    # ... but the MFMA prefill form takes them
+    assert f(None, None, 0, 64, 3, 3, 64, 10, None, None, 0, None, None, 8, None) == OK
+
+
+def test_prefill_visibility_validation(L):
+    f = L.csa2_prefill_visibility
+    # p0, B, T, ratio, n_max, n_vis, stream
+    assert f(FAKE, 1, 4, 0, 10, FAKE, None) == E_ARG        # ratio must be positive
+    assert f(FAKE, -1, 4, 4, 10, FAKE, None) == E_ARG
+    assert f(None, 1, 4, 4, 10, None, None) == E_ARG
+    assert f(None, 0, 4, 4, 10, None, None) == OK           # empty
+    assert f(FAKE, 65536, 65536, 4, 10, FAKE, None) == E_SHAPE
 
 
 def test_topk_and_pool_validation(L):
@@ -178,7 +194,14 @@ def test_layer_step_state_rules(L):
     n = C.c_size_t(0)
     assert L.csa2_layer_workspace_size(0, C.byref(a), C.byref(kv), C.byref(idx), C.byref(n)) == OK
     assert n.value >= 4 * 4096 * 4                                 # at least the score rows
+    # a workspace of the right size that is not 256-byte aligned
+    a.ws, a.ws_bytes = FAKE + 64, n.value
+    assert L.csa2_layer_step(0, C.byref(a), C.byref(kv), C.byref(idx), None) == E_WS
+    a.ws, a.ws_bytes = None, 0
     assert L.csa2_layer_workspace_size(2, C.byref(a), C.byref(kv), C.byref(idx), C.byref(n)) == OK
+    # a key-row width the streaming indexer has no kernel for (3 heads x 64)
+    kv.Hk, a.Hi = 3, 3
+    assert L.csa2_layer_workspace_size(0, C.byref(a), C.byref(kv), C.byref(idx), C.byref(n)) == E_SHAPE
 
 
 def test_layer_step_pool_rules(L):

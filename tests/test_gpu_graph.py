@@ -1,8 +1,8 @@
 """A CSA2 layer step captured into a HIP graph replays bit-identically to the eager call.
 
-The Full and Reindex steps fork their Top-K / attention work onto an auxiliary stream and join it
-back, so capture must follow that fork and join. Several replays run, with eager work on the
-outputs and synchronizations between them, and every replay is compared with the eager result.
+Every kernel of a layer step is enqueued on the caller's stream, so the captured graph is a chain
+of kernel nodes. Several replays run, with eager work on the outputs and synchronizations between
+them, and every replay is compared with the eager result.
 """
 import numpy as np
 import pytest
