@@ -5,9 +5,11 @@ include/csa2.h); `api` is its Python binding. Importing this package does not lo
 the first call does, and fails loudly if it has not been built.
 """
 from .api import (FULL, REINDEX, REUSE, IdxState, KVState, dequant_kv_fp4, hier_pool, index_scores,
-                  index_scores_mxfp4, layer_step, prefill_n_vis, quantize_kv_fp4, row_bytes, sparse_attn,
-                  sparse_attn_swa, sparse_attn_swa_prefill, topk)
+                  index_scores_mxfp4, layer_args, layer_step, layer_workspace_size, prefill_n_vis,
+                  quantize_kv_fp4, row_bytes, sparse_attn, sparse_attn_swa, sparse_attn_swa_prefill,
+                  sparse_attn_workspace_size, topk)
 
 __all__ = ["FULL", "REINDEX", "REUSE", "IdxState", "KVState", "dequant_kv_fp4", "hier_pool", "index_scores",
-           "index_scores_mxfp4", "layer_step", "prefill_n_vis", "quantize_kv_fp4", "row_bytes", "sparse_attn",
-           "sparse_attn_swa", "sparse_attn_swa_prefill", "topk"]
+           "index_scores_mxfp4", "layer_args", "layer_step", "layer_workspace_size", "prefill_n_vis",
+           "quantize_kv_fp4", "row_bytes", "sparse_attn", "sparse_attn_swa", "sparse_attn_swa_prefill",
+           "sparse_attn_workspace_size", "topk"]

@@ -86,11 +86,12 @@ def dequant_kv_fp4(rows: torch.Tensor, dim: int = D_LATENT) -> torch.Tensor:
 
 def index_scores(q_idx: torch.Tensor, k_idx: torch.Tensor, n_vis: Optional[torch.Tensor] = None,
                  cand: Optional[torch.Tensor] = None, block_max: bool = False,
-                 out: Optional[torch.Tensor] = None):
+                 out: Optional[torch.Tensor] = None, block_max_out: Optional[torch.Tensor] = None):
     """Indexer scores. q_idx [B, T, Hi, Di] bf16, k_idx [B, N, Hk, Di] bf16.
 
-    Flat: returns scores [B*T, N] fp32 (entries >= n_vis unwritten) and, with block_max=True,
-    the 8-entry block maxima [B*T, ceil(N/8)]. Pool (cand [B*T, P] int32): scores [B*T, P].
+    Flat: returns scores [B*T, N] fp32 (entries >= n_vis unwritten) and, with block_max=True or
+    a block_max_out buffer, the 8-entry block maxima [B*T, ceil(N/8)]. Pool (cand [B*T, P]
+    int32): scores [B*T, P].
     """
     _need(q_idx, "q_idx", torch.bfloat16)
     _need(k_idx, "k_idx", torch.bfloat16, q_idx.device)
@@ -113,13 +114,17 @@ def index_scores(q_idx: torch.Tensor, k_idx: torch.Tensor, n_vis: Optional[torch
     if out is None:
         out = torch.empty(B * T, ncols, dtype=torch.float32, device=dev)
     _need(out, "out", torch.float32, dev)
-    bm = None
-    if block_max:
+    bm = block_max_out
+    if bm is not None:
+        _need(bm, "block_max_out", torch.float32, dev)
+        if bm.numel() != B * T * ((N + 7) // 8):
+            raise ValueError("block_max_out must be [B*T, ceil(N/8)]")
+    elif block_max:
         bm = torch.empty(B * T, (N + 7) // 8, dtype=torch.float32, device=dev)
     code = _lib.lib().csa2_index_scores(_ptr(q_idx), _ptr(k_idx), B, T, Hi, Hk, Di, N, _ptr(n_vis),
                                         _ptr(cand), P, _ptr(out), _ptr(bm), 8, _stream(dev))
     check("csa2_index_scores", code)
-    return (out, bm) if block_max else out
+    return (out, bm) if bm is not None else out
 
 
 def mxfp4_row_bytes(channels: int) -> int:
@@ -203,8 +208,12 @@ def hier_pool(block_max: torch.Tensor, n_sel_blocks: int, n_vis: Optional[torch.
     return pool
 
 
+def sparse_attn_workspace_size(B: int, T: int, H: int, D: int, K: int) -> int:
+    return int(_lib.lib().csa2_sparse_attn_workspace_size(B, T, H, D, K))
+
+
 def sparse_attn(q: torch.Tensor, rows: torch.Tensor, idx: torch.Tensor, sm_scale: float,
-                with_lse: bool = True, ws: Optional[torch.Tensor] = None):
+                with_lse: bool = True, ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
     """q [B, T, H, 512] bf16, rows [B, N, 288] uint8, idx [B, T, K] int32 -> out fp32 [B, T, H, 512], lse."""
     _need(q, "q", torch.bfloat16)
     dev = q.device
@@ -215,7 +224,11 @@ def sparse_attn(q: torch.Tensor, rows: torch.Tensor, idx: torch.Tensor, sm_scale
     K = idx.shape[-1]
     if rows.shape[0] != B or rows.shape[2] != row_bytes(D) or idx.shape[:2] != (B, T):
         raise ValueError("inconsistent shapes for q / rows / idx")
-    out = torch.empty(B, T, H, D, dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty(B, T, H, D, dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, dev)
+    if out.numel() != B * T * H * D:
+        raise ValueError("out must be [B, T, H, D]")
     lse = torch.empty(B, T, H, dtype=torch.float32, device=dev) if with_lse else None
     L = _lib.lib()
     nbytes = L.csa2_sparse_attn_workspace_size(B, T, H, D, K)
@@ -372,13 +385,12 @@ def layer_workspace_size(mode: int, args: LayerArgs, kv: KVState, idx: IdxState)
     return n.value
 
 
-def layer_step(mode: int, q: torch.Tensor, kv: KVState, idx: IdxState, q_idx: Optional[torch.Tensor] = None,
+def layer_args(mode: int, q: torch.Tensor, kv: KVState, idx: IdxState, q_idx: Optional[torch.Tensor] = None,
                sm_scale: Optional[float] = None, use_pool: bool = False, pool_blocks: int = 0, block: int = 8,
-               with_lse: bool = True, ws: Optional[torch.Tensor] = None,
-               out: Optional[torch.Tensor] = None,
                window: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
-               q_idx_mx: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """One CSA2 layer (FULL / REINDEX / REUSE) over caller-owned shared state; returns (out, lse).
+               q_idx_mx: Optional[torch.Tensor] = None) -> LayerArgs:
+    """The csa2_layer_args struct of one CSA2 layer (FULL / REINDEX / REUSE) over caller-owned
+    shared state, without output, LSE or workspace (layer_step fills those).
 
     window: the layer's sliding window joined to the selected entries as one softmax: decode
     (swa_codes [B, W, D] uint8, swa_exp [B, W] int8, n_win [B] int32), or prefill (swa_codes
@@ -412,6 +424,22 @@ def layer_step(mode: int, q: torch.Tensor, kv: KVState, idx: IdxState, q_idx: Op
                 or n_win.numel() != (B if T == 1 else B * T)):
             raise ValueError("window shapes must be [B, T + W - 1, D], [B, T + W - 1], [B] or [B, T]")
         a.swa_codes, a.swa_exp, a.swa_n, a.swa_W = _ptr(codes), _ptr(exps), _ptr(n_win), Wn
+    return a
+
+
+def layer_step(mode: int, q: torch.Tensor, kv: KVState, idx: IdxState, q_idx: Optional[torch.Tensor] = None,
+               sm_scale: Optional[float] = None, use_pool: bool = False, pool_blocks: int = 0, block: int = 8,
+               with_lse: bool = True, ws: Optional[torch.Tensor] = None,
+               out: Optional[torch.Tensor] = None,
+               window: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+               q_idx_mx: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """One CSA2 layer (FULL / REINDEX / REUSE) over caller-owned shared state; returns (out, lse).
+    Arguments as layer_args; out [B, T, H, D] fp32 (allocated if None), ws a uint8 workspace of at
+    least layer_workspace_size bytes (allocated if None or too small)."""
+    a = layer_args(mode, q, kv, idx, q_idx=q_idx, sm_scale=sm_scale, use_pool=use_pool, pool_blocks=pool_blocks,
+                   block=block, window=window, q_idx_mx=q_idx_mx)
+    dev = q.device
+    B, T, H, D = q.shape
     if out is None:
         out = torch.empty(B, T, H, D, dtype=torch.float32, device=dev)
     lse = torch.empty(B, T, H, dtype=torch.float32, device=dev) if with_lse else None

@@ -157,6 +157,15 @@ def test_index_scores_prefill_mfma(B, T, N, p0, ratio, Hi):
         assert np.all(np.isnan(s[b * T:(b + 1) * T][~mask])), "slots past n_vis must stay unwritten"
 
 
+def test_prefill_visibility_per_sequence():
+    """csa2_prefill_visibility with a start position per sequence, capped at n_max, against the
+    oracle's rule (reading R-6) sequence by sequence: positions before, across and past the cap."""
+    starts, T, ratio, n_max = [0, 5, 131072, 400], 37, 4, 110
+    nv = P.prefill_n_vis(starts, T, ratio, "cuda", n_max=n_max).cpu().numpy().reshape(len(starts), T)
+    for b, p0 in enumerate(starts):
+        assert np.array_equal(nv[b], np.minimum(O.prefill_n_vis(p0, T, ratio), n_max)), b
+
+
 # ---------------------------------------------------------------------------------------------
 TOPK_CASES = [(1, 1, 1), (3, 7, 3), (4, 100, 17), (2, 5000, 512), (32, 16384, 512), (2, 40000, 1024),
               (3, 100000, 512), (2, 262144, 512), (5, 300, 300), (2, 50, 64)]
