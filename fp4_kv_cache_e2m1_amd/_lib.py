@@ -41,6 +41,7 @@ EXPORTS = [
     "csa2_index_scores_mxfp4",
     "csa2_layer_workspace_size",
     "csa2_layer_step",
+    "csa2_layer_step_noalloc",
 ]
 
 
@@ -97,6 +98,7 @@ def _declare(lib):
         "csa2_layer_workspace_size": (i32, [i32, C.POINTER(LayerArgs), C.POINTER(SharedKV),
                                             C.POINTER(SharedIdx), C.POINTER(sz)]),
         "csa2_layer_step": (i32, [i32, C.POINTER(LayerArgs), C.POINTER(SharedKV), C.POINTER(SharedIdx), vp]),
+        "csa2_layer_step_noalloc": (i32, [i32, C.POINTER(LayerArgs), C.POINTER(SharedKV), C.POINTER(SharedIdx), vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

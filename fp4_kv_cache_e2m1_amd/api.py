@@ -432,10 +432,13 @@ def layer_step(mode: int, q: torch.Tensor, kv: KVState, idx: IdxState, q_idx: Op
                with_lse: bool = True, ws: Optional[torch.Tensor] = None,
                out: Optional[torch.Tensor] = None,
                window: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
-               q_idx_mx: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+               q_idx_mx: Optional[torch.Tensor] = None,
+               no_alloc: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """One CSA2 layer (FULL / REINDEX / REUSE) over caller-owned shared state; returns (out, lse).
     Arguments as layer_args; out [B, T, H, D] fp32 (allocated if None), ws a uint8 workspace of at
-    least layer_workspace_size bytes (allocated if None or too small)."""
+    least layer_workspace_size bytes (allocated if None or too small). no_alloc=True calls
+    csa2_layer_step_noalloc instead, which takes its scratch from the library's fixed device array
+    (ws is then ignored)."""
     a = layer_args(mode, q, kv, idx, q_idx=q_idx, sm_scale=sm_scale, use_pool=use_pool, pool_blocks=pool_blocks,
                    block=block, window=window, q_idx_mx=q_idx_mx)
     dev = q.device
@@ -444,6 +447,10 @@ def layer_step(mode: int, q: torch.Tensor, kv: KVState, idx: IdxState, q_idx: Op
         out = torch.empty(B, T, H, D, dtype=torch.float32, device=dev)
     lse = torch.empty(B, T, H, dtype=torch.float32, device=dev) if with_lse else None
     a.out, a.lse = _ptr(out), _ptr(lse)
+    if no_alloc:
+        code = _lib.lib().csa2_layer_step_noalloc(mode, C.byref(a), C.byref(kv.c), C.byref(idx.c), _stream(dev))
+        check("csa2_layer_step_noalloc", code)
+        return out, lse
     nbytes = layer_workspace_size(mode, a, kv, idx)
     ws = _ws(nbytes, dev, ws)
     a.ws, a.ws_bytes = _ptr(ws), nbytes

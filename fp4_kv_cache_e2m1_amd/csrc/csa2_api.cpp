@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/csa2.h"
 #include "launch.h"
@@ -325,20 +326,27 @@ csa2_status csa2_layer_workspace_size(csa2_mode mode, const csa2_layer_args* a, 
   return CSA2_OK;
 }
 
-csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_shared_kv* kv, csa2_shared_idx* idx,
-                            void* stream) {
-  LayerPlan p;
-  csa2_status st = plan_layer(mode, a, kv, idx, &p);
-  if (st != CSA2_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// Argument and state checks of a layer step that do not concern its workspace.
+csa2_status check_layer(csa2_mode mode, const csa2_layer_args* a, const csa2_shared_kv* kv,
+                        const csa2_shared_idx* idx, const LayerPlan& p) {
   if (mode != CSA2_FULL && !kv->valid) return CSA2_E_STATE;
   if (mode == CSA2_REUSE && !idx->topk_valid) return CSA2_E_STATE;
   if (!a->out || !idx->topk || !kv->rows || !a->q) return CSA2_E_ARG;
   if (p.score && (kv->k_mx ? !a->q_idx_mx : (!a->q_idx || !kv->k_idx))) return CSA2_E_ARG;
   if (a->swa_codes && (!a->swa_exp || !a->swa_n)) return CSA2_E_ARG;
-  if (p.total > 0 && (!a->ws || a->ws_bytes < p.total || reinterpret_cast<uintptr_t>(a->ws) % kAlign))
-    return CSA2_E_WORKSPACE;
+  return CSA2_OK;
+}
 
-  uint8_t* ws = static_cast<uint8_t*>(a->ws);
+// Enqueues the kernels of a validated layer step; `ws_base` holds at least p.total bytes and is
+// 256-byte aligned.
+csa2_status run_layer(csa2_mode mode, const csa2_layer_args* a, csa2_shared_kv* kv, csa2_shared_idx* idx,
+                      const LayerPlan& p, void* ws_base, void* stream) {
+  csa2_status st = CSA2_OK;
+  uint8_t* ws = static_cast<uint8_t*>(ws_base);
   float* scores = reinterpret_cast<float*>(ws + p.off_scores);
   float* bmax = p.build_pool ? reinterpret_cast<float*>(ws + p.off_bmax) : nullptr;
   void* sel_ws = ws + p.off_sel;
@@ -401,6 +409,59 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_share
   if (p.build_pool) idx->pool_valid = 1;
   if (mode == CSA2_FULL) kv->valid = 1;
   return CSA2_OK;
+}
+
+// Scratch of csa2_layer_step_noalloc: one copy per device, held until the process ends. Host code
+// never uses the array's name as an address: each device's copy is looked up once with
+// hipGetSymbolAddress (with that device current) and the pointer kept per device.
+static __device__ __align__(256) unsigned char scratch[CSA2_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_for_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr || reinterpret_cast<uintptr_t>(ptr) % kAlign) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_shared_kv* kv, csa2_shared_idx* idx,
+                            void* stream) {
+  LayerPlan p;
+  csa2_status st = plan_layer(mode, a, kv, idx, &p);
+  if (st != CSA2_OK) return st;
+  if ((st = check_layer(mode, a, kv, idx, p)) != CSA2_OK) return st;
+  if (p.total > 0 && (!a->ws || a->ws_bytes < p.total || reinterpret_cast<uintptr_t>(a->ws) % kAlign))
+    return CSA2_E_WORKSPACE;
+  return run_layer(mode, a, kv, idx, p, a->ws, stream);
+}
+
+csa2_status csa2_layer_step_noalloc(csa2_mode mode, const csa2_layer_args* a, csa2_shared_kv* kv,
+                                    csa2_shared_idx* idx, void* stream) {
+  LayerPlan p;
+  csa2_status st = plan_layer(mode, a, kv, idx, &p);
+  if (st != CSA2_OK) return st;
+  if ((st = check_layer(mode, a, kv, idx, p)) != CSA2_OK) return st;
+  if (p.total > CSA2_NOALLOC_SCRATCH_BYTES) return CSA2_E_WORKSPACE;
+  void* ws = nullptr;
+  if (scratch_for_current_device(&ws) != hipSuccess) return CSA2_E_HIP;
+  return run_layer(mode, a, kv, idx, p, ws, stream);
 }
 
 }  // extern "C"

@@ -359,6 +359,27 @@ csa2_status csa2_layer_workspace_size(csa2_mode mode, const csa2_layer_args* a,
 csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_shared_kv* kv,
                             csa2_shared_idx* idx, void* stream);
 
+/* ------------------------------------------------------------------------------------------
+ * csa2_layer_step_noalloc - csa2_layer_step for callers that cannot allocate device memory or
+ * pass a workspace: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments, kernels and results as csa2_layer_step, except that a->ws and
+ * a->ws_bytes are ignored: the scratch comes from a fixed device array inside the library of
+ * CSA2_NOALLOC_SCRATCH_BYTES (64 MiB), one copy per GPU, held until the process ends. The caller
+ * still passes every input and output buffer.
+ *   - CSA2_E_WORKSPACE when the layer needs more scratch than that (csa2_layer_workspace_size
+ *     gives the need: every decode layer of B <= 32 sequences x 65536 entries fits; a 4096-token
+ *     prefill chunk does not). Checked before anything is enqueued.
+ *   - The first call on a device looks up that device's copy of the array (hipGetSymbolAddress)
+ *     and keeps its address; no call allocates or frees memory.
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last call's contents:
+ *     calls that may overlap on one GPU (different streams without ordering between them, or
+ *     several host threads) race and must be serialized by the caller. Calls in order on one
+ *     stream are safe. No kernel relies on the scratch starting at zero.
+ * ------------------------------------------------------------------------------------------ */
+#define CSA2_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+csa2_status csa2_layer_step_noalloc(csa2_mode mode, const csa2_layer_args* a, csa2_shared_kv* kv,
+                                    csa2_shared_idx* idx, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

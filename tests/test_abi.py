@@ -204,6 +204,21 @@ def test_layer_step_state_rules(L):
     assert L.csa2_layer_workspace_size(0, C.byref(a), C.byref(kv), C.byref(idx), C.byref(n)) == E_SHAPE
 
 
+def test_layer_step_noalloc_limit(L):
+    """The no-allocation layer step rejects a layer whose scratch exceeds its fixed array, before
+    touching the device (a 4096-token prefill chunk over 33792 entries needs 528 MiB)."""
+    a, kv, idx = _layer(T=4096, K=1024)
+    kv.B, kv.n_max = 1, 33792
+    n = C.c_size_t(0)
+    assert L.csa2_layer_workspace_size(0, C.byref(a), C.byref(kv), C.byref(idx), C.byref(n)) == OK
+    assert n.value > 64 << 20
+    assert L.csa2_layer_step_noalloc(0, C.byref(a), C.byref(kv), C.byref(idx), None) == E_WS
+    # the same state rules as csa2_layer_step
+    a2, kv2, idx2 = _layer()
+    assert L.csa2_layer_step_noalloc(1, C.byref(a2), C.byref(kv2), C.byref(idx2), None) == E_STATE
+    assert L.csa2_layer_step_noalloc(7, C.byref(a2), C.byref(kv2), C.byref(idx2), None) == E_ARG
+
+
 def test_layer_step_pool_rules(L):
     a, kv, idx = _layer(pool_blocks=128, use_pool=1)
     n = C.c_size_t(0)
