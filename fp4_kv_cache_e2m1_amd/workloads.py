@@ -24,6 +24,7 @@ FULL, REINDEX, REUSE = 0, 1, 2
 
 # tensor ids inside a config's seed space
 TID_KV, TID_KIDX, TID_QIDX, TID_Q, TID_PLANT, TID_SWA, TID_MXFP4 = 1, 2, 3, 4, 5, 6, 7
+TID_TOK_KV, TID_TOK_Z, TID_W_IK = 8, 9, 10
 
 
 @dataclasses.dataclass(frozen=True)
@@ -137,6 +138,21 @@ def mxfp4_rows(wl: Workload, b: int, rows: int, channels: int, copy: int = 0) ->
     out = g.integers(0, 256, size=(rows, channels // 2 + channels // 32), dtype=np.uint8)
     out[:, channels // 2:] = g.integers(123, 130, size=(rows, channels // 32), dtype=np.uint8)
     return out
+
+
+def token_kv(wl: Workload, b: int, n_tok: int, first: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """bf16 bits [n_tok, D] x 2: the per-token KV values and compression weights of tokens
+    first .. first + n_tok - 1 of sequence b (the compressor's inputs), both N(0, 1)."""
+    c = _rng(wl, TID_TOK_KV, b, first).standard_normal((n_tok, wl.D), dtype=np.float32)
+    z = _rng(wl, TID_TOK_Z, b, first).standard_normal((n_tok, wl.D), dtype=np.float32)
+    return to_bf16_bits(c), to_bf16_bits(z)
+
+
+def w_index_k(wl: Workload) -> np.ndarray:
+    """bf16 bits [Hk * Di, D]: the indexer-key projection weight, row o holding the D input
+    weights of key channel o, N(0, 1/D) so that keys of N(0, 1) entries have unit scale."""
+    w = _rng(wl, TID_W_IK).standard_normal((wl.Hk * wl.Di, wl.D), dtype=np.float32)
+    return to_bf16_bits(w * np.float32(1.0 / np.sqrt(wl.D)))
 
 
 def swa_window(wl: Workload, b: int, rows: int) -> Tuple[np.ndarray, np.ndarray]:

@@ -189,6 +189,65 @@ def dequant_kv_fp4(rows: np.ndarray, dim: int = D_LATENT) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------------------------
+# O14 / O15: producing the caches - the simplified compressor and the indexer-K projection.
+# ---------------------------------------------------------------------------------------------
+def compress_kv(c: np.ndarray, z: np.ndarray, ratio: int) -> np.ndarray:
+    """O14. The CSA2 compressor: every `ratio` consecutive tokens become one main-KV entry.
+
+    [walkthrough] 一(三): each layer's KV entries C and their compression weights Z are
+    projections of the same hidden states (C_l = H W^KV_l, Z_l = H W^Z_l). [walkthrough] 一(四):
+    CSA builds an entry from 2m overlapping source entries and adds an absolute position
+    encoding; CSA2 removes both, so entry j is made from tokens jm .. jm+m-1 alone. The pages give
+    no formula for the combination; the reading taken (R-22) is a softmax over the m tokens of the
+    group, per channel, weighting the tokens' KV values:
+        entry[j, d] = sum_i w[i, d] * c[jm + i, d],  w[:, d] = softmax_i(z[jm + i, d]).
+    c, z: [n_tok, D] exact values (bf16 inputs as fp64), n_tok a multiple of ratio.
+    Returns fp32 [n_tok / ratio, D]: the exponentials, normalization and weighted sum in fp64,
+    rounded once to fp32 (the precision the entry is quantized from).
+    """
+    c = np.asarray(c, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    n, d = c.shape
+    assert z.shape == c.shape and ratio >= 1 and n % ratio == 0
+    cg = c.reshape(n // ratio, ratio, d)
+    zg = z.reshape(n // ratio, ratio, d)
+    e = np.exp(zg - zg.max(axis=1, keepdims=True))     # largest weight of each channel is exp(0) = 1
+    w = e / e.sum(axis=1, keepdims=True)
+    return (w * cg).sum(axis=1).astype(np.float32)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """fp64 values rounded to the nearest bf16 value (8 significant bits, ties to even), as fp64.
+
+    Written from the format: x = m * 2^e with m in [0.5, 1); keep 8 bits of m with
+    round-half-to-even (numpy's rint), for values in bf16's normal range (as here).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+
+
+def project_index_k(entries: np.ndarray, w_t: np.ndarray, heads: int, dim: int, rounded: bool = True) -> np.ndarray:
+    """O15. Indexer keys as a projection of the main-KV entries.
+
+    [walkthrough] 一(四): CSA2 obtains indexer K by projecting the main-KV entries, instead of
+    CSA's separate compression path from the hidden states; 一(四)1: a Full layer computes its own
+    main KV and indexer K. Reading (R-22): the projection takes the compressed entry (fp32) in
+    bf16, like the model's other activations, and a weight w_t [heads * dim, D] whose row o holds
+    the D input weights of key channel o; the key is stored in bf16 (the indexer-key format, R-4):
+        k[n, h, d] = bf16( sum_c bf16(entries[n, c]) * w_t[h * dim + d, c] ).
+    entries: fp32 [N, D]; w_t: exact values [heads * dim, D]. Returns fp64 [N, heads, dim], the
+    bf16 values (rounded=True) or the exact sums before the final rounding (rounded=False).
+    Products of two bf16 values are exact in fp64 and the sum is fp64.
+    """
+    x = round_bf16(np.asarray(entries, dtype=np.float32).astype(np.float64))
+    w = np.asarray(w_t, dtype=np.float64)
+    assert w.shape == (heads * dim, x.shape[1])
+    y = x @ w.T
+    return (round_bf16(y) if rounded else y).reshape(-1, heads, dim)
+
+
+# ---------------------------------------------------------------------------------------------
 # O6: the lightweight indexer.
 # ---------------------------------------------------------------------------------------------
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
