@@ -330,6 +330,57 @@ def fp4_indexer_leg(wl, sets, steps, dev, stream):
             "full_step_hbm_frac": round(step_bytes / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def production_leg(wl, sets, state, n_vis, steps, dev, stream):
+    """Producing the caches (csa2_compress_kv: compressor at 4 tokens per entry, FP4 packing and
+    the indexer-K projection) for the workload's new tokens: 4 per sequence in decode (one new
+    entry each, at the end of the cache), the whole chunk in prefill (T / 4 entries after the
+    existing ones). Timed alone, and as part of the first layer (a Full layer that compresses its
+    new tokens before scoring) beside the same layer without it."""
+    import torch
+    import fp4_kv_cache_e2m1_amd as P
+    from fp4_kv_cache_e2m1_amd import workloads as W
+    ratio = 4
+    n_tok = 4 if wl.T == 1 else wl.T
+    n_new = n_tok // ratio
+    first = wl.N - n_new
+    toks = [W.token_kv(wl, b, n_tok, first=ratio * first) for b in range(wl.B)]
+    c = dev_bf16(np.stack([t[0] for t in toks]), dev)
+    z = dev_bf16(np.stack([t[1] for t in toks]), dev)
+    w = dev_bf16(W.w_index_k(wl), dev)
+    e0 = torch.full((wl.B,), first, dtype=torch.int32, device=dev)
+    rows = [s["rows"] for s in sets]
+    keys = [s["kidx"] for s in sets]
+
+    def compress(i):
+        P.compress_kv(c, z, ratio, e0, rows[i % len(rows)], w_t=w, k_idx=keys[i % len(keys)])
+
+    for i in range(3):
+        compress(i)
+    torch.cuda.synchronize()
+    us = time_on_stream(compress, steps, stream) * 1e3
+    kc = wl.Hk * wl.Di
+    nbytes = wl.B * n_tok * wl.D * 2 * 2 + wl.B * n_new * (wl.D // 2 + wl.D // 16 + kc * 2) + kc * wl.D * 2
+    ws = torch.empty(max(256, max(P.layer_workspace_size(0, P.layer_args(0, s_["q"][0], kv, idx, q_idx=s_["qi"][0]),
+                                                         kv, idx) for s_, kv, idx, _ in state)),
+                     dtype=torch.uint8, device=dev)
+
+    def layer(i, produce):
+        s_, kv, idx, outs = state[i % len(state)]
+        P.layer_step(0, s_["q"][0], kv, idx, q_idx=s_["qi"][0], sm_scale=wl.sm_scale, with_lse=False, ws=ws,
+                     out=outs[0], produce=(c, z, ratio, e0, w) if produce else None)
+
+    for i in range(3):
+        layer(i, True)
+    torch.cuda.synchronize()
+    with_us = time_on_stream(lambda i: layer(i, True), steps, stream) * 1e3
+    without_us = time_on_stream(lambda i: layer(i, False), steps, stream) * 1e3
+    return {"kernel": "compress_kv_kernel (compressor + FP4 packing + indexer-K projection)", "bound": "hbm",
+            "new_tokens_per_sequence": n_tok, "new_entries_per_sequence": n_new, "avg_launch_us": round(us, 2),
+            "algorithmic_bytes_per_launch": nbytes, "achieved": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "full_layer_with_production_us": round(with_us, 2), "full_layer_without_us": round(without_us, 2)}
+
+
 def window_leg(wl, sets, state, n_rows, steps, dev, stream):
     """Attention over the last step's Top-K joined with full windows of n_rows FP8 rows
     (csa2_sparse_attn_swa in decode, csa2_sparse_attn_swa_prefill for many query tokens, each
@@ -560,6 +611,8 @@ def measure_workload(wl, args, dev, extras):
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s (f16)",
             "frac": round(aflops / (ams * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "algorithmic_flops_per_launch": aflops, "avg_launch_us": round(ams * 1e3, 2)}
+    if (wl.Hk * wl.Di) % 128 == 0:
+        res["cache_production"] = production_leg(wl, sets, state, n_vis, args.steps, dev, stream)
     if extras:
         fp4_shape = (wl.Hk == wl.Hi and wl.Hi * wl.Di in (256, 512)) or (wl.Hk == 1 and wl.Di == 128)
         if args.fp4_indexer and wl.T == 1 and fp4_shape:

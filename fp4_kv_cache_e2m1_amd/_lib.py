@@ -26,6 +26,7 @@ EXPORTS = [
     "csa2_status_string",
     "csa2_quantize_kv_fp4",
     "csa2_dequant_kv_fp4",
+    "csa2_compress_kv",
     "csa2_index_scores",
     "csa2_prefill_visibility",
     "csa2_topk_workspace_size",
@@ -68,7 +69,8 @@ class LayerArgs(C.Structure):
                 ("pool_blocks", C.c_int32), ("block", C.c_int32), ("out", C.c_void_p),
                 ("lse", C.c_void_p), ("ws", C.c_void_p), ("ws_bytes", C.c_size_t),
                 ("swa_codes", C.c_void_p), ("swa_exp", C.c_void_p), ("swa_n", C.c_void_p), ("swa_W", C.c_int32),
-                ("q_idx_mx", C.c_void_p)]
+                ("q_idx_mx", C.c_void_p), ("new_kv", C.c_void_p), ("new_z", C.c_void_p), ("new_tokens", C.c_int32),
+                ("ratio", C.c_int32), ("new_entry0", C.c_void_p), ("w_ik", C.c_void_p)]
 
 
 _lib = None
@@ -81,6 +83,7 @@ def _declare(lib):
         "csa2_status_string": (C.c_char_p, [i32]),
         "csa2_quantize_kv_fp4": (i32, [vp, i32, i64, i32, vp, vp]),
         "csa2_dequant_kv_fp4": (i32, [vp, i64, i32, vp, vp]),
+        "csa2_compress_kv": (i32, [vp, vp, i32, i32, i32, i32, vp, i32, vp, vp, i32, i32, vp, vp, vp]),
         "csa2_index_scores": (i32, [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, i32, vp, vp, i32, vp]),
         "csa2_prefill_visibility": (i32, [vp, i32, i32, i32, i32, vp, vp]),
         "csa2_topk_workspace_size": (sz, [i64, i32, i32]),

@@ -72,6 +72,39 @@ def quantize_kv_fp4(src: torch.Tensor, out: Optional[torch.Tensor] = None) -> to
     return out
 
 
+def compress_kv(c: torch.Tensor, z: torch.Tensor, ratio: int, entry0: torch.Tensor, rows: torch.Tensor,
+                w_t: Optional[torch.Tensor] = None, k_idx: Optional[torch.Tensor] = None,
+                return_entries: bool = False) -> Optional[torch.Tensor]:
+    """The compressor, FP4 packing and indexer-K projection (csa2_compress_kv).
+
+    c, z [B, n_tok, 512] bf16 (new tokens' KV values and compression weights); entry0 [B] int32
+    (index of each sequence's first new entry); rows [B, n_max, 288] uint8 written in place;
+    w_t [Hk*Di, 512] bf16 and k_idx [B, n_max, Hk, Di] bf16 (written in place), or both None.
+    Returns the fp32 entries [B, n_tok/ratio, 512] when return_entries, else None."""
+    _need(c, "c", torch.bfloat16)
+    dev = c.device
+    _need(z, "z", torch.bfloat16, dev)
+    _need(entry0, "entry0", torch.int32, dev)
+    _need(rows, "rows", torch.uint8, dev)
+    B, n_tok, D = c.shape
+    if z.shape != c.shape or entry0.numel() != B or rows.shape[0] != B or rows.shape[2] != row_bytes(D):
+        raise ValueError("inconsistent shapes for c / z / entry0 / rows")
+    Hk = Di = 0
+    if (w_t is None) != (k_idx is None):
+        raise ValueError("w_t and k_idx go together")
+    if k_idx is not None:
+        _need(w_t, "w_t", torch.bfloat16, dev)
+        _need(k_idx, "k_idx", torch.bfloat16, dev)
+        _, n2, Hk, Di = k_idx.shape
+        if n2 != rows.shape[1] or w_t.shape != (Hk * Di, D):
+            raise ValueError("k_idx must be [B, n_max, Hk, Di] and w_t [Hk*Di, D]")
+    ent = torch.empty(B, n_tok // max(ratio, 1), D, dtype=torch.float32, device=dev) if return_entries else None
+    code = _lib.lib().csa2_compress_kv(_ptr(c), _ptr(z), B, n_tok, D, ratio, _ptr(entry0), rows.shape[1], _ptr(rows),
+                                       _ptr(w_t), Hk, Di, _ptr(k_idx), _ptr(ent), _stream(dev))
+    check("csa2_compress_kv", code)
+    return ent
+
+
 def dequant_kv_fp4(rows: torch.Tensor, dim: int = D_LATENT) -> torch.Tensor:
     """[..., dim/2 + dim/16] uint8 -> [..., dim] fp32 (exact)."""
     _need(rows, "rows", torch.uint8)
@@ -388,7 +421,9 @@ def layer_workspace_size(mode: int, args: LayerArgs, kv: KVState, idx: IdxState)
 def layer_args(mode: int, q: torch.Tensor, kv: KVState, idx: IdxState, q_idx: Optional[torch.Tensor] = None,
                sm_scale: Optional[float] = None, use_pool: bool = False, pool_blocks: int = 0, block: int = 8,
                window: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
-               q_idx_mx: Optional[torch.Tensor] = None) -> LayerArgs:
+               q_idx_mx: Optional[torch.Tensor] = None,
+               produce: Optional[Tuple[torch.Tensor, torch.Tensor, int, torch.Tensor, torch.Tensor]] = None
+               ) -> LayerArgs:
     """The csa2_layer_args struct of one CSA2 layer (FULL / REINDEX / REUSE) over caller-owned
     shared state, without output, LSE or workspace (layer_step fills those).
 
@@ -396,7 +431,9 @@ def layer_args(mode: int, q: torch.Tensor, kv: KVState, idx: IdxState, q_idx: Op
     (swa_codes [B, W, D] uint8, swa_exp [B, W] int8, n_win [B] int32), or prefill (swa_codes
     [B, T + W - 1, D], swa_exp [B, T + W - 1], n_win [B, T]: each token's last n tokens).
     q_idx_mx: [B, T, C/2 + C/32] uint8 MXFP4 indexer query, for a KVState with FP4 keys (then
-    q_idx only gives Hi and may be None with Hi taken from the state)."""
+    q_idx only gives Hi and may be None with Hi taken from the state).
+    produce: (new_kv [B, n_tok, D] bf16, new_z [B, n_tok, D] bf16, ratio, entry0 [B] int32,
+    w_ik [Hk*Di, D] bf16): a Full layer first compresses its new tokens into the shared caches."""
     _need(q, "q", torch.bfloat16, kv.rows.device)
     dev = q.device
     B, T, H, D = q.shape
@@ -424,6 +461,16 @@ def layer_args(mode: int, q: torch.Tensor, kv: KVState, idx: IdxState, q_idx: Op
                 or n_win.numel() != (B if T == 1 else B * T)):
             raise ValueError("window shapes must be [B, T + W - 1, D], [B, T + W - 1], [B] or [B, T]")
         a.swa_codes, a.swa_exp, a.swa_n, a.swa_W = _ptr(codes), _ptr(exps), _ptr(n_win), Wn
+    if produce is not None:
+        nk, nz, ratio, entry0, w_ik = produce
+        _need(nk, "new_kv", torch.bfloat16, dev)
+        _need(nz, "new_z", torch.bfloat16, dev)
+        _need(entry0, "new_entry0", torch.int32, dev)
+        _need(w_ik, "w_ik", torch.bfloat16, dev)
+        if nk.shape != nz.shape or nk.shape[0] != B or nk.shape[2] != D or entry0.numel() != B:
+            raise ValueError("new_kv / new_z must be [B, n_tok, D] and new_entry0 [B]")
+        a.new_kv, a.new_z, a.new_tokens, a.ratio = _ptr(nk), _ptr(nz), nk.shape[1], ratio
+        a.new_entry0, a.w_ik = _ptr(entry0), _ptr(w_ik)
     return a
 
 
@@ -433,14 +480,16 @@ def layer_step(mode: int, q: torch.Tensor, kv: KVState, idx: IdxState, q_idx: Op
                out: Optional[torch.Tensor] = None,
                window: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
                q_idx_mx: Optional[torch.Tensor] = None,
-               no_alloc: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+               no_alloc: bool = False,
+               produce: Optional[Tuple[torch.Tensor, torch.Tensor, int, torch.Tensor, torch.Tensor]] = None
+               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """One CSA2 layer (FULL / REINDEX / REUSE) over caller-owned shared state; returns (out, lse).
     Arguments as layer_args; out [B, T, H, D] fp32 (allocated if None), ws a uint8 workspace of at
     least layer_workspace_size bytes (allocated if None or too small). no_alloc=True calls
     csa2_layer_step_noalloc instead, which takes its scratch from the library's fixed device array
     (ws is then ignored)."""
     a = layer_args(mode, q, kv, idx, q_idx=q_idx, sm_scale=sm_scale, use_pool=use_pool, pool_blocks=pool_blocks,
-                   block=block, window=window, q_idx_mx=q_idx_mx)
+                   block=block, window=window, q_idx_mx=q_idx_mx, produce=produce)
     dev = q.device
     B, T, H, D = q.shape
     if out is None:

@@ -99,6 +99,25 @@ csa2_status csa2_index_scores(const uint16_t* q_idx, const uint16_t* k_idx, int3
                                         block_max, s));
 }
 
+csa2_status csa2_compress_kv(const uint16_t* c, const uint16_t* z, int32_t B, int32_t n_tok, int32_t D,
+                             int32_t ratio, const int32_t* entry0, int32_t n_max, uint8_t* rows, const uint16_t* w_t,
+                             int32_t Hk, int32_t Di, uint16_t* k_idx, float* entries, void* stream) {
+  if (B < 0 || n_tok < 0 || n_max < 0 || ratio <= 0 || Hk < 0 || Di < 0) return CSA2_E_ARG;
+  if (D != 512 || !compress_ratio_supported(ratio) || n_tok % ratio != 0) return CSA2_E_SHAPE;
+  if ((w_t == nullptr) != (k_idx == nullptr)) return CSA2_E_ARG;
+  const int32_t c_out = Hk * Di;
+  if (k_idx && (c_out <= 0 || c_out % 128 != 0 || c_out > 1024)) return CSA2_E_SHAPE;
+  if ((int64_t)B * (n_tok / ratio) > INT32_MAX) return CSA2_E_SHAPE;
+  if (B == 0 || n_tok == 0) return CSA2_OK;
+  if (!c || !z || !entry0 || !rows) return CSA2_E_ARG;
+  if (reinterpret_cast<uintptr_t>(c) % 16 || reinterpret_cast<uintptr_t>(z) % 16 ||
+      reinterpret_cast<uintptr_t>(rows) % 4 || reinterpret_cast<uintptr_t>(w_t) % 16 ||
+      reinterpret_cast<uintptr_t>(k_idx) % 2 || reinterpret_cast<uintptr_t>(entries) % 16)
+    return CSA2_E_ARG;
+  return hip_status(launch_compress_kv(c, z, B, n_tok, ratio, entry0, n_max, rows, w_t, c_out, k_idx, entries,
+                                       as_stream(stream)));
+}
+
 csa2_status csa2_prefill_visibility(const int64_t* p0, int32_t B, int32_t T, int32_t ratio, int32_t n_max,
                                     int32_t* n_vis, void* stream) {
   if (B < 0 || T < 0 || n_max < 0 || ratio <= 0) return CSA2_E_ARG;
@@ -285,6 +304,15 @@ csa2_status plan_layer(csa2_mode mode, const csa2_layer_args* a, const csa2_shar
     p->n_blocks = (kv->n_max + 7) / 8;
   }
   if (p->on_pool && (!idx->pool || idx->P <= 0)) return CSA2_E_SHAPE;
+  if (a->new_kv) {
+    // producing the caches: Full layers with bf16 indexer keys
+    if (mode != CSA2_FULL) return CSA2_E_ARG;
+    if (kv->k_mx) return CSA2_E_UNSUPPORTED;
+    if (kv->D != 512 || a->new_tokens < 0 || !compress_ratio_supported(a->ratio) || a->new_tokens % a->ratio)
+      return CSA2_E_SHAPE;
+    const int32_t c_out = kv->Hk * kv->Di;
+    if (c_out <= 0 || c_out % 128 != 0 || c_out > 1024) return CSA2_E_SHAPE;
+  }
   size_t off = 0;
   p->off_scores = off;
   if (p->score) off = align_up(off + (size_t)p->rows * p->ncols * 4);
@@ -338,6 +366,7 @@ csa2_status check_layer(csa2_mode mode, const csa2_layer_args* a, const csa2_sha
   if (!a->out || !idx->topk || !kv->rows || !a->q) return CSA2_E_ARG;
   if (p.score && (kv->k_mx ? !a->q_idx_mx : (!a->q_idx || !kv->k_idx))) return CSA2_E_ARG;
   if (a->swa_codes && (!a->swa_exp || !a->swa_n)) return CSA2_E_ARG;
+  if (a->new_kv && (!a->new_z || !a->new_entry0 || !a->w_ik || !kv->k_idx)) return CSA2_E_ARG;
   return CSA2_OK;
 }
 
@@ -360,6 +389,13 @@ csa2_status run_layer(csa2_mode mode, const csa2_layer_args* a, csa2_shared_kv* 
   const int64_t rows = p.rows;
   const int32_t* n_vis = kv->n_vis;
   int32_t* pool = idx->pool;
+  if (a->new_kv) {
+    // the Full layer's own main KV and indexer keys, written into the shared caches first
+    st = csa2_compress_kv(a->new_kv, a->new_z, B, a->new_tokens, kv->D, a->ratio, a->new_entry0, kv->n_max,
+                          const_cast<uint8_t*>(kv->rows), a->w_ik, kv->Hk, kv->Di, const_cast<uint16_t*>(kv->k_idx),
+                          nullptr, stream);
+    if (st != CSA2_OK) return st;
+  }
   if (p.score) {
     if (kv->k_mx) {
       st = csa2_index_scores_mxfp4(a->q_idx_mx, kv->k_mx, B, T, a->Hi, kv->Hk, kv->Di, kv->n_max, n_vis,

@@ -34,6 +34,13 @@ hipError_t launch_index_prefill(const uint16_t* q, const uint16_t* k, int B, int
 hipError_t launch_prefill_visibility(const int64_t* p0, int B, int T, int ratio, int n_max, int32_t* n_vis,
                                      hipStream_t s);
 
+// compress.hip: compressor (ratio 1, 2, 4 or 8 tokens per entry) + FP4 packing + indexer-K
+// projection (c_out = Hk * Di key channels; k_idx may be null: no projection)
+bool compress_ratio_supported(int ratio);
+hipError_t launch_compress_kv(const uint16_t* c, const uint16_t* z, int B, int n_tok, int ratio,
+                              const int32_t* entry0, int n_max, uint8_t* rows, const uint16_t* w_t, int c_out,
+                              uint16_t* k_idx, float* entries, hipStream_t s);
+
 // topk.hip
 size_t topk_workspace(int64_t rows, int n_cols, int k);
 // n_valid[r] (nullable) counts valid entries; ceil(n_valid[r] / valid_div) columns take part.

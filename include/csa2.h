@@ -81,6 +81,36 @@ csa2_status csa2_dequant_kv_fp4(const uint8_t* rows, int64_t n_rows, int32_t dim
                                 void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * csa2_compress_kv - producing the caches: compressor, FP4 packing and indexer-K projection.
+ * [walkthrough] 一(三): a layer's KV entries C and their compression weights Z are projections
+ * of the hidden states (C = H W^KV, Z = H W^Z); 一(四): CSA2's compressor turns every `ratio`
+ * consecutive tokens into one main-KV entry, without CSA's overlap between neighbouring entries
+ * and without an absolute position encoding, and indexer K is obtained by projecting the main-KV
+ * entries; 一(五)4: the entries are stored as FP4 (E2M1 + one E4M3 scale per 16 channels).
+ *
+ * For sequence b, new entry j (j < n_tok / ratio) is made from tokens j*ratio .. j*ratio+ratio-1:
+ *   e[d] = sum_i w_i[d] c[b, j*ratio + i, d],   w_.[d] = softmax over the group's z[b, ., d]
+ * (fp32; reading of the pages: softmax weights per channel). It is written, packed as
+ * csa2_quantize_kv_fp4 packs an fp32 row, to rows[b, entry0[b] + j], and its indexer key
+ *   k_idx[b, entry0[b] + j, o] = bf16( sum_d bf16(e[d]) * w_t[o, d] ),  o < Hk * Di
+ * (bf16 products, fp32 accumulation, rounded to nearest even). Entries whose index
+ * entry0[b] + j falls outside [0, n_max) are not written.
+ *
+ * c, z     [B, n_tok, D] bf16 (16-byte aligned): the new tokens' KV values and compression weights.
+ * ratio    tokens per entry: 1, 2, 4 or 8; n_tok a multiple of it. D == 512.
+ * entry0   [B] int32 (device): index of each sequence's first new entry in its cache.
+ * rows     [B, n_max, D/2 + D/16] bytes: the FP4 cache, new entries written.
+ * w_t      [Hk*Di, D] bf16 projection weight (row o: the D input weights of key channel o), and
+ * k_idx    [B, n_max, Hk, Di] bf16 indexer keys, new entries written; both NULL: no projection.
+ *          Hk*Di a multiple of 128, at most 1024.
+ * entries  NULL, or [B, n_tok/ratio, D] fp32: the compressed entries before packing (for checks).
+ * ------------------------------------------------------------------------------------------ */
+csa2_status csa2_compress_kv(const uint16_t* c, const uint16_t* z, int32_t B, int32_t n_tok, int32_t D,
+                             int32_t ratio, const int32_t* entry0, int32_t n_max, uint8_t* rows,
+                             const uint16_t* w_t, int32_t Hk, int32_t Di, uint16_t* k_idx, float* entries,
+                             void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * csa2_index_scores - the lightweight indexer.
  * [walkthrough] 一(四): indexer Q and indexer K score the main-KV entries; 一(四)2: later
  * layers may score only a candidate pool.
@@ -298,7 +328,8 @@ csa2_status csa2_sparse_attn_swa_prefill(const uint16_t* q, const uint8_t* rows,
  *   csa2_shared_idx  the newest Top-K (and pool). FULL and REINDEX write topk and set
  *                    topk_valid; FULL with use_pool writes pool and sets pool_valid.
  * Modes:
- *   FULL     index scores over all visible entries -> Top-K (-> block max -> pool) -> attention.
+ *   FULL     (compress the layer's new tokens into the caches ->) index scores over all visible
+ *            entries -> Top-K (-> block max -> pool) -> attention.
  *   REINDEX  needs kv->valid. With use_pool and idx->pool_valid it scores only the pool;
  *            otherwise all visible entries. -> Top-K -> attention.
  *   REUSE    needs kv->valid and idx->topk_valid. Attention over idx->topk only.
@@ -346,6 +377,17 @@ typedef struct {
   const int32_t* swa_n;     /* [B] or [B*T] window rows (device), clamped to [0, swa_W] */
   int32_t swa_W;            /* rows reserved per sequence, <= 128 */
   const uint8_t* q_idx_mx;  /* [B*T, Hi*Di/2 + Hi*Di/32] MXFP4 indexer query, with shared_kv.k_mx */
+  /* Producing the caches ([walkthrough] 一(四)1: a Full layer computes its own main KV and then
+   * its indexer K from it). FULL only, with new_kv != NULL: the layer first compresses its new
+   * tokens into entries new_entry0[b] .. new_entry0[b] + new_tokens/ratio - 1 of shared_kv->rows
+   * and shared_kv->k_idx (written in place, as csa2_compress_kv; bf16 indexer keys only), then
+   * scores every visible entry as usual. new_kv NULL (a zero-initialized struct): no production. */
+  const uint16_t* new_kv;   /* [B, new_tokens, D] bf16 KV values of the new tokens */
+  const uint16_t* new_z;    /* [B, new_tokens, D] bf16 compression weights */
+  int32_t new_tokens;       /* a multiple of ratio */
+  int32_t ratio;            /* tokens per entry: 1, 2, 4 or 8 */
+  const int32_t* new_entry0; /* [B] int32 (device): first new entry of each sequence */
+  const uint16_t* w_ik;     /* [Hk*Di, D] bf16 indexer-K projection weight */
 } csa2_layer_args;
 
 /* csa2_layer_workspace_size - scratch bytes csa2_layer_step needs for this layer (index scores,
