@@ -13,14 +13,16 @@
 // projection weight on v_mfma_f32_32x32x16_bf16 (exact products, fp32 accumulation), giving the
 // entry's indexer key in bf16.
 //
-// Work split: a workgroup of 4 waves owns 32 consecutive entries of the flattened (sequence,
-// entry) list. A wave compresses 8 of them, two at a time, with a lane holding 8 consecutive
-// channels (16-byte loads of every token of both entries are in flight together); the 8 channels
-// are half of a 16-channel scale group, so the group maximum needs one lane exchange, and the
-// lane's eight 4-bit codes are one 32-bit word of the packed row. The bf16 entries meet in LDS as
-// the A operand of the projection; wave w then computes the keys' channel columns
-// [w C/4, (w+1) C/4) for all 32 entries, with the weight rows as B fragments read from global
-// memory (the weight is shared by every workgroup and stays in L2).
+// Work split: workgroup (x, y) of 8 waves owns 32 consecutive entries x of the flattened
+// (sequence, entry) list and key channels [256 y, 256 y + 256). A wave compresses 4 of the
+// entries with a lane holding 8 consecutive channels; the 16-byte loads of every token of its
+// entries are issued together (two rounds for 8 tokens per entry). The 8 channels are half of a
+// 16-channel scale group, so the group maximum needs one lane exchange, and the lane's eight
+// 4-bit codes are one 32-bit word of the packed row (written by the y = 0 workgroups only). The
+// bf16 entries meet in LDS as the A operand of the projection; wave w then computes the 32 key
+// channels 256 y + 32 w .. for the 32 entries, its 32 weight fragments (one 32 x 512 slice of the
+// weight) all loaded at once, so the whole call costs about two memory round trips when only a
+// few entries are new (decode appends one entry per sequence).
 #include "common.h"
 #include "launch.h"
 
@@ -38,17 +40,82 @@ CSA2_DEV uint32_t f32_to_bf16_rne(float x) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+constexpr int kCmpWaves = 8;
+constexpr int kCmpCols = 32 * kCmpWaves;          // key channels per workgroup
+
+// One entry's 8 channels of this lane from its M tokens' KV values and compression weights
+// (16-byte rows of 8 bf16 each): softmax over the tokens per channel, weighted sum.
 template <int M>
-__global__ __launch_bounds__(256) void compress_kv_kernel(
+CSA2_DEV void compress_lane(const u32x4_t (&cv)[M], const u32x4_t (&zv)[M], float (&e)[8]) {
+#pragma unroll
+  for (int ch = 0; ch < 8; ++ch) {
+    float cf[M], zf[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const uint32_t wc = cv[i][ch >> 1], wz = zv[i][ch >> 1];
+      cf[i] = __uint_as_float((ch & 1) ? (wc & 0xFFFF0000u) : (wc << 16));
+      zf[i] = __uint_as_float((ch & 1) ? (wz & 0xFFFF0000u) : (wz << 16));
+    }
+    if (M == 1) {
+      e[ch] = cf[0];
+    } else {
+      float zm = zf[0];
+#pragma unroll
+      for (int i = 1; i < M; ++i) zm = fmaxf(zm, zf[i]);
+      float s = 0.0f, a = 0.0f;
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        const float w = __expf(zf[i] - zm);
+        s += w;
+        a = fmaf(w, cf[i], a);
+      }
+      e[ch] = a / s;
+    }
+  }
+}
+
+// FP4 packing of the lane's 8 channels (half of a 16-channel scale group, lanes 2g and 2g+1
+// together) into row `row` (null: not written); the wave's 64 lanes cover the 512 channels.
+CSA2_DEV void pack_lane(const float (&e)[8], uint8_t* row, int lane) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int ch = 0; ch < 8; ++ch) amax = fmaxf(amax, fabsf(e[ch]));
+  amax = fmaxf(amax, shfl_xor_f(amax, 1));
+  const uint32_t sc = e4m3_scale_code(amax);
+  const float s = e4m3_mag(sc);
+  uint32_t word = 0;
+#pragma unroll
+  for (int ch = 0; ch < 8; ++ch) {
+    const uint32_t j = s > 0.0f ? e2m1_mag_code(fabsf(e[ch]), s) : 0u;
+    word |= (((__float_as_uint(e[ch]) >> 28) & 8u) | j) << (4 * ch);
+  }
+  if (row) {
+    reinterpret_cast<uint32_t*>(row)[lane] = word;                 // codes of channels 8 lane ..
+    if ((lane & 1) == 0) row[kCmpD / 2 + (lane >> 1)] = (uint8_t)sc;
+  }
+}
+
+CSA2_DEV u32x4_t bf16x8_of(const float (&e)[8]) {
+  u32x4_t packed;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) packed[h] = f32_to_bf16_rne(e[2 * h]) | (f32_to_bf16_rne(e[2 * h + 1]) << 16);
+  return packed;
+}
+
+template <int M>
+__global__ __launch_bounds__(64 * kCmpWaves) void compress_kv_kernel(
     const uint16_t* __restrict__ c, const uint16_t* __restrict__ z, int n_tok, int n_new, int64_t n_entries,
     const int32_t* __restrict__ entry0, int n_max, uint8_t* __restrict__ rows, const uint16_t* __restrict__ w_t,
     int c_out, uint16_t* __restrict__ k_idx, float* __restrict__ entries) {
+  constexpr int EPW = kCmpEntries / kCmpWaves;     // entries per wave
+  constexpr int EB = M <= 2 ? EPW : (M == 4 ? 2 : 1);   // entries whose tokens are loaded together
   __shared__ __attribute__((aligned(16))) uint16_t ebf[kCmpEntries * kCmpPitch];
-  __shared__ int64_t dest[kCmpEntries];    // b * n_max + entry index, or -1 (not written)
+  __shared__ int64_t dest[kCmpEntries];            // b * n_max + entry index, or -1 (not written)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t q0 = (int64_t)blockIdx.x * kCmpEntries;
+  const bool first_cols = blockIdx.y == 0;         // writes the packed rows and fp32 entries
 
   if (tid < kCmpEntries) {
     const int64_t q = q0 + tid;
@@ -60,17 +127,30 @@ __global__ __launch_bounds__(256) void compress_kv_kernel(
     }
     dest[tid] = d;
   }
+  // the wave's 32 x 512 slice of the projection weight: 32 fragments, loaded first so that their
+  // latency overlaps the compression
+  const int lr = lane & 31, lh = lane >> 5;
+  const int o0 = kCmpCols * (int)blockIdx.y + 32 * wave;
+  const bool project = k_idx != nullptr && o0 < c_out;   // uniform per wave
+  const int o = o0 + lr;                                  // this lane's key channel (B column)
+  bf16x8_t bw[kCmpD / 16];
+  if (project) {
+    const uint16_t* wrow = w_t + (int64_t)o * kCmpD + 8 * lh;
+#pragma unroll
+    for (int s = 0; s < kCmpD / 16; ++s) bw[s] = *reinterpret_cast<const bf16x8_t*>(wrow + 16 * s);
+  }
+  __builtin_amdgcn_sched_barrier(0);   // keep every weight load ahead of the compression
   __syncthreads();
 
   // ---- compress, pack, stage the bf16 entry for the projection ----
-#pragma unroll 1
-  for (int p = 0; p < kCmpEntries / 4; p += 2) {
-    int loc[2];
-    bool ok[2];
-    u32x4_t cv[2][M], zv[2][M];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      loc[u] = wave + 4 * (p + u);
+  for (int p = 0; p < EPW; p += EB) {
+    int loc[EB];
+    bool ok[EB];
+    u32x4_t cv[EB][M], zv[EB][M];
+#pragma unroll
+    for (int u = 0; u < EB; ++u) {
+      loc[u] = wave + kCmpWaves * (p + u);
       const int64_t q = q0 + loc[u];
       ok[u] = q < n_entries;
       const int64_t b = ok[u] ? q / n_new : 0, j = ok[u] ? q % n_new : 0;
@@ -86,92 +166,125 @@ __global__ __launch_bounds__(256) void compress_kv_kernel(
       }
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < EB; ++u) {
       float e[8];
-#pragma unroll
-      for (int ch = 0; ch < 8; ++ch) {
-        float cf[M], zf[M];
-#pragma unroll
-        for (int i = 0; i < M; ++i) {
-          const uint32_t wc = cv[u][i][ch >> 1], wz = zv[u][i][ch >> 1];
-          cf[i] = __uint_as_float((ch & 1) ? (wc & 0xFFFF0000u) : (wc << 16));
-          zf[i] = __uint_as_float((ch & 1) ? (wz & 0xFFFF0000u) : (wz << 16));
-        }
-        if (M == 1) {
-          e[ch] = cf[0];
-        } else {
-          float zm = zf[0];
-#pragma unroll
-          for (int i = 1; i < M; ++i) zm = fmaxf(zm, zf[i]);
-          float s = 0.0f, a = 0.0f;
-#pragma unroll
-          for (int i = 0; i < M; ++i) {
-            const float w = __expf(zf[i] - zm);
-            s += w;
-            a = fmaf(w, cf[i], a);
-          }
-          e[ch] = a / s;
+      compress_lane<M>(cv[u], zv[u], e);
+      if (first_cols) {
+        const int64_t d = dest[loc[u]];
+        pack_lane(e, ok[u] && d >= 0 ? rows + d * CSA2_ROW_BYTES(kCmpD) : nullptr, lane);
+        if (entries && ok[u]) {
+          float4* ep = reinterpret_cast<float4*>(entries + (q0 + loc[u]) * kCmpD + 8 * lane);
+          ep[0] = make_float4(e[0], e[1], e[2], e[3]);
+          ep[1] = make_float4(e[4], e[5], e[6], e[7]);
         }
       }
-      // FP4: the lane's 8 channels are half of a 16-channel scale group (lanes 2g, 2g+1)
-      float amax = 0.0f;
-#pragma unroll
-      for (int ch = 0; ch < 8; ++ch) amax = fmaxf(amax, fabsf(e[ch]));
-      amax = fmaxf(amax, shfl_xor_f(amax, 1));
-      const uint32_t sc = e4m3_scale_code(amax);
-      const float s = e4m3_mag(sc);
-      uint32_t word = 0;
-#pragma unroll
-      for (int ch = 0; ch < 8; ++ch) {
-        const uint32_t j = s > 0.0f ? e2m1_mag_code(fabsf(e[ch]), s) : 0u;
-        word |= (((__float_as_uint(e[ch]) >> 28) & 8u) | j) << (4 * ch);
-      }
-      const int64_t d = dest[loc[u]];
-      if (ok[u] && d >= 0) {
-        uint8_t* row = rows + d * CSA2_ROW_BYTES(kCmpD);
-        reinterpret_cast<uint32_t*>(row)[lane] = word;               // codes of channels 8 lane ..
-        if ((lane & 1) == 0) row[kCmpD / 2 + (lane >> 1)] = (uint8_t)sc;
-      }
-      if (entries && ok[u]) {
-        float4* ep = reinterpret_cast<float4*>(entries + (q0 + loc[u]) * kCmpD + 8 * lane);
-        ep[0] = make_float4(e[0], e[1], e[2], e[3]);
-        ep[1] = make_float4(e[4], e[5], e[6], e[7]);
-      }
-      u32x4_t packed;
-#pragma unroll
-      for (int h = 0; h < 4; ++h) packed[h] = f32_to_bf16_rne(e[2 * h]) | (f32_to_bf16_rne(e[2 * h + 1]) << 16);
-      *reinterpret_cast<u32x4_t*>(&ebf[loc[u] * kCmpPitch + 8 * lane]) = packed;
+      *reinterpret_cast<u32x4_t*>(&ebf[loc[u] * kCmpPitch + 8 * lane]) = bf16x8_of(e);
     }
   }
-  if (!k_idx) return;                      // uniform: no projection asked for
-  __syncthreads();
+  if (!k_idx) return;                              // uniform: no projection asked for
+  __syncthreads();                                 // every wave's bf16 entries are in LDS
 
-  // ---- indexer keys: [32 entries x 512] x [512 x c_out], wave w owns columns [w c_out/4, ..) ----
+  // ---- indexer keys: [32 entries x 512] x [512 x 32] per wave, key channels o0 .. o0 + 31 ----
+  if (!project) return;
+  const uint16_t* arow = &ebf[lr * kCmpPitch + 8 * lh];
+  f32x16_t acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < kCmpD / 16; ++s)
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(arow + 16 * s), bw[s], acc,
+                                                  0, 0, 0);
+  // accumulator r: entry 8 (r/4) + 4 (lane/32) + r%4, key channel o
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t d = dest[8 * (r >> 2) + 4 * lh + (r & 3)];
+    if (d >= 0) k_idx[d * c_out + o] = (uint16_t)f32_to_bf16_rne(acc[r]);
+  }
+}
+
+// Few new entries (decode appends one per sequence): workgroup (x, y) of 4 waves owns 4 entries
+// and the 32 key channels 32 y ..; wave w compresses entry w (every workgroup of the row of
+// column groups recomputes it; those with y = 0 write the rows) and multiplies the 4 entries by
+// input channels 128 w .. 128 w + 127 of the weight slice; the 4 partial tiles are added in LDS.
+// Each workgroup then reads 32 KB of weights and 32 KB of tokens, so the call is about two memory
+// round trips on as many CUs as there are column groups times entry groups.
+constexpr int kCmpSmallEntries = 4;
+
+template <int M>
+__global__ __launch_bounds__(256) void compress_kv_small_kernel(
+    const uint16_t* __restrict__ c, const uint16_t* __restrict__ z, int n_tok, int n_new, int64_t n_entries,
+    const int32_t* __restrict__ entry0, int n_max, uint8_t* __restrict__ rows, const uint16_t* __restrict__ w_t,
+    int c_out, uint16_t* __restrict__ k_idx, float* __restrict__ entries) {
+  __shared__ __attribute__((aligned(16))) uint16_t ebf[kCmpEntries * kCmpPitch];
+  __shared__ float part[4][16][64];                // per wave: its partial 32 x 32 tile, accumulator layout
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t q = (int64_t)blockIdx.x * kCmpSmallEntries + wave;   // this wave's entry
+  const bool ok = q < n_entries;
+  const int b = ok ? (int)(q / n_new) : 0, j = ok ? (int)(q % n_new) : 0;
+  const int n = ok ? entry0[b] + j : -1;
+  const int64_t d = (n >= 0 && n < n_max) ? (int64_t)b * n_max + n : -1;
   const int lr = lane & 31, lh = lane >> 5;
-  const int cols = c_out / 4, tiles = cols / 32;
-  for (int t = 0; t < tiles; ++t) {
-    const int o = wave * cols + 32 * t + lr;             // this lane's key channel (B column)
-    const uint16_t* wrow = w_t + (int64_t)o * kCmpD + 8 * lh;
-    const uint16_t* arow = &ebf[lr * kCmpPitch + 8 * lh];
-    f32x16_t acc;
+  const int o = 32 * (int)blockIdx.y + lr;         // this lane's key channel
+  const bool project = k_idx != nullptr;
+  // loads: the entry's M token rows of 16 bytes per lane, and the weight fragments of key channel
+  // o over input channels 128 wave + 16 s + 8 (lane/32)
+  u32x4_t cv[M], zv[M];
+  const int64_t tok = (int64_t)b * n_tok + (int64_t)j * M;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-    bf16x8_t bw[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) bw[s] = *reinterpret_cast<const bf16x8_t*>(wrow + 16 * s);
-#pragma unroll
-    for (int s = 0; s < kCmpD / 16; ++s) {
-      const bf16x8_t b = bw[s & 3];
-      if (s + 4 < kCmpD / 16) bw[s & 3] = *reinterpret_cast<const bf16x8_t*>(wrow + 16 * (s + 4));
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(arow + 16 * s);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+  for (int i = 0; i < M; ++i) {
+    cv[i] = u32x4_t{0u, 0u, 0u, 0u};
+    zv[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if (ok) {
+      cv[i] = *reinterpret_cast<const u32x4_t*>(c + (tok + i) * kCmpD + 8 * lane);
+      zv[i] = *reinterpret_cast<const u32x4_t*>(z + (tok + i) * kCmpD + 8 * lane);
     }
-    // accumulator r: entry 8 (r/4) + 4 (lane/32) + r%4, key channel o
+  }
+  bf16x8_t bw[8];
+  if (project) {
+    const uint16_t* wrow = w_t + (int64_t)o * kCmpD + 128 * wave + 8 * lh;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int ent = 8 * (r >> 2) + 4 * lh + (r & 3);
-      const int64_t d = dest[ent];
-      if (d >= 0) k_idx[d * c_out + o] = (uint16_t)f32_to_bf16_rne(acc[r]);
+    for (int s = 0; s < 8; ++s) bw[s] = *reinterpret_cast<const bf16x8_t*>(wrow + 16 * s);
+  }
+  float e[8];
+  compress_lane<M>(cv, zv, e);
+  if (blockIdx.y == 0) {
+    pack_lane(e, ok && d >= 0 ? rows + d * CSA2_ROW_BYTES(kCmpD) : nullptr, lane);
+    if (entries && ok) {
+      float4* ep = reinterpret_cast<float4*>(entries + q * kCmpD + 8 * lane);
+      ep[0] = make_float4(e[0], e[1], e[2], e[3]);
+      ep[1] = make_float4(e[4], e[5], e[6], e[7]);
+    }
+  }
+  if (!project) return;                            // uniform
+  // A operand rows: the 4 entries, then zeros
+  *reinterpret_cast<u32x4_t*>(&ebf[wave * kCmpPitch + 8 * lane]) = bf16x8_of(e);
+  for (int r = kCmpSmallEntries + wave; r < kCmpEntries; r += 4)
+    *reinterpret_cast<u32x4_t*>(&ebf[r * kCmpPitch + 8 * lane]) = u32x4_t{0u, 0u, 0u, 0u};
+  __syncthreads();
+  const uint16_t* arow = &ebf[lr * kCmpPitch + 128 * wave + 8 * lh];
+  f32x16_t acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(arow + 16 * s), bw[s], acc, 0, 0,
+                                                  0);
+  // rows 0..3 of the tile are accumulator registers 0..3 of lanes 0..31 (entry 4 (lane/32) + r%4)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) part[wave][r][lane] = acc[r];
+  __syncthreads();
+  if (wave == 0 && lh == 0) {
+#pragma unroll
+    for (int r = 0; r < kCmpSmallEntries; ++r) {
+      // the four waves' partial sums, added in wave order
+      const float v = ((part[0][r][lane] + part[1][r][lane]) + part[2][r][lane]) + part[3][r][lane];
+      const int64_t qr = (int64_t)blockIdx.x * kCmpSmallEntries + r;
+      if (qr < n_entries) {
+        const int br = (int)(qr / n_new), jr = (int)(qr % n_new);
+        const int nr = entry0[br] + jr;
+        if (nr >= 0 && nr < n_max) k_idx[((int64_t)br * n_max + nr) * c_out + o] = (uint16_t)f32_to_bf16_rne(v);
+      }
     }
   }
 }
@@ -184,10 +297,19 @@ hipError_t launch_compress_kv(const uint16_t* c, const uint16_t* z, int B, int n
   const int n_new = n_tok / ratio;
   const int64_t n_entries = (int64_t)B * n_new;
   if (n_entries == 0) return hipSuccess;
-  const dim3 grid((unsigned)((n_entries + kCmpEntries - 1) / kCmpEntries)), block(256);
-#define CSA2_CMP(M)                                                                                            \
-  hipLaunchKernelGGL((compress_kv_kernel<M>), grid, block, 0, s, c, z, n_tok, n_new, n_entries, entry0, n_max, \
-                     rows, w_t, c_out, k_idx, entries)
+  // few entries: 4 per workgroup and 32 key channels per workgroup, so the weight and the tokens
+  // are spread over many CUs; many entries: 32 per workgroup, 256 key channels per workgroup
+  const bool small = n_entries <= 512;
+  const int col_groups = k_idx ? (c_out + (small ? 32 : kCmpCols) - 1) / (small ? 32 : kCmpCols) : 1;
+  const int per = small ? kCmpSmallEntries : kCmpEntries;
+  const dim3 grid((unsigned)((n_entries + per - 1) / per), (unsigned)col_groups), block(small ? 256 : 64 * kCmpWaves);
+#define CSA2_CMP(M)                                                                                                \
+  if (small)                                                                                                       \
+    hipLaunchKernelGGL((compress_kv_small_kernel<M>), grid, block, 0, s, c, z, n_tok, n_new, n_entries, entry0,    \
+                       n_max, rows, w_t, c_out, k_idx, entries);                                                   \
+  else                                                                                                             \
+    hipLaunchKernelGGL((compress_kv_kernel<M>), grid, block, 0, s, c, z, n_tok, n_new, n_entries, entry0, n_max,   \
+                       rows, w_t, c_out, k_idx, entries)
   switch (ratio) {
     case 1: CSA2_CMP(1); break;
     case 2: CSA2_CMP(2); break;
