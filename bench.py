@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_FP4_PEAK_TFLOPS = 10100.0
 PROFILES = os.path.join(ROOT, "profiles")
 INDEX_SOURCES = ["fp4_kv_cache_e2m1_amd/csrc/index_decode.hip", "fp4_kv_cache_e2m1_amd/csrc/common.h"]
 
@@ -328,6 +329,38 @@ def fp4_indexer_leg(wl, sets, steps, dev, stream):
             "full_step_us": round(step_us, 2), "full_step_query_tokens_per_s": round(R / (step_us * 1e-6), 1),
             "full_step_algorithmic_bytes": step_bytes,
             "full_step_hbm_frac": round(step_bytes / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def fp4_prefill_leg(wl, n_vis, steps, dev, stream):
+    """The prefill indexer over FP4 (MXFP4) query and key rows (seeded synthetic codes and scales,
+    two alternating key copies): csa2_index_scores_mxfp4 on the scaled FP4 MFMA, causal, against
+    the FP4 dense MFMA peak; the fp32 score writes are reported against the HBM peak too, since
+    the contraction itself needs a quarter of the bf16 form's bytes and they dominate its traffic."""
+    import torch
+    import fp4_kv_cache_e2m1_amd as P
+    from fp4_kv_cache_e2m1_amd import workloads as W
+    C = wl.Hi * wl.Di
+    keys = [torch.from_numpy(np.stack([W.mxfp4_rows(wl, b, wl.N, C, copy=c) for b in range(wl.B)])).to(dev)
+            for c in range(2)]
+    q = torch.from_numpy(np.stack([W.mxfp4_rows(wl, b, wl.T, C, copy=2) for b in range(wl.B)])).to(dev)
+    out = torch.empty(wl.B * wl.T, wl.N, dtype=torch.float32, device=dev)
+
+    def call(i):
+        P.index_scores_mxfp4(q, keys[i % 2], C, n_vis=n_vis, out=out)
+
+    for i in range(3):
+        call(i)
+    torch.cuda.synchronize()
+    us = time_on_stream(call, steps, stream) * 1e3
+    pairs = float(n_vis.clamp(min=0, max=wl.N).sum().item())
+    flops = 2.0 * C * pairs
+    wbytes = 4.0 * pairs
+    tf = flops / (us * 1e-6) / 1e12
+    return {"kernel": "index_mxfp4_prefill_kernel (causal indexer scores, FP4 x FP4 MFMA)", "bound": "mfma",
+            "achieved": round(tf, 1), "peak": MFMA_FP4_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / MFMA_FP4_PEAK_TFLOPS, 4),
+            "algorithmic_flops_per_launch": flops, "avg_launch_us": round(us, 2),
+            "score_write_bytes": wbytes, "score_write_gbs": round(wbytes / (us * 1e-6) / 1e9, 1),
+            "score_write_frac_of_hbm": round(wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def production_leg(wl, sets, state, n_vis, steps, dev, stream):
@@ -636,6 +669,8 @@ def measure_workload(wl, args, dev, extras):
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s (f16)",
             "frac": round(aflops / (ams * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "algorithmic_flops_per_launch": aflops, "avg_launch_us": round(ams * 1e3, 2)}
+    if wl.T > 1 and wl.Hk == wl.Hi and wl.Hi * wl.Di in (256, 512):
+        res["fp4_indexer"] = fp4_prefill_leg(wl, n_vis, args.steps, dev, stream)
     if (wl.Hk * wl.Di) % 128 == 0:
         res["cache_production"] = production_leg(wl, sets, state, n_vis, args.steps, dev, stream)
     if extras:

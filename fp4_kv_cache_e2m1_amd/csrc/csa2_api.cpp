@@ -148,6 +148,8 @@ csa2_status csa2_index_scores_mxfp4(const uint8_t* q_rows, const uint8_t* k_rows
   if (reinterpret_cast<uintptr_t>(q_rows) % 8 || reinterpret_cast<uintptr_t>(k_rows) % 8 ||
       reinterpret_cast<uintptr_t>(scores) % 4)
     return CSA2_E_ARG;
+  if (!cand && !block_max && index_mxfp4_prefill_supported(T, Hi, Hk, Di))
+    return hip_status(launch_index_mxfp4_prefill(q_rows, k_rows, B, T, Hi, Di, n_max, n_vis, scores, as_stream(stream)));
   return hip_status(launch_index_mxfp4(q_rows, k_rows, B, T, Hi, Hk, Di, n_max, n_vis, cand, P, scores, block_max,
                                        as_stream(stream)));
 }

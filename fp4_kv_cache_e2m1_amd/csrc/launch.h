@@ -27,6 +27,11 @@ hipError_t launch_index_mxfp4(const uint8_t* q, const uint8_t* k, int B, int T, 
                               int n_max, const int32_t* n_vis, const int32_t* cand, int P, float* scores,
                               float* block_max, hipStream_t s);
 
+// index_mxfp4_prefill.hip: many query rows on the scaled FP4 MFMA (Hk == Hi, 256 or 512 channels)
+bool index_mxfp4_prefill_supported(int T, int Hi, int Hk, int Di);
+hipError_t launch_index_mxfp4_prefill(const uint8_t* q, const uint8_t* k, int B, int T, int Hi, int Di, int n_max,
+                                      const int32_t* n_vis, float* scores, hipStream_t s);
+
 // index_prefill.hip: MFMA tiles for many query rows, causal tile skipping
 bool index_prefill_supported(int T, int Hi, int Hk, int Di);
 hipError_t launch_index_prefill(const uint16_t* q, const uint16_t* k, int B, int T, int Hi, int Di,

@@ -182,6 +182,10 @@ csa2_status csa2_prefill_visibility(const int64_t* p0, int32_t B, int32_t T, int
  * scores  [B*T, n_max] fp32 (flat) or [B*T, P] (pool).
  * Requires Hk == Hi with Hi * Di in {256, 512}, or Hk == 1, Di == 128 and Hi <= 64
  * (CSA2_E_SHAPE otherwise); finite scales (code 255 is NaN).
+ * Decode-shaped calls stream the keys once per query row on the vector ALUs. Prefill calls (T >= 16,
+ * flat mode without block_max, Hk == Hi) run as tiles on the scaled FP4 matrix cores
+ * (v_mfma_scale_f32_32x32x64_f8f6f4: the rows' 32-channel blocks and E8M0 scales are its operand
+ * format), exact products accumulated in fp32, with causal tile skipping.
  * ------------------------------------------------------------------------------------------ */
 csa2_status csa2_index_scores_mxfp4(const uint8_t* q_rows, const uint8_t* k_rows, int32_t B,
                                     int32_t T, int32_t Hi, int32_t Hk, int32_t Di, int32_t n_max,

@@ -472,6 +472,41 @@ def test_index_scores_mxfp4(B, T, N, C, spread):
             assert np.all(s[r][~mask] == 7.0)
 
 
+@pytest.mark.parametrize("B,T,N,C,p0,rows", [
+    (1, 1100, 3000, 512, 9000, None),      # three 512-row slabs, ragged keys and rows
+    (2, 300, 1234, 256, 4000, None),       # 256 channels, two sequences
+    (1, 64, 40, 512, 0, None),             # fewer keys than one tile, early rows see none
+    (1, 4096, 33792, 512, 131072, [0, 1, 2, 3, 511, 512, 1023, 2047, 2048, 3000, 4093, 4095])])
+def test_index_scores_mxfp4_prefill_mfma(B, T, N, C, p0, rows):
+    """FP4 (MXFP4) indexer on the scaled FP4 MFMA (T >= 16, one key head per index head) against
+    the oracle: causal visibility from the prefill rule, several query slabs, ragged key tiles,
+    both channel counts, and the 4096-token prefill chunk over 33792 entries at full size (sampled
+    rows, every visible column). Block magnitudes spread over 2^-3 .. 2^3 so the blocks' E8M0
+    scales differ. Slots past n_vis stay as they were."""
+    g = np.random.default_rng(T + N + C)
+    spread = lambda n: np.ldexp(1.0, g.integers(-3, 4, size=(n, C // 32))).repeat(32, 1).astype(np.float32)
+    xq = g.standard_normal((B * T, C)).astype(np.float32) * spread(B * T)
+    xk = g.standard_normal((B * N, C)).astype(np.float32) * spread(B * N)
+    q_rows = O.quantize_mxfp4(xq).reshape(B, T, -1)
+    k_rows = O.quantize_mxfp4(xk).reshape(B, N, -1)
+    nv = np.minimum(O.prefill_n_vis(p0, T, 4), N).astype(np.int32)
+    nv_all = np.concatenate([nv] * B)
+    out = torch.full((B * T, N), 7.0, dtype=torch.float32).cuda()
+    s = _sync_np(P.index_scores_mxfp4(torch.from_numpy(q_rows).cuda(), torch.from_numpy(k_rows).cuda(), C,
+                                      n_vis=torch.from_numpy(nv_all).cuda(), out=out))
+    rs = range(T) if rows is None else rows
+    for b in range(B):
+        kd = O.dequant_mxfp4(k_rows[b], C)
+        qrows = q_rows[b][list(rs)]
+        ref = O.index_scores_mxfp4(qrows, k_rows[b], C, nv[list(rs)])
+        qd = O.dequant_mxfp4(qrows, C)
+        absdot = np.abs(qd) @ np.abs(kd).T
+        for i, t in enumerate(rs):
+            mask = np.arange(N) < nv[t]
+            check_scores(s[b * T + t], ref[i], absdot[i], mask, f"mxfp4 prefill b={b} t={t}")
+            assert np.all(s[b * T + t][~mask] == 7.0)
+
+
 @pytest.mark.parametrize("B,T,N,Hi", [(2, 1, 3001, 32), (3, 2, 500, 1), (1, 1, 70000, 32), (4, 1, 1, 16)])
 def test_index_scores_mxfp4_shared_key(B, T, N, Hi):
     """FP4 indexer with one shared 128-channel key per entry and Hi query heads (the paper-scale
