@@ -312,6 +312,18 @@ struct DecodeSmem {
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
+// The two 16-entry halves of a chunk as one K = 32 operand of v_mfma_f32_16x16x32_f16: lane
+// group g (lane / 16) holds entries 4 g .. 4 g + 3 of the first half and then of the second half,
+// in the A operand (transposed X, from two ds_read_b64_tr_b16) and in the B operand (P) alike, so
+// the MFMA's k index pairs the same entries on both sides. One K = 32 MFMA does the work of two
+// K = 16 ones at the doubled rate gfx950 gives the K = 32 form.
+CSA2_DEV f16x8_t cat_halves(f16x4_t lo, f16x4_t hi) { return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7); }
+CSA2_DEV f16x8_t xt_chunk(const uint16_t* p, int pitch) {
+  const s16x4_t a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
+  const s16x4_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 16 * pitch));
+  return cat_halves(__builtin_bit_cast(f16x4_t, a0), __builtin_bit_cast(f16x4_t, a1));
+}
+
 // Two E4M3 scale bytes (low half of w) as f16 (exact: E4M3 values fit f16).
 CSA2_DEV f16x2_t e4m3x2_to_f16(uint32_t w) { return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false); }
 
@@ -552,14 +564,14 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
         pb[s][i] = pv;
       }
     l_run += head_sum(psum);
-    // O^T += X^T P^T: this wave's 8 channel tiles over the chunk's entry steps
+    // O^T += X^T P^T: this wave's 8 channel tiles over the chunk's 32 entries, one K = 32 MFMA each
+    static_assert(NS == 2, "a chunk is two 16-entry halves");
+    {
+      const f16x8_t p8 = cat_halves(pb[0], pb[1]);
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(xtr + 16 * s * kXPitch + 16 * j));
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), pb[s], acc[j], 0, 0, 0);
-      }
+      for (int j = 0; j < 8; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xt_chunk(xtr + 16 * j, kXPitch), p8, acc[j], 0, 0, 0);
+    }
   }
 
   // merge the sub-groups: groups 1.. leave (max, sum) and their tiles in LDS, group 0 combines
@@ -858,14 +870,14 @@ __global__ __launch_bounds__(256 * NG) void swa_attn_kernel(
         pb[s][i] = pv;
       }
     l_run += head_sum(psum);
-    // O^T += X^T P^T: this wave's 8 channel tiles over the chunk's entry steps
+    // O^T += X^T P^T: this wave's 8 channel tiles over the chunk's 32 entries, one K = 32 MFMA each
+    static_assert(NS == 2, "a chunk is two 16-entry halves");
+    {
+      const f16x8_t p8 = cat_halves(pb[0], pb[1]);
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(xtr + 16 * s * kXPitch + 16 * j));
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), pb[s], acc[j], 0, 0, 0);
-      }
+      for (int j = 0; j < 8; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xt_chunk(xtr + 16 * j, kXPitch), p8, acc[j], 0, 0, 0);
+    }
   }
 
   // merge the sub-groups: groups 1.. leave (max, sum) and their tiles in LDS, group 0 combines
@@ -1171,17 +1183,17 @@ __global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
           for (int j = 0; j < 8; ++j) acc[ht][j] *= a4[ht];
       }
     }
+    static_assert(NS == 2, "a chunk is two 16-entry halves");
+    {
+      f16x8_t pb[4];
 #pragma unroll
-    for (int t = 0; t < NS; ++t) {
-      f16x4_t pb[4];
-#pragma unroll
-      for (int ht = 0; ht < 4; ++ht) pb[ht] = pbuf[(ht * NS + t) * 64 + lane];
+      for (int ht = 0; ht < 4; ++ht) pb[ht] = cat_halves(pbuf[(ht * NS) * 64 + lane], pbuf[(ht * NS + 1) * 64 + lane]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(xtr + 16 * t * XP + 16 * j));
+        const f16x8_t a = xt_chunk(xtr + 16 * j, XP);
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht)
-          acc[ht][j] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), pb[ht], acc[ht][j], 0, 0, 0);
+          acc[ht][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[ht], acc[ht][j], 0, 0, 0);
       }
     }
   }
