@@ -255,7 +255,7 @@ csa2_status csa2_sparse_attn_swa_prefill(const uint16_t* q, const uint8_t* rows,
       reinterpret_cast<uintptr_t>(out) % 16 || reinterpret_cast<uintptr_t>(swa_codes) % 16)
     return CSA2_E_ARG;
   const size_t need = csa2_sparse_attn_swa_prefill_workspace_size(B, T, H, D, K);
-  if (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 256) return CSA2_E_WORKSPACE;
+  if (need > 0 && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 256)) return CSA2_E_WORKSPACE;
   return hip_status(launch_sparse_attn_swa_prefill(q, rows, n_max, idx, B, T, H, D, K, swa_codes, swa_exp, n_win, W,
                                                    sm_scale, out, lse, ws, as_stream(stream)));
 }

@@ -951,7 +951,8 @@ template <int PF, int OCC, int XP>
 __global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ rows, int n_max,
     const int32_t* __restrict__ idx, int T, int H, int K, float sm_scale, float* __restrict__ out,
-    float* __restrict__ lse, int n_rows, int per_xcd) {
+    float* __restrict__ lse, int n_rows, int per_xcd, const uint8_t* __restrict__ swa_codes,
+    const int8_t* __restrict__ swa_exp, const int32_t* __restrict__ n_win, int W) {
   constexpr int KC = kPKC, NS = KC / 16;
   __shared__ __attribute__((aligned(16))) uint16_t xs[KC * XP];     // X[entry][channel], f16
   // partial S, component-major ([wave][t][ht][i][lane]) so every 4-byte access is lane-contiguous
@@ -1069,33 +1070,10 @@ __global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
   const uint16_t* xtr = xs + (4 * g + (l16 >> 2)) * XP + 128 * w + 4 * (l16 & 3);
   const uint16_t* xr = xs + l16 * XP + 128 * w + 8 * g;
 
-  for (int cg = 0; cg < nk; cg += PF * KC)
-#pragma unroll
-  for (int v = 0; v < PF; ++v) {
-    const int c0 = cg + v * KC;
-    if (c0 >= nk) break;
-    {
-      // the next gather's position is read before this chunk's X writes, so waiting for it does
-      // not wait for them
-      const int ks = c0 + PF * KC + gkey;
-      const int pnext = (c0 + PF * KC < nk && ks < nk) ? sidx[ks] : -1;
-      // dequantize this lane's slab into X (read by this wave only; a wave's LDS operations
-      // complete in order, so the reads below see these writes)
-      const Piece& pc = gr[v];
-      const f16x2_t s01 = e4m3x2_to_f16(pc.sc), s23 = e4m3x2_to_f16(pc.sc >> 16);
-      const f16x2_t sgm[4] = {f16x2_t{s01[0], s01[0]}, f16x2_t{s01[1], s01[1]}, f16x2_t{s23[0], s23[0]},
-                              f16x2_t{s23[1], s23[1]}};
-      const uint32_t cw[8] = {pc.c01.x, pc.c01.y, pc.c01.z, pc.c01.w, pc.c23.x, pc.c23.y, pc.c23.z, pc.c23.w};
-      uint4* dst = reinterpret_cast<uint4*>(xs + gkey * XP + 64 * gcs);
-#pragma unroll
-      for (int wi = 0; wi < 8; ++wi) {
-        uint32_t vv[4];
-        e2m1x8_to_f16(cw[wi], sgm[wi >> 1], vv);
-        dst[wi] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
-      }
-      if (c0 + PF * KC < nk) gather_at(gr[v], pnext);
-    }
-    __builtin_amdgcn_wave_barrier();
+  // The chunk's math once its 32 entries are in X (this wave's slab written by this wave):
+  // partial scores, their sum and the online softmax of the owned head tile, P.V. vmask bit e:
+  // entry e of the chunk is real.
+  auto chunk_math = [&](uint64_t vmask) {
     // partial S^T over this wave's channels: tile (t, ht), lane holds entries 16 t + 4 g + i of head 16 ht + l16
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
@@ -1122,12 +1100,6 @@ __global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
     __syncthreads();
     // head tile w: complete scores, online softmax, publish P and the rescale factor
     {
-      uint64_t vmask;              // bit e: entry c0 + e is a real entry
-      {
-        int pe = -1;
-        if (lane < KC && c0 + lane < nk) pe = sidx[c0 + lane];
-        vmask = __ballot(pe >= 0);
-      }
       float tv[NS][4];
       float cmax = -INFINITY;
 #pragma unroll
@@ -1195,6 +1167,85 @@ __global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
         for (int ht = 0; ht < 4; ++ht)
           acc[ht][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[ht], acc[ht][j], 0, 0, 0);
       }
+    }
+  };
+
+  for (int cg = 0; cg < nk; cg += PF * KC)
+#pragma unroll
+  for (int v = 0; v < PF; ++v) {
+    const int c0 = cg + v * KC;
+    if (c0 >= nk) break;
+    {
+      // the next gather's position is read before this chunk's X writes, so waiting for it does
+      // not wait for them
+      const int ks = c0 + PF * KC + gkey;
+      const int pnext = (c0 + PF * KC < nk && ks < nk) ? sidx[ks] : -1;
+      // dequantize this lane's slab into X (read by this wave only; a wave's LDS operations
+      // complete in order, so the reads below see these writes)
+      const Piece& pc = gr[v];
+      const f16x2_t s01 = e4m3x2_to_f16(pc.sc), s23 = e4m3x2_to_f16(pc.sc >> 16);
+      const f16x2_t sgm[4] = {f16x2_t{s01[0], s01[0]}, f16x2_t{s01[1], s01[1]}, f16x2_t{s23[0], s23[0]},
+                              f16x2_t{s23[1], s23[1]}};
+      const uint32_t cw[8] = {pc.c01.x, pc.c01.y, pc.c01.z, pc.c01.w, pc.c23.x, pc.c23.y, pc.c23.z, pc.c23.w};
+      uint4* dst = reinterpret_cast<uint4*>(xs + gkey * XP + 64 * gcs);
+#pragma unroll
+      for (int wi = 0; wi < 8; ++wi) {
+        uint32_t vv[4];
+        e2m1x8_to_f16(cw[wi], sgm[wi >> 1], vv);
+        dst[wi] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
+      }
+      if (c0 + PF * KC < nk) gather_at(gr[v], pnext);
+    }
+    __builtin_amdgcn_wave_barrier();
+    uint64_t vmask;                // bit e: entry c0 + e is a real entry
+    {
+      int pe = -1;
+      if (lane < KC && c0 + lane < nk) pe = sidx[c0 + lane];
+      vmask = __ballot(pe >= 0);
+    }
+    chunk_math(vmask);
+  }
+
+  // The query's own sliding window ([walkthrough] 一(四)), joined to the same softmax as up to
+  // W / 32 more chunks: the sequence's buffer holds T + W - 1 FP8 rows (row i = token
+  // p0 - W + 1 + i) and query t takes its last n = min(n_win, W) tokens up to its own, rows
+  // t + W - n .. t + W - 1. A row's value is its E4M3 codes times its power of two 2^e, exact in
+  // f16 for e in [-15, 7].
+  if (W > 0) {
+    const int t_in = qr - b * T;
+    const int n_w = max(0, min(n_win[qr], W));
+    const uint8_t* wrow0 = swa_codes + ((int64_t)b * (T + W - 1) + t_in + (W - n_w)) * kD + 64 * gcs;
+    const int8_t* erow0 = swa_exp + (int64_t)b * (T + W - 1) + t_in + (W - n_w);
+    for (int c0 = 0; c0 < n_w; c0 += KC) {
+      // a lane's 64-byte slab of window row r (zeros past the window); loading it a chunk ahead
+      // measured no faster and costs registers
+      const int r = c0 + gkey;
+      uint4 wc[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+      int we = 0;
+      if (r < n_w) {
+        const uint4* rp = reinterpret_cast<const uint4*>(wrow0 + (int64_t)r * kD);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) wc[m] = rp[m];
+        we = erow0[r];
+      }
+      const _Float16 sc = (_Float16)ldexpf(1.0f, we);
+      const f16x2_t s2 = f16x2_t{sc, sc};
+      uint4* dst = reinterpret_cast<uint4*>(xs + gkey * XP + 64 * gcs);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t cw[4] = {wc[m].x, wc[m].y, wc[m].z, wc[m].w};
+        uint32_t vv[8];
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+          vv[2 * t4] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cw[t4], 1.0f, false) * s2);
+          vv[2 * t4 + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cw[t4] >> 16, 1.0f, false) * s2);
+        }
+        dst[2 * m] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
+        dst[2 * m + 1] = make_uint4(vv[4], vv[5], vv[6], vv[7]);
+      }
+      __builtin_amdgcn_wave_barrier();
+      const int rows_here = min(KC, n_w - c0);
+      chunk_math((1ull << rows_here) - 1ull);
     }
   }
 
@@ -1366,7 +1417,7 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* rows, int n_max,
     const int64_t items = nq * (H / 64);
     const int per_xcd = (int)((items + 7) / 8);
     hipLaunchKernelGGL((sparse_attn_prefill_kernel<1, 2, kPXPitch>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, q, rows, n_max,
-                       idx, T, H, K, sm_scale, out, lse, (int)nq, per_xcd);
+                       idx, T, H, K, sm_scale, out, lse, (int)nq, per_xcd, nullptr, nullptr, nullptr, 0);
     return hipGetLastError();
   }
   if (use_decode_form(B, T)) {
@@ -1475,6 +1526,7 @@ hipError_t launch_sparse_attn_swa(const uint16_t* q, const uint8_t* rows, int n_
 // output (its log-sum-exp alongside), slot 1 the window's partials; one combine pass.
 constexpr int kSwaPrefillSlots = 2;
 size_t attn_swa_prefill_workspace(int B, int T, int H, int D, int K) {
+  if (use_prefill_form(B, T, H, K)) return 0;       // the window joins the prefill form's own loop
   const size_t rows_h = (size_t)B * T * H;
   const size_t slots = kSwaPrefillSlots;
   const size_t parts = ((slots * rows_h * (size_t)D * 4 + slots * rows_h * 8 + rows_h * 4) + 255) & ~(size_t)255;
@@ -1487,6 +1539,13 @@ hipError_t launch_sparse_attn_swa_prefill(const uint16_t* q, const uint8_t* rows
                                           float* out, float* lse, void* ws, hipStream_t s) {
   if (B == 0 || T == 0 || H == 0) return hipSuccess;
   const int64_t nq = (int64_t)B * T, rows_h = nq * H;
+  if (use_prefill_form(B, T, H, K)) {
+    // one pass: each query's window rows run as further chunks of the same online softmax
+    const int per_xcd = (int)((nq * (H / 64) + 7) / 8);
+    hipLaunchKernelGGL((sparse_attn_prefill_kernel<1, 2, kPXPitch>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, q, rows,
+                       n_max, idx, T, H, K, sm_scale, out, lse, (int)nq, per_xcd, swa_codes, swa_exp, n_win, W);
+    return hipGetLastError();
+  }
   const size_t slots = kSwaPrefillSlots;
   float* part_o = static_cast<float*>(ws);
   float* part_ml = part_o + slots * (size_t)rows_h * kD;

@@ -305,7 +305,9 @@ csa2_status csa2_sparse_attn_swa(const uint16_t* q, const uint8_t* rows, int32_t
  * swa_codes [B, T + W - 1, D] uint8 E4M3 codes (16-byte aligned); swa_exp [B, T + W - 1] int8
  *           exponents in [-15, 7]; n_win [B, T] int32 (device); W <= 128.
  * out [B, T, H, D] fp32; lse [B, T, H] fp32 or NULL.
- * ws        scratch of csa2_sparse_attn_swa_prefill_workspace_size() bytes, 256-byte aligned.
+ * ws        scratch of csa2_sparse_attn_swa_prefill_workspace_size() bytes, 256-byte aligned;
+ *           may be NULL when that size is 0 (B * T >= 512, H % 64 == 0 and 0 < K <= 1024: the
+ *           window runs as further chunks of the selected entries' own pass).
  * Requires D == 512, H % 16 == 0.
  * ------------------------------------------------------------------------------------------ */
 size_t csa2_sparse_attn_swa_prefill_workspace_size(int32_t B, int32_t T, int32_t H, int32_t D,

@@ -277,10 +277,16 @@ def test_sparse_attn_swa_prefill_validation(L):
              None) == E_SHAPE
     assert f(FAKE, FAKE, 10, FAKE, 1, 4, 64, 512, 8, FAKE, FAKE, None, 128, 1.0, FAKE, None, FAKE, 1 << 30,
              None) == E_ARG
-    need = L.csa2_sparse_attn_swa_prefill_workspace_size(1, 600, 64, 512, 64)
-    assert need >= 2 * 600 * 64 * 512 * 4                          # the sparse slot and one window slot
-    assert f(FAKE, FAKE, 10, FAKE, 1, 600, 64, 512, 64, FAKE, FAKE, FAKE, 128, 1.0, FAKE, None, FAKE, need - 1,
+    # 64-head groups with one split of selected entries: the window runs inside that pass, no scratch
+    assert L.csa2_sparse_attn_swa_prefill_workspace_size(1, 600, 64, 512, 64) == 0
+    assert L.csa2_sparse_attn_swa_prefill_workspace_size(1, 600, 128, 512, 1024) == 0
+    # 32 heads: the sparse slot and one window slot, merged by a combine pass
+    need = L.csa2_sparse_attn_swa_prefill_workspace_size(1, 600, 32, 512, 64)
+    assert need >= 2 * 600 * 32 * 512 * 4
+    assert f(FAKE, FAKE, 10, FAKE, 1, 600, 32, 512, 64, FAKE, FAKE, FAKE, 128, 1.0, FAKE, None, FAKE, need - 1,
              None) == E_WS
-    assert f(FAKE, FAKE, 10, FAKE, 1, 600, 64, 512, 64, FAKE, FAKE, FAKE, 128, 1.0, FAKE, None, FAKE + 16, need,
+    assert f(FAKE, FAKE, 10, FAKE, 1, 600, 32, 512, 64, FAKE, FAKE, FAKE, 128, 1.0, FAKE, None, None, need,
+             None) == E_WS                                          # missing
+    assert f(FAKE, FAKE, 10, FAKE, 1, 600, 32, 512, 64, FAKE, FAKE, FAKE, 128, 1.0, FAKE, None, FAKE + 16, need,
              None) == E_WS                                          # workspace not 256-byte aligned
     assert f(None, None, 10, None, 1, 0, 64, 512, 8, None, None, None, 128, 1.0, None, None, None, 0, None) == 0
