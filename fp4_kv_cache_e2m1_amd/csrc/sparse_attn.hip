@@ -280,9 +280,10 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
 //     waves hold the same scores;
 //   - every wave runs the same online softmax (identical inputs and arithmetic, so the running
 //     (max, sum) agree across the sub-group), then O^T += X^T P^T for its 128 channels over the
-//     chunk (16x16x16 f16 MFMA). The A operand (4 consecutive entries of one channel per lane)
-//     comes straight from X through the transposing LDS read ds_read_b64_tr_b16; the B operand
-//     (4 entries of one head per lane) is the lane's own softmax output.
+//     chunk (16x16x32 f16 MFMA, the chunk's two 16-entry halves as one operand). The A operand
+//     (8 entries of one channel per lane) comes straight from X through two transposing LDS
+//     reads ds_read_b64_tr_b16; the B operand (the same 8 entries of one head per lane) is the
+//     lane's own softmax output.
 // At the end the sub-groups' (max, sum, output) states merge in LDS, so a query row needs no
 // second kernel unless its entries are also split over workgroups. The gathers of the next PF
 // chunks are in flight while a chunk is processed (the query is loaded first, so it does not
@@ -932,18 +933,20 @@ __global__ __launch_bounds__(256 * NG) void swa_attn_kernel(
 // 128w .. 128w+127 throughout, as in the decode form, but every wave serves all 64 heads:
 //   - gather + dequantize: a lane fetches one entry's 64-channel slab (32 code bytes, 4 scale
 //     bytes) straight into registers, PF chunks ahead, and writes it as f16 (exact) into the
-//     wave's own slab of X[entry][channel], which only that wave reads;
+//     wave's own slab of X[entry][channel], which only that wave reads (window chunks: 64 FP8
+//     codes and the row's exponent of one window row, the same way);
 //   - partial scores S^T = X Q^T over the wave's 128 channels for 32 entries x 64 heads
 //     (16x16x32 f16 MFMA); each X fragment read from LDS feeds the four 16-head tiles;
 //   - the four partials meet in LDS (the chunk's first barrier); wave w then owns head tile w:
 //     it adds them, runs the online softmax of those 16 heads (fp32, exp2 domain, lazy rescale)
 //     and publishes their probabilities (f16, already in the B-operand layout of P.V) and
 //     rescale factors (the second barrier);
-//   - O^T += X^T P^T for the wave's channels and all 64 heads (16x16x16 f16 MFMA, the A operand
+//   - O^T += X^T P^T for the wave's channels and all 64 heads (16x16x32 f16 MFMA, the A operand
 //     from the transposing LDS read ds_read_b64_tr_b16), after applying the published factors.
-// At 256 registers per lane and ~76 KB of LDS two workgroups share a CU, so one's gathers and
-// softmax overlap the other's matrix work. Workgroups of consecutive query rows, whose selections
-// overlap, run on one XCD and share its L2.
+// The selected entries' chunks come first, then (for the windowed call) the query's window rows
+// as further chunks of the same softmax. At 256 registers per lane and ~77 KB of LDS two
+// workgroups share a CU, so one's gathers and softmax overlap the other's matrix work.
+// Workgroups of consecutive query rows, whose selections overlap, run on one XCD and share its L2.
 constexpr int kPKC = 32;                         // prefill entries per chunk
 constexpr int kPXPitch = kD + 24;                // f16 elements per X row of the prefill form (measured best)
 
