@@ -584,6 +584,7 @@ def test_index_scores_mxfp4_exact_blocks():
 
 
 @pytest.mark.parametrize("B,T,H,N,K,Wn,p0", [(1, 600, 64, 700, 64, 128, 50), (2, 260, 64, 900, 300, 100, 0),
+                                             (1, 520, 128, 600, 64, 32, -3),
                                              (2, 40, 16, 300, 33, 64, 10),
                                              (1, 520, 32, 200, 40, 100, 500), (1, 3, 16, 20, 0, 8, 0),
                                              (2, 1, 16, 300, 33, 64, 10), (3, 1, 64, 500, 64, 128, 1000)])
@@ -591,7 +592,8 @@ def test_sparse_attn_swa_prefill(B, T, H, N, K, Wn, p0):
     """Prefill with each query token's own window (its last n tokens up to its own, n < W near the
     start of the sequence) joined to its selected entries, against the oracle: the 64-head prefill
     form with the window as further chunks of its own pass (600 rows; two sequences with ragged
-    selections and windows, from 1 to 100 rows), the decode form with several query tokens (split path), the wide
+    selections and windows, from 1 to 100 rows; 128 heads in two groups with one-chunk windows,
+    the first three tokens' windows empty), the decode form with several query tokens (split path), the wide
     32-head form, no selected entries, and one-token chunks (T = 1: the window buffer holds W rows
     and the token takes its last n of them, with n < W and n = W)."""
     rows, qb, idx = _attn_case(B, T, H, N, K, seed=T + K + Wn, oob=K > 0) if K > 0 else _attn_case(B, T, H, N, 1, seed=5)
@@ -600,7 +602,7 @@ def test_sparse_attn_swa_prefill(B, T, H, N, K, Wn, p0):
     g = np.random.default_rng(T + Wn)
     codes, exps = O.quantize_swa_fp8(g.standard_normal((B * (T + Wn - 1), 512)).astype(np.float32))
     codes, exps = codes.reshape(B, T + Wn - 1, 512), exps.reshape(B, T + Wn - 1)
-    n_win = np.array([[min(Wn, p0 + t + 1) for t in range(T)] for _ in range(B)], np.int32)
+    n_win = np.array([[max(0, min(Wn, p0 + t + 1)) for t in range(T)] for _ in range(B)], np.int32)
     scale = 1 / np.sqrt(512)
     out, lse = P.sparse_attn_swa_prefill(dev_bf16(qb), torch.from_numpy(rows).cuda(), torch.from_numpy(idx).cuda(),
                                          torch.from_numpy(codes).cuda(), torch.from_numpy(exps).cuda(),
