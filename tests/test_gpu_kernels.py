@@ -613,3 +613,28 @@ def test_sparse_attn_swa_prefill(B, T, H, N, K, Wn, p0):
         clean = np.where((idx[b] >= 0) & (idx[b] < N), idx[b], -1)
         ref, lref = O.sparse_attn_swa(f64(qb[b]), O.dequant_kv_fp4(rows[b]), clean, win, n_win[b], scale)
         check_attn(out[b], ref, lse[b], lref, f"swa prefill B={B} T={T} H={H} K={K} b={b}")
+
+
+@pytest.mark.timeout(300)
+def test_sparse_attn_swa_prefill_full_size():
+    """The windowed prefill call at the prefill workload's full size, in the launch the bench times
+    (T = 4096 tokens, 33792 entries, 64 heads, Top-1024, 128-row windows, partial windows for the
+    first tokens of the sequence): sampled query rows against the oracle, one by one."""
+    T, N, H, K, Wn, p0 = 4096, 33792, 64, 1024, 128, 60
+    rng = np.random.default_rng(11)
+    rows = O.quantize_kv_fp4(rng.standard_normal((N, 512)).astype(np.float32))
+    qb = W.to_bf16_bits(rng.standard_normal((T, H, 512), dtype=np.float32))
+    idx = rng.integers(0, N, size=(T, K), dtype=np.int32)
+    idx[:, ::97] = -1
+    codes, exps = O.quantize_swa_fp8(rng.standard_normal((T + Wn - 1, 512)).astype(np.float32))
+    n_win = np.array([min(Wn, p0 + t + 1) for t in range(T)], np.int32)
+    scale = 1 / np.sqrt(512)
+    out, lse = P.sparse_attn_swa_prefill(dev_bf16(qb[None]), torch.from_numpy(rows[None]).cuda(),
+                                         torch.from_numpy(idx[None]).cuda(), torch.from_numpy(codes[None]).cuda(),
+                                         torch.from_numpy(exps[None]).cuda(), torch.from_numpy(n_win[None]).cuda(),
+                                         scale)
+    tr = np.array([0, 1, 59, 60, 61, 127, 2048, 4095])
+    out, lse = _sync_np(out)[0, tr], _sync_np(lse)[0, tr]
+    win = O.prefill_windows(O.dequant_swa_fp8(codes, exps), n_win, Wn)[tr]
+    ref, lref = O.sparse_attn_swa(f64(qb[tr]), O.dequant_kv_fp4(rows), idx[tr], win, n_win[tr], scale)
+    check_attn(out, ref, lse, lref, "windowed prefill at full size")
