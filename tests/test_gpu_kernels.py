@@ -619,7 +619,8 @@ def test_sparse_attn_swa_prefill(B, T, H, N, K, Wn, p0):
 def test_sparse_attn_swa_prefill_full_size():
     """The windowed prefill call at the prefill workload's full size, in the launch the bench times
     (T = 4096 tokens, 33792 entries, 64 heads, Top-1024, 128-row windows, partial windows for the
-    first tokens of the sequence): sampled query rows against the oracle, one by one."""
+    first tokens of the sequence): sampled query rows against the oracle, one by one, and two
+    identical calls bit-identical."""
     T, N, H, K, Wn, p0 = 4096, 33792, 64, 1024, 128, 60
     rng = np.random.default_rng(11)
     rows = O.quantize_kv_fp4(rng.standard_normal((N, 512)).astype(np.float32))
@@ -629,10 +630,12 @@ def test_sparse_attn_swa_prefill_full_size():
     codes, exps = O.quantize_swa_fp8(rng.standard_normal((T + Wn - 1, 512)).astype(np.float32))
     n_win = np.array([min(Wn, p0 + t + 1) for t in range(T)], np.int32)
     scale = 1 / np.sqrt(512)
-    out, lse = P.sparse_attn_swa_prefill(dev_bf16(qb[None]), torch.from_numpy(rows[None]).cuda(),
-                                         torch.from_numpy(idx[None]).cuda(), torch.from_numpy(codes[None]).cuda(),
-                                         torch.from_numpy(exps[None]).cuda(), torch.from_numpy(n_win[None]).cuda(),
-                                         scale)
+    args = (dev_bf16(qb[None]), torch.from_numpy(rows[None]).cuda(), torch.from_numpy(idx[None]).cuda(),
+            torch.from_numpy(codes[None]).cuda(), torch.from_numpy(exps[None]).cuda(),
+            torch.from_numpy(n_win[None]).cuda(), scale)
+    out, lse = P.sparse_attn_swa_prefill(*args)
+    out2, lse2 = P.sparse_attn_swa_prefill(*args)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2), "two identical calls differ"
     tr = np.array([0, 1, 59, 60, 61, 127, 2048, 4095])
     out, lse = _sync_np(out)[0, tr], _sync_np(lse)[0, tr]
     win = O.prefill_windows(O.dequant_swa_fp8(codes, exps), n_win, Wn)[tr]
