@@ -328,7 +328,7 @@ def sparse_attn_swa_prefill(q: torch.Tensor, rows: torch.Tensor, idx: torch.Tens
     lse = torch.empty(B, T, H, dtype=torch.float32, device=dev) if with_lse else None
     L = _lib.lib()
     nbytes = L.csa2_sparse_attn_swa_prefill_workspace_size(B, T, H, D, K)
-    ws = _ws(max(nbytes, 1), dev, ws)
+    ws = _ws(nbytes, dev, ws)              # none for wide calls: the window runs inside their pass
     code = L.csa2_sparse_attn_swa_prefill(_ptr(q), _ptr(rows), N, _ptr(idx), B, T, H, D, K, _ptr(swa_codes),
                                           _ptr(swa_exp), _ptr(n_win), W, float(sm_scale), _ptr(out), _ptr(lse),
                                           _ptr(ws), nbytes, _stream(dev))
