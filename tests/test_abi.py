@@ -290,3 +290,23 @@ def test_sparse_attn_swa_prefill_validation(L):
     assert f(FAKE, FAKE, 10, FAKE, 1, 600, 32, 512, 64, FAKE, FAKE, FAKE, 128, 1.0, FAKE, None, FAKE + 16, need,
              None) == E_WS                                          # workspace not 256-byte aligned
     assert f(None, None, 10, None, 1, 0, 64, 512, 8, None, None, None, 128, 1.0, None, None, None, 0, None) == 0
+
+
+def test_compress_kv_validation(L):
+    f = L.csa2_compress_kv
+    # c, z, B, n_tok, D, ratio, entry0, n_max, rows, w_t, Hk, Di, k_idx, entries, stream
+    assert f(FAKE, FAKE, 1, 8, 256, 4, FAKE, 64, FAKE, FAKE, 8, 64, FAKE, None, None) == E_SHAPE   # D
+    assert f(FAKE, FAKE, 1, 9, 512, 3, FAKE, 64, FAKE, FAKE, 8, 64, FAKE, None, None) == E_SHAPE   # ratio 3
+    assert f(FAKE, FAKE, 1, 6, 512, 4, FAKE, 64, FAKE, FAKE, 8, 64, FAKE, None, None) == E_SHAPE   # n_tok % ratio
+    assert f(FAKE, FAKE, 1, 8, 512, 4, FAKE, 64, FAKE, FAKE, 3, 32, FAKE, None, None) == E_SHAPE   # 96 key channels
+    assert f(FAKE, FAKE, 1, 8, 512, 4, FAKE, 64, FAKE, FAKE, 8, 256, FAKE, None, None) == E_SHAPE  # 2048 > 1024
+    assert f(FAKE, FAKE, 1, 8, 512, 4, FAKE, 64, FAKE, None, 8, 64, FAKE, None, None) == E_ARG     # weight without keys
+    assert f(FAKE, FAKE, 1, 8, 512, 4, FAKE, 64, FAKE, FAKE, 8, 64, None, None, None) == E_ARG     # keys without weight
+    assert f(None, FAKE, 1, 8, 512, 4, FAKE, 64, FAKE, None, 8, 64, None, None, None) == E_ARG     # no c
+    assert f(FAKE, FAKE, 1, 8, 512, 4, None, 64, FAKE, None, 8, 64, None, None, None) == E_ARG     # no entry0
+    assert f(FAKE + 8, FAKE, 1, 8, 512, 4, FAKE, 64, FAKE, None, 8, 64, None, None, None) == E_ARG  # c misaligned
+    assert f(FAKE, FAKE, 1, 8, 512, 0, FAKE, 64, FAKE, None, 8, 64, None, None, None) == E_ARG     # ratio 0
+    assert f(FAKE, FAKE, -1, 8, 512, 4, FAKE, 64, FAKE, None, 8, 64, None, None, None) == E_ARG    # B < 0
+    # nothing to do: no call is made
+    assert f(None, None, 0, 8, 512, 4, None, 64, None, None, 8, 64, None, None, None) == OK
+    assert f(None, None, 2, 0, 512, 4, None, 64, None, None, 8, 64, None, None, None) == OK
