@@ -507,22 +507,28 @@ __global__ __launch_bounds__(kTopkThreads) void pool_topk_kernel(TopkArgs pa, To
 template <int SRC, int DST>
 static hipError_t launch_one(dim3 grid, const TopkArgs& a, int seg_len, int k, hipStream_t s) {
   const dim3 blk(kTopkThreads);
-  if (seg_len <= kTopkThreads * 1)
-    hipLaunchKernelGGL((topk_kernel<SRC, DST, 1>), grid, blk, 0, s, a, seg_len, k);
-  else if (seg_len <= kTopkThreads * 2)
-    hipLaunchKernelGGL((topk_kernel<SRC, DST, 2>), grid, blk, 0, s, a, seg_len, k);
-  else if (seg_len <= kTopkThreads * 4)
-    hipLaunchKernelGGL((topk_kernel<SRC, DST, 4>), grid, blk, 0, s, a, seg_len, k);
-  else if (seg_len <= kTopkThreads * 8)
-    hipLaunchKernelGGL((topk_kernel<SRC, DST, 8>), grid, blk, 0, s, a, seg_len, k);
-  else if (seg_len <= kTopkThreads * 16)
-    hipLaunchKernelGGL((topk_kernel<SRC, DST, 16>), grid, blk, 0, s, a, seg_len, k);
-  else if (seg_len <= kTopkThreads * 24)
-    hipLaunchKernelGGL((topk_kernel<SRC, DST, 24>), grid, blk, 0, s, a, seg_len, k);
-  else if (seg_len <= kTopkThreads * 32)
-    hipLaunchKernelGGL((topk_kernel<SRC, DST, 32>), grid, blk, 0, s, a, seg_len, k);
-  else
-    hipLaunchKernelGGL((topk_kernel<SRC, DST, 40>), grid, blk, 0, s, a, seg_len, k);
+#define CSA2_TOPK_EPL(E)                                                          \
+  if (seg_len <= kTopkThreads * (E)) {                                             \
+    hipLaunchKernelGGL((topk_kernel<SRC, DST, E>), grid, blk, 0, s, a, seg_len, k); \
+    return hipGetLastError();                                                      \
+  }
+  // Whole score rows (prefill, one workgroup per row) take register counts in steps of 4 and the
+  // 33 of a 33792-column row (32768 + 1024 entries): loads and per-register passes over register
+  // rows that only repeat a row's last column are the selection's main waste at these lengths.
+  constexpr bool kRows = SRC == kSrcScores && DST == kDstIdx;
+  CSA2_TOPK_EPL(1)
+  CSA2_TOPK_EPL(2)
+  CSA2_TOPK_EPL(4)
+  CSA2_TOPK_EPL(8)
+  if constexpr (kRows) { CSA2_TOPK_EPL(12) }
+  CSA2_TOPK_EPL(16)
+  if constexpr (kRows) { CSA2_TOPK_EPL(20) }
+  CSA2_TOPK_EPL(24)
+  if constexpr (kRows) { CSA2_TOPK_EPL(28) }
+  CSA2_TOPK_EPL(32)
+  if constexpr (kRows) { CSA2_TOPK_EPL(33) CSA2_TOPK_EPL(36) }
+#undef CSA2_TOPK_EPL
+  hipLaunchKernelGGL((topk_kernel<SRC, DST, 40>), grid, blk, 0, s, a, seg_len, k);
   return hipGetLastError();
 }
 

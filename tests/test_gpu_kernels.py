@@ -181,6 +181,19 @@ def test_topk_bitexact(rows, n, k, dist):
     assert np.array_equal(got, want), f"rows differ: {np.where((got != want).any(1))[0][:5]}"
 
 
+@pytest.mark.parametrize("n", [10000, 19000, 27000, 33792, 35000, 40960])
+@pytest.mark.parametrize("dist", ["normal", "ties"])
+def test_topk_whole_rows_bitexact(n, dist):
+    """Many rows (one workgroup per whole row, as in prefill) at row lengths that take each register
+    count of that form (12, 20, 28, 33, 36, 40 columns per lane), with ragged valid counts."""
+    rows, k = 260, 1024
+    s = W.random_scores(n + 7, rows, n, dist)
+    nv = np.array([n - (r * 131) % (n // 2) for r in range(rows)], np.int32)
+    got = _sync_np(P.topk(torch.from_numpy(s).cuda(), k, n_valid=torch.from_numpy(nv).cuda()))
+    want = O.topk(s, k, n_valid=nv)
+    assert np.array_equal(got, want), f"rows differ: {np.where((got != want).any(1))[0][:5]}"
+
+
 def test_topk_const_rows_and_pool_columns():
     s = W.random_scores(3, 4, 3000, "const")
     got = _sync_np(P.topk(torch.from_numpy(s).cuda(), 100))
