@@ -25,7 +25,9 @@
 //   3. compaction in ascending column order with ballot + mbcnt per register row (no shuffles),
 //      so the result is deterministic.
 // With many rows (prefill) one workgroup per row keeps the chip busy, so rows up to 40960 columns
-// are one segment. With few rows (decode) rows longer than 32768 columns are split for
+// are one segment; such whole rows run a lean form that fits two workgroups on a CU (a row's loads
+// are exposed latency otherwise: every CU loads its row at the same time, then selects while HBM
+// idles). With few rows (decode) rows longer than 32768 columns are split for
 // parallelism: each segment's k best (key, position) pairs go to scratch, and the same kernel
 // selects again over those candidates; the global k best always survive their segment.
 #include <algorithm>
@@ -161,11 +163,11 @@ CSA2_DEV uint32_t prefix_mask(int rb) { return rb >= 32 ? 0u : ~0u << rb; }
 // barrier: a phase fills its buffer, clears the one two phases ahead, and every wave then reads
 // its own copy of the answer; the buffer cleared in a phase was last read before the previous
 // phase's barrier.
-template <int NLIST>
+template <int NLIST, typename PosT = int32_t>
 struct TopkSmem {
   TopkHist hist[3];
   uint32_t list_key[NLIST];      // survivors of the pruning bound, in column order
-  int32_t list_pos[NLIST];
+  PosT list_pos[NLIST];           // uint16_t: column within the segment
   int totals[3];                 // valid columns, non-empty lane groups, non-empty half groups
   uint32_t kmax, kmin;           // largest and smallest key
   uint32_t gmin[2];              // smallest non-empty group maximum (whole, half groups)
@@ -180,8 +182,8 @@ struct TopkSmem {
 // selection so far are close in value, and a digit over bits they all share would send them to
 // a few bins, whose LDS atomics then serialize. DENSE: most register slots hold candidates. The
 // first radix pass fills hist[1] (clear on entry) and clears hist[2].
-template <int SRC, int DST, int R, bool EXPL, bool DENSE, int NPOS, int NLIST>
-CSA2_DEV void topk_finish(const TopkArgs& a, TopkSmem<NLIST>& sm, uint32_t (&key)[R], const int32_t (&pos)[NPOS],
+template <int SRC, int DST, int R, bool EXPL, bool DENSE, int NPOS, int NLIST, typename PosT>
+CSA2_DEV void topk_finish(const TopkArgs& a, TopkSmem<NLIST, PosT>& sm, uint32_t (&key)[R], const int32_t (&pos)[NPOS],
                           int col0, int k, int kk, bool sel, uint32_t lo0, uint32_t hi0, int r, int seg) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -304,8 +306,10 @@ CSA2_DEV void topk_finish(const TopkArgs& a, TopkSmem<NLIST>& sm, uint32_t (&key
 }
 
 // Selection of the k best columns of segment `seg` of row r by the whole workgroup.
-template <int SRC, int DST, int EPL, int NLIST>
-CSA2_DEV void topk_segment(const TopkArgs& a, int seg_len, int k, TopkSmem<NLIST>& sm, int r, int seg) {
+template <int SRC, int DST, int EPL, bool LEAN = false, int NLIST, typename PosT>
+CSA2_DEV void topk_segment(const TopkArgs& a, int seg_len, int k, TopkSmem<NLIST, PosT>& sm, int r, int seg) {
+  static_assert(!LEAN || SRC == kSrcScores, "lean form reloads scores");
+  static_assert(sizeof(PosT) == 4 || SRC == kSrcScores, "16-bit list positions are segment columns");
   // pruning survivors are packed when there are more than 4 registers per lane to gain from it
   constexpr bool kPack = EPL > 4;
   static_assert(!kPack || NLIST >= kCompact, "room for the packed survivors");
@@ -328,7 +332,16 @@ CSA2_DEV void topk_segment(const TopkArgs& a, int seg_len, int k, TopkSmem<NLIST
   uint32_t key[EPL];
   int32_t pos[NP];
   float sv[EPL];
-  if (lim > 0) {
+  // the segment's valid columns as a buffer: loads past lim return 0 (and are masked below)
+  const uint64_t ra = SRC == kSrcScores ? reinterpret_cast<uint64_t>(a.scores + rowoff) : 0u;
+  const uint32_t ra_lo = __builtin_amdgcn_readfirstlane((uint32_t)ra), ra_hi = __builtin_amdgcn_readfirstlane((uint32_t)(ra >> 32));
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(((uint64_t)ra_hi << 32) | ra_lo), 0, SRC == kSrcScores ? max(lim, 0) * 4 : 0, 0x00020000);
+  const int vo = (wbase + lane) * 4;
+  if (SRC == kSrcScores && lim > 0) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) sv[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, vo + 256 * i, 0, 0));
+  } else if (lim > 0) {
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = min(wbase + 64 * i + lane, lim - 1);  // clamped: every load is in bounds
@@ -416,6 +429,17 @@ CSA2_DEV void topk_segment(const TopkArgs& a, int seg_len, int k, TopkSmem<NLIST
   const bool halves = EPL >= 8 && 2 * kk > sm.totals[1];
   const int ng = sm.totals[halves ? 2 : 1];
 
+  // lean form: the keys are not kept past the packing pass; the paths that need all of them read
+  // the row again (floor_key: the pruning bound, or 1 for every valid column)
+  auto reload = [&](uint32_t floor_key) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) sv[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, vo + 256 * i, 0, 0));
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const uint32_t kv = wbase + 64 * i + lane < lim ? score_key(sv[i]) : 0u;
+      key[i] = kv >= floor_key ? kv : 0u;
+    }
+  };
   // 1. pruning bound: at least kk (disjoint) group maxima are >= the kk-th largest group maximum,
   //    so the kk-th best column is too; every column below that maximum's bin is dropped. The
   //    bins are up to 12 bits below the common prefix of the group maxima.
@@ -456,7 +480,8 @@ CSA2_DEV void topk_segment(const TopkArgs& a, int seg_len, int k, TopkSmem<NLIST
         const int j = o + lanes_below(m);
         if (live && j < kWaveSlots) {
           sm.list_key[wave * kWaveSlots + j] = key[i];
-          sm.list_pos[wave * kWaveSlots + j] = SRC != kSrcScores ? pos[i % NP] : c0 + wbase + 64 * i + lane;
+          sm.list_pos[wave * kWaveSlots + j] =
+              (PosT)(SRC != kSrcScores ? pos[i % NP] : (sizeof(PosT) == 4 ? c0 : 0) + wbase + 64 * i + lane);
         }
         o += (int)__popcll(m);
       }
@@ -470,16 +495,18 @@ CSA2_DEV void topk_segment(const TopkArgs& a, int seg_len, int k, TopkSmem<NLIST
         for (int u = 0; u < 4; ++u) {
           const int j = 64 * u + lane;
           key4[u] = j < o ? sm.list_key[wave * kWaveSlots + j] : 0u;
-          pos4[u] = sm.list_pos[wave * kWaveSlots + j];
+          pos4[u] = (int32_t)sm.list_pos[wave * kWaveSlots + j] + (sizeof(PosT) == 4 ? 0 : c0);
         }
         topk_finish<SRC, DST, 4, true, false>(a, sm, key4, pos4, 0, k, kk, true, L, kmax, r, seg);
         return;
       }
       // wcnt is rewritten only after the next barrier, which every wave reaches after reading it
     }
+    if constexpr (LEAN) reload(L);
     topk_finish<SRC, DST, EPL, SRC != kSrcScores, true>(a, sm, key, pos, c0 + wbase, k, kk, true, L, kmax, r, seg);
     return;
   }
+  if constexpr (LEAN) reload(1u);
   topk_finish<SRC, DST, EPL, SRC != kSrcScores, true>(a, sm, key, pos, c0 + wbase, k, kk, sel, kmin, kmax, r, seg);
 }
 
@@ -487,6 +514,17 @@ template <int SRC, int DST, int EPL>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a, int seg_len, int k) {
   __shared__ TopkSmem<(EPL > 4 ? kCompact : 1)> sm;
   topk_segment<SRC, DST, EPL>(a, seg_len, k, sm, blockIdx.x, blockIdx.y);
+}
+
+// Whole score rows (one segment per row, k best as indices): the lean form. Keys live in registers
+// only until the pruning survivors are packed (the rare paths that need every key again read the
+// row again), and list positions are 16-bit segment columns, so the kernel fits 64 registers per
+// lane and 75 KB of LDS: two rows share a CU, and one row's loads run under the other's selection.
+template <int EPL>
+__global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8))) void topk_rows_kernel(
+    TopkArgs a, int seg_len, int k) {
+  __shared__ TopkSmem<kCompact, uint16_t> sm;
+  topk_segment<kSrcScores, kDstIdx, EPL, true>(a, seg_len, k, sm, blockIdx.x, blockIdx.y);
 }
 
 // HSI Full layer in one workgroup per row: the pool (the k_blocks best blocks of the block
@@ -507,15 +545,18 @@ __global__ __launch_bounds__(kTopkThreads) void pool_topk_kernel(TopkArgs pa, To
 template <int SRC, int DST>
 static hipError_t launch_one(dim3 grid, const TopkArgs& a, int seg_len, int k, hipStream_t s) {
   const dim3 blk(kTopkThreads);
-#define CSA2_TOPK_EPL(E)                                                          \
-  if (seg_len <= kTopkThreads * (E)) {                                             \
-    hipLaunchKernelGGL((topk_kernel<SRC, DST, E>), grid, blk, 0, s, a, seg_len, k); \
-    return hipGetLastError();                                                      \
+  constexpr bool kRows = SRC == kSrcScores && DST == kDstIdx;
+#define CSA2_TOPK_EPL(E)                                                                \
+  if (seg_len <= kTopkThreads * (E)) {                                                   \
+    if constexpr (kRows && (E) >= 8)                                                     \
+      hipLaunchKernelGGL((topk_rows_kernel<E>), grid, blk, 0, s, a, seg_len, k);         \
+    else                                                                                 \
+      hipLaunchKernelGGL((topk_kernel<SRC, DST, E>), grid, blk, 0, s, a, seg_len, k);   \
+    return hipGetLastError();                                                            \
   }
   // Whole score rows (prefill, one workgroup per row) take register counts in steps of 4 and the
   // 33 of a 33792-column row (32768 + 1024 entries): loads and per-register passes over register
   // rows that only repeat a row's last column are the selection's main waste at these lengths.
-  constexpr bool kRows = SRC == kSrcScores && DST == kDstIdx;
   CSA2_TOPK_EPL(1)
   CSA2_TOPK_EPL(2)
   CSA2_TOPK_EPL(4)
@@ -528,7 +569,10 @@ static hipError_t launch_one(dim3 grid, const TopkArgs& a, int seg_len, int k, h
   CSA2_TOPK_EPL(32)
   if constexpr (kRows) { CSA2_TOPK_EPL(33) CSA2_TOPK_EPL(36) }
 #undef CSA2_TOPK_EPL
-  hipLaunchKernelGGL((topk_kernel<SRC, DST, 40>), grid, blk, 0, s, a, seg_len, k);
+  if constexpr (kRows)
+    hipLaunchKernelGGL((topk_rows_kernel<40>), grid, blk, 0, s, a, seg_len, k);
+  else
+    hipLaunchKernelGGL((topk_kernel<SRC, DST, 40>), grid, blk, 0, s, a, seg_len, k);
   return hipGetLastError();
 }
 

@@ -181,14 +181,27 @@ def test_topk_bitexact(rows, n, k, dist):
     assert np.array_equal(got, want), f"rows differ: {np.where((got != want).any(1))[0][:5]}"
 
 
-@pytest.mark.parametrize("n", [10000, 19000, 27000, 33792, 35000, 40960])
-@pytest.mark.parametrize("dist", ["normal", "ties"])
+@pytest.mark.parametrize("n", [7000, 10000, 19000, 27000, 33792, 35000, 40960])
+@pytest.mark.parametrize("dist", ["normal", "ties", "const", "signed_zero"])
 def test_topk_whole_rows_bitexact(n, dist):
     """Many rows (one workgroup per whole row, as in prefill) at row lengths that take each register
-    count of that form (12, 20, 28, 33, 36, 40 columns per lane), with ragged valid counts."""
+    count of that form (8, 12, 20, 28, 33, 36, 40 columns per lane), with ragged valid counts. Tied,
+    constant and ±0 rows overflow the packed survivor list, and rows with few valid columns skip
+    the pruning bound: both read the row again in this form."""
     rows, k = 260, 1024
     s = W.random_scores(n + 7, rows, n, dist)
     nv = np.array([n - (r * 131) % (n // 2) for r in range(rows)], np.int32)
+    got = _sync_np(P.topk(torch.from_numpy(s).cuda(), k, n_valid=torch.from_numpy(nv).cuda()))
+    want = O.topk(s, k, n_valid=nv)
+    assert np.array_equal(got, want), f"rows differ: {np.where((got != want).any(1))[0][:5]}"
+
+
+def test_topk_whole_rows_short_and_empty():
+    """A many-row call whose rows hold 0 to ~2000 valid columns of 33792: empty rows, rows with
+    fewer valid columns than k (no selection, everything taken) and rows just above k."""
+    rows, n, k = 300, 33792, 1024
+    s = W.random_scores(5, rows, n, "normal")
+    nv = np.array([(r * 7) % 2100 for r in range(rows)], np.int32)
     got = _sync_np(P.topk(torch.from_numpy(s).cuda(), k, n_valid=torch.from_numpy(nv).cuda()))
     want = O.topk(s, k, n_valid=nv)
     assert np.array_equal(got, want), f"rows differ: {np.where((got != want).any(1))[0][:5]}"
