@@ -13,6 +13,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <atomic>
+
 namespace csa2 {
 
 constexpr int kIdxThreads = 256;           // 4 waves, 32 rows per row step
@@ -163,6 +165,24 @@ static hipError_t launch_nch(bool shared, bool pool, bool bmax, dim3 grid, hipSt
   return hipGetLastError();
 }
 
+int device_cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 hipError_t launch_index_stream(const uint16_t* q, const uint16_t* k, int B, int T, int Hi, int Hk,
                                int Di, int n_max, const int32_t* n_vis, const int32_t* cand, int P,
                                float* scores, float* block_max, hipStream_t s) {
@@ -171,16 +191,27 @@ hipError_t launch_index_stream(const uint16_t* q, const uint16_t* k, int B, int 
   if (rows == 0 || ncols == 0) return hipSuccess;
   const int ch = Hk * Di * 2 / 16;  // 16-byte chunks per key row (multiple of 8)
   const int nch = ch / 8;
-  // Tile size: enough workgroups to cover the chip several times over, in whole iterations (short
-  // key rows take 8 / nch rows per lane group and iteration).
+  // Tile size. Flat scoring of rows of 1 KiB or more: one workgroup per CU when the rows split
+  // evenly enough, each streaming one contiguous tile (4 x 262144 and 16 x 65536 entries:
+  // 165 -> 151 us, 7.1 TB/s; a grid just over one workgroup per CU is much slower, its second
+  // round running on a few CUs, and two per CU are no faster than many). Otherwise enough
+  // workgroups to cover the chip several times over, in whole iterations (short key rows take
+  // 8 / nch rows per lane group and iteration).
+  const int cus = device_cu_count();
+  const int per_row = rows <= cus ? cus / rows : 0;
   int tile_rows = kRowsPerIter * (nch >= 8 ? 1 : 8 / nch);
-  while (tile_rows < 1024 && (int64_t)((ncols + 2 * tile_rows - 1) / (2 * tile_rows)) * rows >= 2048)
-    tile_rows *= 2;
-  // short key rows: a workgroup streams as many bytes as it would with 1 KiB rows when the grid
-  // keeps at least 512 workgroups (measured: 256-byte rows, 4 x 262144 entries, 54 -> 47 us)
-  if (nch < 8) {
-    const int big = tile_rows * (8 / nch);
-    if ((int64_t)((ncols + big - 1) / big) * rows >= 512) tile_rows = big;
+  if (!cand && nch >= 8 && per_row > 0 && 4 * (int64_t)rows * per_row >= 3 * (int64_t)cus &&
+      ncols >= per_row * kRowsPerIter) {
+    tile_rows = ((ncols + per_row - 1) / per_row + kRowsPerIter - 1) / kRowsPerIter * kRowsPerIter;
+  } else {
+    while (tile_rows < 1024 && (int64_t)((ncols + 2 * tile_rows - 1) / (2 * tile_rows)) * rows >= 2048)
+      tile_rows *= 2;
+    // short key rows: a workgroup streams as many bytes as it would with 1 KiB rows when the grid
+    // keeps at least 512 workgroups (measured: 256-byte rows, 4 x 262144 entries, 54 -> 47 us)
+    if (nch < 8) {
+      const int big = tile_rows * (8 / nch);
+      if ((int64_t)((ncols + big - 1) / big) * rows >= 512) tile_rows = big;
+    }
   }
   while ((ncols + tile_rows - 1) / tile_rows > 65535) tile_rows *= 2;  // grid.y limit
   dim3 grid((unsigned)rows, (unsigned)((ncols + tile_rows - 1) / tile_rows));

@@ -15,6 +15,9 @@ hipError_t launch_quantize(const void* src, bool bf16, int64_t n_rows, int dim, 
                            hipStream_t s);
 hipError_t launch_dequant(const uint8_t* rows, int64_t n_rows, int dim, float* out, hipStream_t s);
 
+// Compute units of the current device (queried once per device; 256 if the query fails).
+int device_cu_count();
+
 // index_decode.hip: streaming indexer (flat or pool), optional fused 8-block max
 hipError_t launch_index_stream(const uint16_t* q, const uint16_t* k, int B, int T, int Hi, int Hk,
                                int Di, int n_max, const int32_t* n_vis, const int32_t* cand, int P,
