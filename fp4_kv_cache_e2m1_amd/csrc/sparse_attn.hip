@@ -1105,18 +1105,21 @@ __global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
     {
       float tv[NS][4];
       float cmax = -INFINITY;
+      // all partials are read first and masked entries get -inf added (not selected), so no read
+      // is moved into a branch
 #pragma unroll
-      for (int t = 0; t < NS; ++t) {
-        float sv[4];
+      for (int t = 0; t < NS; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float* src = spf + (t * 4 + w) * 256 + 64 * i + lane;
-          sv[i] = src[0] + src[NS * 4 * 256] + src[2 * NS * 4 * 256] + src[3 * NS * 4 * 256];
+          tv[t][i] = src[0] + src[NS * 4 * 256] + src[2 * NS * 4 * 256] + src[3 * NS * 4 * 256];
         }
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
         const uint32_t vb = (uint32_t)(vmask >> (16 * t + 4 * g)) & 15u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          tv[t][i] = ((vb >> i) & 1u) ? sv[i] * qscale : -INFINITY;
+          tv[t][i] = tv[t][i] * qscale + (((vb >> i) & 1u) ? 0.0f : -INFINITY);
           cmax = fmaxf(cmax, tv[t][i]);
         }
       }
@@ -1131,13 +1134,15 @@ __global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
         m_run = mn;
       }
       float psum = 0.0f;
+      // with no real entry yet every tv is -inf and so is m_run: exp2(-inf - 0) = 0
+      const float m_use = m_run == -INFINITY ? 0.0f : m_run;
 #pragma unroll
       for (int t = 0; t < NS; ++t) {
         f16x4_t pb;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           // exponent <= 8 (lazy rescale); v_exp_f32 directly: the result is rounded to f16 anyway
-          const _Float16 pv = m_run == -INFINITY ? (_Float16)0.0f : (_Float16)__builtin_amdgcn_exp2f(tv[t][i] - m_run);
+          const _Float16 pv = (_Float16)__builtin_amdgcn_exp2f(tv[t][i] - m_use);
           psum += (float)pv;       // normalize by the weights the f16 MFMA actually uses
           pb[i] = pv;
         }
