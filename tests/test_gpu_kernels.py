@@ -113,6 +113,29 @@ def test_index_scores_decode(B, N, Hi, Hk, Di):
         assert np.array_equal(bm[b, :nb], own)
 
 
+@pytest.mark.parametrize("B,N,Hi,Di", [(3, 50000, 8, 64), (1, 40000, 4, 128), (5, 33000, 8, 128), (200, 9000, 8, 64),
+                                       (100, 12345, 8, 64)])
+def test_index_scores_decode_one_workgroup_per_cu(B, N, Hi, Di):
+    """Flat decode scoring of 1 KiB and 2 KiB key rows at sizes that run one workgroup per CU (a few
+    rows split into up to 256 tiles whose last one is ragged, one tile per row at 200 rows, two at
+    100), with ragged visible counts (full, half, 3, 0 and scattered) and the fused block max."""
+    g = np.random.default_rng(B * N + Di)
+    qb = W.to_bf16_bits(g.standard_normal((B, 1, Hi, Di)).astype(np.float32))
+    kb = W.to_bf16_bits(g.standard_normal((B, N, Hi, Di)).astype(np.float32))
+    n_vis = np.array([N, N // 2, 3, 0] + [int(x) for x in g.integers(1, N + 1, size=max(0, B - 4))],
+                     np.int32)[:B]
+    s, bm = P.index_scores(dev_bf16(qb), dev_bf16(kb), n_vis=torch.from_numpy(n_vis).cuda(), block_max=True)
+    s, bm = _sync_np(s), _sync_np(bm)
+    for b in range(B):
+        nvb = int(n_vis[b])
+        if nvb == 0:
+            continue
+        ref = O.index_scores(f64(qb[b]), f64(kb[b, :nvb]), [nvb])[0]
+        check_scores(s[b, :nvb], ref, _abs_dot(f64(qb[b]), f64(kb[b, :nvb]))[0], np.ones(nvb, bool), f"b={b}")
+        nb = -(-nvb // 8)
+        assert np.array_equal(bm[b, :nb], O.block_max(s[b:b + 1], [nvb])[0][:nb]), f"block max b={b}"
+
+
 def test_index_scores_pool():
     g = np.random.default_rng(5)
     B, N, P_ = 3, 5000, 96
