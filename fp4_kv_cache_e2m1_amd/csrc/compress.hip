@@ -13,9 +13,11 @@
 // projection weight on v_mfma_f32_32x32x16_bf16 (exact products, fp32 accumulation), giving the
 // entry's indexer key in bf16.
 //
-// Work split: workgroup (x, y) of 8 waves owns 32 consecutive entries x of the flattened
-// (sequence, entry) list and key channels [256 y, 256 y + 256). A wave compresses 4 of the
-// entries with a lane holding 8 consecutive channels; the 16-byte loads of every token of its
+// Work split: workgroup (x, y) of 8 waves owns NE (8, 16 or 32) consecutive entries x of the
+// flattened (sequence, entry) list and key channels [256 y, 256 y + 256), NE the smallest that
+// keeps the grid to one workgroup per CU (the call is a chain of memory round trips, so spreading
+// it over the CUs shortens it: 1024 entries 24.2 -> 15.0 us, 2048 entries 25.1 -> 18.6 us). A
+// wave compresses NE / 8 of the entries with a lane holding 8 consecutive channels; the 16-byte loads of every token of its
 // entries are issued together (two rounds for 8 tokens per entry). The 8 channels are half of a
 // 16-channel scale group, so the group maximum needs one lane exchange, and the lane's eight
 // 4-bit codes are one 32-bit word of the packed row (written by the y = 0 workgroups only). The
@@ -102,25 +104,28 @@ CSA2_DEV u32x4_t bf16x8_of(const float (&e)[8]) {
   return packed;
 }
 
-template <int M>
+template <int M, int NE>
 __global__ __launch_bounds__(64 * kCmpWaves) void compress_kv_kernel(
     const uint16_t* __restrict__ c, const uint16_t* __restrict__ z, int n_tok, int n_new, int64_t n_entries,
     const int32_t* __restrict__ entry0, int n_max, uint8_t* __restrict__ rows, const uint16_t* __restrict__ w_t,
     int c_out, uint16_t* __restrict__ k_idx, float* __restrict__ entries) {
-  constexpr int EPW = kCmpEntries / kCmpWaves;     // entries per wave
-  constexpr int EB = M <= 2 ? EPW : (M == 4 ? 2 : 1);   // entries whose tokens are loaded together
+  constexpr int EPW = NE / kCmpWaves;              // entries per wave
+  static_assert(EPW >= 1 && NE <= kCmpEntries, "entries per workgroup");
+  constexpr int EB = M <= 2 ? EPW : (M == 4 ? (EPW < 2 ? EPW : 2) : 1);   // entries whose tokens are loaded together
   __shared__ __attribute__((aligned(16))) uint16_t ebf[kCmpEntries * kCmpPitch];
   __shared__ int64_t dest[kCmpEntries];            // b * n_max + entry index, or -1 (not written)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t q0 = (int64_t)blockIdx.x * kCmpEntries;
+  const int64_t q0 = (int64_t)blockIdx.x * NE;
   const bool first_cols = blockIdx.y == 0;         // writes the packed rows and fp32 entries
 
+  // rows NE .. 31 of the projection's A operand are never written: their products land in
+  // accumulator rows that are not stored (dest -1)
   if (tid < kCmpEntries) {
     const int64_t q = q0 + tid;
     int64_t d = -1;
-    if (q < n_entries) {
+    if (tid < NE && q < n_entries) {
       const int b = (int)(q / n_new), j = (int)(q % n_new);
       const int n = entry0[b] + j;
       if (n >= 0 && n < n_max) d = (int64_t)b * n_max + n;
@@ -301,15 +306,27 @@ hipError_t launch_compress_kv(const uint16_t* c, const uint16_t* z, int B, int n
   // are spread over many CUs; many entries: 32 per workgroup, 256 key channels per workgroup
   const bool small = n_entries <= 512;
   const int col_groups = k_idx ? (c_out + (small ? 32 : kCmpCols) - 1) / (small ? 32 : kCmpCols) : 1;
-  const int per = small ? kCmpSmallEntries : kCmpEntries;
+  int ne = kCmpEntries;
+  for (int cand = 8; cand < kCmpEntries; cand *= 2)
+    if ((n_entries + cand - 1) / cand * col_groups <= device_cu_count()) {
+      ne = cand;
+      break;
+    }
+  const int per = small ? kCmpSmallEntries : ne;
   const dim3 grid((unsigned)((n_entries + per - 1) / per), (unsigned)col_groups), block(small ? 256 : 64 * kCmpWaves);
 #define CSA2_CMP(M)                                                                                                \
   if (small)                                                                                                       \
     hipLaunchKernelGGL((compress_kv_small_kernel<M>), grid, block, 0, s, c, z, n_tok, n_new, n_entries, entry0,    \
                        n_max, rows, w_t, c_out, k_idx, entries);                                                   \
+  else if (ne == 8)                                                                                                \
+    hipLaunchKernelGGL((compress_kv_kernel<M, 8>), grid, block, 0, s, c, z, n_tok, n_new, n_entries, entry0, n_max, \
+                       rows, w_t, c_out, k_idx, entries);                                                            \
+  else if (ne == 16)                                                                                               \
+    hipLaunchKernelGGL((compress_kv_kernel<M, 16>), grid, block, 0, s, c, z, n_tok, n_new, n_entries, entry0,       \
+                       n_max, rows, w_t, c_out, k_idx, entries);                                                     \
   else                                                                                                             \
-    hipLaunchKernelGGL((compress_kv_kernel<M>), grid, block, 0, s, c, z, n_tok, n_new, n_entries, entry0, n_max,   \
-                       rows, w_t, c_out, k_idx, entries)
+    hipLaunchKernelGGL((compress_kv_kernel<M, 32>), grid, block, 0, s, c, z, n_tok, n_new, n_entries, entry0,       \
+                       n_max, rows, w_t, c_out, k_idx, entries)
   switch (ratio) {
     case 1: CSA2_CMP(1); break;
     case 2: CSA2_CMP(2); break;

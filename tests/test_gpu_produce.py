@@ -70,7 +70,9 @@ def _run(B, n_tok, ratio, n_max, entry0, Hk, Di, seed, project=True):
     (4, 33, 1, 40, [0, 7, 5, 2], 8, 64),               # ratio 1: the entry is the token
     (2, 4 * 5, 4, 8, [-2, 6], 8, 64),                  # entries before 0 or past n_max are skipped
     (2, 4 * 300, 4, 700, [0, 450], 1, 128),            # many entries (32-entry workgroups), ragged
-    (3, 2 * 250, 2, 300, [5, 0, 60], 8, 64)])          # many entries, 512 key channels
+    (3, 2 * 250, 2, 300, [5, 0, 60], 8, 64),           # many entries, 512 key channels
+    (1, 4 * 1500, 4, 1600, [0], 8, 64),                # 16-entry workgroups, ragged last one
+    (2, 4 * 1300, 4, 1400, [0, 200], 8, 64)])          # 32-entry workgroups, past n_max
 def test_compress_kv(B, n_tok, ratio, n_max, entry0, Hk, Di):
     cb, zb, w_bits, rows, kidx, ent = _run(B, n_tok, ratio, n_max, entry0, Hk, Di, seed=n_tok + ratio)
     n_new = n_tok // ratio
