@@ -168,9 +168,9 @@ struct TopkSmem {
   TopkHist hist[3];
   uint32_t list_key[NLIST];      // survivors of the pruning bound, in column order
   PosT list_pos[NLIST];           // uint16_t: column within the segment
-  int totals[3];                 // valid columns, non-empty lane groups, non-empty half groups
+  int totals[4];                 // valid columns, non-empty lane / half / quarter groups
   uint32_t kmax, kmin;           // largest and smallest key
-  uint32_t gmin[2];              // smallest non-empty group maximum (whole, half groups)
+  uint32_t gmin[3];              // smallest non-empty group maximum (whole, half, quarter groups)
   int wcnt[kTopkWaves][2];
 };
 
@@ -363,12 +363,13 @@ CSA2_DEV void topk_segment(const TopkArgs& a, int seg_len, int k, TopkSmem<NLIST
   // the first two phases' buffers are cleared while the loads are in flight
   clear_hist(sm.hist[0]);
   clear_hist(sm.hist[1]);
-  if (tid < 3) sm.totals[tid] = 0;
+  if (tid < 4) sm.totals[tid] = 0;
   if (tid == 0) {
     sm.kmax = 0u;
     sm.kmin = 0xFFFFFFFFu;
     sm.gmin[0] = 0xFFFFFFFFu;
     sm.gmin[1] = 0xFFFFFFFFu;
+    sm.gmin[2] = 0xFFFFFFFFu;
   }
   __syncthreads();
   if (lim > 0) {
@@ -391,14 +392,19 @@ CSA2_DEV void topk_segment(const TopkArgs& a, int seg_len, int k, TopkSmem<NLIST
 #pragma unroll
     for (int i = 0; i < EPL; ++i) key[i] = 0u;
   }
-  // group maxima: a lane's EPL columns (gm) and its two halves (gh[0], gh[1])
+  // group maxima: a lane's EPL columns (gm), its two halves (gh[0], gh[1]) and, for pool block
+  // selections (k of the order of the lane count or more), its four quarters (gq)
   constexpr int HALF = EPL >= 8 ? EPL / 2 : EPL;
+  constexpr bool kQuarters = DST == kDstExpand && EPL >= 16;
+  constexpr int QTR = EPL / 4;
   int cnt = 0;
   uint32_t gh[2] = {0u, 0u}, mn = 0u;       // mn: complement of the smallest key
+  uint32_t gq[kQuarters ? 4 : 1] = {};
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     cnt += key[i] != 0;
     gh[i / HALF > 0] = max(gh[i / HALF > 0], key[i]);
+    if constexpr (kQuarters) gq[min(3, i / QTR)] = max(gq[min(3, i / QTR)], key[i]);
     mn = max(mn, key[i] ? ~key[i] : 0u);
   }
   const uint32_t gm = max(gh[0], gh[1]);
@@ -418,16 +424,32 @@ CSA2_DEV void topk_segment(const TopkArgs& a, int seg_len, int k, TopkSmem<NLIST
       atomicMin(&sm.gmin[0], ~wgmn);
       atomicMin(&sm.gmin[1], ~whmn);
     }
+    if constexpr (kQuarters) {
+      int wq = 0;
+      uint32_t qmn = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        wq += (int)__popcll(__ballot(gq[j] != 0));
+        qmn = max(qmn, gq[j] ? ~gq[j] : 0u);
+      }
+      const uint32_t wqmn = wave_max(qmn);
+      if (lane == 0) {
+        atomicAdd(&sm.totals[3], wq);
+        atomicMin(&sm.gmin[2], ~wqmn);
+      }
+    }
   }
   __syncthreads();
   const int total = sm.totals[0];
   const uint32_t kmax = sm.kmax, kmin = sm.kmin;
   const int kk = min(k, total);
   const bool sel = kk > 0 && kk < total;
-  // half groups when kk is more than half the lane groups: the kk-th largest of the lane group
-  // maxima would be a weak bound
+  // half groups when kk is more than half the lane groups (the kk-th largest of the lane group
+  // maxima would be a weak bound), quarter groups when it is more than half the half groups too
   const bool halves = EPL >= 8 && 2 * kk > sm.totals[1];
-  const int ng = sm.totals[halves ? 2 : 1];
+  const bool quarters = kQuarters && halves && 2 * kk > sm.totals[2];
+  const int level = quarters ? 2 : (halves ? 1 : 0);
+  const int ng = sm.totals[level + 1];
 
   // lean form: the keys are not kept past the packing pass; the paths that need all of them read
   // the row again (floor_key: the pruning bound, or 1 for every valid column)
@@ -444,7 +466,7 @@ CSA2_DEV void topk_segment(const TopkArgs& a, int seg_len, int k, TopkSmem<NLIST
   //    so the kk-th best column is too; every column below that maximum's bin is dropped. The
   //    bins are up to 12 bits below the common prefix of the group maxima.
   if (EPL >= 4 && sel && ng >= kk) {
-    const uint32_t gmin = sm.gmin[halves ? 1 : 0];
+    const uint32_t gmin = sm.gmin[level];
     const int rb = low_bits(gmin, kmax);
     uint32_t L = kmax;                      // all group maxima equal
     if (rb > 0) {
@@ -452,7 +474,11 @@ CSA2_DEV void topk_segment(const TopkArgs& a, int seg_len, int k, TopkSmem<NLIST
       // every positive one in a single bin
       const int bits = min(12, rb), shift = rb - bits, fshift = max(0, bits - 6);
       const uint32_t dm = (1u << bits) - 1u;
-      if (halves) {
+      if (quarters) {
+#pragma unroll
+        for (int j = 0; j < (kQuarters ? 4 : 0); ++j)
+          if (gq[kQuarters ? j : 0] != 0) hist_add<true>(sm.hist[0], (gq[kQuarters ? j : 0] >> shift) & dm, fshift);
+      } else if (halves) {
         if (gh[0] != 0) hist_add<true>(sm.hist[0], (gh[0] >> shift) & dm, fshift);
         if (gh[1] != 0) hist_add<true>(sm.hist[0], (gh[1] >> shift) & dm, fshift);
       } else {

@@ -242,7 +242,8 @@ def test_topk_const_rows_and_pool_columns():
     assert np.array_equal(got, O.topk(s, 256, col_to_pos=pool))
 
 
-@pytest.mark.parametrize("rows,n_pos,n_sel", [(2, 4003, 64), (4, 262144, 1024), (3, 800, 200), (1, 80, 16)])
+@pytest.mark.parametrize("rows,n_pos,n_sel", [(2, 4003, 64), (4, 262144, 1024), (3, 800, 200), (1, 80, 16),
+                                            (2, 262144, 2048), (3, 200000, 3000), (2, 131072, 4096)])
 @pytest.mark.parametrize("dist", ["normal", "ties"])
 def test_hier_pool_bitexact(rows, n_pos, n_sel, dist):
     s = W.random_scores(n_pos + n_sel, rows, n_pos, dist)
