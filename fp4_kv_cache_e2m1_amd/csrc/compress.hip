@@ -17,12 +17,12 @@
 // flattened (sequence, entry) list and key channels [256 y, 256 y + 256), NE the smallest that
 // keeps the grid to one workgroup per CU (the call is a chain of memory round trips, so spreading
 // it over the CUs shortens it: 1024 entries 24.2 -> 15.0 us, 2048 entries 25.1 -> 18.6 us). A
-// wave compresses NE / 8 of the entries with a lane holding 8 consecutive channels; the 16-byte loads of every token of its
-// entries are issued together (two rounds for 8 tokens per entry). The 8 channels are half of a
-// 16-channel scale group, so the group maximum needs one lane exchange, and the lane's eight
-// 4-bit codes are one 32-bit word of the packed row (written by the y = 0 workgroups only). The
-// bf16 entries meet in LDS as the A operand of the projection; wave w then computes the 32 key
-// channels 256 y + 32 w .. for the 32 entries, its 32 weight fragments (one 32 x 512 slice of the
+// wave compresses NE / 8 of the entries with a lane holding 8 consecutive channels; the 16-byte
+// loads of every token of its entries are issued together (two rounds for 8 tokens per entry).
+// The 8 channels are half of a 16-channel scale group, so the group maximum needs one lane
+// exchange, and the lane's eight 4-bit codes are one 32-bit word of the packed row (written by
+// the y = 0 workgroups only). The bf16 entries meet in LDS as the A operand of the projection
+// (rows past NE unused); wave w then computes the 32 key channels 256 y + 32 w .. for the entries, its 32 weight fragments (one 32 x 512 slice of the
 // weight) all loaded at once, so the whole call costs about two memory round trips when only a
 // few entries are new (decode appends one entry per sequence).
 #include "common.h"

@@ -475,9 +475,11 @@ CSA2_DEV void topk_segment(const TopkArgs& a, int seg_len, int k, TopkSmem<NLIST
       const int bits = min(12, rb), shift = rb - bits, fshift = max(0, bits - 6);
       const uint32_t dm = (1u << bits) - 1u;
       if (quarters) {
+        if constexpr (kQuarters) {
 #pragma unroll
-        for (int j = 0; j < (kQuarters ? 4 : 0); ++j)
-          if (gq[kQuarters ? j : 0] != 0) hist_add<true>(sm.hist[0], (gq[kQuarters ? j : 0] >> shift) & dm, fshift);
+          for (int j = 0; j < 4; ++j)
+            if (gq[j] != 0) hist_add<true>(sm.hist[0], (gq[j] >> shift) & dm, fshift);
+        }
       } else if (halves) {
         if (gh[0] != 0) hist_add<true>(sm.hist[0], (gh[0] >> shift) & dm, fshift);
         if (gh[1] != 0) hist_add<true>(sm.hist[0], (gh[1] >> shift) & dm, fshift);
