@@ -22,9 +22,10 @@
 // The 8 channels are half of a 16-channel scale group, so the group maximum needs one lane
 // exchange, and the lane's eight 4-bit codes are one 32-bit word of the packed row (written by
 // the y = 0 workgroups only). The bf16 entries meet in LDS as the A operand of the projection
-// (rows past NE unused); wave w then computes the 32 key channels 256 y + 32 w .. for the entries, its 32 weight fragments (one 32 x 512 slice of the
-// weight) all loaded at once, so the whole call costs about two memory round trips when only a
-// few entries are new (decode appends one entry per sequence).
+// (rows past NE unused); wave w then computes the 32 key channels 256 y + 32 w .. for the
+// entries, its 32 weight fragments (one 32 x 512 slice of the weight) all loaded at once, so the
+// whole call costs about two memory round trips when only a few entries are new (decode appends
+// one entry per sequence).
 #include "common.h"
 #include "launch.h"
 
