@@ -31,6 +31,7 @@
 // parallelism: each segment's k best (key, position) pairs go to scratch, and the same kernel
 // selects again over those candidates; the global k best always survive their segment.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -45,7 +46,6 @@ constexpr int kSegSingle = 32768;     // few rows: longest row kept in one workg
 constexpr int kHistBins = 4096;       // largest radix digit: 12 bits
 constexpr int kCoarse = 64;           // coarse bins: the top 6 bits of a digit
 constexpr int kCompact = 4 * kTopkThreads;  // pruning survivors packed 4 per lane
-constexpr int kWaveSlots = kCompact / kTopkWaves;
 
 enum TopkSrc { kSrcScores = 0, kSrcMapped = 1, kSrcCand = 2, kSrcGather = 3, kSrcBlocks = 4 };
 enum TopkDst { kDstIdx = 0, kDstExpand = 1, kDstCand = 2 };
@@ -496,19 +496,21 @@ CSA2_DEV void topk_segment(const TopkArgs& a, int seg_len, int k, TopkSmem<NLIST
     for (int i = 0; i < EPL; ++i)
       if (key[i] < L) key[i] = 0;
     // The survivors are usually a few percent of the columns. When they fit, they are packed in
-    // column order into 4 rows per lane, so the passes below touch 4 registers, not EPL.
+    // column order into NLIST / 1024 rows per lane (4; 8 for block selections, whose bound is the
+    // looser one of many small groups), so the passes below touch those registers, not EPL.
     if constexpr (kPack) {
-      // each wave packs its survivors, in column order, into its own kWaveSlots slots; when no
-      // wave overflows, every wave continues from its slots (the slot order keeps column order)
+      constexpr int kSlots = NLIST / kTopkWaves, kRP = kSlots / 64;
+      // each wave packs its survivors, in column order, into its own kSlots slots; when no wave
+      // overflows, every wave continues from its slots (the slot order keeps column order)
       int o = 0;
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
         const bool live = key[i] != 0;
         const uint64_t m = __ballot(live);
         const int j = o + lanes_below(m);
-        if (live && j < kWaveSlots) {
-          sm.list_key[wave * kWaveSlots + j] = key[i];
-          sm.list_pos[wave * kWaveSlots + j] =
+        if (live && j < kSlots) {
+          sm.list_key[wave * kSlots + j] = key[i];
+          sm.list_pos[wave * kSlots + j] =
               (PosT)(SRC != kSrcScores ? pos[i % NP] : (sizeof(PosT) == 4 ? c0 : 0) + wbase + 64 * i + lane);
         }
         o += (int)__popcll(m);
@@ -516,16 +518,28 @@ CSA2_DEV void topk_segment(const TopkArgs& a, int seg_len, int k, TopkSmem<NLIST
       if (lane == 0) sm.wcnt[wave][0] = o;
       __syncthreads();
       const int most = (int)wave_max((uint32_t)(lane < kTopkWaves ? sm.wcnt[lane][0] : 0));
-      if (most <= kWaveSlots) {
-        uint32_t key4[4];
-        int32_t pos4[4];
+      // the passes over the packed list cost in proportion to its registers, so a list that fits
+      // half the slots takes the half-width form
+      auto finish_packed = [&](auto rp) {
+        constexpr int RP = decltype(rp)::value;
+        uint32_t keyp[RP];
+        int32_t posp[RP];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < RP; ++u) {
           const int j = 64 * u + lane;
-          key4[u] = j < o ? sm.list_key[wave * kWaveSlots + j] : 0u;
-          pos4[u] = (int32_t)sm.list_pos[wave * kWaveSlots + j] + (sizeof(PosT) == 4 ? 0 : c0);
+          keyp[u] = j < o ? sm.list_key[wave * kSlots + j] : 0u;
+          posp[u] = (int32_t)sm.list_pos[wave * kSlots + j] + (sizeof(PosT) == 4 ? 0 : c0);
         }
-        topk_finish<SRC, DST, 4, true, false>(a, sm, key4, pos4, 0, k, kk, true, L, kmax, r, seg);
+        topk_finish<SRC, DST, RP, true, false>(a, sm, keyp, posp, 0, k, kk, true, L, kmax, r, seg);
+      };
+      if constexpr (kRP > 4) {
+        if (most <= kSlots / 2) {
+          finish_packed(std::integral_constant<int, kRP / 2>{});
+          return;
+        }
+      }
+      if (most <= kSlots) {
+        finish_packed(std::integral_constant<int, kRP>{});
         return;
       }
       // wcnt is rewritten only after the next barrier, which every wave reaches after reading it
@@ -540,7 +554,8 @@ CSA2_DEV void topk_segment(const TopkArgs& a, int seg_len, int k, TopkSmem<NLIST
 
 template <int SRC, int DST, int EPL>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a, int seg_len, int k) {
-  __shared__ TopkSmem<(EPL > 4 ? kCompact : 1)> sm;
+  // block selections (pool) pack up to 512 survivors per wave
+  __shared__ TopkSmem<(EPL > 4 ? (DST == kDstExpand ? 2 * kCompact : kCompact) : 1)> sm;
   topk_segment<SRC, DST, EPL>(a, seg_len, k, sm, blockIdx.x, blockIdx.y);
 }
 
@@ -561,7 +576,7 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8)
 constexpr int kSelMax = kSegMax / 8;        // pool blocks: up to 40960 positions
 template <int EPL_A, int EPL_B>
 __global__ __launch_bounds__(kTopkThreads) void pool_topk_kernel(TopkArgs pa, TopkArgs pb, int k_blocks, int k) {
-  __shared__ TopkSmem<kCompact> sm;
+  __shared__ TopkSmem<2 * kCompact> sm;   // up to 512 pool-block survivors per wave
   __shared__ int32_t sel[kSelMax];
   pa.sel = sel;
   topk_segment<kSrcScores, kDstExpand, EPL_A>(pa, pa.n_in, k_blocks, sm, blockIdx.x, 0);

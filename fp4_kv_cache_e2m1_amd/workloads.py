@@ -180,7 +180,9 @@ def random_scores(seed: int, rows: int, n: int, dist: str = "normal") -> np.ndar
     """fp32 score rows for stand-alone Top-K tests.
 
     dist: "normal" (distinct values), "ties" (values drawn from 8 levels, many exact ties),
-    "const" (every value equal), "signed_zero" (a mix of +0, -0 and a few normals).
+    "const" (every value equal), "signed_zero" (a mix of +0, -0 and a few normals),
+    "bounded" (the sum of 4 uniforms: a tail that ends, so the maxima of small groups bunch up
+    near the top).
     """
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, rows, n])))
     if dist == "normal":
@@ -194,4 +196,6 @@ def random_scores(seed: int, rows: int, n: int, dist: str = "normal") -> np.ndar
         few = g.random((rows, n)) < 0.01
         x[few] = g.standard_normal(int(few.sum()), dtype=np.float32)
         return x
+    if dist == "bounded":
+        return (g.random((rows, n, 4), dtype=np.float32).sum(-1) - np.float32(2.0)) * np.float32(20.0)
     raise ValueError(dist)

@@ -244,7 +244,7 @@ def test_topk_const_rows_and_pool_columns():
 
 @pytest.mark.parametrize("rows,n_pos,n_sel", [(2, 4003, 64), (4, 262144, 1024), (3, 800, 200), (1, 80, 16),
                                             (2, 262144, 2048), (3, 200000, 3000), (2, 131072, 4096)])
-@pytest.mark.parametrize("dist", ["normal", "ties"])
+@pytest.mark.parametrize("dist", ["normal", "ties", "bounded"])
 def test_hier_pool_bitexact(rows, n_pos, n_sel, dist):
     s = W.random_scores(n_pos + n_sel, rows, n_pos, dist)
     n_vis = np.array([n_pos - 13 * r for r in range(rows)], np.int32)

@@ -55,7 +55,7 @@ def _topk_bruteforce(row, k, pos=None):
     return sel + [-1] * (k - len(sel))
 
 
-@pytest.mark.parametrize("dist", ["normal", "ties", "const", "signed_zero"])
+@pytest.mark.parametrize("dist", ["normal", "ties", "const", "signed_zero", "bounded"])
 def test_topk_bruteforce(dist):
     for n in (1, 5, 17, 64):
         s = W.random_scores(n, 4, n, dist)
