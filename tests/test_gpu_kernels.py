@@ -195,7 +195,7 @@ TOPK_CASES = [(1, 1, 1), (3, 7, 3), (4, 100, 17), (2, 5000, 512), (32, 16384, 51
 
 
 @pytest.mark.parametrize("rows,n,k", TOPK_CASES)
-@pytest.mark.parametrize("dist", ["normal", "ties", "signed_zero"])
+@pytest.mark.parametrize("dist", ["normal", "ties", "signed_zero", "bounded"])
 def test_topk_bitexact(rows, n, k, dist):
     s = W.random_scores(rows * 31 + k, rows, n, dist)
     nv = np.array([n - (r * 37) % max(1, n // 3) for r in range(rows)], np.int32)
@@ -205,7 +205,7 @@ def test_topk_bitexact(rows, n, k, dist):
 
 
 @pytest.mark.parametrize("n", [7000, 10000, 19000, 27000, 33792, 35000, 40960])
-@pytest.mark.parametrize("dist", ["normal", "ties", "const", "signed_zero"])
+@pytest.mark.parametrize("dist", ["normal", "ties", "const", "signed_zero", "bounded"])
 def test_topk_whole_rows_bitexact(n, dist):
     """Many rows (one workgroup per whole row, as in prefill) at row lengths that take each register
     count of that form (8, 12, 20, 28, 33, 36, 40 columns per lane), with ragged valid counts. Tied,
