@@ -1263,17 +1263,30 @@ __global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
     mlb[2 * (16 * w + l16) + 1] = l_run;
   }
   __syncthreads();
+  // The output leaves one head tile at a time through the wave's own part of X (free now): the
+  // accumulator layout gives a lane 16 bytes of one head per store, so a direct store writes 16
+  // pieces of 64 bytes; staged, each store writes two heads' 512 contiguous bytes. Rows of the
+  // stage are 132 words apart so the 16 heads' writes fall in different banks.
+  constexpr int kStRow = 132;
+  static_assert(4 * 16 * kStRow * 4 <= KC * XP * 2, "the output stage fits in X");
+  float* stage = reinterpret_cast<float*>(xs) + w * 16 * kStRow;
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht) {
     const int hh = 16 * ht + l16;
     const float L = mlb[2 * hh + 1];
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    float* dst = out + ((int64_t)qr * H + hbase + hh) * kD + 128 * w + 4 * g;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const f32x4_t o = acc[ht][j] * inv;
-      *reinterpret_cast<float4*>(dst + 16 * j) = make_float4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<float4*>(stage + l16 * kStRow + 16 * j + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
     }
+    __builtin_amdgcn_wave_barrier();
+    float* dst = out + ((int64_t)qr * H + hbase + 16 * ht + (lane >> 5)) * kD + 128 * w + 4 * (lane & 31);
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2)
+      *reinterpret_cast<float4*>(dst + 2 * s2 * kD) =
+          *reinterpret_cast<const float4*>(stage + (2 * s2 + (lane >> 5)) * kStRow + 4 * (lane & 31));
+    __builtin_amdgcn_wave_barrier();
   }
   if (lse && g == 0) {
     const float L = l_run;
