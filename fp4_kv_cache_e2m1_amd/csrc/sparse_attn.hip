@@ -1294,7 +1294,8 @@ __global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
   }
 }
 
-// Merge of split results: one wave per (query row, head), lane owns 8 channels. The first 8
+// Merge of split results: one wave per (query row, head); a lane owns channels 4 lane .. +3 and
+// 256 + 4 lane .. +3, so every load and store of the wave covers 1 KB contiguous. The first 8
 // splits' partial rows are loaded together with all splits' (max, sum) pairs, so the common case
 // waits on memory once. Workgroups are placed on the XCD whose L2 holds the partials: the
 // attention kernels give each XCD a contiguous range of query rows, and so does this mapping.
@@ -1337,9 +1338,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
 #pragma unroll
   for (int sp = 0; sp < 8; ++sp) {
     if (sp < n_splits) {
-      const float4* pp = reinterpret_cast<const float4*>(part_o + (sp * n_rows_h + rh) * kD) + 2 * lane;
+      const float4* pp = reinterpret_cast<const float4*>(part_o + (sp * n_rows_h + rh) * kD) + lane;
       a[sp] = pp[0];
-      c[sp] = pp[1];
+      c[sp] = pp[64];
     }
   }
   // lane s < n_splits holds split s's (m, l)
@@ -1368,13 +1369,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   for (int sp = 0; sp < 8; ++sp)
     if (sp < n_splits) add(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), sp)), a[sp], c[sp]);
   for (int sp = 8; sp < n_splits; ++sp) {
-    const float4* pp = reinterpret_cast<const float4*>(part_o + (sp * n_rows_h + rh) * kD) + 2 * lane;
-    add(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), sp)), pp[0], pp[1]);
+    const float4* pp = reinterpret_cast<const float4*>(part_o + (sp * n_rows_h + rh) * kD) + lane;
+    add(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), sp)), pp[0], pp[64]);
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  float4* op = reinterpret_cast<float4*>(out + rh * kD) + 2 * lane;
+  float4* op = reinterpret_cast<float4*>(out + rh * kD) + lane;
   op[0] = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
-  op[1] = make_float4(o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
+  op[64] = make_float4(o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
   if (lse && lane == 0) lse[rh] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
