@@ -958,8 +958,8 @@ __global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
     const int8_t* __restrict__ swa_exp, const int32_t* __restrict__ n_win, int W) {
   constexpr int KC = kPKC, NS = KC / 16;
   __shared__ __attribute__((aligned(16))) uint16_t xs[KC * XP];     // X[entry][channel], f16
-  // partial S, component-major ([wave][t][ht][i][lane]) so every 4-byte access is lane-contiguous
-  __shared__ __attribute__((aligned(16))) float spf[4 * NS * 4 * 4 * 64];
+  // partial S, [wave][t][ht][lane] of 4 components: one 16-byte access per lane, lane-contiguous
+  __shared__ __attribute__((aligned(16))) f32x4_t spf[4 * NS * 4 * 64];
   __shared__ __attribute__((aligned(16))) f16x4_t pbuf[4 * NS * 64];     // P: [ht][s][lane]
   __shared__ __attribute__((aligned(16))) float abuf[64];                // rescale factors: [l16][head tile]
   __shared__ float amx[4 * 64];                                          // per-wave |q| max per head
@@ -1093,11 +1093,7 @@ __global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
           for (int h2 = 0; h2 < 2; ++h2)
             sv[h2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[kk], qb[hp + h2][kk], sv[h2], 0, 0, 0);
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          float* dst = spf + ((w * NS + t) * 4 + hp + h2) * 256 + lane;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dst[64 * i] = sv[h2][i];
-        }
+        for (int h2 = 0; h2 < 2; ++h2) spf[((w * NS + t) * 4 + hp + h2) * 64 + lane] = sv[h2];
       }
     }
     __syncthreads();
@@ -1108,12 +1104,12 @@ __global__ __launch_bounds__(256, OCC) void sparse_attn_prefill_kernel(
       // all partials are read first and masked entries get -inf added (not selected), so no read
       // is moved into a branch
 #pragma unroll
-      for (int t = 0; t < NS; ++t)
+      for (int t = 0; t < NS; ++t) {
+        const f32x4_t* src = spf + (t * 4 + w) * 64 + lane;
+        const f32x4_t sum = src[0] + src[NS * 4 * 64] + src[2 * NS * 4 * 64] + src[3 * NS * 4 * 64];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float* src = spf + (t * 4 + w) * 256 + 64 * i + lane;
-          tv[t][i] = src[0] + src[NS * 4 * 256] + src[2 * NS * 4 * 256] + src[3 * NS * 4 * 256];
-        }
+        for (int i = 0; i < 4; ++i) tv[t][i] = sum[i];
+      }
 #pragma unroll
       for (int t = 0; t < NS; ++t) {
         const uint32_t vb = (uint32_t)(vmask >> (16 * t + 4 * g)) & 15u;
