@@ -496,8 +496,9 @@ CSA2_DEV void topk_segment(const TopkArgs& a, int seg_len, int k, TopkSmem<NLIST
     for (int i = 0; i < EPL; ++i)
       if (key[i] < L) key[i] = 0;
     // The survivors are usually a few percent of the columns. When they fit, they are packed in
-    // column order into NLIST / 1024 rows per lane (4; 8 for block selections, whose bound is the
-    // looser one of many small groups), so the passes below touch those registers, not EPL.
+    // column order into at most NLIST / 1024 rows per lane (4; block selections, whose bound is
+    // the looser one of many small groups, have room for 8 and use 4 when every wave's
+    // survivors fit 256 slots), so the passes below touch those registers, not EPL.
     if constexpr (kPack) {
       constexpr int kSlots = NLIST / kTopkWaves, kRP = kSlots / 64;
       // each wave packs its survivors, in column order, into its own kSlots slots; when no wave
