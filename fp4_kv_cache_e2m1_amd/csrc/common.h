@@ -64,16 +64,15 @@ CSA2_DEV uint32_t e4m3_scale_code(float amax) {
 // to the even code, via exact compares against s * {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5}.
 // Thresholds between an odd code and the next even code count ">=" (a tie goes up to the even
 // code); the others count ">" (a tie stays on the even code).
+// The seven predicates are monotone (the thresholds strictly increase for s >= 2^-9, and every
+// product is exact), so the code is the number of them that hold, found by a three-step binary
+// search: 1.75 s first, then 0.75 s or 3.5 s, then one of the ">" thresholds.
 CSA2_DEV uint32_t e2m1_mag_code(float ax, float s) {
-  uint32_t j = 0;
-  j += ax > 0.25f * s;
-  j += ax >= 0.75f * s;
-  j += ax > 1.25f * s;
-  j += ax >= 1.75f * s;
-  j += ax > 2.5f * s;
-  j += ax >= 3.5f * s;
-  j += ax > 5.0f * s;
-  return j;
+  const bool hi = ax >= 1.75f * s;
+  const bool b2 = ax >= (hi ? 3.5f : 0.75f) * s;
+  const float t3 = hi ? (b2 ? 5.0f : 2.5f) : (b2 ? 1.25f : 0.25f);
+  const bool b3 = ax > t3 * s;
+  return (hi ? 4u : 0u) + (b2 ? 2u : 0u) + (b3 ? 1u : 0u);
 }
 
 // Twice the E2M1 magnitude of codes 0..7 is {0,1,2,3,4,6,8,12}: bytes of two words, looked up
