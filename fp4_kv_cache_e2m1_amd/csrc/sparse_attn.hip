@@ -612,13 +612,26 @@ __global__ __launch_bounds__(256 * NG) void sparse_attn_decode_kernel(
 
   // every wave holds the same (M, L) and disjoint channels: write directly (final_out: the only
   // split, normalized; else an unnormalized partial of split `split` for the combine pass)
+  // The 16 heads' rows leave through LDS past the merge tiles: a lane holds 16 bytes of one head
+  // per store in the accumulator layout, staged each store writes two heads' 512 contiguous bytes
   const int64_t orow = (int64_t)qr * H + head;
   const float scale = final_out ? (L > 0.0f ? 1.0f / L : 0.0f) : 1.0f;
-  float* dst = final_out ? out + orow * kD : part_o + ((int64_t)split * n_rows * H + orow) * kD;
+  {
+    constexpr int kStRow = 132;
+    static_assert((NG - 1) * Sm::kOut + 4 * 16 * kStRow * 4 <= NG * Sm::kGroup, "the output stage fits");
+    if constexpr (NG == 1) __syncthreads();   // the stage overlaps the other waves' X slabs
+    float* stage = reinterpret_cast<float*>(smem + (NG - 1) * Sm::kOut) + w4 * 16 * kStRow;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const f32x4_t v = acc[j] * scale;
-    *reinterpret_cast<float4*>(dst + 128 * w4 + 16 * j + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<f32x4_t*>(stage + l16 * kStRow + 16 * j + 4 * g) = acc[j] * scale;
+    __builtin_amdgcn_wave_barrier();
+    const int64_t row0 = (int64_t)qr * H + hg * 16;
+    float* dst = (final_out ? out + row0 * kD : part_o + ((int64_t)split * n_rows * H + row0) * kD) +
+                 (lane >> 5) * kD + 128 * w4 + 4 * (lane & 31);
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2)
+      *reinterpret_cast<float4*>(dst + 2 * s2 * kD) =
+          *reinterpret_cast<const float4*>(stage + (2 * s2 + (lane >> 5)) * kStRow + 4 * (lane & 31));
   }
   if (w4 == 0 && g == 0) {
     if (final_out) {
