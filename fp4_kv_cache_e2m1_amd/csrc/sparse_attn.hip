@@ -929,12 +929,23 @@ __global__ __launch_bounds__(256 * NG) void swa_attn_kernel(
     }
   }
 
-  // the workgroup's partial: unnormalized output and (max, sum) in the exp2 domain
+  // the workgroup's partial: unnormalized output and (max, sum) in the exp2 domain; the 16 heads'
+  // rows leave through LDS as in the decode form (two heads' 512 contiguous bytes per store)
   const int64_t prow = (int64_t)(slot0 + wsplit) * n_rows * H + (int64_t)qr * H + head;
-  float* dst = part_o + prow * kD;
+  {
+    constexpr int kStRow = 132;
+    static_assert((NG - 1) * Sm::kOut + 4 * 16 * kStRow * 4 <= NG * Sm::kGroup, "the output stage fits");
+    if constexpr (NG == 1) __syncthreads();   // the stage overlaps the other waves' X slabs
+    float* stage = reinterpret_cast<float*>(smem + (NG - 1) * Sm::kOut) + w4 * 16 * kStRow;
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    *reinterpret_cast<float4*>(dst + 128 * w4 + 16 * j + 4 * g) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+    for (int j = 0; j < 8; ++j) *reinterpret_cast<f32x4_t*>(stage + l16 * kStRow + 16 * j + 4 * g) = acc[j];
+    __builtin_amdgcn_wave_barrier();
+    float* dst = part_o + (prow - l16 + (lane >> 5)) * kD + 128 * w4 + 4 * (lane & 31);
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2)
+      *reinterpret_cast<float4*>(dst + 2 * s2 * kD) =
+          *reinterpret_cast<const float4*>(stage + (2 * s2 + (lane >> 5)) * kStRow + 4 * (lane & 31));
+  }
   if (w4 == 0 && g == 0) {
     part_ml[2 * prow] = M;
     part_ml[2 * prow + 1] = L;
